@@ -1,0 +1,278 @@
+"""Pins of the CPU fp64 oracle against facts fixed outside it.
+
+Each test checks the oracle against something the oracle does not compute itself:
+hand-placed galaxies with closed-form angles, exact integer arithmetic on the
+equator, the exact totals N_a * N_b, the closed-form pair-separation distribution
+of a uniform sphere, a numpy library evaluation of the dot-product form, and
+hand-computed Landy-Szalay values.  Definitions: "CUDA Deep Dive: 10B Galaxy Pairs
+on an RTX 5080", section "The problem" (angle, bins, estimator, sums of N^2) and
+section "L1: DD/RR symmetry" (the symmetric weights).
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import oracle
+from two_point_angular_amd import catalogs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_five():
+    gal, pairs = [], []
+    with open(os.path.join(GOLDEN, "five_galaxies.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if not line:
+                continue
+            parts = line.split()
+            if parts[0].startswith("G"):
+                gal.append((float(parts[1]), float(parts[2])))
+            else:
+                pairs.append((int(parts[0]), int(parts[1]), float(parts[2]), int(parts[3])))
+    return np.array(gal, dtype=np.float32), pairs
+
+
+def _closed_form_deg(g, i, j):
+    """Equator, meridian and right-spherical-triangle closed forms (no law of cosines)."""
+    g = np.asarray(g, dtype=np.float64)
+    (ai, di), (aj, dj) = g[i] / 60.0, g[j] / 60.0
+    if di == 0 and dj == 0:
+        d = abs(ai - aj) % 360.0
+        return min(d, 360.0 - d)
+    if ai == aj:
+        return abs(di - dj)
+    # one on the equator at G0's meridian offset, the other on G0's meridian
+    eq, pole = (i, j) if di == 0 else (j, i)
+    dalpha = math.radians(abs(g[eq][0] - g[pole][0]) / 60.0)
+    b = math.radians(abs(g[pole][1]) / 60.0)
+    return math.degrees(math.acos(math.cos(dalpha) * math.cos(b)))
+
+
+def test_five_galaxies_fixture_is_closed_form():
+    g, pairs = _read_five()
+    for i, j, theta, b in pairs:
+        assert abs(_closed_form_deg(g, i, j) - theta) < 5e-7
+        assert b == math.floor(theta / 0.25)
+        # every fixture angle is well away from a bin edge
+        assert min(theta % 0.25, 0.25 - theta % 0.25) >= 0.0499
+
+
+def test_five_galaxies_oracle_angles_and_histogram():
+    g, pairs = _read_five()
+    for i, j, theta, b in pairs:
+        exact = _closed_form_deg(g, i, j)
+        assert abs(oracle.pair_angle_deg(g[i, 0], g[i, 1], g[j, 0], g[j, 1]) - exact) < 1e-9
+        assert abs(oracle.pair_angle_deg(g[j, 0], g[j, 1], g[i, 0], g[i, 1]) - exact) < 1e-9
+    expected = np.zeros(720, dtype=np.uint64)
+    expected[0] = 5
+    for _, _, _, b in pairs:
+        expected[b] += 2
+    for sym in (False, True):
+        fam = oracle.family_rows(g[:, 0], g[:, 1], g[:, 0], g[:, 1], 720, 0.25, symmetric=sym)
+        np.testing.assert_array_equal(fam.hist, expected)
+    res = oracle.histograms(g[:, 0], g[:, 1], g[:, 0], g[:, 1], 720, 0.25)
+    for name in oracle.FAMILIES:
+        np.testing.assert_array_equal(res.family(name).hist, expected)
+
+
+def _equator_catalog(residues, rng, unit, modulus):
+    """alpha = (modulus * m + r) * unit arcmin on the equator; exact in fp32."""
+    m = rng.integers(0, (21600 * 64) // modulus, len(residues))
+    k = m * modulus + np.asarray(residues)
+    ra = (k * unit).astype(np.float32)
+    assert np.all(ra.astype(np.float64) == k * unit)
+    return ra, np.zeros(len(k), dtype=np.float32), k
+
+
+def _equator_expected(ka, kb, edge_num, edge_den, nbins):
+    """Exact bins from integer arithmetic: theta = min(|dk|, FULL - |dk|) in 1/64 arcmin;
+    bin = floor(theta * edge_den / edge_num) clamped, where one bin is edge_num/edge_den units."""
+    full = 21600 * 64
+    d = np.abs(ka[:, None] - kb[None, :])
+    theta = np.minimum(d, full - d)
+    b = (theta * edge_den) // edge_num
+    return np.minimum(b, nbins - 1).ravel()
+
+
+@pytest.mark.parametrize("nbins,w_deg,edge_num,edge_den,modulus,n", [
+    (720, 0.25, 960, 1, 960, 300),     # 0.25 deg = 15' = 960 units of 1/64'
+    (3600, 0.05, 192, 1, 192, 90),     # 0.05 deg = 3' = 192 units
+    (1500, 0.001, 384, 100, 96, 45),   # 0.001 deg = 0.06' = 3.84 units; overflow bin
+])
+def test_equator_exact_integer_bins(nbins, w_deg, edge_num, edge_den, modulus, n):
+    """Galaxies on the equator are |delta alpha| apart (mod 360 deg).  With alpha on a
+    1/64-arcmin grid and residues chosen so no pair sits on an edge, the bin of every pair
+    is an exact integer computation."""
+    rng = np.random.default_rng(7 + nbins)
+    res = rng.permutation(modulus)[: 2 * n]
+    ra_d, dec_d, kd = _equator_catalog(res[:n], rng, 1.0 / 64.0, modulus)
+    ra_r, dec_r, kr = _equator_catalog(res[n:], rng, 1.0 / 64.0, modulus)
+    for (ra_a, dec_a, ka), (ra_b, dec_b, kb) in [((ra_d, dec_d, kd), (ra_d, dec_d, kd)),
+                                                ((ra_d, dec_d, kd), (ra_r, dec_r, kr))]:
+        want = np.bincount(_equator_expected(ka, kb, edge_num, edge_den, nbins), minlength=nbins)
+        bins = oracle.pair_bins(ra_a, dec_a, ra_b, dec_b, nbins, w_deg)
+        np.testing.assert_array_equal(bins.ravel(), _equator_expected(ka, kb, edge_num, edge_den, nbins))
+        sym = ra_a is ra_b
+        fam = oracle.family_rows(ra_a, dec_a, ra_b, dec_b, nbins, w_deg, symmetric=sym)
+        np.testing.assert_array_equal(fam.hist, want.astype(np.uint64))
+
+
+def test_equator_near_edge_counters():
+    """Pairs placed within / outside 1e-5 deg of an edge are counted / not counted."""
+    u = 2.0 ** -12  # arcmin; 2^-12' = 4.07e-6 deg
+    base = 1000.0
+    ra = np.array([base, base + 15.0 + u, base + 30.0 - u, base + 45.0 + 4 * u, base + 60.0 - 4 * u],
+                  dtype=np.float32)
+    # distances from galaxy 0: 0.25 deg + 4.07e-6 (bin 1, just above edge 1), 0.5 deg - 4.07e-6
+    # (bin 1, just below edge 2), 0.75 deg + 1.6e-5 and 1.0 deg - 1.6e-5 (bin 3, both outside
+    # the 1e-5 deg window of edges 3 and 4).
+    dec = np.zeros_like(ra)
+    assert float(ra[1]) - base == 15.0 + u
+    fam = oracle.family_rows(ra[:1], dec[:1], ra, dec, 720, 0.25)
+    assert list(np.nonzero(fam.hist)[0]) == [0, 1, 3]
+    assert fam.hist[0] == 1 and fam.hist[1] == 2 and fam.hist[3] == 2
+    assert fam.hi[1] == 1 and fam.lo[2] == 1
+    assert int(fam.lo.sum()) == 1 and int(fam.hi.sum()) == 1
+
+
+@pytest.mark.parametrize("n_d,n_r", [(0, 5), (5, 0), (1, 1), (37, 53), (200, 200)])
+def test_totals_are_exact(n_d, n_r):
+    D = catalogs.clustered(max(n_d, 1), 3).subset(0, n_d)
+    R = catalogs.uniform_sphere(max(n_r, 1), 4).subset(0, n_r)
+    res = oracle.histograms(D.ra, D.dec, R.ra, R.dec, 720, 0.25)
+    assert int(res.dd.hist.sum()) == n_d * n_d
+    assert int(res.dr.hist.sum()) == n_d * n_r
+    assert int(res.rr.hist.sum()) == n_r * n_r
+    if n_d:
+        assert int(res.dd.hist[0]) >= n_d
+
+
+def test_symmetric_mode_equals_full_mode_bitwise():
+    D, R = catalogs.WORKLOADS["clustered100k_720"].catalogs(n=1500)
+    for nbins, w in ((720, 0.25), (3600, 0.05)):
+        a = oracle.histograms(D.ra, D.dec, R.ra, R.dec, nbins, w, symmetric=True)
+        b = oracle.histograms(D.ra, D.dec, R.ra, R.dec, nbins, w, symmetric=False)
+        for f in oracle.FAMILIES:
+            np.testing.assert_array_equal(a.family(f).hist, b.family(f).hist)
+            np.testing.assert_array_equal(a.family(f).lo, b.family(f).lo)
+            np.testing.assert_array_equal(a.family(f).hi, b.family(f).hi)
+    # DR of a catalog against itself is its DD
+    dd = oracle.family_rows(D.ra, D.dec, D.ra, D.dec, 720, 0.25, symmetric=True)
+    dr = oracle.family_rows(D.ra, D.dec, D.ra, D.dec, 720, 0.25, symmetric=False)
+    np.testing.assert_array_equal(dd.hist, dr.hist)
+
+
+def test_per_pair_literal_form_equals_histogram_loop():
+    """gco_pair_bins evaluates the law-of-cosines line per pair; the histogram loop hoists
+    sin/cos of each declination.  Both must produce identical histograms."""
+    D, R = catalogs.WORKLOADS["clustered100k_720"].catalogs(n=400)
+    bins = oracle.pair_bins(D.ra, D.dec, R.ra, R.dec, 720, 0.25)
+    fam = oracle.family_rows(D.ra, D.dec, R.ra, R.dec, 720, 0.25)
+    np.testing.assert_array_equal(np.bincount(bins.ravel(), minlength=720).astype(np.uint64), fam.hist)
+
+
+def _unit_vectors_np(cat):
+    a = cat.ra.astype(np.float64) * (np.pi / 10800.0)
+    d = cat.dec.astype(np.float64) * (np.pi / 10800.0)
+    return np.stack([np.cos(d) * np.cos(a), np.cos(d) * np.sin(a), np.sin(d)], axis=1)
+
+
+@pytest.mark.parametrize("kind,nbins,w", [("clustered", 720, 0.25), ("clustered", 3600, 0.05),
+                                           ("patch", 1500, 0.001)])
+def test_numpy_dot_product_form_agrees(kind, nbins, w):
+    """The dot-product form (numpy matmul + arccos + floor) gives the same bin for every pair
+    except pairs within 1e-9 deg of an edge, where both are within rounding."""
+    wl = {"clustered": catalogs.WORKLOADS["clustered100k_720"],
+          "patch": catalogs.WORKLOADS["patch100k_1500"]}[kind]
+    D, R = wl.catalogs(n=1200)
+    for A, B in ((D, R), (D, D)):
+        c = np.clip(_unit_vectors_np(A) @ _unit_vectors_np(B).T, -1.0, 1.0)
+        theta = np.degrees(np.arccos(c))
+        nb = np.minimum(np.floor(theta / w), nbins - 1).astype(np.int64)
+        ob = oracle.pair_bins(A.ra, A.dec, B.ra, B.dec, nbins, w)
+        diff = nb != ob
+        if diff.any():
+            t = theta[diff]
+            dist = np.abs(t / w - np.round(t / w)) * w
+            assert np.all(dist < 1e-9), (int(diff.sum()), float(dist.max()))
+        assert diff.sum() <= 2
+
+
+def test_uniform_sphere_pair_distribution_chi2():
+    """For points uniform on the sphere, P(theta in [t0, t1)) = (cos t0 - cos t1)/2.
+    By isotropy the pair counts are degenerate U-statistics, so an ordered-pair bin count
+    of DR has variance ~E and of RR (off-diagonal, each pair counted twice) ~2E."""
+    wl = catalogs.WORKLOADS["uniform10k_720"]
+    D, R = wl.catalogs()
+    n = len(D)
+    res = oracle.histograms(D.ra, D.dec, R.ra, R.dec, 720, 0.25)
+    edges = np.radians(np.arange(721) * 0.25)
+    p = (np.cos(edges[:-1]) - np.cos(edges[1:])) / 2.0
+    assert abs(p.sum() - 1.0) < 1e-12
+    dof = 719
+    limit = dof + 6.0 * math.sqrt(2 * dof)
+    e_dr = n * n * p
+    chi_dr = float(np.sum((res.dr.hist.astype(np.float64) - e_dr) ** 2 / e_dr))
+    assert chi_dr < limit, chi_dr
+    for fam in (res.dd, res.rr):
+        off = fam.hist.astype(np.float64)
+        off[0] -= n
+        e = n * (n - 1) * p
+        chi = float(np.sum((off - e) ** 2 / (2 * e)))
+        assert chi < limit, chi
+    # a plausible slip (declination drawn uniformly instead of uniform on the sphere) fails;
+    # with one side still isotropic DR would not see it, so plant it on both sides of RR
+    rng = np.random.default_rng(0)
+    bad_dec = ((rng.random(n) * 2 - 1) * 5400).astype(np.float32)
+    bad = oracle.family_rows(R.ra, bad_dec, R.ra, bad_dec, 720, 0.25, symmetric=True)
+    off = bad.hist.astype(np.float64)
+    off[0] -= n
+    chi_bad = float(np.sum((off - n * (n - 1) * p) ** 2 / (2 * n * (n - 1) * p)))
+    assert chi_bad > 10 * limit, chi_bad
+
+
+def test_coincident_points_land_in_bin_zero():
+    D = catalogs.clustered(50, 11)
+    R = catalogs.Catalog(D.ra.copy(), D.dec.copy(), "R")
+    fam = oracle.family_rows(D.ra, D.dec, R.ra, R.dec, 1500, 0.001)
+    assert int(fam.hist[0]) >= 50
+
+
+def test_omega_closed_form():
+    dd = np.array([40, 10, 0, 7], dtype=np.uint64)
+    dr = np.array([30, 12, 3, 7], dtype=np.uint64)
+    rr = np.array([20, 16, 0, 7], dtype=np.uint64)
+    om = oracle.omega(dd, dr, rr, 10, 10)
+    assert om[0] == (40 - 60 + 20) / 20 == 0.0
+    assert om[1] == (10 - 24 + 16) / 16 == 0.125
+    assert math.isnan(om[2])
+    assert om[3] == 0.0
+    # unequal sizes: the normalised estimator; n_d = 2, n_r = 4
+    om2 = oracle.omega(np.array([8], np.uint64), np.array([12], np.uint64), np.array([32], np.uint64), 2, 4)
+    # DD/4 - 2*DR/8 + RR/16 = 2 - 3 + 2 = 1 over RR/16 = 2 -> 0.5
+    assert om2[0] == 0.5
+
+
+def test_flow_check_rules():
+    """The comparison rule itself: a count moved across an edge with no near-edge pairs is
+    rejected, one moved across an edge with enough near-edge pairs is accepted, and a
+    changed total is rejected."""
+    hist = np.array([10, 10, 10, 10], dtype=np.uint64)
+    lo = np.array([0, 0, 2, 0], dtype=np.uint64)
+    hi = np.array([0, 0, 1, 0], dtype=np.uint64)
+    fam = oracle.FamilyResult(hist, lo, hi)
+    assert oracle.flow_check(hist, fam, 40, moved_budget=1.0).ok
+    up = hist.copy(); up[1] -= 2; up[2] += 2   # two pairs moved up across edge 2: <= lo[2]
+    assert oracle.flow_check(up, fam, 40, moved_budget=1.0).ok
+    up3 = hist.copy(); up3[1] -= 3; up3[2] += 3
+    assert not oracle.flow_check(up3, fam, 40, moved_budget=1.0).ok
+    down = hist.copy(); down[2] -= 1; down[1] += 1  # one pair moved down across edge 2: <= hi[2]
+    assert oracle.flow_check(down, fam, 40, moved_budget=1.0).ok
+    far = hist.copy(); far[0] -= 1; far[1] += 1     # edge 1 has no near-edge pairs
+    assert not oracle.flow_check(far, fam, 40, moved_budget=1.0).ok
+    tot = hist.copy(); tot[3] += 1
+    assert not oracle.flow_check(tot, fam, 40, moved_budget=1.0).ok
+    assert not oracle.flow_check(up, fam, 40, moved_budget=1e-6).ok
