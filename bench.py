@@ -1,0 +1,158 @@
+"""Benchmark: all-pairs angular-separation histograms (DD + DR + RR) on one MI355X.
+
+Workload (default): 100,000 clustered D galaxies + 100,000 uniform R galaxies (fp32
+arcmin, seeds 1 and 2), 720 bins of 0.25 deg -- the shape of the 100k + 100k problem of
+"CUDA Deep Dive: 10B Galaxy Pairs on an RTX 5080", section "The problem", on synthetic
+catalogs.  One step = the whole path on device-resident inputs: prepare D and R (unit
+vectors), the pair kernel + merge (DD, DR, RR), the totals reduction and omega.
+
+Prints one JSON line.  value = ordered pairs per second (N_D^2 + N_D N_R + N_R^2 per step).
+roofline: the pair kernel's algorithmic FP32 work (25 flops per evaluated pair, where the
+symmetric families evaluate N(N+1)/2 pairs) over its event-timed duration, against the
+MI355X FP32 vector peak.  cpu_baseline: the fp64 oracle on a bounded sample of the same
+workload (rows of D against all of R), on the host's cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+FLOPS_PER_PAIR = 25.0          # algorithmic FP32 flops per evaluated pair (FMA = 2)
+FP32_PEAK_TFLOPS = 157.3       # MI355X FP32 vector peak (published)
+
+
+def cpu_baseline(D, R, nbins, w, target_s=12.0):
+    import numpy as np
+    from oracle import oracle
+
+    threads = oracle.max_threads()
+    rows = 200
+    t0 = time.perf_counter()
+    oracle.family_rows(D.ra, D.dec, R.ra, R.dec, nbins, w, row0=0, row1=rows)
+    dt = time.perf_counter() - t0
+    rows2 = int(min(len(D), max(rows, rows * target_s / max(dt, 1e-3))))
+    t0 = time.perf_counter()
+    fam = oracle.family_rows(D.ra, D.dec, R.ra, R.dec, nbins, w, row0=0, row1=rows2)
+    dt2 = time.perf_counter() - t0
+    pairs = rows2 * len(R)
+    assert int(fam.hist.sum()) == pairs
+    return {"value": pairs / dt2, "unit": "pairs/s", "cores": threads, "kind": "oracle",
+            "sample": f"DR rows D[0:{rows2}] x R[0:{len(R)}] ({pairs:.3e} ordered pairs, fp64, "
+                      f"{dt2:.1f} s on {threads} threads)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="clustered100k_720")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--dot", type=int, default=0, help="tuning: dot-product precision (0 auto, 32, 64)")
+    ap.add_argument("--k", type=int, default=0, help="tuning: i galaxies per lane (0 auto, 4, 8)")
+    ap.add_argument("--blocks-per-cu", type=int, default=0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: the histogram path has no multi-GPU mode "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import two_point_angular_amd as gc
+    from two_point_angular_amd import catalogs
+
+    wl = catalogs.WORKLOADS[args.workload]
+    D, R = wl.catalogs()
+    n_d, n_r, nbins, w = len(D), len(R), wl.nbins, wl.bin_width_deg
+    dev = torch.device("cuda:0")
+    gc.load()
+    ra_d, dec_d = torch.from_numpy(D.ra).to(dev), torch.from_numpy(D.dec).to(dev)
+    ra_r, dec_r = torch.from_numpy(R.ra).to(dev), torch.from_numpy(R.dec).to(dev)
+    pd = torch.empty(gc.prepared_bytes(n_d), dtype=torch.uint8, device=dev)
+    pr = torch.empty(gc.prepared_bytes(n_r), dtype=torch.uint8, device=dev)
+    out = torch.empty((3, nbins), dtype=torch.int64, device=dev)
+    ws = torch.empty(gc.workspace_bytes(nbins), dtype=torch.uint8, device=dev)
+    om = torch.empty(nbins, dtype=torch.float64, device=dev)
+    totals = torch.empty((args.steps + args.warmup, 3), dtype=torch.int64, device=dev)
+    tuning = None
+    if args.dot or args.k or args.blocks_per_cu:
+        tuning = gc.Tuning(dot_precision=args.dot, i_per_lane=args.k, blocks_per_cu=args.blocks_per_cu)
+
+    def step(idx, ev=None):
+        gc.prepare(ra_d, dec_d, out=pd)
+        gc.prepare(ra_r, dec_r, out=pr)
+        if ev is not None:
+            ev[0].record()
+        dd, dr, rr = gc.histogram_dd_dr_rr(pd, n_d, pr, n_r, nbins, w, out=out, workspace=ws, tuning=tuning)
+        if ev is not None:
+            ev[1].record()
+        gc.histogram_totals(dd, dr, rr, out=totals[idx])
+        gc.omega(dd, dr, rr, n_d, n_r, out=om)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    tot = totals.cpu().numpy().view(np.uint64)
+    want = np.array([n_d * n_d, n_d * n_r, n_r * n_r], dtype=np.uint64)
+    if not np.all(tot == want[None, :]):
+        print(f"totals mismatch: {tot[:3]} vs {want}", file=sys.stderr)
+        sys.exit(1)
+    kern_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    ms_per_step = elapsed * 1e3 / args.steps
+    ordered = float(n_d * n_d + n_d * n_r + n_r * n_r)
+    evaluated = float(n_d * n_r + n_d * (n_d + 1) // 2 + n_r * (n_r + 1) // 2)
+    kernel_s = float(np.mean(kern_ms)) / 1e3
+    achieved = evaluated * FLOPS_PER_PAIR / kernel_s / 1e12
+
+    line = {
+        "metric": "galaxy pairs/sec (DD+DR+RR, 100k×100k, 720 bins); % FP32 VALU peak",
+        "value": ordered / (ms_per_step / 1e3),
+        "unit": "pairs/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "n_d": n_d, "n_r": n_r, "nbins": nbins, "bin_width_deg": w,
+                   "catalogs": f"D {wl.kind} seed 1, R uniform seed 2" if wl.kind == "clustered" else
+                   f"D {wl.kind} seed 1, R {wl.kind} seed 2",
+                   "ordered_pairs_per_step": ordered, "evaluated_pairs_per_step": evaluated,
+                   "parallelism": "1 GPU"},
+        "kernel_ms": {"mean": float(np.mean(kern_ms)), "median": float(np.median(kern_ms)),
+                      "min": float(np.min(kern_ms)), "what": "pair kernel + merge, HIP events"},
+        "roofline": {"bound": "alu", "achieved": achieved, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / FP32_PEAK_TFLOPS, "traffic": None,
+                     "note": f"{FLOPS_PER_PAIR:.0f} algorithmic FP32 flops per evaluated pair"},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        sub_n = min(len(D), 100_000)
+        line["cpu_baseline"] = cpu_baseline(D, R, nbins, w) if sub_n else None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

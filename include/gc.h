@@ -1,0 +1,163 @@
+/*
+ * gc.h -- all-pairs angular-separation histograms (DD, DR, RR) and the
+ * Landy-Szalay two-point angular correlation estimator, on one AMD MI355X
+ * (gfx950) GPU.
+ *
+ * The operation is the one stated in "CUDA Deep Dive: 10B Galaxy Pairs on an
+ * RTX 5080", section "The problem":
+ *   - two catalogs, D (observed) and R (random), each a list of galaxies given
+ *     as right ascension alpha and declination delta in arcminutes;
+ *   - for every ordered pair of galaxies the angular separation
+ *       theta = acos( sin d1 sin d2 + cos d1 cos d2 cos(a1 - a2) ),
+ *     i.e. the angle between the two radius vectors;
+ *   - theta binned into fixed-width bins for the three families DD (D x D),
+ *     DR (D x R) and RR (R x R), each covering every ordered pair including
+ *     self-pairs, so each histogram sums to exactly N_a * N_b;
+ *   - omega = (DD - 2 DR + RR) / RR per bin.
+ * Bin k covers [k*w, (k+1)*w) degrees; theta >= nbins*w goes to bin nbins-1
+ * (truncation and clamping as in the appendix listing's histogram-index
+ * helper).  Results equal an fp64 evaluation except for pairs whose fp64 angle
+ * lies within rounding (well under 1e-5 degrees) of a bin edge.
+ *
+ * Conventions shared by every call:
+ *   - Pointers named d_* or documented "device" are device pointers on the
+ *     current HIP device; the caller owns every buffer and keeps it alive until
+ *     the work enqueued on `stream` has completed.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; 0 is the null stream).
+ *   - The library allocates no device memory, prints nothing and never exits.
+ *   - Arguments are validated on the host before anything is enqueued.  On any
+ *     error status nothing has been enqueued and the outputs are untouched.
+ *   - Thread-safe: the only state is a per-device property cache filled once,
+ *     and a per-thread record of the last HIP error.
+ */
+#ifndef GC_H_
+#define GC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *gc_stream_t; /* the same type as hipStream_t */
+
+typedef enum {
+    GC_OK = 0,
+    GC_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, nbins <= 0, width <= 0 or not
+                                    finite, misaligned buffer, bad tuning field */
+    GC_ERR_UNSUPPORTED = 2,      /* nbins above GC_MAX_BINS, n above GC_MAX_GALAXIES */
+    GC_ERR_WORKSPACE = 3,        /* workspace smaller than gc_workspace_bytes() */
+    GC_ERR_DEVICE = 4            /* a HIP call or kernel launch failed; see gc_last_device_error() */
+} gc_status;
+
+#define GC_MAX_BINS 8192                 /* bins per histogram (LDS-resident per wavefront) */
+#define GC_MAX_GALAXIES 2147483647LL     /* galaxies per catalog (2^31 - 1) */
+#define GC_ALIGNMENT 256                 /* required alignment of prepared blobs and workspace */
+
+/* ---------------------------------------------------------------- prepare ----
+ * Convert one catalog to the library's prepared form: per galaxy the unit
+ * radius vector (cos d cos a, cos d sin a, sin d), computed in fp64 from the
+ * exact fp32 arcminute inputs (a = alpha * pi/10800, d = delta * pi/10800),
+ * stored as structure-of-arrays in fp32 (correctly rounded) and in fp64.  The
+ * angle between two galaxies is the arccos of their vectors' dot product
+ * (section "The problem"); precomputing per-galaxy trigonometry is the page's
+ * section "L2: precomputed sin/cos", taken one step further.
+ *
+ *   d_ra_arcmin, d_dec_arcmin : device, n fp32 values each; must be finite
+ *                               (non-finite values give unspecified bins but the
+ *                               totals still hold).
+ *   n                         : number of galaxies, 0 <= n <= GC_MAX_GALAXIES.
+ *   d_prepared                : device, gc_prepared_bytes(n) bytes, GC_ALIGNMENT-aligned;
+ *                               its layout is private to the library.  May be null
+ *                               only when n == 0.
+ */
+size_t gc_prepared_bytes(int64_t n);
+gc_status gc_prepare(const float *d_ra_arcmin, const float *d_dec_arcmin, int64_t n,
+                     void *d_prepared, gc_stream_t stream);
+
+/* -------------------------------------------------------------- histogram ----
+ * DD, DR and RR over all ordered pairs of the prepared catalogs (section "The
+ * problem"; DD and RR use the i <= j symmetry of section "L1: DD/RR symmetry",
+ * which changes no count).
+ *
+ *   d_prepared_d, n_d : prepared catalog D (from gc_prepare) and its size.
+ *   d_prepared_r, n_r : prepared catalog R and its size.  D and R may be the same
+ *                       blob; then DR is the full ordered D x D histogram.
+ *   nbins             : 1 <= nbins <= GC_MAX_BINS.
+ *   bin_width_deg     : w > 0, finite.  Bin k = [k*w, (k+1)*w) degrees; larger angles
+ *                       go to bin nbins-1.
+ *   d_dd, d_dr, d_rr  : device, nbins uint64 each, 8-byte aligned; OVERWRITTEN.
+ *                       Sums: n_d^2, n_d*n_r, n_r^2.  A family with no pairs is all zero.
+ *   d_workspace       : device scratch of at least gc_workspace_bytes(nbins) bytes,
+ *                       GC_ALIGNMENT-aligned; contents on entry are ignored.  Must not
+ *                       be used by another call until this one has completed.
+ * Returns GC_OK once the work is enqueued.
+ */
+size_t gc_workspace_bytes(int32_t nbins);
+gc_status gc_histogram_dd_dr_rr(const void *d_prepared_d, int64_t n_d,
+                                const void *d_prepared_r, int64_t n_r,
+                                int32_t nbins, double bin_width_deg,
+                                uint64_t *d_dd, uint64_t *d_dr, uint64_t *d_rr,
+                                void *d_workspace, size_t workspace_bytes,
+                                gc_stream_t stream);
+
+/* Optional overrides of the launch plan, for tuning sweeps and tests.  Every field
+ * 0 means "the library's choice"; gc_histogram_dd_dr_rr is this call with all zeros.
+ * The result does not depend on these fields (only speed does). */
+typedef struct {
+    int32_t dot_precision;   /* 0 auto, 32: fp32 dot product, 64: fp64 dot product */
+    int32_t i_per_lane;      /* 0 auto, or 4 or 8 galaxies held per lane */
+    int32_t blocks_per_cu;   /* 0 auto (occupancy), else 1..8 workgroups per compute unit */
+    int32_t reserved;        /* must be 0 */
+    int64_t flush_interval;  /* 0 auto; else j-steps between flushes of the 32-bit per-wave
+                                histograms into 64-bit totals (>= 1) */
+} gc_tuning;
+
+gc_status gc_histogram_dd_dr_rr_tuned(const void *d_prepared_d, int64_t n_d,
+                                      const void *d_prepared_r, int64_t n_r,
+                                      int32_t nbins, double bin_width_deg,
+                                      uint64_t *d_dd, uint64_t *d_dr, uint64_t *d_rr,
+                                      void *d_workspace, size_t workspace_bytes,
+                                      const gc_tuning *tuning, gc_stream_t stream);
+
+/* ----------------------------------------------------------------- totals ----
+ * The three histogram sums, for the exact-total check of section "The problem"
+ * (each family must sum to N_a * N_b).  d_totals: device, 3 uint64 (DD, DR, RR
+ * order), overwritten. */
+gc_status gc_histogram_totals(const uint64_t *d_dd, const uint64_t *d_dr, const uint64_t *d_rr,
+                              int32_t nbins, uint64_t *d_totals, gc_stream_t stream);
+
+/* ------------------------------------------------------------------ omega ----
+ * Landy-Szalay estimator per bin in fp64 (section "The problem"):
+ *   omega = (DD - 2 DR + RR) / RR                       when n_d == n_r,
+ *   omega = (DD/n_d^2 - 2 DR/(n_d n_r) + RR/n_r^2) / (RR/n_r^2)   otherwise,
+ * and NaN where RR == 0 (the page's program skips such bins).
+ *   d_dd, d_dr, d_rr : device, nbins uint64 each.   d_omega: device, nbins fp64, overwritten. */
+gc_status gc_omega(const uint64_t *d_dd, const uint64_t *d_dr, const uint64_t *d_rr,
+                   int32_t nbins, int64_t n_d, int64_t n_r, double *d_omega, gc_stream_t stream);
+
+/* ------------------------------------------------------------ diagnostics ----
+ * Evaluate the pair kernel's per-pair angle-to-bin core on given cosines, exactly as
+ * the pair kernel does, for numerical verification of its guard.
+ *   dot_precision 32: reads d_x32 (n fp32 cosines); 64: reads d_x64 (n fp64 cosines).
+ *   d_bin_out : device, n int32: the fast-path bin.
+ *   d_trip_out: device, n uint8: 1 where the guard sends the pair to the exact fp64
+ *               recheck.
+ *   d_exact_out: device, n int32 (may be null): the exact fp64 recheck's bin of the
+ *               same cosine (fp32 cosines are widened exactly). */
+gc_status gc_eval_angle_core(const float *d_x32, const double *d_x64, int64_t n,
+                             int32_t nbins, double bin_width_deg, int32_t dot_precision,
+                             int32_t *d_bin_out, uint8_t *d_trip_out, int32_t *d_exact_out,
+                             gc_stream_t stream);
+
+/* ----------------------------------------------------------------- status ---- */
+const char *gc_status_string(gc_status status);
+int gc_last_device_error(void); /* last hipError_t seen by this thread (0 if none) */
+const char *gc_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GC_H_ */

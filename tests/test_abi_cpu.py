@@ -1,0 +1,123 @@
+"""The C ABI on a machine without a GPU: the library loads, exports every function that
+include/gc.h declares, and every argument check returns its status before any HIP call.
+Device pointers passed here are never dereferenced: each call fails validation first."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import two_point_angular_amd as gc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gc.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, DEVICE = 0, 1, 2, 3, 4
+A = 4096  # a 256-aligned fake device address; never dereferenced
+NO_GPU = not os.path.exists("/dev/kfd")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gc.library_path()):
+        from two_point_angular_amd import build
+        build.build()
+    return gc.load()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gc_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(lib):
+    names = header_functions()
+    assert len(names) >= 11
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_sizes(lib):
+    assert lib.gc_prepared_bytes(-1) == 0
+    assert lib.gc_prepared_bytes(0) == 64 * 36
+    assert lib.gc_prepared_bytes(100) == (128 + 64) * 36
+    assert lib.gc_prepared_bytes(gc.MAX_GALAXIES + 1) == 0
+    assert lib.gc_prepared_bytes(10**5) % gc.ALIGNMENT == 0
+    assert lib.gc_workspace_bytes(0) == 0
+    assert lib.gc_workspace_bytes(gc.MAX_BINS + 1) == 0
+    assert lib.gc_workspace_bytes(720) == 2048 * 720 * 8
+
+
+def test_status_strings(lib):
+    assert lib.gc_status_string(0) == b"ok"
+    assert lib.gc_status_string(3) == b"workspace too small"
+    assert lib.gc_status_string(99) == b"unknown status"
+    assert lib.gc_version().startswith(b"gc ")
+    assert lib.gc_last_device_error() == 0
+
+
+def test_prepare_validation(lib):
+    P = ctypes.c_void_p
+    assert lib.gc_prepare(None, None, -1, P(A), None) == INVALID
+    assert lib.gc_prepare(P(A), P(A), gc.MAX_GALAXIES + 1, P(A), None) == UNSUPPORTED
+    assert lib.gc_prepare(None, P(A), 5, P(A), None) == INVALID
+    assert lib.gc_prepare(P(A), P(A), 5, None, None) == INVALID
+    assert lib.gc_prepare(P(A), P(A), 5, P(A + 8), None) == INVALID      # misaligned blob
+    assert lib.gc_prepare(None, None, 0, None, None) == OK               # empty, nothing enqueued
+
+
+def _hist(lib, **kw):
+    P = ctypes.c_void_p
+    a = dict(pd=P(A), nd=10, pr=P(A), nr=10, nbins=720, w=0.25, dd=P(A), dr=P(A + 8192), rr=P(A + 16384),
+             ws=P(A), wsb=gc.workspace_bytes(720) if kw.get("nbins", 720) in (720,) else 1 << 40, tuning=None)
+    a.update(kw)
+    if a["tuning"] is None:
+        return lib.gc_histogram_dd_dr_rr(a["pd"], a["nd"], a["pr"], a["nr"], a["nbins"], a["w"], a["dd"],
+                                         a["dr"], a["rr"], a["ws"], a["wsb"], None)
+    return lib.gc_histogram_dd_dr_rr_tuned(a["pd"], a["nd"], a["pr"], a["nr"], a["nbins"], a["w"], a["dd"],
+                                           a["dr"], a["rr"], a["ws"], a["wsb"], ctypes.byref(a["tuning"]),
+                                           None)
+
+
+def test_histogram_validation(lib):
+    P = ctypes.c_void_p
+    assert _hist(lib, nbins=0) == INVALID
+    assert _hist(lib, nbins=-5) == INVALID
+    assert _hist(lib, nbins=gc.MAX_BINS + 1) == UNSUPPORTED
+    for w in (0.0, -0.25, float("inf"), float("nan")):
+        assert _hist(lib, w=w) == INVALID
+    assert _hist(lib, nd=-1) == INVALID
+    assert _hist(lib, nr=gc.MAX_GALAXIES + 1) == UNSUPPORTED
+    assert _hist(lib, pd=None) == INVALID
+    assert _hist(lib, pr=P(A + 4)) == INVALID
+    assert _hist(lib, dd=None) == INVALID
+    assert _hist(lib, rr=P(A + 4)) == INVALID
+    assert _hist(lib, ws=None) == INVALID
+    assert _hist(lib, ws=P(A + 128)) == INVALID
+    assert _hist(lib, wsb=gc.workspace_bytes(720) - 1) == WORKSPACE
+    for bad in (gc._Tuning(33, 0, 0, 0, 0), gc._Tuning(0, 5, 0, 0, 0), gc._Tuning(0, 0, 9, 0, 0),
+                gc._Tuning(0, 0, -1, 0, 0), gc._Tuning(0, 0, 0, 1, 0), gc._Tuning(0, 0, 0, 0, -3)):
+        assert _hist(lib, tuning=bad) == INVALID
+
+
+@pytest.mark.skipif(not NO_GPU, reason="exercises the no-device error path; only without a GPU")
+def test_histogram_reports_device_error_without_gpu(lib):
+    # valid arguments: planning needs the device, which is absent -> GC_ERR_DEVICE
+    assert _hist(lib) == DEVICE
+    assert lib.gc_last_device_error() != 0
+
+
+def test_totals_omega_core_validation(lib):
+    P = ctypes.c_void_p
+    assert lib.gc_histogram_totals(P(A), P(A), P(A), 0, P(A), None) == INVALID
+    assert lib.gc_histogram_totals(P(A), P(A), P(A), gc.MAX_BINS + 1, P(A), None) == UNSUPPORTED
+    assert lib.gc_histogram_totals(None, P(A), P(A), 10, P(A), None) == INVALID
+    assert lib.gc_omega(P(A), P(A), P(A), 0, 1, 1, P(A), None) == INVALID
+    assert lib.gc_omega(P(A), P(A), P(A), 10, -1, 1, P(A), None) == INVALID
+    assert lib.gc_omega(P(A), P(A), None, 10, 1, 1, P(A), None) == INVALID
+    assert lib.gc_omega(P(A), P(A), P(A), 10, 1, 1, P(A + 4), None) == INVALID
+    assert lib.gc_eval_angle_core(P(A), None, 10, 720, 0.25, 16, P(A), P(A), None, None) == INVALID
+    assert lib.gc_eval_angle_core(None, None, 10, 720, 0.25, 32, P(A), P(A), None, None) == INVALID
+    assert lib.gc_eval_angle_core(P(A), None, 0, 720, 0.25, 32, P(A), P(A), None, None) == OK
+    assert lib.gc_eval_angle_core(P(A), None, 10, 0, 0.25, 32, P(A), P(A), None, None) == INVALID

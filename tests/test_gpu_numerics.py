@@ -1,0 +1,100 @@
+"""The pair kernel's angle-to-bin core on the GPU, checked exhaustively near every bin edge.
+
+For a pair whose true cosine is x, the kernel sees x~ with |x~ - x| <= g, where g is the
+dot-product error bound (fp32 dot of fp32-rounded unit vectors: 5 * 2^-24; fp64 dot of
+fp64 unit vectors: well under 1e-14).  The kernel either rechecks the pair in fp64 (trip)
+or bins it from x~ alone.  Soundness: for every x~ that does not trip, every x in
+[x~ - g, x~ + g] must truncate to the same bin (acos is monotone, so the two ends decide).
+The cosines tested are every fp32 value within 4096 ulps of each edge's cosine (fp32
+core), a dense fp64 sweep across each edge (fp64 core), and random cosines.
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+G32 = 5.0 * 2.0 ** -24 * (1 + 1e-6) + 1e-12
+G64 = 1e-14
+
+
+@pytest.fixture(scope="module")
+def gc():
+    import torch
+    import two_point_angular_amd as gcm
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gcm.load()
+    return gcm
+
+
+def true_bins(x, nbins, w_deg):
+    t = np.degrees(np.arccos(np.clip(x, -1.0, 1.0))) / w_deg
+    return np.minimum(np.floor(t), nbins - 1).astype(np.int64), t
+
+
+def run_core(gc, x, nbins, w):
+    import torch
+    xt = torch.from_numpy(x).to("cuda")
+    b, trip, exact = gc.eval_angle_core(xt, nbins, w)
+    torch.cuda.synchronize()
+    return b.cpu().numpy().astype(np.int64), trip.cpu().numpy().astype(bool), exact.cpu().numpy().astype(np.int64)
+
+
+def edge_neighbourhood_f32(nbins, w_deg, ulps=4096):
+    c = np.cos(np.radians(np.arange(1, nbins) * w_deg)).astype(np.float32)
+    bits = c.view(np.int32).astype(np.int64)
+    offs = np.arange(-ulps, ulps + 1, dtype=np.int64)
+    # fp32 bit patterns are monotone in value within one sign; handle negatives separately
+    allb = (bits[:, None] + np.where(c[:, None] >= 0, offs[None, :], -offs[None, :])).ravel()
+    allb = allb[(allb >= np.int64(np.iinfo(np.int32).min)) & (allb <= np.int64(np.iinfo(np.int32).max))]
+    x = allb.astype(np.int32).view(np.float32)
+    return x[np.isfinite(x) & (np.abs(x) <= 1.0)]
+
+
+def check_sound(x_exact_in, b, trip, nbins, w, g):
+    keep = ~trip
+    xk = x_exact_in[keep]
+    lo, _ = true_bins(np.clip(xk + g, -1, 1), nbins, w)   # larger cosine -> smaller angle
+    hi, _ = true_bins(np.clip(xk - g, -1, 1), nbins, w)
+    bad = (lo != b[keep]) | (hi != b[keep])
+    assert not bad.any(), (int(bad.sum()), xk[bad][:5], b[keep][bad][:5], lo[bad][:5], hi[bad][:5])
+
+
+@pytest.mark.parametrize("nbins,w", [(720, 0.25), (3600, 0.05), (1500, 0.001)])
+def test_fp32_core_sound_near_edges(gc, nbins, w):
+    print(f"[gpu] fp32 core near edges nbins={nbins}", flush=True)
+    rng = np.random.default_rng(nbins)
+    x = np.concatenate([edge_neighbourhood_f32(nbins, w),
+                        rng.uniform(-1, 1, 2_000_000).astype(np.float32),
+                        (1 - rng.random(200_000) * 1e-4).astype(np.float32),
+                        np.array([1.0, -1.0, 0.0, -0.0, 0.5, -0.5], np.float32)])
+    b, trip, exact = run_core(gc, x, nbins, w)
+    xd = x.astype(np.float64)
+    assert b.min() >= 0 and b.max() <= nbins - 1
+    check_sound(xd, b, trip, nbins, w, G32)
+    tb, t = true_bins(xd, nbins, w)
+    near = np.abs(t - np.round(t)) < 1e-9
+    assert np.all((exact == tb) | near)
+    if nbins != 1500:
+        r = trip[len(x) - 2_200_006: len(x) - 200_006].mean()
+        assert r < 5e-3, r
+
+
+@pytest.mark.parametrize("nbins,w", [(720, 0.25), (3600, 0.05), (1500, 0.001)])
+def test_fp64_core_sound_near_edges(gc, nbins, w):
+    print(f"[gpu] fp64 core near edges nbins={nbins}", flush=True)
+    rng = np.random.default_rng(nbins + 1)
+    e = np.arange(1, nbins)
+    u = np.linspace(-0.02, 0.02, 801)
+    th = np.radians((e[:, None] + u[None, :]) * w).ravel()
+    x = np.concatenate([np.cos(th), rng.uniform(-1, 1, 2_000_000),
+                        np.cos(np.radians(rng.uniform(0, 3.0, 1_000_000))),
+                        np.array([1.0, -1.0, 0.0, -0.0])])
+    b, trip, exact = run_core(gc, x, nbins, w)
+    assert b.min() >= 0 and b.max() <= nbins - 1
+    check_sound(x, b, trip, nbins, w, G64)
+    tb, t = true_bins(x, nbins, w)
+    near = np.abs(t - np.round(t)) < 1e-9
+    assert np.all((exact == tb) | near)
+    r = trip[len(th): len(th) + 2_000_000].mean()
+    assert r < 5e-3, r

@@ -1,0 +1,219 @@
+"""Python binding of libgc: all-pairs angular-separation histograms on an MI355X.
+
+The computation is the one of "CUDA Deep Dive: 10B Galaxy Pairs on an RTX 5080",
+section "The problem": DD, DR and RR histograms of the angle between the radius
+vectors of every ordered pair of galaxies, and the Landy-Szalay estimator
+omega = (DD - 2 DR + RR) / RR.
+
+Every function here marshals torch tensors (device memory, current HIP stream) into
+the C ABI declared in include/gc.h; all arithmetic runs in the library's HIP kernels.
+There is no CPU fallback: without the built library every call raises.
+
+Typical use::
+
+    import torch, two_point_angular_amd as gc
+    pd = gc.prepare(ra_d, dec_d)            # fp32 arcmin tensors on cuda
+    pr = gc.prepare(ra_r, dec_r)
+    dd, dr, rr = gc.histogram_dd_dr_rr(pd, len(ra_d), pr, len(ra_r), 720, 0.25)
+    w = gc.omega(dd, dr, rr, len(ra_d), len(ra_r))
+
+Histograms are returned as int64 tensors holding the library's uint64 counts (all
+counts here are below 2^63).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+__all__ = ["GCError", "Tuning", "library_path", "load", "prepared_bytes", "workspace_bytes",
+           "prepare", "histogram_dd_dr_rr", "histogram_totals", "omega", "eval_angle_core",
+           "MAX_BINS", "MAX_GALAXIES", "ALIGNMENT"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "lib", "libgc.so")
+
+MAX_BINS = 8192
+MAX_GALAXIES = 2147483647
+ALIGNMENT = 256
+
+GC_OK = 0
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported size", 3: "workspace too small",
+           4: "device error"}
+
+
+class GCError(RuntimeError):
+    def __init__(self, status: int, where: str, hip_error: int = 0):
+        self.status = status
+        self.hip_error = hip_error
+        msg = f"{where}: {_STATUS.get(status, 'unknown')} (status {status})"
+        if status == 4:
+            msg += f", hipError {hip_error}"
+        super().__init__(msg)
+
+
+class _Tuning(ctypes.Structure):
+    _fields_ = [("dot_precision", ctypes.c_int32), ("i_per_lane", ctypes.c_int32),
+                ("blocks_per_cu", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("flush_interval", ctypes.c_int64)]
+
+
+@dataclass
+class Tuning:
+    """Launch-plan overrides (0 = library's choice); results do not depend on them."""
+
+    dot_precision: int = 0
+    i_per_lane: int = 0
+    blocks_per_cu: int = 0
+    flush_interval: int = 0
+
+    def _c(self) -> _Tuning:
+        return _Tuning(self.dot_precision, self.i_per_lane, self.blocks_per_cu, 0, self.flush_interval)
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libgc.so (built by two_point_angular_amd.build); raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"libgc.so not built ({_LIB_PATH}); run python -m two_point_angular_amd.build")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    sig = {
+        "gc_prepared_bytes": (sz, [i64]),
+        "gc_prepare": (i32, [vp, vp, i64, vp, vp]),
+        "gc_workspace_bytes": (sz, [i32]),
+        "gc_histogram_dd_dr_rr": (i32, [vp, i64, vp, i64, i32, ctypes.c_double, vp, vp, vp, vp, sz, vp]),
+        "gc_histogram_dd_dr_rr_tuned": (i32, [vp, i64, vp, i64, i32, ctypes.c_double, vp, vp, vp, vp, sz,
+                                              ctypes.POINTER(_Tuning), vp]),
+        "gc_histogram_totals": (i32, [vp, vp, vp, i32, vp, vp]),
+        "gc_omega": (i32, [vp, vp, vp, i32, i64, i64, vp, vp]),
+        "gc_eval_angle_core": (i32, [vp, vp, i64, i32, ctypes.c_double, i32, vp, vp, vp, vp]),
+        "gc_status_string": (ctypes.c_char_p, [i32]),
+        "gc_last_device_error": (ctypes.c_int, []),
+        "gc_version": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int, where: str):
+    if status != GC_OK:
+        raise GCError(status, where, load().gc_last_device_error() if status == 4 else 0)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _need(t, dtype, name, device=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous {dtype} CUDA tensor")
+    return t
+
+
+def prepared_bytes(n: int) -> int:
+    return int(load().gc_prepared_bytes(int(n)))
+
+
+def workspace_bytes(nbins: int) -> int:
+    return int(load().gc_workspace_bytes(int(nbins)))
+
+
+def prepare(ra_arcmin, dec_arcmin, out=None, stream=None):
+    """Prepared (unit-vector) form of one catalog, as an opaque uint8 device tensor."""
+    torch = _torch()
+    _need(ra_arcmin, torch.float32, "ra_arcmin")
+    _need(dec_arcmin, torch.float32, "dec_arcmin")
+    n = ra_arcmin.numel()
+    if dec_arcmin.numel() != n:
+        raise ValueError("ra and dec must have the same length")
+    nbytes = prepared_bytes(n)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=ra_arcmin.device)
+    elif out.numel() < nbytes:
+        raise ValueError("prepared buffer too small")
+    _check(load().gc_prepare(_ptr(ra_arcmin), _ptr(dec_arcmin), n, _ptr(out), _stream(stream)), "gc_prepare")
+    return out
+
+
+def histogram_dd_dr_rr(prep_d, n_d: int, prep_r, n_r: int, nbins: int, bin_width_deg: float,
+                       out=None, workspace=None, tuning: Tuning | None = None, stream=None):
+    """(DD, DR, RR) int64 device tensors of nbins counts each."""
+    torch = _torch()
+    dev = prep_d.device if prep_d is not None else prep_r.device
+    if out is None:
+        out = torch.empty((3, nbins), dtype=torch.int64, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(workspace_bytes(nbins), 1), dtype=torch.uint8, device=dev)
+    dd, dr, rr = out[0], out[1], out[2]
+    args = [_ptr(prep_d), int(n_d), _ptr(prep_r), int(n_r), int(nbins), float(bin_width_deg),
+            _ptr(dd), _ptr(dr), _ptr(rr), _ptr(workspace), workspace.numel()]
+    lib = load()
+    if tuning is None:
+        st = lib.gc_histogram_dd_dr_rr(*args, _stream(stream))
+    else:
+        tc = tuning._c()
+        st = lib.gc_histogram_dd_dr_rr_tuned(*args, ctypes.byref(tc), _stream(stream))
+    _check(st, "gc_histogram_dd_dr_rr")
+    return dd, dr, rr
+
+
+def histogram_totals(dd, dr, rr, out=None, stream=None):
+    torch = _torch()
+    if out is None:
+        out = torch.empty(3, dtype=torch.int64, device=dd.device)
+    _check(load().gc_histogram_totals(_ptr(dd), _ptr(dr), _ptr(rr), dd.numel(), _ptr(out), _stream(stream)),
+           "gc_histogram_totals")
+    return out
+
+
+def omega(dd, dr, rr, n_d: int, n_r: int, out=None, stream=None):
+    torch = _torch()
+    if out is None:
+        out = torch.empty(dd.numel(), dtype=torch.float64, device=dd.device)
+    _check(load().gc_omega(_ptr(dd), _ptr(dr), _ptr(rr), dd.numel(), int(n_d), int(n_r), _ptr(out),
+                           _stream(stream)), "gc_omega")
+    return out
+
+
+def eval_angle_core(x, nbins: int, bin_width_deg: float, with_exact: bool = True, stream=None):
+    """The pair kernel's angle-to-bin core on cosines x (fp32 -> fp32-dot core, fp64 ->
+    fp64-dot core).  Returns (bin, trip, exact_bin) device tensors."""
+    torch = _torch()
+    n = x.numel()
+    dot = 64 if x.dtype == torch.float64 else 32
+    bins = torch.empty(n, dtype=torch.int32, device=x.device)
+    trip = torch.empty(n, dtype=torch.uint8, device=x.device)
+    exact = torch.empty(n, dtype=torch.int32, device=x.device) if with_exact else None
+    x32 = x if dot == 32 else None
+    x64 = x if dot == 64 else None
+    _check(load().gc_eval_angle_core(_ptr(x32), _ptr(x64), n, int(nbins), float(bin_width_deg), dot,
+                                     _ptr(bins), _ptr(trip), _ptr(exact), _stream(stream)),
+           "gc_eval_angle_core")
+    return bins, trip, exact

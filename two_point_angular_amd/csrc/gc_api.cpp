@@ -1,0 +1,339 @@
+// C ABI of libgc: argument validation, launch planning and kernel launches.
+// Every check runs on the host before any HIP call, so every error path is reachable
+// without a GPU.
+#include <math.h>
+#include <mutex>
+#include <string.h>
+
+#include "../../include/gc.h"
+#include "gc_acos_poly.h"
+#include "gc_internal.h"
+
+namespace gc {
+namespace {
+
+thread_local int t_last_hip_error = 0;
+
+gc_status device_error(hipError_t e) {
+  t_last_hip_error = static_cast<int>(e);
+  return GC_ERR_DEVICE;
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// ---- per-device cache: CU count and pair-kernel occupancy -----------------------------
+struct DeviceInfo {
+  bool valid = false;
+  int cus = 0;
+  // occupancy per (dot64, k index, lds bytes)
+  struct Occ { size_t lds; int blocks; };
+  Occ occ[2][2][8];
+  int nocc[2][2] = {{0, 0}, {0, 0}};
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_mu;
+DeviceInfo g_dev[kMaxDevices];
+
+hipError_t device_info(int *cus, bool dot64, int k, size_t lds, int *blocks_per_cu) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceInfo &d = g_dev[dev];
+  if (!d.valid) {
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    d.cus = n;
+    d.valid = true;
+  }
+  *cus = d.cus;
+  if (!blocks_per_cu) return hipSuccess;
+  const int ki = k == 4 ? 0 : 1;
+  const int di = dot64 ? 1 : 0;
+  for (int q = 0; q < d.nocc[di][ki]; ++q)
+    if (d.occ[di][ki][q].lds == lds) {
+      *blocks_per_cu = d.occ[di][ki][q].blocks;
+      return hipSuccess;
+    }
+  int blocks = 0;
+  e = pairs_occupancy(dot64, k, lds, &blocks);
+  if (e != hipSuccess) return e;
+  if (d.nocc[di][ki] < 8) d.occ[di][ki][d.nocc[di][ki]++] = {lds, blocks};
+  *blocks_per_cu = blocks;
+  return hipSuccess;
+}
+
+// ---- binning constants and the certified guard -----------------------------------------
+// Error model (all in units of bins, t = theta / w):
+//  fp32 dot: the unit vectors are fp32 roundings of fp64 ones (|e| <= 2^-24 per component)
+//    and the dot product takes three fp32 roundings, so |x~ - x| <= g_x = 5 * 2^-24 (+ the
+//    fp64 prep error).  Since acos(1 - y) has derivative <= 1/sqrt(y), a cosine error g_x
+//    moves theta by at most 2 g_x / s, s = sqrt(1 - |x~|) as computed (2.02 covers the
+//    rounding of s).  The arccos core adds at most E_core (rad), and forming t in fp32
+//    adds 2^-24 (t + 2h) (roundings of 1/w, (pi/2)/w and the final fma).  The kernel
+//    rechecks iff |t - round(t)| * s < g32 = 2.02 g_x / w + C, C = E_core / w + 2^-24 (nbins
+//    + 1 + 2h), which is implied by |t - round(t)| < 2.02 g_x / (s w) + C because s <= 1.
+//  fp64 dot: the cosine error is ~1e-15, so the dominant error is the fp32 core, relative
+//    to t: |t~ - t| <= rho t with rho covering sqrt, polynomial, narrowing and t roundings.
+//    Recheck iff |t - round(t)| * s < g64k1 * s + g64k2, g64k1 = rho (nbins + 1),
+//    g64k2 = 2.02 g64 / w.
+constexpr double kTwoM24 = 5.9604644775390625e-08;  // 2^-24
+constexpr double kPi = 3.14159265358979323846;
+
+BinParams make_bins(int32_t nbins, double w_deg) {
+  const double w_rad = w_deg * (kPi / 180.0);
+  BinParams bp;
+  bp.nbins = nbins;
+  bp.invw = static_cast<float>(1.0 / w_rad);
+  bp.h = static_cast<float>((kPi / 2.0) / w_rad);
+  bp.pinvw = static_cast<float>(kPi / w_rad);
+  bp.tmax = static_cast<float>(nbins) - 0.5f;
+  bp.invw64 = 1.0 / w_rad;
+  // fp32-dot guard
+  const double g_x = 5.0 * kTwoM24 * (1.0 + 1e-6) + 1e-12;
+  // core error: exhaustive emulated bound plus one ulp of hardware sqrt (times P <= pi/2)
+  const double e_core = (GC_ACOS_CORE_ERR + 2.0 * kTwoM24 * (kPi / 2.0)) * 1.25;
+  const double h = (kPi / 2.0) / w_rad;
+  const double c = e_core / w_rad + kTwoM24 * (static_cast<double>(nbins) + 1.0 + 2.0 * h) * 1.01;
+  bp.g32 = static_cast<float>((2.02 * g_x / w_rad + c) * (1.0 + 1e-6));
+  // fp64-dot guard
+  const double rho = ((GC_ACOS_FIT_ERR + 4.0 * kTwoM24 * (kPi / 2.0)) / 1.41 + 8.0 * kTwoM24) * 1.25;
+  const double g64 = 1e-14;
+  bp.g64k1 = static_cast<float>(rho * (static_cast<double>(nbins) + 1.0) * (1.0 + 1e-6));
+  bp.g64k2 = static_cast<float>(2.02 * g64 / w_rad * (1.0 + 1e-6));
+  return bp;
+}
+
+// ---- validation ------------------------------------------------------------------------------
+gc_status check_bins(int32_t nbins, double w) {
+  if (nbins <= 0 || !(w > 0.0) || !isfinite(w)) return GC_ERR_INVALID_ARGUMENT;
+  if (nbins > GC_MAX_BINS) return GC_ERR_UNSUPPORTED;
+  return GC_OK;
+}
+
+gc_status check_catalog(const void *prep, int64_t n) {
+  if (n < 0) return GC_ERR_INVALID_ARGUMENT;
+  if (n > GC_MAX_GALAXIES) return GC_ERR_UNSUPPORTED;
+  if (n > 0 && (!prep || !aligned(prep, GC_ALIGNMENT))) return GC_ERR_INVALID_ARGUMENT;
+  return GC_OK;
+}
+
+size_t workspace_bytes(int32_t nbins) {
+  return static_cast<size_t>(kMaxWorkgroups) * static_cast<size_t>(nbins) * sizeof(unsigned long long);
+}
+
+// j-steps of one family: cross (n_i blocks x n_j) or self (upper triangle by blocks).
+int64_t family_steps(int64_t n_i, int64_t n_j, bool sym, int k) {
+  if (n_i == 0 || n_j == 0) return 0;
+  const int64_t bi = static_cast<int64_t>(kWave) * k;
+  const int64_t nb = (n_i + bi - 1) / bi;
+  if (!sym) return nb * n_j;
+  return nb * n_j - bi * nb * (nb - 1) / 2;
+}
+
+}  // namespace
+}  // namespace gc
+
+using namespace gc;
+
+extern "C" {
+
+const char *gc_version(void) { return "gc 0.1 (gfx950)"; }
+
+const char *gc_status_string(gc_status s) {
+  switch (s) {
+    case GC_OK: return "ok";
+    case GC_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case GC_ERR_UNSUPPORTED: return "unsupported size";
+    case GC_ERR_WORKSPACE: return "workspace too small";
+    case GC_ERR_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+int gc_last_device_error(void) { return t_last_hip_error; }
+
+size_t gc_prepared_bytes(int64_t n) {
+  if (n < 0 || n > GC_MAX_GALAXIES) return 0;
+  return prepared_bytes_for(n);
+}
+
+gc_status gc_prepare(const float *ra, const float *dec, int64_t n, void *prepared, gc_stream_t stream) {
+  if (n < 0) return GC_ERR_INVALID_ARGUMENT;
+  if (n > GC_MAX_GALAXIES) return GC_ERR_UNSUPPORTED;
+  if (n > 0 && (!ra || !dec)) return GC_ERR_INVALID_ARGUMENT;
+  if (!prepared) return n == 0 ? GC_OK : GC_ERR_INVALID_ARGUMENT;
+  if (!aligned(prepared, GC_ALIGNMENT)) return GC_ERR_INVALID_ARGUMENT;
+  hipError_t e = launch_prepare(ra, dec, n, prepared, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GC_OK : device_error(e);
+}
+
+size_t gc_workspace_bytes(int32_t nbins) {
+  if (nbins <= 0 || nbins > GC_MAX_BINS) return 0;
+  return workspace_bytes(nbins);
+}
+
+gc_status gc_histogram_dd_dr_rr_tuned(const void *prep_d, int64_t n_d, const void *prep_r, int64_t n_r,
+                                      int32_t nbins, double w_deg, uint64_t *dd, uint64_t *dr,
+                                      uint64_t *rr, void *workspace, size_t ws_bytes,
+                                      const gc_tuning *tuning, gc_stream_t stream) {
+  gc_status st;
+  if ((st = check_bins(nbins, w_deg)) != GC_OK) return st;
+  if ((st = check_catalog(prep_d, n_d)) != GC_OK) return st;
+  if ((st = check_catalog(prep_r, n_r)) != GC_OK) return st;
+  if (!dd || !dr || !rr || !aligned(dd, 8) || !aligned(dr, 8) || !aligned(rr, 8))
+    return GC_ERR_INVALID_ARGUMENT;
+  if (!workspace || !aligned(workspace, GC_ALIGNMENT)) return GC_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < workspace_bytes(nbins)) return GC_ERR_WORKSPACE;
+  gc_tuning tu;
+  memset(&tu, 0, sizeof(tu));
+  if (tuning) tu = *tuning;
+  if ((tu.dot_precision != 0 && tu.dot_precision != 32 && tu.dot_precision != 64) ||
+      (tu.i_per_lane != 0 && tu.i_per_lane != 4 && tu.i_per_lane != 8) || tu.blocks_per_cu < 0 ||
+      tu.blocks_per_cu > kMaxBlocksPerCU || tu.reserved != 0 || tu.flush_interval < 0)
+    return GC_ERR_INVALID_ARGUMENT;
+
+  // Plan.  Bins narrower than 0.01 deg put most pairs where the fp32 dot product cannot
+  // certify the bin; those use the fp64 dot-product instantiation.
+  const bool dot64 = tu.dot_precision == 64 || (tu.dot_precision == 0 && w_deg < 0.01);
+  const int k = tu.i_per_lane ? tu.i_per_lane : 8;
+  const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+
+  PairArgs a;
+  memset(&a, 0, sizeof(a));
+  a.nbins = nbins;
+  a.hist_words = (nbins + 63) / 64 * 64;
+  a.wave_lds_words = a.hist_words + 2 * kQueueCap;
+  a.bp = make_bins(nbins, w_deg);
+  a.slots = static_cast<unsigned long long *>(workspace);
+  const int64_t max_inc = 2ll * kWave * k;  // largest increase of one bin per j-step
+  const int64_t auto_flush = static_cast<int64_t>(0xffffffffll / max_inc) - 8;
+  a.flush_interval = tu.flush_interval ? (tu.flush_interval < auto_flush ? tu.flush_interval : auto_flush)
+                                       : auto_flush;
+
+  const Prepared pd = prepared_view(prep_d, n_d), pr = prepared_view(prep_r, n_r);
+  const int64_t nn[3][2] = {{n_d, n_d}, {n_d, n_r}, {n_r, n_r}};
+  const Prepared cc[3][2] = {{pd, pd}, {pd, pr}, {pr, pr}};
+  int64_t steps[3], total = 0;
+  for (int f = 0; f < 3; ++f) {
+    const bool sym = f != 1;
+    steps[f] = family_steps(nn[f][0], nn[f][1], sym, k);
+    total += steps[f];
+    FamilyWork &fw = a.fam[f];
+    fw.ci = cc[f][0];
+    fw.cj = cc[f][1];
+    fw.n_i = nn[f][0];
+    fw.n_j = nn[f][1];
+    fw.total_steps = steps[f];
+    fw.sym = sym ? 1 : 0;
+  }
+
+  int32_t wb[3] = {0, 0, 0}, we[3] = {0, 0, 0};
+  int num_wg = 0;
+  if (total > 0) {
+    const size_t lds = static_cast<size_t>(kWavesPerWG) * a.wave_lds_words * sizeof(uint32_t);
+    int cus = 0, occ = 0;
+    hipError_t e = device_info(&cus, dot64, k, lds, &occ);
+    if (e != hipSuccess) return device_error(e);
+    int per_cu = tu.blocks_per_cu ? tu.blocks_per_cu : (occ < kMaxBlocksPerCU ? occ : kMaxBlocksPerCU);
+    if (per_cu < 1) return GC_ERR_UNSUPPORTED;
+    int64_t g = static_cast<int64_t>(per_cu) * cus;
+    if (g > kMaxWorkgroups) g = kMaxWorkgroups;
+    // at least ~32 j-steps per wave
+    const int64_t want = (total + 32 * kWavesPerWG - 1) / (32 * kWavesPerWG);
+    if (g > want) g = want;
+    int nonzero = 0;
+    for (int f = 0; f < 3; ++f) nonzero += steps[f] > 0;
+    if (g < nonzero) g = nonzero;
+    // split workgroups among families in proportion to their j-steps
+    int64_t gf[3];
+    int64_t used = 0;
+    double frac[3];
+    for (int f = 0; f < 3; ++f) {
+      const double exact = static_cast<double>(g) * static_cast<double>(steps[f]) / static_cast<double>(total);
+      gf[f] = steps[f] > 0 ? static_cast<int64_t>(exact) : 0;
+      if (steps[f] > 0 && gf[f] < 1) gf[f] = 1;
+      frac[f] = exact - static_cast<double>(gf[f]);
+      used += gf[f];
+    }
+    while (used < g) {
+      int best = -1;
+      for (int f = 0; f < 3; ++f)
+        if (steps[f] > 0 && (best < 0 || frac[f] > frac[best])) best = f;
+      gf[best] += 1;
+      frac[best] -= 1.0;
+      ++used;
+    }
+    while (used > g) {  // only when the minimum of one workgroup per family overshot
+      int best = -1;
+      for (int f = 0; f < 3; ++f)
+        if (gf[f] > 1 && (best < 0 || frac[f] < frac[best])) best = f;
+      gf[best] -= 1;
+      frac[best] += 1.0;
+      --used;
+    }
+    int32_t cur = 0;
+    for (int f = 0; f < 3; ++f) {
+      wb[f] = cur;
+      cur += static_cast<int32_t>(gf[f]);
+      we[f] = cur;
+      a.fam[f].wg_begin = wb[f];
+      a.fam[f].wg_end = we[f];
+    }
+    num_wg = cur;
+    e = launch_pairs(a, num_wg, dot64, k, hs);
+    if (e != hipSuccess) return device_error(e);
+  }
+  uint64_t *outs[3] = {dd, dr, rr};
+  hipError_t e = launch_merge(a.slots, nbins, wb, we, outs, hs);
+  if (e != hipSuccess) return device_error(e);
+  return GC_OK;
+}
+
+gc_status gc_histogram_dd_dr_rr(const void *prep_d, int64_t n_d, const void *prep_r, int64_t n_r,
+                                int32_t nbins, double w_deg, uint64_t *dd, uint64_t *dr, uint64_t *rr,
+                                void *workspace, size_t ws_bytes, gc_stream_t stream) {
+  return gc_histogram_dd_dr_rr_tuned(prep_d, n_d, prep_r, n_r, nbins, w_deg, dd, dr, rr, workspace,
+                                     ws_bytes, nullptr, stream);
+}
+
+gc_status gc_histogram_totals(const uint64_t *dd, const uint64_t *dr, const uint64_t *rr, int32_t nbins,
+                              uint64_t *totals, gc_stream_t stream) {
+  if (nbins <= 0) return GC_ERR_INVALID_ARGUMENT;
+  if (nbins > GC_MAX_BINS) return GC_ERR_UNSUPPORTED;
+  if (!dd || !dr || !rr || !totals || !aligned(dd, 8) || !aligned(dr, 8) || !aligned(rr, 8) ||
+      !aligned(totals, 8))
+    return GC_ERR_INVALID_ARGUMENT;
+  hipError_t e = launch_totals(dd, dr, rr, nbins, totals, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GC_OK : device_error(e);
+}
+
+gc_status gc_omega(const uint64_t *dd, const uint64_t *dr, const uint64_t *rr, int32_t nbins, int64_t n_d,
+                   int64_t n_r, double *omega, gc_stream_t stream) {
+  if (nbins <= 0 || n_d < 0 || n_r < 0) return GC_ERR_INVALID_ARGUMENT;
+  if (nbins > GC_MAX_BINS) return GC_ERR_UNSUPPORTED;
+  if (!dd || !dr || !rr || !omega || !aligned(dd, 8) || !aligned(dr, 8) || !aligned(rr, 8) ||
+      !aligned(omega, 8))
+    return GC_ERR_INVALID_ARGUMENT;
+  hipError_t e = launch_omega(dd, dr, rr, nbins, n_d, n_r, omega, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GC_OK : device_error(e);
+}
+
+gc_status gc_eval_angle_core(const float *x32, const double *x64, int64_t n, int32_t nbins, double w_deg,
+                             int32_t dot_precision, int32_t *bin_out, uint8_t *trip_out, int32_t *exact_out,
+                             gc_stream_t stream) {
+  gc_status st;
+  if ((st = check_bins(nbins, w_deg)) != GC_OK) return st;
+  if (n < 0 || (dot_precision != 32 && dot_precision != 64)) return GC_ERR_INVALID_ARGUMENT;
+  if (n == 0) return GC_OK;
+  const bool d64 = dot_precision == 64;
+  if ((d64 && !x64) || (!d64 && !x32) || !bin_out || !trip_out) return GC_ERR_INVALID_ARGUMENT;
+  const BinParams bp = make_bins(nbins, w_deg);
+  hipError_t e = launch_eval_core(x32, x64, n, bp, d64, bin_out, trip_out, exact_out,
+                                  reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GC_OK : device_error(e);
+}
+
+}  // extern "C"

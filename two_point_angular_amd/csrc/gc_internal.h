@@ -1,0 +1,98 @@
+// Internal declarations shared by the HIP kernels (gc_kernels.hip) and the C ABI
+// (gc_api.cpp).  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gc {
+
+constexpr int kWave = 64;            // CDNA wavefront width
+constexpr int kWavesPerWG = 4;       // pair-kernel workgroup = 4 independent wavefronts
+constexpr int kWGThreads = kWave * kWavesPerWG;
+constexpr int kQueueCap = 128;       // per-wave recheck queue entries (power of two, >= 2*64)
+constexpr int kMaxWorkgroups = 2048; // partial-histogram slots held by the workspace
+constexpr int kMaxBlocksPerCU = 8;
+
+// ---- prepared catalog layout ---------------------------------------------------
+// Six structure-of-arrays vectors of `padded` elements each: fp32 x, y, z then fp64
+// x, y, z of the unit radius vector.  padded = roundup(n, 64) + 64 keeps every array
+// 256-byte aligned and lets wave-uniform batches of j read a few elements past n.
+inline int64_t padded_count(int64_t n) { return ((n + 63) / 64) * 64 + 64; }
+inline size_t prepared_bytes_for(int64_t n) { return (size_t)padded_count(n) * 36u; }
+
+struct Prepared {
+  const float *x, *y, *z;
+  const double *x64, *y64, *z64;
+};
+
+inline Prepared prepared_view(const void *blob, int64_t n) {
+  const int64_t p = padded_count(n);
+  const char *b = static_cast<const char *>(blob);
+  Prepared v;
+  v.x = reinterpret_cast<const float *>(b);
+  v.y = v.x + p;
+  v.z = v.y + p;
+  v.x64 = reinterpret_cast<const double *>(b + 12 * p);
+  v.y64 = v.x64 + p;
+  v.z64 = v.y64 + p;
+  return v;
+}
+
+// ---- binning constants -----------------------------------------------------------
+// Bin k = [k w, (k+1) w).  The fast path works in units of bins: t = theta / w.
+struct BinParams {
+  float invw;    // 1 / w_rad                       (fp32)
+  float h;       // (pi/2) / w_rad                   (fp32)
+  float pinvw;   // pi / w_rad                       (fp32)
+  float tmax;    // nbins - 0.5: clamp of t before truncation
+  float g32;     // fp32-dot guard: recheck iff |t - round(t)| * s < g32
+  float g64k1;   // fp64-dot guard: recheck iff |t - round(t)| * s < g64k1 * s + g64k2
+  float g64k2;
+  int32_t nbins;
+  double invw64; // 1 / w_rad (fp64), used by the exact recheck
+};
+
+// ---- pair-kernel work description ---------------------------------------------------
+// One family (DD, DR or RR): the i catalog is held in registers, the j catalog streamed.
+// Its work is a list of "j-steps": one j galaxy against one i-block of 64*K galaxies.
+// Block b (i in [b*BI, b*BI + BI)) has j in [0, n_j) (cross family) or [b*BI, n_j)
+// (self family, i <= j).  The family's workgroups [wg_begin, wg_end) split the j-steps
+// evenly among their wavefronts.
+struct FamilyWork {
+  Prepared ci, cj;
+  int64_t n_i, n_j;
+  int64_t total_steps;
+  int32_t sym;       // 1: self family (j >= i, weight 2 off the diagonal, 1 on it)
+  int32_t wg_begin, wg_end;
+  int32_t pad_;
+};
+
+struct PairArgs {
+  FamilyWork fam[3];           // DD, DR, RR
+  BinParams bp;
+  unsigned long long *slots;   // [num_workgroups][nbins] 64-bit partial histograms
+  int64_t flush_interval;      // j-steps between flushes of the 32-bit LDS histograms
+  int32_t nbins;
+  int32_t hist_words;          // LDS words of one wave's histogram (>= nbins)
+  int32_t wave_lds_words;      // hist_words + 2 * kQueueCap
+  int32_t pad_;
+};
+
+// ---- launchers (gc_kernels.hip) ----------------------------------------------------------
+hipError_t launch_prepare(const float *ra, const float *dec, int64_t n, void *blob, hipStream_t s);
+// dot64: fp64 dot-product variant; k: galaxies per lane (4 or 8)
+hipError_t launch_pairs(const PairArgs &a, int num_wg, bool dot64, int k, hipStream_t s);
+hipError_t pairs_occupancy(bool dot64, int k, size_t lds_bytes, int *blocks_per_cu);
+hipError_t launch_merge(const unsigned long long *slots, int32_t nbins, const int32_t wg_begin[3],
+                        const int32_t wg_end[3], uint64_t *out[3], hipStream_t s);
+hipError_t launch_totals(const uint64_t *dd, const uint64_t *dr, const uint64_t *rr, int32_t nbins,
+                         uint64_t *totals, hipStream_t s);
+hipError_t launch_omega(const uint64_t *dd, const uint64_t *dr, const uint64_t *rr, int32_t nbins,
+                        int64_t n_d, int64_t n_r, double *omega, hipStream_t s);
+hipError_t launch_eval_core(const float *x32, const double *x64, int64_t n, const BinParams &bp,
+                            bool dot64, int32_t *bin_out, uint8_t *trip_out, int32_t *exact_out,
+                            hipStream_t s);
+
+}  // namespace gc

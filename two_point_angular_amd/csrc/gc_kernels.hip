@@ -1,0 +1,506 @@
+// HIP kernels for gfx950 (MI355X): all-pairs angular-separation histograms.
+//
+// The operation ("CUDA Deep Dive: 10B Galaxy Pairs on an RTX 5080", section "The
+// problem"): for every ordered pair of galaxies, theta = the angle between their
+// radius vectors, binned into nbins bins of width w, for the families DD, DR, RR.
+//
+// Kernels:
+//   prepare_kernel - (alpha, delta) arcmin -> unit radius vector, fp64 math, stored
+//                    as SoA fp32 (correctly rounded) and fp64.
+//   pairs_kernel   - the hot loop.  Persistent grid; every wavefront owns a contiguous
+//                    range of "j-steps" (one j galaxy against an i-block of 64*K
+//                    galaxies held K per lane in VGPRs).  j is wave-uniform, so it is
+//                    streamed through the scalar unit (s_load into SGPRs, used directly
+//                    as VALU operands) instead of being staged in LDS.  Per pair: dot
+//                    product, clamp, arccos core (sqrt times a fitted polynomial), bin
+//                    index, certified guard; ds_add_u32 into the wave's private LDS
+//                    histogram.  Pairs the guard cannot certify are queued in LDS and
+//                    re-binned in fp64, 64 at a time with all lanes busy.
+//   merge_kernel   - sums the per-workgroup 64-bit partial histograms into the outputs.
+//   totals_kernel  - per-family sums (wave-shuffle reduction) for the exact N^2 check.
+//   omega_kernel   - Landy-Szalay estimator in fp64.
+//   eval_core_kernel - the pair kernel's angle-to-bin core on given cosines (diagnostic).
+#include "gc_acos_poly.h"
+#include "gc_internal.h"
+
+namespace gc {
+namespace {
+
+static_assert(GC_ACOS_DEGREE == 6, "acos core is written for a degree-6 polynomial");
+
+typedef __attribute__((address_space(4))) const float cfloat_t;
+typedef __attribute__((address_space(4))) const double cdouble_t;
+
+// Reads through the constant address space: with a wave-uniform index these become
+// scalar-unit loads (s_load_*) whose results feed VALU instructions as SGPR operands.
+// Valid because the prepared catalogs are never written while a pair kernel runs.
+__device__ __forceinline__ float ld_uniform(const float *p, int64_t i) {
+  return ((const cfloat_t *)p)[i];
+}
+__device__ __forceinline__ double ld_uniform(const double *p, int64_t i) {
+  return ((const cdouble_t *)p)[i];
+}
+
+constexpr float kHalfPiF = 1.57079632679489661923f;
+
+// P(a) with acos(a) ~= sqrt(1 - a) * P(a) on [0, 1] (Horner, fp32 FMA).
+__device__ __forceinline__ float acos_poly(float a) {
+  float p = GC_ACOS_C6;
+  p = fmaf(p, a, GC_ACOS_C5);
+  p = fmaf(p, a, GC_ACOS_C4);
+  p = fmaf(p, a, GC_ACOS_C3);
+  p = fmaf(p, a, GC_ACOS_C2);
+  p = fmaf(p, a, GC_ACOS_C1);
+  p = fmaf(p, a, GC_ACOS_C0);
+  return p;
+}
+
+// fp32-dot core.  x is the fp32 dot product of the two fp32 unit vectors.
+//   s  = sqrt(1 - |x|) (clamped at 0),  q = pi/2 - s P(|x|) = pi/2 - acos(|x|)
+//   theta = pi/2 - sign(x) q,  t = theta / w,  tc = clamp(t, 0.5, nbins - 0.5)
+//   k = trunc(tc); recheck iff |tc - round(tc)| * s < g32, i.e. iff an inner bin edge
+//   lies within the certified error bound 2.02 g_x / (s w) + C of t.
+__device__ __forceinline__ void core32(float x, const BinParams &bp, uint32_t &k, bool &trip) {
+  const float a = fabsf(x);
+  const float s = __builtin_amdgcn_sqrtf(__builtin_amdgcn_fmed3f(1.0f - a, 0.0f, 1.0f));
+  const float q = fmaf(-s, acos_poly(a), kHalfPiF);
+  const float t = fmaf(copysignf(q, x), -bp.invw, bp.h);
+  const float tc = __builtin_amdgcn_fmed3f(t, 0.5f, bp.tmax);
+  k = static_cast<uint32_t>(tc);
+  trip = fabsf(tc - __builtin_rintf(tc)) * s < bp.g32;
+}
+
+// fp64-dot core.  x is the fp64 dot product of the fp64 unit vectors; 1 - |x| is formed
+// in fp64 before narrowing, so small angles keep full relative precision.
+//   r = sqrt(1 - |x|) P(|x|) = acos(|x|);  t = r / w (x >= 0) or (pi - r) / w (x < 0).
+//   recheck iff |tc - round(tc)| * s < g64k1 * s + g64k2.
+__device__ __forceinline__ void core64(double x, const BinParams &bp, uint32_t &k, bool &trip) {
+  const double ax = fabs(x);
+  const float y = static_cast<float>(fmax(1.0 - ax, 0.0));
+  const float a = static_cast<float>(ax);
+  const float s = __builtin_amdgcn_sqrtf(y);
+  const float r = s * acos_poly(a);
+  const int hi = __double2hiint(x);
+  const float cr = copysignf(r, __int_as_float(hi));
+  const float off = __int_as_float((hi >> 31) & __float_as_int(bp.pinvw));
+  const float t = fmaf(cr, bp.invw, off);
+  const float tc = __builtin_amdgcn_fmed3f(t, 0.5f, bp.tmax);
+  k = static_cast<uint32_t>(tc);
+  trip = fabsf(tc - __builtin_rintf(tc)) * s < fmaf(s, bp.g64k1, bp.g64k2);
+}
+
+// Exact recheck: the fp64 angle, then truncation and clamping.
+__device__ __forceinline__ uint32_t exact_bin(double x, const BinParams &bp) {
+  const double c = fmin(fmax(x, -1.0), 1.0);
+  const double t = floor(acos(c) * bp.invw64);
+  const double top = static_cast<double>(bp.nbins - 1);
+  return static_cast<uint32_t>(t < top ? t : top);
+}
+
+__device__ __forceinline__ double dot64(const Prepared &a, int64_t i, const Prepared &b, int64_t j) {
+  return fma(a.x64[i], b.x64[j], fma(a.y64[i], b.y64[j], a.z64[i] * b.z64[j]));
+}
+
+// ----------------------------------------------------------------------------- prepare
+__global__ void __launch_bounds__(256) prepare_kernel(const float *__restrict__ ra,
+                                                      const float *__restrict__ dec, int64_t n,
+                                                      int64_t padded, float *x, float *y, float *z,
+                                                      double *x64, double *y64, double *z64) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= padded) return;
+  double ux = 0.0, uy = 0.0, uz = 0.0;
+  if (idx < n) {
+    const double arcmin = 3.14159265358979323846 / 10800.0;
+    const double a = static_cast<double>(ra[idx]) * arcmin;
+    const double d = static_cast<double>(dec[idx]) * arcmin;
+    double sa, ca, sd, cd;
+    sincos(a, &sa, &ca);
+    sincos(d, &sd, &cd);
+    ux = cd * ca;
+    uy = cd * sa;
+    uz = sd;
+  }
+  x[idx] = static_cast<float>(ux);
+  y[idx] = static_cast<float>(uy);
+  z[idx] = static_cast<float>(uz);
+  x64[idx] = ux;
+  y64[idx] = uy;
+  z64[idx] = uz;
+}
+
+// ------------------------------------------------------------------------------- pairs
+struct FastTag { static constexpr bool value = false; };
+struct GenericTag { static constexpr bool value = true; };
+
+template <bool D64> struct Real;
+template <> struct Real<false> { typedef float T; };
+template <> struct Real<true> { typedef double T; };
+
+template <int K, bool D64>
+__global__ void __launch_bounds__(kWGThreads) pairs_kernel(const PairArgs A) {
+  typedef typename Real<D64>::T real;
+  constexpr int BI = kWave * K;       // i-block: galaxies per wave
+  constexpr int JB = D64 ? 4 : 8;     // j galaxies per scalar batch
+  extern __shared__ uint32_t lds[];
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x / kWave;
+  uint32_t *const hist = lds + wv * A.wave_lds_words;
+  uint32_t *const queue = hist + A.hist_words;
+  const int g = blockIdx.x;
+  const int fi = g < A.fam[0].wg_end ? 0 : (g < A.fam[1].wg_end ? 1 : 2);
+  const FamilyWork &F = A.fam[fi];
+  const BinParams &bp = A.bp;
+  const uint32_t W = F.sym ? 2u : 1u;
+
+  unsigned long long *const slot = A.slots + static_cast<size_t>(g) * A.nbins;
+  for (int b = threadIdx.x; b < A.nbins; b += kWGThreads) slot[b] = 0ull;
+  for (int b = lane; b < A.hist_words; b += kWave) hist[b] = 0u;
+  __threadfence();
+  __syncthreads();
+
+  // This wave's share [s, s_end) of the family's j-steps: floor(T v / V) .. floor(T (v+1) / V).
+  const int64_t V = static_cast<int64_t>(F.wg_end - F.wg_begin) * kWavesPerWG;
+  const int64_t v = static_cast<int64_t>(g - F.wg_begin) * kWavesPerWG + wv;
+  const int64_t tq = F.total_steps / V, tr = F.total_steps % V;
+  int64_t s = tq * v + (tr * v) / V;
+  const int64_t s_end = tq * (v + 1) + (tr * (v + 1)) / V;
+
+  // Locate block b and its j: cross family L(b) = n_j; self family L(b) = n - b BI,
+  // prefix P(b) = b n - BI b (b - 1) / 2.
+  int64_t b = 0, j = 0;
+  if (s < s_end) {
+    if (!F.sym) {
+      b = s / F.n_j;
+      j = s - b * F.n_j;
+    } else {
+      int64_t lo = 0, hi = (F.n_i + BI - 1) / BI - 1;
+      while (lo < hi) {
+        const int64_t mid = (lo + hi + 1) >> 1;
+        const int64_t pm = mid * F.n_j - static_cast<int64_t>(BI) * mid * (mid - 1) / 2;
+        if (pm <= s) lo = mid; else hi = mid - 1;
+      }
+      b = lo;
+      j = b * BI + (s - (b * F.n_j - static_cast<int64_t>(BI) * b * (b - 1) / 2));
+    }
+  }
+
+  int64_t since_flush = 0;
+  int qhead = 0, qcount = 0;
+  int64_t i0 = 0;
+  real ix[K], iy[K], iz[K];
+
+  // Re-bin up to 64 queued pairs exactly (one per lane) and move their counts.
+  auto drain = [&](int c) __attribute__((always_inline)) {
+    __builtin_amdgcn_wave_barrier();
+    if (lane < c) {
+      const int e = (qhead + lane) & (kQueueCap - 1);
+      const uint32_t jj = queue[2 * e];
+      const uint32_t p = queue[2 * e + 1];
+      const uint32_t kf = p & 0xffffu;
+      const uint32_t ke = exact_bin(dot64(F.ci, i0 + (p >> 16), F.cj, jj), bp);
+      if (ke != kf) {
+        atomicSub(hist + kf, W);
+        atomicAdd(hist + ke, W);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    qhead = (qhead + c) & (kQueueCap - 1);
+    qcount -= c;
+  };
+  auto drain_all = [&]() __attribute__((always_inline)) {
+    while (qcount > 0) drain(qcount < kWave ? qcount : kWave);
+    qhead = 0;
+  };
+  // Add this wave's 32-bit LDS histogram into the workgroup's 64-bit slot; zero it.
+  auto flush = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_wave_barrier();
+    for (int bb = lane; bb < A.nbins; bb += kWave) {
+      const uint32_t c = hist[bb];
+      if (c) {
+        atomicAdd(slot + bb, static_cast<unsigned long long>(c));
+        hist[bb] = 0u;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  };
+
+  // One j against this lane's K i-galaxies.
+  auto step = [&](real xj, real yj, real zj, int64_t jg, auto generic_tag) __attribute__((always_inline)) {
+    constexpr bool GENERIC = decltype(generic_tag)::value;
+    uint32_t kk[K];
+    bool tp[K];
+    bool any = false;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const real x = fma(ix[k], xj, fma(iy[k], yj, iz[k] * zj));
+      if constexpr (D64) core64(x, bp, kk[k], tp[k]);
+      else core32(x, bp, kk[k], tp[k]);
+      if constexpr (GENERIC) {
+        const int64_t ig = i0 + lane + kWave * k;
+        const bool valid = ig < F.n_i && (!F.sym || jg >= ig);
+        const bool self = jg == ig;
+        if (self) kk[k] = 0u;  // a galaxy with itself: separation 0
+        tp[k] = tp[k] && valid && !self;
+        if (valid) atomicAdd(hist + kk[k], self ? 1u : W);
+      } else {
+        atomicAdd(hist + kk[k], W);
+      }
+      any = any || tp[k];
+    }
+    if (__ballot(any)) {
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const unsigned long long m = __ballot(tp[k]);
+        if (m) {
+          if (tp[k]) {
+            const uint32_t below = __builtin_amdgcn_mbcnt_hi(
+                static_cast<uint32_t>(m >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+            const int e = (qhead + qcount + static_cast<int>(below)) & (kQueueCap - 1);
+            queue[2 * e] = static_cast<uint32_t>(jg);
+            queue[2 * e + 1] = (static_cast<uint32_t>(lane + kWave * k) << 16) | kk[k];
+          }
+          qcount += __popcll(m);
+          if (qcount >= kWave) drain(kWave);
+        }
+      }
+    }
+  };
+
+  auto run = [&](int64_t ja, int64_t jb, auto generic_tag) __attribute__((always_inline)) {
+    int64_t jj = ja;
+    while (jj < jb) {
+      if (jj + JB <= jb) {
+        real xs[JB], ys[JB], zs[JB];
+#pragma unroll
+        for (int u = 0; u < JB; ++u) {
+          if constexpr (D64) {
+            xs[u] = ld_uniform(F.cj.x64, jj + u);
+            ys[u] = ld_uniform(F.cj.y64, jj + u);
+            zs[u] = ld_uniform(F.cj.z64, jj + u);
+          } else {
+            xs[u] = ld_uniform(F.cj.x, jj + u);
+            ys[u] = ld_uniform(F.cj.y, jj + u);
+            zs[u] = ld_uniform(F.cj.z, jj + u);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < JB; ++u) step(xs[u], ys[u], zs[u], jj + u, generic_tag);
+        jj += JB;
+        since_flush += JB;
+      } else {
+        real xs, ys, zs;
+        if constexpr (D64) {
+          xs = ld_uniform(F.cj.x64, jj); ys = ld_uniform(F.cj.y64, jj); zs = ld_uniform(F.cj.z64, jj);
+        } else {
+          xs = ld_uniform(F.cj.x, jj); ys = ld_uniform(F.cj.y, jj); zs = ld_uniform(F.cj.z, jj);
+        }
+        step(xs, ys, zs, jj, generic_tag);
+        jj += 1;
+        since_flush += 1;
+      }
+      if (since_flush >= A.flush_interval) {
+        drain_all();
+        flush();
+        since_flush = 0;
+      }
+    }
+  };
+
+  while (s < s_end) {
+    const int64_t nsteps = (s_end - s) < (F.n_j - j) ? (s_end - s) : (F.n_j - j);
+    const int64_t j1 = j + nsteps;
+    i0 = b * BI;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int64_t ig = i0 + lane + kWave * k;
+      const int64_t il = ig < F.n_i ? ig : i0;
+      if constexpr (D64) {
+        ix[k] = F.ci.x64[il]; iy[k] = F.ci.y64[il]; iz[k] = F.ci.z64[il];
+      } else {
+        ix[k] = F.ci.x[il]; iy[k] = F.ci.y[il]; iz[k] = F.ci.z[il];
+      }
+    }
+    const bool full = i0 + BI <= F.n_i;
+    if (F.sym) {
+      // j in [i0, i0 + BI) meets this block's own galaxies: per-pair weights there.
+      const int64_t dz = j1 < i0 + BI ? j1 : i0 + BI;
+      if (!full) {
+        run(j, j1, GenericTag());
+      } else {
+        if (j < dz) run(j, dz, GenericTag());
+        const int64_t jf = j > dz ? j : dz;
+        if (jf < j1) run(jf, j1, FastTag());
+      }
+    } else {
+      if (full) run(j, j1, FastTag());
+      else run(j, j1, GenericTag());
+    }
+    drain_all();
+    s += nsteps;
+    ++b;
+    j = F.sym ? b * BI : 0;
+  }
+  flush();
+}
+
+// ------------------------------------------------------------------------------- merge
+// out_f[bin] = sum of slots of family f's workgroups.  Block: 256 threads = 4 waves over
+// the slot list, one bin per lane; grid (ceil(nbins / 64), 3).
+__global__ void __launch_bounds__(256) merge_kernel(const unsigned long long *__restrict__ slots,
+                                                    int32_t nbins, int32_t b0, int32_t b1, int32_t b2,
+                                                    int32_t e0, int32_t e1, int32_t e2, uint64_t *o0,
+                                                    uint64_t *o1, uint64_t *o2) {
+  __shared__ unsigned long long part[4][kWave];
+  const int f = blockIdx.y;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x / kWave;
+  const int bin = blockIdx.x * kWave + lane;
+  const int gb = f == 0 ? b0 : (f == 1 ? b1 : b2);
+  const int ge = f == 0 ? e0 : (f == 1 ? e1 : e2);
+  unsigned long long acc = 0ull;
+  if (bin < nbins)
+    for (int gg = gb + wv; gg < ge; gg += 4) acc += slots[static_cast<size_t>(gg) * nbins + bin];
+  part[wv][lane] = acc;
+  __syncthreads();
+  if (wv == 0 && bin < nbins) {
+    uint64_t *o = f == 0 ? o0 : (f == 1 ? o1 : o2);
+    o[bin] = part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane];
+  }
+}
+
+// ------------------------------------------------------------------------------ totals
+__global__ void __launch_bounds__(256) totals_kernel(const uint64_t *dd, const uint64_t *dr,
+                                                     const uint64_t *rr, int32_t nbins,
+                                                     uint64_t *totals) {
+  __shared__ unsigned long long part[4];
+  const int f = blockIdx.x;
+  const uint64_t *h = f == 0 ? dd : (f == 1 ? dr : rr);
+  unsigned long long acc = 0ull;
+  for (int bb = threadIdx.x; bb < nbins; bb += 256) acc += h[bb];
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, kWave);
+  if ((threadIdx.x & (kWave - 1)) == 0) part[threadIdx.x / kWave] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) totals[f] = part[0] + part[1] + part[2] + part[3];
+}
+
+// ------------------------------------------------------------------------------- omega
+__global__ void __launch_bounds__(256) omega_kernel(const uint64_t *dd, const uint64_t *dr,
+                                                    const uint64_t *rr, int32_t nbins, int64_t n_d,
+                                                    int64_t n_r, double *omega) {
+  const int bb = blockIdx.x * blockDim.x + threadIdx.x;
+  if (bb >= nbins) return;
+  const double d = static_cast<double>(dd[bb]);
+  const double m = static_cast<double>(dr[bb]);
+  const double r = static_cast<double>(rr[bb]);
+  double w;
+  if (rr[bb] == 0) {
+    w = __builtin_nan("");
+  } else if (n_d == n_r) {
+    w = (d - 2.0 * m + r) / r;
+  } else {
+    const double nd = static_cast<double>(n_d), nr = static_cast<double>(n_r);
+    const double frr = r / (nr * nr);
+    w = (d / (nd * nd) - 2.0 * (m / (nd * nr)) + frr) / frr;
+  }
+  omega[bb] = w;
+}
+
+// -------------------------------------------------------------------------- eval core
+__global__ void __launch_bounds__(256) eval_core_kernel(const float *x32, const double *x64,
+                                                        int64_t n, const BinParams bp, int dot64,
+                                                        int32_t *bin_out, uint8_t *trip_out,
+                                                        int32_t *exact_out) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= n) return;
+  uint32_t k;
+  bool trip;
+  double xe;
+  if (dot64) {
+    xe = x64[idx];
+    core64(xe, bp, k, trip);
+  } else {
+    const float xf = x32[idx];
+    xe = static_cast<double>(xf);
+    core32(xf, bp, k, trip);
+  }
+  bin_out[idx] = static_cast<int32_t>(k);
+  trip_out[idx] = trip ? 1 : 0;
+  if (exact_out) exact_out[idx] = static_cast<int32_t>(exact_bin(xe, bp));
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------- launchers
+hipError_t launch_prepare(const float *ra, const float *dec, int64_t n, void *blob, hipStream_t st) {
+  const int64_t p = padded_count(n);
+  char *b = static_cast<char *>(blob);
+  float *x = reinterpret_cast<float *>(b);
+  double *x64 = reinterpret_cast<double *>(b + 12 * p);
+  const int64_t blocks = (p + 255) / 256;
+  hipLaunchKernelGGL(prepare_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, ra, dec, n,
+                     p, x, x + p, x + 2 * p, x64, x64 + p, x64 + 2 * p);
+  return hipGetLastError();
+}
+
+template <int K, bool D64> static void *pairs_fn() {
+  return reinterpret_cast<void *>(&pairs_kernel<K, D64>);
+}
+
+static const void *select_pairs(bool dot64, int k) {
+  if (dot64) return k == 4 ? pairs_fn<4, true>() : pairs_fn<8, true>();
+  return k == 4 ? pairs_fn<4, false>() : pairs_fn<8, false>();
+}
+
+hipError_t pairs_occupancy(bool dot64, int k, size_t lds_bytes, int *blocks_per_cu) {
+  const void *fn = select_pairs(dot64, k);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     static_cast<int>(lds_bytes));
+  if (e != hipSuccess) return e;
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, fn, kWGThreads, lds_bytes);
+}
+
+hipError_t launch_pairs(const PairArgs &a, int num_wg, bool dot64, int k, hipStream_t st) {
+  const size_t lds = static_cast<size_t>(kWavesPerWG) * a.wave_lds_words * sizeof(uint32_t);
+  if (dot64) {
+    if (k == 4) hipLaunchKernelGGL((pairs_kernel<4, true>), dim3(num_wg), dim3(kWGThreads), lds, st, a);
+    else hipLaunchKernelGGL((pairs_kernel<8, true>), dim3(num_wg), dim3(kWGThreads), lds, st, a);
+  } else {
+    if (k == 4) hipLaunchKernelGGL((pairs_kernel<4, false>), dim3(num_wg), dim3(kWGThreads), lds, st, a);
+    else hipLaunchKernelGGL((pairs_kernel<8, false>), dim3(num_wg), dim3(kWGThreads), lds, st, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const unsigned long long *slots, int32_t nbins, const int32_t wb[3],
+                        const int32_t we[3], uint64_t *out[3], hipStream_t st) {
+  dim3 grid((nbins + kWave - 1) / kWave, 3);
+  hipLaunchKernelGGL(merge_kernel, grid, dim3(256), 0, st, slots, nbins, wb[0], wb[1], wb[2], we[0], we[1],
+                     we[2], out[0], out[1], out[2]);
+  return hipGetLastError();
+}
+
+hipError_t launch_totals(const uint64_t *dd, const uint64_t *dr, const uint64_t *rr, int32_t nbins,
+                         uint64_t *totals, hipStream_t st) {
+  hipLaunchKernelGGL(totals_kernel, dim3(3), dim3(256), 0, st, dd, dr, rr, nbins, totals);
+  return hipGetLastError();
+}
+
+hipError_t launch_omega(const uint64_t *dd, const uint64_t *dr, const uint64_t *rr, int32_t nbins,
+                        int64_t n_d, int64_t n_r, double *omega, hipStream_t st) {
+  hipLaunchKernelGGL(omega_kernel, dim3((nbins + 255) / 256), dim3(256), 0, st, dd, dr, rr, nbins, n_d,
+                     n_r, omega);
+  return hipGetLastError();
+}
+
+hipError_t launch_eval_core(const float *x32, const double *x64, int64_t n, const BinParams &bp,
+                            bool dot64, int32_t *bin_out, uint8_t *trip_out, int32_t *exact_out,
+                            hipStream_t st) {
+  const int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(eval_core_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, x32, x64, n,
+                     bp, dot64 ? 1 : 0, bin_out, trip_out, exact_out);
+  return hipGetLastError();
+}
+
+}  // namespace gc
