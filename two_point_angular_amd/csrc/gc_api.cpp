@@ -205,7 +205,7 @@ gc_status gc_histogram_dd_dr_rr_tuned(const void *prep_d, int64_t n_d, const voi
   memset(&a, 0, sizeof(a));
   a.nbins = nbins;
   a.hist_words = (nbins + 63) / 64 * 64;
-  a.wave_lds_words = a.hist_words + 2 * kQueueCap;
+  a.wave_lds_words = a.hist_words + kQueueWords;
   a.bp = make_bins(nbins, w_deg);
   a.slots = static_cast<unsigned long long *>(workspace);
   const int64_t max_inc = 2ll * kWave * k;  // largest increase of one bin per j-step

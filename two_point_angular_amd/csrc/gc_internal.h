@@ -11,7 +11,8 @@ namespace gc {
 constexpr int kWave = 64;            // CDNA wavefront width
 constexpr int kWavesPerWG = 4;       // pair-kernel workgroup = 4 independent wavefronts
 constexpr int kWGThreads = kWave * kWavesPerWG;
-constexpr int kQueueCap = 128;       // per-wave recheck queue entries (power of two, >= 2*64)
+constexpr int kMaxK = 8;             // largest i galaxies per lane
+constexpr int kQueueWords = 2 * kWave * (kMaxK + 1);  // per-wave recheck queue (8-byte entries)
 constexpr int kMaxWorkgroups = 2048; // partial-histogram slots held by the workspace
 constexpr int kMaxBlocksPerCU = 8;
 
@@ -76,7 +77,7 @@ struct PairArgs {
   int64_t flush_interval;      // j-steps between flushes of the 32-bit LDS histograms
   int32_t nbins;
   int32_t hist_words;          // LDS words of one wave's histogram (>= nbins)
-  int32_t wave_lds_words;      // hist_words + 2 * kQueueCap
+  int32_t wave_lds_words;      // hist_words + kQueueWords
   int32_t pad_;
 };
 

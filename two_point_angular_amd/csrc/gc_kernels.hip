@@ -136,8 +136,32 @@ template <bool D64> struct Real;
 template <> struct Real<false> { typedef float T; };
 template <> struct Real<true> { typedef double T; };
 
+// Re-bin c <= 64 queued pairs of one wave exactly in fp64 (one pair per lane) and move
+// their counts from the fast-path bin to the exact bin.  Queue entry e (a ring of `cap`
+// entries): word 2e = j, word 2e+1 = (i - i0) << 16 | fast-path bin.
+__device__ __forceinline__ void drain_queue(uint32_t *hist, const uint32_t *queue, int qhead, int c, int cap,
+                                            const Prepared &ci, const Prepared &cj, int64_t i0, uint32_t w,
+                                            const BinParams &bp) {
+  const int lane = threadIdx.x & (kWave - 1);
+  __builtin_amdgcn_wave_barrier();
+  if (lane < c) {
+    int e = qhead + lane;
+    if (e >= cap) e -= cap;
+    const uint32_t jj = queue[2 * e];
+    const uint32_t p = queue[2 * e + 1];
+    const uint32_t kf = p & 0xffffu;
+    const uint32_t ke = exact_bin(dot64(ci, i0 + (p >> 16), cj, jj), bp);
+    if (ke != kf) {
+      atomicSub(hist + kf, w);
+      atomicAdd(hist + ke, w);
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
 template <int K, bool D64>
-__global__ void __launch_bounds__(kWGThreads) pairs_kernel(const PairArgs A) {
+__global__ void __launch_bounds__(kWGThreads)
+pairs_kernel(const PairArgs A) {
   typedef typename Real<D64>::T real;
   constexpr int BI = kWave * K;       // i-block: galaxies per wave
   constexpr int JB = D64 ? 4 : 8;     // j galaxies per scalar batch
@@ -190,22 +214,11 @@ __global__ void __launch_bounds__(kWGThreads) pairs_kernel(const PairArgs A) {
   int64_t i0 = 0;
   real ix[K], iy[K], iz[K];
 
-  // Re-bin up to 64 queued pairs exactly (one per lane) and move their counts.
+  constexpr int QCAP = kWave * (K + 1);  // < 64 left over + up to 64 K from one j-step
   auto drain = [&](int c) __attribute__((always_inline)) {
-    __builtin_amdgcn_wave_barrier();
-    if (lane < c) {
-      const int e = (qhead + lane) & (kQueueCap - 1);
-      const uint32_t jj = queue[2 * e];
-      const uint32_t p = queue[2 * e + 1];
-      const uint32_t kf = p & 0xffffu;
-      const uint32_t ke = exact_bin(dot64(F.ci, i0 + (p >> 16), F.cj, jj), bp);
-      if (ke != kf) {
-        atomicSub(hist + kf, W);
-        atomicAdd(hist + ke, W);
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-    qhead = (qhead + c) & (kQueueCap - 1);
+    drain_queue(hist, queue, qhead, c, QCAP, F.ci, F.cj, i0, W, bp);
+    qhead += c;
+    if (qhead >= QCAP) qhead -= QCAP;
     qcount -= c;
   };
   auto drain_all = [&]() __attribute__((always_inline)) {
@@ -224,6 +237,13 @@ __global__ void __launch_bounds__(kWGThreads) pairs_kernel(const PairArgs A) {
     }
     __builtin_amdgcn_wave_barrier();
   };
+  auto load_j = [&](int64_t jj, real &x, real &y, real &z) __attribute__((always_inline)) {
+    if constexpr (D64) {
+      x = ld_uniform(F.cj.x64, jj); y = ld_uniform(F.cj.y64, jj); z = ld_uniform(F.cj.z64, jj);
+    } else {
+      x = ld_uniform(F.cj.x, jj); y = ld_uniform(F.cj.y, jj); z = ld_uniform(F.cj.z, jj);
+    }
+  };
 
   // One j against this lane's K i-galaxies.
   auto step = [&](real xj, real yj, real zj, int64_t jg, auto generic_tag) __attribute__((always_inline)) {
@@ -239,8 +259,8 @@ __global__ void __launch_bounds__(kWGThreads) pairs_kernel(const PairArgs A) {
       if constexpr (GENERIC) {
         const int64_t ig = i0 + lane + kWave * k;
         const bool valid = ig < F.n_i && (!F.sym || jg >= ig);
-        const bool self = jg == ig;
-        if (self) kk[k] = 0u;  // a galaxy with itself: separation 0
+        const bool self = F.sym && jg == ig;  // only a self family pairs a galaxy with itself
+        if (self) kk[k] = 0u;                  // separation 0
         tp[k] = tp[k] && valid && !self;
         if (valid) atomicAdd(hist + kk[k], self ? 1u : W);
       } else {
@@ -256,54 +276,72 @@ __global__ void __launch_bounds__(kWGThreads) pairs_kernel(const PairArgs A) {
           if (tp[k]) {
             const uint32_t below = __builtin_amdgcn_mbcnt_hi(
                 static_cast<uint32_t>(m >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
-            const int e = (qhead + qcount + static_cast<int>(below)) & (kQueueCap - 1);
+            int e = qhead + qcount + static_cast<int>(below);
+            if (e >= QCAP) e -= QCAP;
             queue[2 * e] = static_cast<uint32_t>(jg);
             queue[2 * e + 1] = (static_cast<uint32_t>(lane + kWave * k) << 16) | kk[k];
           }
           qcount += __popcll(m);
-          if (qcount >= kWave) drain(kWave);
         }
       }
+      while (qcount >= kWave) drain(kWave);
     }
   };
 
-  auto run = [&](int64_t ja, int64_t jb, auto generic_tag) __attribute__((always_inline)) {
+  auto check_flush = [&]() __attribute__((always_inline)) {
+    if (since_flush >= A.flush_interval) {
+      drain_all();
+      flush();
+      since_flush = 0;
+    }
+  };
+
+  // Diagonal / ragged j-steps: per-pair weights; rare, so a rolled loop.
+  auto run_generic = [&](int64_t ja, int64_t jb) __attribute__((always_inline)) {
+#pragma unroll 1
+    for (int64_t jj = ja; jj < jb; ++jj) {
+      real xs, ys, zs;
+      load_j(jj, xs, ys, zs);
+      step(xs, ys, zs, jj, GenericTag());
+      since_flush += 1;
+      check_flush();
+    }
+  };
+
+  // Off-diagonal j-steps of a full i-block: batches of JB j galaxies read by the scalar
+  // unit, the next batch requested before the current one is processed.
+  auto run_fast = [&](int64_t ja, int64_t jb) __attribute__((always_inline)) {
     int64_t jj = ja;
-    while (jj < jb) {
-      if (jj + JB <= jb) {
-        real xs[JB], ys[JB], zs[JB];
+    if (jj + JB <= jb) {
+      real xs[JB], ys[JB], zs[JB];
 #pragma unroll
-        for (int u = 0; u < JB; ++u) {
-          if constexpr (D64) {
-            xs[u] = ld_uniform(F.cj.x64, jj + u);
-            ys[u] = ld_uniform(F.cj.y64, jj + u);
-            zs[u] = ld_uniform(F.cj.z64, jj + u);
-          } else {
-            xs[u] = ld_uniform(F.cj.x, jj + u);
-            ys[u] = ld_uniform(F.cj.y, jj + u);
-            zs[u] = ld_uniform(F.cj.z, jj + u);
-          }
+      for (int u = 0; u < JB; ++u) load_j(jj + u, xs[u], ys[u], zs[u]);
+      while (true) {
+        const bool more = jj + 2 * JB <= jb;
+        real nx[JB], ny[JB], nz[JB];
+        if (more) {
+#pragma unroll
+          for (int u = 0; u < JB; ++u) load_j(jj + JB + u, nx[u], ny[u], nz[u]);
         }
 #pragma unroll
-        for (int u = 0; u < JB; ++u) step(xs[u], ys[u], zs[u], jj + u, generic_tag);
+        for (int u = 0; u < JB; ++u) step(xs[u], ys[u], zs[u], jj + u, FastTag());
         jj += JB;
         since_flush += JB;
-      } else {
-        real xs, ys, zs;
-        if constexpr (D64) {
-          xs = ld_uniform(F.cj.x64, jj); ys = ld_uniform(F.cj.y64, jj); zs = ld_uniform(F.cj.z64, jj);
-        } else {
-          xs = ld_uniform(F.cj.x, jj); ys = ld_uniform(F.cj.y, jj); zs = ld_uniform(F.cj.z, jj);
+        check_flush();
+        if (!more) break;
+#pragma unroll
+        for (int u = 0; u < JB; ++u) {
+          xs[u] = nx[u]; ys[u] = ny[u]; zs[u] = nz[u];
         }
-        step(xs, ys, zs, jj, generic_tag);
-        jj += 1;
-        since_flush += 1;
       }
-      if (since_flush >= A.flush_interval) {
-        drain_all();
-        flush();
-        since_flush = 0;
-      }
+    }
+#pragma unroll 1
+    for (; jj < jb; ++jj) {
+      real xs, ys, zs;
+      load_j(jj, xs, ys, zs);
+      step(xs, ys, zs, jj, FastTag());
+      since_flush += 1;
+      check_flush();
     }
   };
 
@@ -326,15 +364,15 @@ __global__ void __launch_bounds__(kWGThreads) pairs_kernel(const PairArgs A) {
       // j in [i0, i0 + BI) meets this block's own galaxies: per-pair weights there.
       const int64_t dz = j1 < i0 + BI ? j1 : i0 + BI;
       if (!full) {
-        run(j, j1, GenericTag());
+        run_generic(j, j1);
       } else {
-        if (j < dz) run(j, dz, GenericTag());
+        if (j < dz) run_generic(j, dz);
         const int64_t jf = j > dz ? j : dz;
-        if (jf < j1) run(jf, j1, FastTag());
+        if (jf < j1) run_fast(jf, j1);
       }
     } else {
-      if (full) run(j, j1, FastTag());
-      else run(j, j1, GenericTag());
+      if (full) run_fast(j, j1);
+      else run_generic(j, j1);
     }
     drain_all();
     s += nsteps;
