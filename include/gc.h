@@ -141,15 +141,16 @@ gc_status gc_omega(const uint64_t *d_dd, const uint64_t *d_dr, const uint64_t *d
  * Evaluate the pair kernel's per-pair angle-to-bin core on given cosines, exactly as
  * the pair kernel does, for numerical verification of its guard.
  *   dot_precision 32: reads d_x32 (n fp32 cosines); 64: reads d_x64 (n fp64 cosines).
- *   d_bin_out : device, n int32: the fast-path bin.
- *   d_trip_out: device, n uint8: 1 where the guard sends the pair to the exact fp64
- *               recheck.
- *   d_exact_out: device, n int32 (may be null): the exact fp64 recheck's bin of the
- *               same cosine (fp32 cosines are widened exactly). */
+ *   d_bin_out  : device, n int32: the fast-path bin.
+ *   d_trip_out : device, n uint8: 1 where the guard sends the pair to the exact recheck.
+ *   d_exact_out: device, n int32, or null: the exact recheck's bin of the same cosine
+ *                (fp32 cosines are widened exactly), found from the fast-path bin by the
+ *                kernel's own edge-cosine search.  Needs d_workspace (at least
+ *                gc_workspace_bytes(nbins) bytes, GC_ALIGNMENT-aligned) for the edge table. */
 gc_status gc_eval_angle_core(const float *d_x32, const double *d_x64, int64_t n,
                              int32_t nbins, double bin_width_deg, int32_t dot_precision,
                              int32_t *d_bin_out, uint8_t *d_trip_out, int32_t *d_exact_out,
-                             gc_stream_t stream);
+                             void *d_workspace, size_t workspace_bytes, gc_stream_t stream);
 
 /* ----------------------------------------------------------------- status ---- */
 const char *gc_status_string(gc_status status);

@@ -46,7 +46,7 @@ def test_sizes(lib):
     assert lib.gc_prepared_bytes(10**5) % gc.ALIGNMENT == 0
     assert lib.gc_workspace_bytes(0) == 0
     assert lib.gc_workspace_bytes(gc.MAX_BINS + 1) == 0
-    assert lib.gc_workspace_bytes(720) == 2048 * 720 * 8
+    assert lib.gc_workspace_bytes(720) == 2048 * 720 * 8 + (721 * 8 + 255) // 256 * 256
 
 
 def test_status_strings(lib):
@@ -117,7 +117,10 @@ def test_totals_omega_core_validation(lib):
     assert lib.gc_omega(P(A), P(A), P(A), 10, -1, 1, P(A), None) == INVALID
     assert lib.gc_omega(P(A), P(A), None, 10, 1, 1, P(A), None) == INVALID
     assert lib.gc_omega(P(A), P(A), P(A), 10, 1, 1, P(A + 4), None) == INVALID
-    assert lib.gc_eval_angle_core(P(A), None, 10, 720, 0.25, 16, P(A), P(A), None, None) == INVALID
-    assert lib.gc_eval_angle_core(None, None, 10, 720, 0.25, 32, P(A), P(A), None, None) == INVALID
-    assert lib.gc_eval_angle_core(P(A), None, 0, 720, 0.25, 32, P(A), P(A), None, None) == OK
-    assert lib.gc_eval_angle_core(P(A), None, 10, 0, 0.25, 32, P(A), P(A), None, None) == INVALID
+    ev = lambda *a: lib.gc_eval_angle_core(*a)  # noqa: E731
+    assert ev(P(A), None, 10, 720, 0.25, 16, P(A), P(A), None, None, 0, None) == INVALID
+    assert ev(None, None, 10, 720, 0.25, 32, P(A), P(A), None, None, 0, None) == INVALID
+    assert ev(P(A), None, 0, 720, 0.25, 32, P(A), P(A), None, None, 0, None) == OK
+    assert ev(P(A), None, 10, 0, 0.25, 32, P(A), P(A), None, None, 0, None) == INVALID
+    assert ev(P(A), None, 10, 720, 0.25, 32, P(A), P(A), P(A), None, 0, None) == INVALID     # exact, no ws
+    assert ev(P(A), None, 10, 720, 0.25, 32, P(A), P(A), P(A), P(A), 100, None) == WORKSPACE

@@ -96,7 +96,7 @@ def load():
                                               ctypes.POINTER(_Tuning), vp]),
         "gc_histogram_totals": (i32, [vp, vp, vp, i32, vp, vp]),
         "gc_omega": (i32, [vp, vp, vp, i32, i64, i64, vp, vp]),
-        "gc_eval_angle_core": (i32, [vp, vp, i64, i32, ctypes.c_double, i32, vp, vp, vp, vp]),
+        "gc_eval_angle_core": (i32, [vp, vp, i64, i32, ctypes.c_double, i32, vp, vp, vp, vp, sz, vp]),
         "gc_status_string": (ctypes.c_char_p, [i32]),
         "gc_last_device_error": (ctypes.c_int, []),
         "gc_version": (ctypes.c_char_p, []),
@@ -213,7 +213,9 @@ def eval_angle_core(x, nbins: int, bin_width_deg: float, with_exact: bool = True
     exact = torch.empty(n, dtype=torch.int32, device=x.device) if with_exact else None
     x32 = x if dot == 32 else None
     x64 = x if dot == 64 else None
+    ws = torch.empty(workspace_bytes(nbins), dtype=torch.uint8, device=x.device) if with_exact else None
     _check(load().gc_eval_angle_core(_ptr(x32), _ptr(x64), n, int(nbins), float(bin_width_deg), dot,
-                                     _ptr(bins), _ptr(trip), _ptr(exact), _stream(stream)),
+                                     _ptr(bins), _ptr(trip), _ptr(exact), _ptr(ws),
+                                     ws.numel() if ws is not None else 0, _stream(stream)),
            "gc_eval_angle_core")
     return bins, trip, exact

@@ -5,7 +5,8 @@ The pair kernel evaluates, for a = |x| in [0, 1],
     acos(a) ~= sqrt(1 - a) * P(a),
 
 with P a degree-6 polynomial minimising max |P(a) - acos(a)/sqrt(1 - a)| over [0, 1]
-(a linear-programming minimax fit on a dense grid, in the Chebyshev basis).  The
+(a linear-programming minimax fit on a dense grid, with the coefficients rounded to fp32
+one at a time and the rest refitted).  The
 ratio acos(a)/sqrt(1 - a) is smooth on [0, 1] (it tends to sqrt(2) at a = 1), so a
 low-degree polynomial suffices; sqrt(1 - a) carries the square-root behaviour of acos
 at a = 1.  This is the same square-root-times-polynomial form as the handbook
@@ -41,25 +42,47 @@ def target(a):
     return out
 
 
-def fit(degree=DEGREE):
-    a = np.unique(np.concatenate([np.linspace(0.0, 1.0, 40001), 1.0 - np.logspace(-14, -1, 4000)]))
-    u = 2.0 * a - 1.0
-    T = np.polynomial.chebyshev.chebvander(u, degree)
-    g = target(a)
-    n = degree + 1
+def _lp_correction(V, resid):
+    """Minimax LP for d with V d ~= resid; the residual is normalised to unit size first,
+    because the solver's absolute tolerances (~1e-7) are as large as the errors fitted."""
+    scale = float(np.max(np.abs(resid))) or 1.0
+    r = resid / scale
+    n = V.shape[1]
     c = np.zeros(n + 1)
     c[-1] = 1.0
-    A = np.vstack([np.hstack([T, -np.ones((len(a), 1))]), np.hstack([-T, -np.ones((len(a), 1))])])
-    b = np.concatenate([g, -g])
+    A = np.vstack([np.hstack([V, -np.ones((len(r), 1))]), np.hstack([-V, -np.ones((len(r), 1))])])
+    b = np.concatenate([r, -r])
     res = linprog(c, A_ub=A, b_ub=b, bounds=[(None, None)] * n + [(0, None)], method="highs")
     if not res.success:
         raise RuntimeError(res.message)
-    cheb = res.x[:n]
-    # Chebyshev series in u = 2a - 1  ->  power series in a
-    mono_u = np.polynomial.chebyshev.cheb2poly(cheb)
-    mono_a = np.polynomial.polynomial.polycompose(mono_u, [-1.0, 2.0]) if hasattr(
-        np.polynomial.polynomial, "polycompose") else _compose(mono_u)
-    return mono_a
+    return res.x[:n] * scale
+
+
+def _fit_free(a, g, degree, fixed, passes=4):
+    """Minimax power-series coefficients of P with fixed[k] (not None) held at that value."""
+    n = degree + 1
+    V = np.vander(a, n, increasing=True)
+    free = [k for k in range(n) if fixed[k] is None]
+    coef = np.array([0.0 if f is None else f for f in fixed])
+    for _ in range(passes):
+        resid = g - V @ coef
+        d = _lp_correction(V[:, free], resid)
+        coef[free] += d
+    return coef
+
+
+def fit(degree=DEGREE):
+    """Minimax fit, then fp32 rounding one coefficient at a time (lowest order first), each
+    time re-solving the still-free coefficients, so the rounding error is absorbed."""
+    a = np.unique(np.concatenate([np.linspace(0.0, 1.0, 20001), 1.0 - np.logspace(-14, -1, 2000)]))
+    g = target(a)
+    fixed = [None] * (degree + 1)
+    coef = _fit_free(a, g, degree, fixed)
+    for k in range(degree + 1):
+        fixed[k] = float(np.float32(coef[k]))
+        if k < degree:
+            coef = _fit_free(a, g, degree, fixed)
+    return np.array(fixed, dtype=np.float64)
 
 
 def _compose(mono_u):

@@ -90,7 +90,6 @@ BinParams make_bins(int32_t nbins, double w_deg) {
   bp.h = static_cast<float>((kPi / 2.0) / w_rad);
   bp.pinvw = static_cast<float>(kPi / w_rad);
   bp.tmax = static_cast<float>(nbins) - 0.5f;
-  bp.invw64 = 1.0 / w_rad;
   // fp32-dot guard
   const double g_x = 5.0 * kTwoM24 * (1.0 + 1e-6) + 1e-12;
   // core error: exhaustive emulated bound plus one ulp of hardware sqrt (times P <= pi/2)
@@ -121,7 +120,8 @@ gc_status check_catalog(const void *prep, int64_t n) {
 }
 
 size_t workspace_bytes(int32_t nbins) {
-  return static_cast<size_t>(kMaxWorkgroups) * static_cast<size_t>(nbins) * sizeof(unsigned long long);
+  return edge_table_bytes(nbins) +
+         static_cast<size_t>(kMaxWorkgroups) * static_cast<size_t>(nbins) * sizeof(unsigned long long);
 }
 
 // j-steps of one family: cross (n_i blocks x n_j) or self (upper triangle by blocks).
@@ -207,7 +207,9 @@ gc_status gc_histogram_dd_dr_rr_tuned(const void *prep_d, int64_t n_d, const voi
   a.hist_words = (nbins + 63) / 64 * 64;
   a.wave_lds_words = a.hist_words + kQueueWords;
   a.bp = make_bins(nbins, w_deg);
-  a.slots = static_cast<unsigned long long *>(workspace);
+  double *edge_cos = static_cast<double *>(workspace);
+  a.edge_cos = edge_cos;
+  a.slots = reinterpret_cast<unsigned long long *>(static_cast<char *>(workspace) + edge_table_bytes(nbins));
   const int64_t max_inc = 2ll * kWave * k;  // largest increase of one bin per j-step
   const int64_t auto_flush = static_cast<int64_t>(0xffffffffll / max_inc) - 8;
   a.flush_interval = tu.flush_interval ? (tu.flush_interval < auto_flush ? tu.flush_interval : auto_flush)
@@ -283,6 +285,8 @@ gc_status gc_histogram_dd_dr_rr_tuned(const void *prep_d, int64_t n_d, const voi
       a.fam[f].wg_end = we[f];
     }
     num_wg = cur;
+    e = launch_edges(nbins, w_deg, edge_cos, hs);
+    if (e != hipSuccess) return device_error(e);
     e = launch_pairs(a, num_wg, dot64, k, hs);
     if (e != hipSuccess) return device_error(e);
   }
@@ -323,16 +327,22 @@ gc_status gc_omega(const uint64_t *dd, const uint64_t *dr, const uint64_t *rr, i
 
 gc_status gc_eval_angle_core(const float *x32, const double *x64, int64_t n, int32_t nbins, double w_deg,
                              int32_t dot_precision, int32_t *bin_out, uint8_t *trip_out, int32_t *exact_out,
-                             gc_stream_t stream) {
+                             void *workspace, size_t ws_bytes, gc_stream_t stream) {
   gc_status st;
   if ((st = check_bins(nbins, w_deg)) != GC_OK) return st;
   if (n < 0 || (dot_precision != 32 && dot_precision != 64)) return GC_ERR_INVALID_ARGUMENT;
-  if (n == 0) return GC_OK;
   const bool d64 = dot_precision == 64;
-  if ((d64 && !x64) || (!d64 && !x32) || !bin_out || !trip_out) return GC_ERR_INVALID_ARGUMENT;
+  if (n > 0 && ((d64 && !x64) || (!d64 && !x32) || !bin_out || !trip_out)) return GC_ERR_INVALID_ARGUMENT;
+  if (exact_out && (!workspace || !aligned(workspace, GC_ALIGNMENT))) return GC_ERR_INVALID_ARGUMENT;
+  if (exact_out && ws_bytes < edge_table_bytes(nbins)) return GC_ERR_WORKSPACE;
+  if (n == 0) return GC_OK;
   const BinParams bp = make_bins(nbins, w_deg);
-  hipError_t e = launch_eval_core(x32, x64, n, bp, d64, bin_out, trip_out, exact_out,
-                                  reinterpret_cast<hipStream_t>(stream));
+  const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  double *edge_cos = static_cast<double *>(workspace);
+  hipError_t e = hipSuccess;
+  if (exact_out) e = launch_edges(nbins, w_deg, edge_cos, hs);
+  if (e == hipSuccess)
+    e = launch_eval_core(x32, x64, n, bp, d64, exact_out ? edge_cos : nullptr, bin_out, trip_out, exact_out, hs);
   return e == hipSuccess ? GC_OK : device_error(e);
 }
 

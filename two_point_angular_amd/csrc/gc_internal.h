@@ -52,7 +52,6 @@ struct BinParams {
   float g64k1;   // fp64-dot guard: recheck iff |t - round(t)| * s < g64k1 * s + g64k2
   float g64k2;
   int32_t nbins;
-  double invw64; // 1 / w_rad (fp64), used by the exact recheck
 };
 
 // ---- pair-kernel work description ---------------------------------------------------
@@ -74,6 +73,7 @@ struct PairArgs {
   FamilyWork fam[3];           // DD, DR, RR
   BinParams bp;
   unsigned long long *slots;   // [num_workgroups][nbins] 64-bit partial histograms
+  const double *edge_cos;      // [nbins + 1] cos(e w) in fp64, for the exact recheck
   int64_t flush_interval;      // j-steps between flushes of the 32-bit LDS histograms
   int32_t nbins;
   int32_t hist_words;          // LDS words of one wave's histogram (>= nbins)
@@ -92,8 +92,14 @@ hipError_t launch_totals(const uint64_t *dd, const uint64_t *dr, const uint64_t 
                          uint64_t *totals, hipStream_t s);
 hipError_t launch_omega(const uint64_t *dd, const uint64_t *dr, const uint64_t *rr, int32_t nbins,
                         int64_t n_d, int64_t n_r, double *omega, hipStream_t s);
+hipError_t launch_edges(int32_t nbins, double w_deg, double *edge_cos, hipStream_t s);
 hipError_t launch_eval_core(const float *x32, const double *x64, int64_t n, const BinParams &bp,
-                            bool dot64, int32_t *bin_out, uint8_t *trip_out, int32_t *exact_out,
-                            hipStream_t s);
+                            bool dot64, const double *edge_cos, int32_t *bin_out, uint8_t *trip_out,
+                            int32_t *exact_out, hipStream_t s);
+
+// Workspace layout: the edge-cosine table, then the per-workgroup 64-bit partial histograms.
+inline size_t edge_table_bytes(int32_t nbins) {
+  return ((static_cast<size_t>(nbins) + 1) * sizeof(double) + 255) / 256 * 256;
+}
 
 }  // namespace gc

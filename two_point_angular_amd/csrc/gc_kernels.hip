@@ -89,12 +89,16 @@ __device__ __forceinline__ void core64(double x, const BinParams &bp, uint32_t &
   trip = fabsf(tc - __builtin_rintf(tc)) * s < fmaf(s, bp.g64k1, bp.g64k2);
 }
 
-// Exact recheck: the fp64 angle, then truncation and clamping.
-__device__ __forceinline__ uint32_t exact_bin(double x, const BinParams &bp) {
-  const double c = fmin(fmax(x, -1.0), 1.0);
-  const double t = floor(acos(c) * bp.invw64);
-  const double top = static_cast<double>(bp.nbins - 1);
-  return static_cast<uint32_t>(t < top ? t : top);
+// Exact recheck in the cosine domain.  theta >= e w  <=>  x <= cos(e w), so bin k holds x
+// iff c[k+1] < x <= c[k], with c[e] = cos(e w) in fp64 (c[0] = 1; c[e] = -inf past 180
+// degrees).  Starting from the fast-path bin k, walk to the bin that satisfies this.  The
+// result differs from truncating the fp64 angle only for x within fp64 rounding of an
+// edge cosine (angles within ~1e-11 degrees of an edge).
+__device__ __forceinline__ uint32_t exact_bin(double x, uint32_t k, const double *__restrict__ c,
+                                              int32_t nbins) {
+  while (k > 0 && x > c[k]) --k;
+  while (k + 1 < static_cast<uint32_t>(nbins) && x <= c[k + 1]) ++k;
+  return k;
 }
 
 __device__ __forceinline__ double dot64(const Prepared &a, int64_t i, const Prepared &b, int64_t j) {
@@ -141,7 +145,7 @@ template <> struct Real<true> { typedef double T; };
 // entries): word 2e = j, word 2e+1 = (i - i0) << 16 | fast-path bin.
 __device__ __forceinline__ void drain_queue(uint32_t *hist, const uint32_t *queue, int qhead, int c, int cap,
                                             const Prepared &ci, const Prepared &cj, int64_t i0, uint32_t w,
-                                            const BinParams &bp) {
+                                            const double *edge_cos, int32_t nbins) {
   const int lane = threadIdx.x & (kWave - 1);
   __builtin_amdgcn_wave_barrier();
   if (lane < c) {
@@ -150,7 +154,7 @@ __device__ __forceinline__ void drain_queue(uint32_t *hist, const uint32_t *queu
     const uint32_t jj = queue[2 * e];
     const uint32_t p = queue[2 * e + 1];
     const uint32_t kf = p & 0xffffu;
-    const uint32_t ke = exact_bin(dot64(ci, i0 + (p >> 16), cj, jj), bp);
+    const uint32_t ke = exact_bin(dot64(ci, i0 + (p >> 16), cj, jj), kf, edge_cos, nbins);
     if (ke != kf) {
       atomicSub(hist + kf, w);
       atomicAdd(hist + ke, w);
@@ -160,7 +164,7 @@ __device__ __forceinline__ void drain_queue(uint32_t *hist, const uint32_t *queu
 }
 
 template <int K, bool D64>
-__global__ void __launch_bounds__(kWGThreads)
+__global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu(D64 ? 3 : 4)))
 pairs_kernel(const PairArgs A) {
   typedef typename Real<D64>::T real;
   constexpr int BI = kWave * K;       // i-block: galaxies per wave
@@ -216,7 +220,7 @@ pairs_kernel(const PairArgs A) {
 
   constexpr int QCAP = kWave * (K + 1);  // < 64 left over + up to 64 K from one j-step
   auto drain = [&](int c) __attribute__((always_inline)) {
-    drain_queue(hist, queue, qhead, c, QCAP, F.ci, F.cj, i0, W, bp);
+    drain_queue(hist, queue, qhead, c, QCAP, F.ci, F.cj, i0, W, A.edge_cos, A.nbins);
     qhead += c;
     if (qhead >= QCAP) qhead -= QCAP;
     qcount -= c;
@@ -245,47 +249,42 @@ pairs_kernel(const PairArgs A) {
     }
   };
 
-  // One j against this lane's K i-galaxies.
+  // One j against this lane's K i-galaxies.  Pairs the guard flags are appended to the
+  // wave's queue right after their atomic (each bin index dies at once), and the queue is
+  // drained in full-wave batches after the step.
   auto step = [&](real xj, real yj, real zj, int64_t jg, auto generic_tag) __attribute__((always_inline)) {
     constexpr bool GENERIC = decltype(generic_tag)::value;
-    uint32_t kk[K];
-    bool tp[K];
-    bool any = false;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
+      uint32_t kk;
+      bool tp;
       const real x = fma(ix[k], xj, fma(iy[k], yj, iz[k] * zj));
-      if constexpr (D64) core64(x, bp, kk[k], tp[k]);
-      else core32(x, bp, kk[k], tp[k]);
+      if constexpr (D64) core64(x, bp, kk, tp);
+      else core32(x, bp, kk, tp);
       if constexpr (GENERIC) {
         const int64_t ig = i0 + lane + kWave * k;
         const bool valid = ig < F.n_i && (!F.sym || jg >= ig);
         const bool self = F.sym && jg == ig;  // only a self family pairs a galaxy with itself
-        if (self) kk[k] = 0u;                  // separation 0
-        tp[k] = tp[k] && valid && !self;
-        if (valid) atomicAdd(hist + kk[k], self ? 1u : W);
+        if (self) kk = 0u;                     // separation 0
+        tp = tp && valid && !self;
+        if (valid) atomicAdd(hist + kk, self ? 1u : W);
       } else {
-        atomicAdd(hist + kk[k], W);
+        atomicAdd(hist + kk, W);
       }
-      any = any || tp[k];
-    }
-    if (__ballot(any)) {
-#pragma unroll
-      for (int k = 0; k < K; ++k) {
-        const unsigned long long m = __ballot(tp[k]);
-        if (m) {
-          if (tp[k]) {
-            const uint32_t below = __builtin_amdgcn_mbcnt_hi(
-                static_cast<uint32_t>(m >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
-            int e = qhead + qcount + static_cast<int>(below);
-            if (e >= QCAP) e -= QCAP;
-            queue[2 * e] = static_cast<uint32_t>(jg);
-            queue[2 * e + 1] = (static_cast<uint32_t>(lane + kWave * k) << 16) | kk[k];
-          }
-          qcount += __popcll(m);
+      const unsigned long long m = __ballot(tp);
+      if (m) {
+        if (tp) {
+          const uint32_t below = __builtin_amdgcn_mbcnt_hi(
+              static_cast<uint32_t>(m >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+          int e = qhead + qcount + static_cast<int>(below);
+          if (e >= QCAP) e -= QCAP;
+          queue[2 * e] = static_cast<uint32_t>(jg);
+          queue[2 * e + 1] = (static_cast<uint32_t>(lane + kWave * k) << 16) | kk;
         }
+        qcount += __popcll(m);
       }
-      while (qcount >= kWave) drain(kWave);
     }
+    while (qcount >= kWave) drain(kWave);
   };
 
   auto check_flush = [&]() __attribute__((always_inline)) {
@@ -382,6 +381,15 @@ pairs_kernel(const PairArgs A) {
   flush();
 }
 
+// ------------------------------------------------------------------------------- edges
+// c[e] = cos(e w) for e = 0..nbins (fp64); -inf where e w exceeds 180 degrees.
+__global__ void __launch_bounds__(256) edges_kernel(int32_t nbins, double w_deg, double *c) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e > nbins) return;
+  const double deg = static_cast<double>(e) * w_deg;
+  c[e] = deg <= 180.0 ? cos(deg * (3.14159265358979323846 / 180.0)) : -__builtin_inf();
+}
+
 // ------------------------------------------------------------------------------- merge
 // out_f[bin] = sum of slots of family f's workgroups.  Block: 256 threads = 4 waves over
 // the slot list, one bin per lane; grid (ceil(nbins / 64), 3).
@@ -448,8 +456,8 @@ __global__ void __launch_bounds__(256) omega_kernel(const uint64_t *dd, const ui
 // -------------------------------------------------------------------------- eval core
 __global__ void __launch_bounds__(256) eval_core_kernel(const float *x32, const double *x64,
                                                         int64_t n, const BinParams bp, int dot64,
-                                                        int32_t *bin_out, uint8_t *trip_out,
-                                                        int32_t *exact_out) {
+                                                        const double *edge_cos, int32_t *bin_out,
+                                                        uint8_t *trip_out, int32_t *exact_out) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (idx >= n) return;
   uint32_t k;
@@ -465,7 +473,7 @@ __global__ void __launch_bounds__(256) eval_core_kernel(const float *x32, const 
   }
   bin_out[idx] = static_cast<int32_t>(k);
   trip_out[idx] = trip ? 1 : 0;
-  if (exact_out) exact_out[idx] = static_cast<int32_t>(exact_bin(xe, bp));
+  if (exact_out) exact_out[idx] = static_cast<int32_t>(exact_bin(xe, k, edge_cos, bp.nbins));
 }
 
 }  // namespace
@@ -532,12 +540,17 @@ hipError_t launch_omega(const uint64_t *dd, const uint64_t *dr, const uint64_t *
   return hipGetLastError();
 }
 
+hipError_t launch_edges(int32_t nbins, double w_deg, double *edge_cos, hipStream_t st) {
+  hipLaunchKernelGGL(edges_kernel, dim3((nbins + 1 + 255) / 256), dim3(256), 0, st, nbins, w_deg, edge_cos);
+  return hipGetLastError();
+}
+
 hipError_t launch_eval_core(const float *x32, const double *x64, int64_t n, const BinParams &bp,
-                            bool dot64, int32_t *bin_out, uint8_t *trip_out, int32_t *exact_out,
-                            hipStream_t st) {
+                            bool dot64, const double *edge_cos, int32_t *bin_out, uint8_t *trip_out,
+                            int32_t *exact_out, hipStream_t st) {
   const int64_t blocks = (n + 255) / 256;
   hipLaunchKernelGGL(eval_core_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, x32, x64, n,
-                     bp, dot64 ? 1 : 0, bin_out, trip_out, exact_out);
+                     bp, dot64 ? 1 : 0, edge_cos, bin_out, trip_out, exact_out);
   return hipGetLastError();
 }
 
