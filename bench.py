@@ -25,6 +25,29 @@ sys.path.insert(0, ROOT)
 
 FLOPS_PER_PAIR = 25.0          # algorithmic FP32 flops per evaluated pair (FMA = 2)
 FP32_PEAK_TFLOPS = 157.3       # MI355X FP32 vector peak (published)
+DEVICE_SOURCES = ("two_point_angular_amd/csrc/gc_kernels.hip", "two_point_angular_amd/csrc/gc_internal.h",
+                  "two_point_angular_amd/csrc/gc_acos_poly.h", "two_point_angular_amd/csrc/gc_api.cpp")
+
+
+def measured_traffic(workload):
+    """HBM bytes per pair-kernel launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary of this workload, or None when there is none or the device sources changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"pairs_kernel_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        parts = line.strip().split(": ")
+        if len(parts) == 2 and parts[0] in ("traffic_bytes_per_launch", "device_source_sha256"):
+            vals[parts[0]] = parts[1]
+    h = hashlib.sha256()
+    for f in DEVICE_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if vals.get("device_source_sha256") != h.hexdigest() or "traffic_bytes_per_launch" not in vals:
+        return None
+    return float(vals["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(D, R, nbins, w, target_s=12.0):
@@ -57,6 +80,9 @@ def main():
     ap.add_argument("--dot", type=int, default=0, help="tuning: dot-product precision (0 auto, 32, 64)")
     ap.add_argument("--k", type=int, default=0, help="tuning: i galaxies per lane (0 auto, 4, 8)")
     ap.add_argument("--blocks-per-cu", type=int, default=0)
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="after timing, copy this many bytes device-to-device with a plain copy kernel "
+                         "(reference dispatch for scaling FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -111,6 +137,14 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
+    if args.copy_bytes:
+        src = torch.ones(args.copy_bytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     tot = totals.cpu().numpy().view(np.uint64)
     want = np.array([n_d * n_d, n_d * n_r, n_r * n_r], dtype=np.uint64)
     if not np.all(tot == want[None, :]):
@@ -144,7 +178,7 @@ def main():
         "kernel_ms": {"mean": float(np.mean(kern_ms)), "median": float(np.median(kern_ms)),
                       "min": float(np.min(kern_ms)), "what": "pair kernel + merge, HIP events"},
         "roofline": {"bound": "alu", "achieved": achieved, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / FP32_PEAK_TFLOPS, "traffic": None,
+                     "frac": achieved / FP32_PEAK_TFLOPS, "traffic": measured_traffic(wl.name),
                      "note": f"{FLOPS_PER_PAIR:.0f} algorithmic FP32 flops per evaluated pair"},
         "cpu_baseline": None,
     }

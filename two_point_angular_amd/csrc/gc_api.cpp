@@ -92,8 +92,9 @@ BinParams make_bins(int32_t nbins, double w_deg) {
   bp.tmax = static_cast<float>(nbins) - 0.5f;
   // fp32-dot guard
   const double g_x = 5.0 * kTwoM24 * (1.0 + 1e-6) + 1e-12;
-  // core error: exhaustive emulated bound plus one ulp of hardware sqrt (times P <= pi/2)
-  const double e_core = (GC_ACOS_CORE_ERR + 2.0 * kTwoM24 * (kPi / 2.0)) * 1.25;
+  // core error: the exhaustive fp32 bound (computed with a correctly rounded square root)
+  // plus the extra half ulp a 1-ulp hardware square root may add, times P <= pi/2; 25 % margin
+  const double e_core = (GC_ACOS_CORE_ERR + kTwoM24 * (kPi / 2.0)) * 1.25;
   const double h = (kPi / 2.0) / w_rad;
   const double c = e_core / w_rad + kTwoM24 * (static_cast<double>(nbins) + 1.0 + 2.0 * h) * 1.01;
   bp.g32 = static_cast<float>((2.02 * g_x / w_rad + c) * (1.0 + 1e-6));

@@ -55,16 +55,26 @@ __device__ __forceinline__ float acos_poly(float a) {
   return p;
 }
 
+// A wave-uniform constant held in a VGPR.  A VALU instruction on this target reads at most
+// one scalar operand, so fma(a, sgpr, sgpr) needs one constant in a VGPR; the opaque move
+// keeps the compiler from re-materialising it (one v_mov per use) inside the pair loop.
+__device__ __forceinline__ float in_vgpr(float v) {
+  float r;
+  asm("v_mov_b32 %0, %1" : "=v"(r) : "s"(v));
+  return r;
+}
+
 // fp32-dot core.  x is the fp32 dot product of the two fp32 unit vectors.
 //   s  = sqrt(1 - |x|) (clamped at 0),  q = pi/2 - s P(|x|) = pi/2 - acos(|x|)
 //   theta = pi/2 - sign(x) q,  t = theta / w,  tc = clamp(t, 0.5, nbins - 0.5)
 //   k = trunc(tc); recheck iff |tc - round(tc)| * s < g32, i.e. iff an inner bin edge
 //   lies within the certified error bound 2.02 g_x / (s w) + C of t.
-__device__ __forceinline__ void core32(float x, const BinParams &bp, uint32_t &k, bool &trip) {
+// h_v is (pi/2)/w held in a VGPR (see in_vgpr).
+__device__ __forceinline__ void core32(float x, const BinParams &bp, float h_v, uint32_t &k, bool &trip) {
   const float a = fabsf(x);
   const float s = __builtin_amdgcn_sqrtf(__builtin_amdgcn_fmed3f(1.0f - a, 0.0f, 1.0f));
   const float q = fmaf(-s, acos_poly(a), kHalfPiF);
-  const float t = fmaf(copysignf(q, x), -bp.invw, bp.h);
+  const float t = fmaf(copysignf(q, x), -bp.invw, h_v);
   const float tc = __builtin_amdgcn_fmed3f(t, 0.5f, bp.tmax);
   k = static_cast<uint32_t>(tc);
   trip = fabsf(tc - __builtin_rintf(tc)) * s < bp.g32;
@@ -180,6 +190,7 @@ pairs_kernel(const PairArgs A) {
   const FamilyWork &F = A.fam[fi];
   const BinParams &bp = A.bp;
   const uint32_t W = F.sym ? 2u : 1u;
+  const float h_v = in_vgpr(bp.h);
 
   unsigned long long *const slot = A.slots + static_cast<size_t>(g) * A.nbins;
   for (int b = threadIdx.x; b < A.nbins; b += kWGThreads) slot[b] = 0ull;
@@ -260,7 +271,7 @@ pairs_kernel(const PairArgs A) {
       bool tp;
       const real x = fma(ix[k], xj, fma(iy[k], yj, iz[k] * zj));
       if constexpr (D64) core64(x, bp, kk, tp);
-      else core32(x, bp, kk, tp);
+      else core32(x, bp, h_v, kk, tp);
       if constexpr (GENERIC) {
         const int64_t ig = i0 + lane + kWave * k;
         const bool valid = ig < F.n_i && (!F.sym || jg >= ig);
@@ -469,7 +480,7 @@ __global__ void __launch_bounds__(256) eval_core_kernel(const float *x32, const 
   } else {
     const float xf = x32[idx];
     xe = static_cast<double>(xf);
-    core32(xf, bp, k, trip);
+    core32(xf, bp, bp.h, k, trip);
   }
   bin_out[idx] = static_cast<int32_t>(k);
   trip_out[idx] = trip ? 1 : 0;
