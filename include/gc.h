@@ -109,7 +109,8 @@ typedef struct {
     int32_t dot_precision;   /* 0 auto, 32: fp32 dot product, 64: fp64 dot product */
     int32_t i_per_lane;      /* 0 auto, or 4 or 8 galaxies held per lane */
     int32_t blocks_per_cu;   /* 0 auto (occupancy), else 1..8 workgroups per compute unit */
-    int32_t reserved;        /* must be 0 */
+    int32_t shared_histogram; /* 0 auto; 1: one private LDS histogram per wavefront;
+                                 2: one LDS histogram per workgroup, shared by its wavefronts */
     int64_t flush_interval;  /* 0 auto; else j-steps between flushes of the 32-bit per-wave
                                 histograms into 64-bit totals (>= 1) */
 } gc_tuning;

@@ -97,7 +97,8 @@ def test_histogram_validation(lib):
     assert _hist(lib, ws=P(A + 128)) == INVALID
     assert _hist(lib, wsb=gc.workspace_bytes(720) - 1) == WORKSPACE
     for bad in (gc._Tuning(33, 0, 0, 0, 0), gc._Tuning(0, 5, 0, 0, 0), gc._Tuning(0, 0, 9, 0, 0),
-                gc._Tuning(0, 0, -1, 0, 0), gc._Tuning(0, 0, 0, 1, 0), gc._Tuning(0, 0, 0, 0, -3)):
+                gc._Tuning(0, 0, -1, 0, 0), gc._Tuning(0, 0, 0, 3, 0), gc._Tuning(0, 0, 0, -1, 0),
+                gc._Tuning(0, 0, 0, 0, -3)):
         assert _hist(lib, tuning=bad) == INVALID
 
 

@@ -193,7 +193,8 @@ gc_status gc_histogram_dd_dr_rr_tuned(const void *prep_d, int64_t n_d, const voi
   if (tuning) tu = *tuning;
   if ((tu.dot_precision != 0 && tu.dot_precision != 32 && tu.dot_precision != 64) ||
       (tu.i_per_lane != 0 && tu.i_per_lane != 4 && tu.i_per_lane != 8) || tu.blocks_per_cu < 0 ||
-      tu.blocks_per_cu > kMaxBlocksPerCU || tu.reserved != 0 || tu.flush_interval < 0)
+      tu.blocks_per_cu > kMaxBlocksPerCU || tu.shared_histogram < 0 || tu.shared_histogram > 2 ||
+      tu.flush_interval < 0)
     return GC_ERR_INVALID_ARGUMENT;
 
   // Plan.  Bins narrower than 0.01 deg put most pairs where the fp32 dot product cannot
@@ -211,10 +212,6 @@ gc_status gc_histogram_dd_dr_rr_tuned(const void *prep_d, int64_t n_d, const voi
   double *edge_cos = static_cast<double *>(workspace);
   a.edge_cos = edge_cos;
   a.slots = reinterpret_cast<unsigned long long *>(static_cast<char *>(workspace) + edge_table_bytes(nbins));
-  const int64_t max_inc = 2ll * kWave * k;  // largest increase of one bin per j-step
-  const int64_t auto_flush = static_cast<int64_t>(0xffffffffll / max_inc) - 8;
-  a.flush_interval = tu.flush_interval ? (tu.flush_interval < auto_flush ? tu.flush_interval : auto_flush)
-                                       : auto_flush;
 
   const Prepared pd = prepared_view(prep_d, n_d), pr = prepared_view(prep_r, n_r);
   const int64_t nn[3][2] = {{n_d, n_d}, {n_d, n_r}, {n_r, n_r}};
@@ -236,10 +233,22 @@ gc_status gc_histogram_dd_dr_rr_tuned(const void *prep_d, int64_t n_d, const voi
   int32_t wb[3] = {0, 0, 0}, we[3] = {0, 0, 0};
   int num_wg = 0;
   if (total > 0) {
-    const size_t lds = static_cast<size_t>(kWavesPerWG) * a.wave_lds_words * sizeof(uint32_t);
-    int cus = 0, occ = 0;
-    hipError_t e = device_info(&cus, dot64, k, lds, &occ);
+    // Histogram placement: one private histogram per wave unless sharing one per workgroup
+    // lets more workgroups fit in LDS.
+    int cus = 0, occ = 0, occ_shared = 0;
+    hipError_t e = device_info(&cus, dot64, k, pairs_lds_bytes(a.hist_words, false), &occ);
     if (e != hipSuccess) return device_error(e);
+    e = device_info(&cus, dot64, k, pairs_lds_bytes(a.hist_words, true), &occ_shared);
+    if (e != hipSuccess) return device_error(e);
+    bool shared = tu.shared_histogram == 2 || (tu.shared_histogram == 0 && occ_shared > occ);
+    if (shared) occ = occ_shared;
+    a.shared_hist = shared ? 1 : 0;
+    // Between two flushes a bin must stay within +-2^31: each j-step adds at most 2 * 64 K
+    // per wave, and in shared mode four waves add to the same histogram.
+    const int64_t max_inc = 2ll * kWave * k * (shared ? kWavesPerWG : 1);
+    const int64_t auto_flush = static_cast<int64_t>(0x7fffffffll / max_inc) - 8;
+    a.flush_interval = tu.flush_interval ? (tu.flush_interval < auto_flush ? tu.flush_interval : auto_flush)
+                                         : auto_flush;
     int per_cu = tu.blocks_per_cu ? tu.blocks_per_cu : (occ < kMaxBlocksPerCU ? occ : kMaxBlocksPerCU);
     if (per_cu < 1) return GC_ERR_UNSUPPORTED;
     int64_t g = static_cast<int64_t>(per_cu) * cus;

@@ -78,8 +78,15 @@ struct PairArgs {
   int32_t nbins;
   int32_t hist_words;          // LDS words of one wave's histogram (>= nbins)
   int32_t wave_lds_words;      // hist_words + kQueueWords
-  int32_t pad_;
+  int32_t shared_hist;         // 0: one histogram per wave; 1: one per workgroup (4 waves)
 };
+
+// LDS bytes of one pair-kernel workgroup.
+inline size_t pairs_lds_bytes(int32_t hist_words, bool shared_hist) {
+  const size_t words = shared_hist ? hist_words + static_cast<size_t>(kWavesPerWG) * kQueueWords
+                                   : static_cast<size_t>(kWavesPerWG) * (hist_words + kQueueWords);
+  return words * sizeof(uint32_t);
+}
 
 // ---- launchers (gc_kernels.hip) ----------------------------------------------------------
 hipError_t launch_prepare(const float *ra, const float *dec, int64_t n, void *blob, hipStream_t s);

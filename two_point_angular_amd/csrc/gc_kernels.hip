@@ -150,17 +150,16 @@ template <bool D64> struct Real;
 template <> struct Real<false> { typedef float T; };
 template <> struct Real<true> { typedef double T; };
 
-// Re-bin c <= 64 queued pairs of one wave exactly in fp64 (one pair per lane) and move
-// their counts from the fast-path bin to the exact bin.  Queue entry e (a ring of `cap`
-// entries): word 2e = j, word 2e+1 = (i - i0) << 16 | fast-path bin.
-__device__ __forceinline__ void drain_queue(uint32_t *hist, const uint32_t *queue, int qhead, int c, int cap,
+// Re-bin the c <= 64 queued pairs in entries [first, first + c) exactly in fp64 (one pair
+// per lane) and move their counts from the fast-path bin to the exact bin.  Entry e: word
+// 2e = j, word 2e+1 = (i - i0) << 16 | fast-path bin.
+__device__ __forceinline__ void drain_queue(uint32_t *hist, const uint32_t *queue, int first, int c,
                                             const Prepared &ci, const Prepared &cj, int64_t i0, uint32_t w,
                                             const double *edge_cos, int32_t nbins) {
   const int lane = threadIdx.x & (kWave - 1);
   __builtin_amdgcn_wave_barrier();
   if (lane < c) {
-    int e = qhead + lane;
-    if (e >= cap) e -= cap;
+    const int e = first + lane;
     const uint32_t jj = queue[2 * e];
     const uint32_t p = queue[2 * e + 1];
     const uint32_t kf = p & 0xffffu;
@@ -183,8 +182,10 @@ pairs_kernel(const PairArgs A) {
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x / kWave;
-  uint32_t *const hist = lds + wv * A.wave_lds_words;
-  uint32_t *const queue = hist + A.hist_words;
+  // LDS: private mode, per wave [histogram | queue]; shared mode, [histogram | 4 queues].
+  const bool shared_hist = A.shared_hist != 0;
+  uint32_t *const hist = shared_hist ? lds : lds + wv * (A.hist_words + kQueueWords);
+  uint32_t *const queue = shared_hist ? lds + A.hist_words + wv * kQueueWords : hist + A.hist_words;
   const int g = blockIdx.x;
   const int fi = g < A.fam[0].wg_end ? 0 : (g < A.fam[1].wg_end ? 1 : 2);
   const FamilyWork &F = A.fam[fi];
@@ -194,7 +195,11 @@ pairs_kernel(const PairArgs A) {
 
   unsigned long long *const slot = A.slots + static_cast<size_t>(g) * A.nbins;
   for (int b = threadIdx.x; b < A.nbins; b += kWGThreads) slot[b] = 0ull;
-  for (int b = lane; b < A.hist_words; b += kWave) hist[b] = 0u;
+  if (shared_hist) {
+    for (int b = threadIdx.x; b < A.hist_words; b += kWGThreads) hist[b] = 0u;
+  } else {
+    for (int b = lane; b < A.hist_words; b += kWave) hist[b] = 0u;
+  }
   __threadfence();
   __syncthreads();
 
@@ -225,30 +230,30 @@ pairs_kernel(const PairArgs A) {
   }
 
   int64_t since_flush = 0;
-  int qhead = 0, qcount = 0;
+  int qcount = 0;  // queue entries [0, qcount) are pending
+  const uint32_t lane_tag = static_cast<uint32_t>(lane) << 16;
   int64_t i0 = 0;
   real ix[K], iy[K], iz[K];
 
-  constexpr int QCAP = kWave * (K + 1);  // < 64 left over + up to 64 K from one j-step
+  // A j-step appends at most 64 K entries to fewer than 64 pending ones, and the queue is
+  // drained (64 at a time, from the top) after every j-step: 64 (K + 1) entries suffice.
+  static_assert(2 * kWave * (K + 1) <= kQueueWords, "recheck queue too small");
   auto drain = [&](int c) __attribute__((always_inline)) {
-    drain_queue(hist, queue, qhead, c, QCAP, F.ci, F.cj, i0, W, A.edge_cos, A.nbins);
-    qhead += c;
-    if (qhead >= QCAP) qhead -= QCAP;
+    drain_queue(hist, queue, qcount - c, c, F.ci, F.cj, i0, W, A.edge_cos, A.nbins);
     qcount -= c;
   };
   auto drain_all = [&]() __attribute__((always_inline)) {
     while (qcount > 0) drain(qcount < kWave ? qcount : kWave);
-    qhead = 0;
   };
-  // Add this wave's 32-bit LDS histogram into the workgroup's 64-bit slot; zero it.
+  // Move the LDS histogram into the workgroup's 64-bit slot.  Each bin is taken with an
+  // atomic exchange, so in shared mode other waves may keep adding meanwhile; the value is
+  // read as signed because a pending recheck may have moved a count out of a bin that an
+  // earlier flush already emptied (the flush interval keeps every bin within +-2^31).
   auto flush = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_wave_barrier();
     for (int bb = lane; bb < A.nbins; bb += kWave) {
-      const uint32_t c = hist[bb];
-      if (c) {
-        atomicAdd(slot + bb, static_cast<unsigned long long>(c));
-        hist[bb] = 0u;
-      }
+      const uint32_t c = atomicExch(hist + bb, 0u);
+      if (c) atomicAdd(slot + bb, static_cast<unsigned long long>(static_cast<long long>(static_cast<int>(c))));
     }
     __builtin_amdgcn_wave_barrier();
   };
@@ -285,12 +290,12 @@ pairs_kernel(const PairArgs A) {
       const unsigned long long m = __ballot(tp);
       if (m) {
         if (tp) {
-          const uint32_t below = __builtin_amdgcn_mbcnt_hi(
-              static_cast<uint32_t>(m >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
-          int e = qhead + qcount + static_cast<int>(below);
-          if (e >= QCAP) e -= QCAP;
+          // slot = pending count + number of flagged lanes below this one
+          const uint32_t e = __builtin_amdgcn_mbcnt_hi(
+              static_cast<uint32_t>(m >> 32),
+              __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), static_cast<uint32_t>(qcount)));
           queue[2 * e] = static_cast<uint32_t>(jg);
-          queue[2 * e + 1] = (static_cast<uint32_t>(lane + kWave * k) << 16) | kk;
+          queue[2 * e + 1] = (lane_tag + (static_cast<uint32_t>(kWave * k) << 16)) | kk;
         }
         qcount += __popcll(m);
       }
@@ -519,7 +524,7 @@ hipError_t pairs_occupancy(bool dot64, int k, size_t lds_bytes, int *blocks_per_
 }
 
 hipError_t launch_pairs(const PairArgs &a, int num_wg, bool dot64, int k, hipStream_t st) {
-  const size_t lds = static_cast<size_t>(kWavesPerWG) * a.wave_lds_words * sizeof(uint32_t);
+  const size_t lds = pairs_lds_bytes(a.hist_words, a.shared_hist != 0);
   if (dot64) {
     if (k == 4) hipLaunchKernelGGL((pairs_kernel<4, true>), dim3(num_wg), dim3(kWGThreads), lds, st, a);
     else hipLaunchKernelGGL((pairs_kernel<8, true>), dim3(num_wg), dim3(kWGThreads), lds, st, a);
