@@ -96,10 +96,13 @@ def test_histogram_validation(lib):
     assert _hist(lib, ws=None) == INVALID
     assert _hist(lib, ws=P(A + 128)) == INVALID
     assert _hist(lib, wsb=gc.workspace_bytes(720) - 1) == WORKSPACE
-    for bad in (gc._Tuning(33, 0, 0, 0, 0), gc._Tuning(0, 5, 0, 0, 0), gc._Tuning(0, 0, 9, 0, 0),
-                gc._Tuning(0, 0, -1, 0, 0), gc._Tuning(0, 0, 0, 3, 0), gc._Tuning(0, 0, 0, -1, 0),
-                gc._Tuning(0, 0, 0, 0, -3)):
+    T = gc._Tuning  # dot, K, blocks/CU, shared histogram, full span, reserved, flush interval
+    for bad in (T(33, 0, 0, 0, 0, 0, 0), T(0, 5, 0, 0, 0, 0, 0), T(0, 0, 9, 0, 0, 0, 0),
+                T(0, 0, -1, 0, 0, 0, 0), T(0, 0, 0, 3, 0, 0, 0), T(0, 0, 0, -1, 0, 0, 0),
+                T(0, 0, 0, 0, 3, 0, 0), T(0, 0, 0, 0, 0, 1, 0), T(0, 0, 0, 0, 0, 0, -3),
+                T(64, 0, 0, 0, 2, 0, 0)):                      # full span needs the fp32 kernel
         assert _hist(lib, tuning=bad) == INVALID
+    assert _hist(lib, nbins=700, tuning=T(0, 0, 0, 0, 2, 0, 0)) == INVALID  # 700 x 0.25 < 180 deg
 
 
 @pytest.mark.skipif(not NO_GPU, reason="exercises the no-device error path; only without a GPU")

@@ -188,7 +188,8 @@ def test_outputs_overwritten_and_self_pairs(gc):
                                     dict(blocks_per_cu=1), dict(flush_interval=3),
                                     dict(flush_interval=17, i_per_lane=4, dot_precision=64),
                                     dict(shared_histogram=1), dict(shared_histogram=2),
-                                    dict(shared_histogram=2, flush_interval=5)])
+                                    dict(shared_histogram=2, flush_interval=5),
+                                    dict(full_span=1), dict(full_span=2, i_per_lane=4)])
 def test_tuning_does_not_change_results(gc, tuning):
     print(f"[gpu] tuning {tuning}", flush=True)
     D, R = catalogs.WORKLOADS["clustered100k_720"].catalogs(n=6000)

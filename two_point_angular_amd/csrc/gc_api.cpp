@@ -25,16 +25,16 @@ bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 struct DeviceInfo {
   bool valid = false;
   int cus = 0;
-  // occupancy per (dot64, k index, lds bytes)
+  // occupancy per (kernel variant, lds bytes); variant = dot64 * 4 + full_span * 2 + (k == 8)
   struct Occ { size_t lds; int blocks; };
-  Occ occ[2][2][8];
-  int nocc[2][2] = {{0, 0}, {0, 0}};
+  Occ occ[8][8];
+  int nocc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 };
 constexpr int kMaxDevices = 64;
 std::mutex g_mu;
 DeviceInfo g_dev[kMaxDevices];
 
-hipError_t device_info(int *cus, bool dot64, int k, size_t lds, int *blocks_per_cu) {
+hipError_t device_info(int *cus, bool dot64, int k, bool full_span, size_t lds, int *blocks_per_cu) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -50,17 +50,16 @@ hipError_t device_info(int *cus, bool dot64, int k, size_t lds, int *blocks_per_
   }
   *cus = d.cus;
   if (!blocks_per_cu) return hipSuccess;
-  const int ki = k == 4 ? 0 : 1;
-  const int di = dot64 ? 1 : 0;
-  for (int q = 0; q < d.nocc[di][ki]; ++q)
-    if (d.occ[di][ki][q].lds == lds) {
-      *blocks_per_cu = d.occ[di][ki][q].blocks;
+  const int vi = (dot64 ? 4 : 0) + (full_span ? 2 : 0) + (k == 8 ? 1 : 0);
+  for (int q = 0; q < d.nocc[vi]; ++q)
+    if (d.occ[vi][q].lds == lds) {
+      *blocks_per_cu = d.occ[vi][q].blocks;
       return hipSuccess;
     }
   int blocks = 0;
-  e = pairs_occupancy(dot64, k, lds, &blocks);
+  e = pairs_occupancy(dot64, k, full_span, lds, &blocks);
   if (e != hipSuccess) return e;
-  if (d.nocc[di][ki] < 8) d.occ[di][ki][d.nocc[di][ki]++] = {lds, blocks};
+  if (d.nocc[vi] < 8) d.occ[vi][d.nocc[vi]++] = {lds, blocks};
   *blocks_per_cu = blocks;
   return hipSuccess;
 }
@@ -194,19 +193,24 @@ gc_status gc_histogram_dd_dr_rr_tuned(const void *prep_d, int64_t n_d, const voi
   if ((tu.dot_precision != 0 && tu.dot_precision != 32 && tu.dot_precision != 64) ||
       (tu.i_per_lane != 0 && tu.i_per_lane != 4 && tu.i_per_lane != 8) || tu.blocks_per_cu < 0 ||
       tu.blocks_per_cu > kMaxBlocksPerCU || tu.shared_histogram < 0 || tu.shared_histogram > 2 ||
-      tu.flush_interval < 0)
+      tu.full_span < 0 || tu.full_span > 2 || tu.reserved != 0 || tu.flush_interval < 0)
     return GC_ERR_INVALID_ARGUMENT;
 
   // Plan.  Bins narrower than 0.01 deg put most pairs where the fp32 dot product cannot
   // certify the bin; those use the fp64 dot-product instantiation.
   const bool dot64 = tu.dot_precision == 64 || (tu.dot_precision == 0 && w_deg < 0.01);
   const int k = tu.i_per_lane ? tu.i_per_lane : 8;
+  // When the bins reach 180 deg (up to half a bin), t cannot exceed nbins + 1 and the fp32
+  // kernel needs no clamp of t (a spare bin takes t = nbins).
+  const bool span_ok = (static_cast<double>(nbins) + 0.5) * w_deg >= 180.0;
+  if (tu.full_span == 2 && (dot64 || !span_ok)) return GC_ERR_INVALID_ARGUMENT;
+  const bool full_span = !dot64 && span_ok && tu.full_span != 1;
   const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
 
   PairArgs a;
   memset(&a, 0, sizeof(a));
   a.nbins = nbins;
-  a.hist_words = (nbins + 63) / 64 * 64;
+  a.hist_words = (nbins + 1 + 63) / 64 * 64;  // bin nbins: spare bin of the full-span kernel
   a.wave_lds_words = a.hist_words + kQueueWords;
   a.bp = make_bins(nbins, w_deg);
   double *edge_cos = static_cast<double *>(workspace);
@@ -236,9 +240,9 @@ gc_status gc_histogram_dd_dr_rr_tuned(const void *prep_d, int64_t n_d, const voi
     // Histogram placement: one private histogram per wave unless sharing one per workgroup
     // lets more workgroups fit in LDS.
     int cus = 0, occ = 0, occ_shared = 0;
-    hipError_t e = device_info(&cus, dot64, k, pairs_lds_bytes(a.hist_words, false), &occ);
+    hipError_t e = device_info(&cus, dot64, k, full_span, pairs_lds_bytes(a.hist_words, false), &occ);
     if (e != hipSuccess) return device_error(e);
-    e = device_info(&cus, dot64, k, pairs_lds_bytes(a.hist_words, true), &occ_shared);
+    e = device_info(&cus, dot64, k, full_span, pairs_lds_bytes(a.hist_words, true), &occ_shared);
     if (e != hipSuccess) return device_error(e);
     bool shared = tu.shared_histogram == 2 || (tu.shared_histogram == 0 && occ_shared > occ);
     if (shared) occ = occ_shared;
@@ -297,7 +301,7 @@ gc_status gc_histogram_dd_dr_rr_tuned(const void *prep_d, int64_t n_d, const voi
     num_wg = cur;
     e = launch_edges(nbins, w_deg, edge_cos, hs);
     if (e != hipSuccess) return device_error(e);
-    e = launch_pairs(a, num_wg, dot64, k, hs);
+    e = launch_pairs(a, num_wg, dot64, k, full_span, hs);
     if (e != hipSuccess) return device_error(e);
   }
   uint64_t *outs[3] = {dd, dr, rr};

@@ -76,7 +76,7 @@ struct PairArgs {
   const double *edge_cos;      // [nbins + 1] cos(e w) in fp64, for the exact recheck
   int64_t flush_interval;      // j-steps between flushes of the 32-bit LDS histograms
   int32_t nbins;
-  int32_t hist_words;          // LDS words of one wave's histogram (>= nbins)
+  int32_t hist_words;          // LDS words of one histogram (>= nbins + 1: bin nbins is a spare)
   int32_t wave_lds_words;      // hist_words + kQueueWords
   int32_t shared_hist;         // 0: one histogram per wave; 1: one per workgroup (4 waves)
 };
@@ -90,9 +90,10 @@ inline size_t pairs_lds_bytes(int32_t hist_words, bool shared_hist) {
 
 // ---- launchers (gc_kernels.hip) ----------------------------------------------------------
 hipError_t launch_prepare(const float *ra, const float *dec, int64_t n, void *blob, hipStream_t s);
-// dot64: fp64 dot-product variant; k: galaxies per lane (4 or 8)
-hipError_t launch_pairs(const PairArgs &a, int num_wg, bool dot64, int k, hipStream_t s);
-hipError_t pairs_occupancy(bool dot64, int k, size_t lds_bytes, int *blocks_per_cu);
+// dot64: fp64 dot-product variant; k: galaxies per lane (4 or 8); full_span: nbins w covers
+// 180 deg (fp32 variant only: no clamp of t, spare bin instead)
+hipError_t launch_pairs(const PairArgs &a, int num_wg, bool dot64, int k, bool full_span, hipStream_t s);
+hipError_t pairs_occupancy(bool dot64, int k, bool full_span, size_t lds_bytes, int *blocks_per_cu);
 hipError_t launch_merge(const unsigned long long *slots, int32_t nbins, const int32_t wg_begin[3],
                         const int32_t wg_end[3], uint64_t *out[3], hipStream_t s);
 hipError_t launch_totals(const uint64_t *dd, const uint64_t *dr, const uint64_t *rr, int32_t nbins,

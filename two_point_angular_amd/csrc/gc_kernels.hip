@@ -69,13 +69,18 @@ __device__ __forceinline__ float in_vgpr(float v) {
 //   theta = pi/2 - sign(x) q,  t = theta / w,  tc = clamp(t, 0.5, nbins - 0.5)
 //   k = trunc(tc); recheck iff |tc - round(tc)| * s < g32, i.e. iff an inner bin edge
 //   lies within the certified error bound 2.02 g_x / (s w) + C of t.
+// FULL_SPAN (nbins w >= 180 deg - w/2): t stays below nbins + 1, so the clamp is dropped;
+// t = nbins lands in a spare bin that the flush folds into bin nbins - 1, and t in (-1, 0)
+// truncates to 0.  Without the clamp the guard can only trip more often (near t = 0 and
+// t = nbins, where no inner edge lies), never less.
 // h_v is (pi/2)/w held in a VGPR (see in_vgpr).
+template <bool FULL_SPAN>
 __device__ __forceinline__ void core32(float x, const BinParams &bp, float h_v, uint32_t &k, bool &trip) {
   const float a = fabsf(x);
   const float s = __builtin_amdgcn_sqrtf(__builtin_amdgcn_fmed3f(1.0f - a, 0.0f, 1.0f));
   const float q = fmaf(-s, acos_poly(a), kHalfPiF);
   const float t = fmaf(copysignf(q, x), -bp.invw, h_v);
-  const float tc = __builtin_amdgcn_fmed3f(t, 0.5f, bp.tmax);
+  const float tc = FULL_SPAN ? t : __builtin_amdgcn_fmed3f(t, 0.5f, bp.tmax);
   k = static_cast<uint32_t>(tc);
   trip = fabsf(tc - __builtin_rintf(tc)) * s < bp.g32;
 }
@@ -172,7 +177,7 @@ __device__ __forceinline__ void drain_queue(uint32_t *hist, const uint32_t *queu
   __builtin_amdgcn_wave_barrier();
 }
 
-template <int K, bool D64>
+template <int K, bool D64, bool FULL_SPAN>
 __global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu(D64 ? 3 : 4)))
 pairs_kernel(const PairArgs A) {
   typedef typename Real<D64>::T real;
@@ -251,9 +256,11 @@ pairs_kernel(const PairArgs A) {
   // earlier flush already emptied (the flush interval keeps every bin within +-2^31).
   auto flush = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_wave_barrier();
-    for (int bb = lane; bb < A.nbins; bb += kWave) {
+    for (int bb = lane; bb <= A.nbins; bb += kWave) {  // bin nbins is the spare bin
       const uint32_t c = atomicExch(hist + bb, 0u);
-      if (c) atomicAdd(slot + bb, static_cast<unsigned long long>(static_cast<long long>(static_cast<int>(c))));
+      if (c)
+        atomicAdd(slot + (bb < A.nbins ? bb : A.nbins - 1),
+                  static_cast<unsigned long long>(static_cast<long long>(static_cast<int>(c))));
     }
     __builtin_amdgcn_wave_barrier();
   };
@@ -276,7 +283,7 @@ pairs_kernel(const PairArgs A) {
       bool tp;
       const real x = fma(ix[k], xj, fma(iy[k], yj, iz[k] * zj));
       if constexpr (D64) core64(x, bp, kk, tp);
-      else core32(x, bp, h_v, kk, tp);
+      else core32<FULL_SPAN>(x, bp, h_v, kk, tp);
       if constexpr (GENERIC) {
         const int64_t ig = i0 + lane + kWave * k;
         const bool valid = ig < F.n_i && (!F.sym || jg >= ig);
@@ -485,7 +492,7 @@ __global__ void __launch_bounds__(256) eval_core_kernel(const float *x32, const 
   } else {
     const float xf = x32[idx];
     xe = static_cast<double>(xf);
-    core32(xf, bp, bp.h, k, trip);
+    core32<false>(xf, bp, bp.h, k, trip);
   }
   bin_out[idx] = static_cast<int32_t>(k);
   trip_out[idx] = trip ? 1 : 0;
@@ -506,33 +513,31 @@ hipError_t launch_prepare(const float *ra, const float *dec, int64_t n, void *bl
   return hipGetLastError();
 }
 
-template <int K, bool D64> static void *pairs_fn() {
-  return reinterpret_cast<void *>(&pairs_kernel<K, D64>);
+template <int K, bool D64, bool FS> static const void *pairs_fn() {
+  return reinterpret_cast<const void *>(&pairs_kernel<K, D64, FS>);
 }
 
-static const void *select_pairs(bool dot64, int k) {
-  if (dot64) return k == 4 ? pairs_fn<4, true>() : pairs_fn<8, true>();
-  return k == 4 ? pairs_fn<4, false>() : pairs_fn<8, false>();
+// Instantiations: K in {4, 8}; fp32 dot with and without the full-span specialisation;
+// fp64 dot (always clamped).
+static const void *select_pairs(bool dot64, int k, bool full_span) {
+  if (dot64) return k == 4 ? pairs_fn<4, true, false>() : pairs_fn<8, true, false>();
+  if (full_span) return k == 4 ? pairs_fn<4, false, true>() : pairs_fn<8, false, true>();
+  return k == 4 ? pairs_fn<4, false, false>() : pairs_fn<8, false, false>();
 }
 
-hipError_t pairs_occupancy(bool dot64, int k, size_t lds_bytes, int *blocks_per_cu) {
-  const void *fn = select_pairs(dot64, k);
+hipError_t pairs_occupancy(bool dot64, int k, bool full_span, size_t lds_bytes, int *blocks_per_cu) {
+  const void *fn = select_pairs(dot64, k, full_span);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      static_cast<int>(lds_bytes));
   if (e != hipSuccess) return e;
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, fn, kWGThreads, lds_bytes);
 }
 
-hipError_t launch_pairs(const PairArgs &a, int num_wg, bool dot64, int k, hipStream_t st) {
+hipError_t launch_pairs(const PairArgs &a, int num_wg, bool dot64, int k, bool full_span, hipStream_t st) {
   const size_t lds = pairs_lds_bytes(a.hist_words, a.shared_hist != 0);
-  if (dot64) {
-    if (k == 4) hipLaunchKernelGGL((pairs_kernel<4, true>), dim3(num_wg), dim3(kWGThreads), lds, st, a);
-    else hipLaunchKernelGGL((pairs_kernel<8, true>), dim3(num_wg), dim3(kWGThreads), lds, st, a);
-  } else {
-    if (k == 4) hipLaunchKernelGGL((pairs_kernel<4, false>), dim3(num_wg), dim3(kWGThreads), lds, st, a);
-    else hipLaunchKernelGGL((pairs_kernel<8, false>), dim3(num_wg), dim3(kWGThreads), lds, st, a);
-  }
-  return hipGetLastError();
+  const void *fn = select_pairs(dot64, k, full_span);
+  void *args[] = {const_cast<PairArgs *>(&a)};
+  return hipLaunchKernel(fn, dim3(num_wg), dim3(kWGThreads), args, lds, st);
 }
 
 hipError_t launch_merge(const unsigned long long *slots, int32_t nbins, const int32_t wb[3],
