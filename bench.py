@@ -9,8 +9,9 @@ vectors), the pair kernel + merge (DD, DR, RR), the totals reduction and omega.
 Prints one JSON line.  value = ordered pairs per second (N_D^2 + N_D N_R + N_R^2 per step).
 roofline: the pair kernel's algorithmic FP32 work (25 flops per evaluated pair, where the
 symmetric families evaluate N(N+1)/2 pairs) over its event-timed duration, against the
-MI355X FP32 vector peak.  cpu_baseline: the fp64 oracle on a bounded sample of the same
-workload (rows of D against all of R), on the host's cores.
+MI355X FP32 vector peak.  ceilings: measured VALU and LDS-atomic rates of this GPU, and the
+pair kernel's time expressed in those units.  cpu_baseline: the fp64 oracle on a bounded
+sample of the same workload (rows of D against all of R), on the host's cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
 """
@@ -25,6 +26,7 @@ sys.path.insert(0, ROOT)
 
 FLOPS_PER_PAIR = 25.0          # algorithmic FP32 flops per evaluated pair (FMA = 2)
 FP32_PEAK_TFLOPS = 157.3       # MI355X FP32 vector peak (published)
+NOMINAL_LANE_OPS = 256 * 64 * 2.4e9  # non-packed VALU lane operations per second at 2.4 GHz
 DEVICE_SOURCES = ("two_point_angular_amd/csrc/gc_kernels.hip", "two_point_angular_amd/csrc/gc_internal.h",
                   "two_point_angular_amd/csrc/gc_acos_poly.h", "two_point_angular_amd/csrc/gc_api.cpp")
 
@@ -77,6 +79,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="clustered100k_720")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the VALU / LDS ceiling microbenchmarks")
     ap.add_argument("--dot", type=int, default=0, help="tuning: dot-product precision (0 auto, 32, 64)")
     ap.add_argument("--k", type=int, default=0, help="tuning: i galaxies per lane (0 auto, 4, 8)")
     ap.add_argument("--blocks-per-cu", type=int, default=0)
@@ -182,6 +185,23 @@ def main():
                      "note": f"{FLOPS_PER_PAIR:.0f} algorithmic FP32 flops per evaluated pair"},
         "cpu_baseline": None,
     }
+    if not args.no_ceilings:
+        fma = gc.ceiling_valu(0)
+        sqrt = gc.ceiling_valu(1, iters=2048)
+        fma64 = gc.ceiling_valu(2)
+        lds_spread = gc.ceiling_lds_atomic(nbins)
+        lds_same = gc.ceiling_lds_atomic(nbins, same_bin=True, iters=256)
+        line["ceilings"] = {
+            "what": "measured on this GPU in this run: 8 independent chains per lane (VALU) and "
+                    "pure ds_add_u32 streams into per-wave LDS histograms (LDS)",
+            "fp32_fma_lane_ops_per_s": fma,
+            "fp32_fma_frac_of_nominal_2p4ghz": fma / NOMINAL_LANE_OPS,
+            "fp32_sqrt_lane_ops_per_s": sqrt,
+            "fp64_fma_lane_ops_per_s": fma64,
+            "lds_atomic_lane_ops_per_s": {"spread_bins": lds_spread, "same_bin": lds_same},
+            "pair_kernel_fma_slots_per_pair": fma * kernel_s / evaluated,
+            "pair_kernel_lds_atomic_frac": (evaluated / kernel_s) / lds_spread,
+        }
     if not args.no_cpu:
         sub_n = min(len(D), 100_000)
         line["cpu_baseline"] = cpu_baseline(D, R, nbins, w) if sub_n else None

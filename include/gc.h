@@ -156,6 +156,24 @@ gc_status gc_eval_angle_core(const float *d_x32, const double *d_x64, int64_t n,
                              int32_t *d_bin_out, uint8_t *d_trip_out, int32_t *d_exact_out,
                              void *d_workspace, size_t workspace_bytes, gc_stream_t stream);
 
+/* --------------------------------------------------------------- ceilings ----
+ * Microbenchmarks of the two resources the pair kernel uses, for reading its measured
+ * rate against what this GPU sustains (not part of the histogram computation).  Each
+ * launches 2048 workgroups of 256 threads on `stream`; the caller times the launch (HIP
+ * events on the same stream) and divides *ops_out / *atomics_out by the time.
+ *   gc_ceiling_valu: kind 0 = fp32 FMA, 1 = fp32 square root, 2 = fp64 FMA; 8 independent
+ *     chains per lane, `iters` iterations; *ops_out = lane operations executed.
+ *   gc_ceiling_lds_atomic: every lane adds 1 to its wavefront's private LDS histogram of
+ *     nbins words, 16 x iters times, at 16 pseudo-random bins (same_bin = 0) or always bin 0;
+ *     *atomics_out = lane atomics executed.
+ *   d_sink: device scratch of gc_ceiling_sink_bytes() bytes (results are discarded).
+ *   ops_out, atomics_out: host pointers. */
+size_t gc_ceiling_sink_bytes(void);
+gc_status gc_ceiling_valu(int32_t kind, int64_t iters, void *d_sink, size_t sink_bytes,
+                          uint64_t *ops_out, gc_stream_t stream);
+gc_status gc_ceiling_lds_atomic(int32_t nbins, int32_t same_bin, int64_t iters, void *d_sink,
+                                size_t sink_bytes, uint64_t *atomics_out, gc_stream_t stream);
+
 /* ----------------------------------------------------------------- status ---- */
 const char *gc_status_string(gc_status status);
 int gc_last_device_error(void); /* last hipError_t seen by this thread (0 if none) */

@@ -128,3 +128,12 @@ def test_totals_omega_core_validation(lib):
     assert ev(P(A), None, 10, 0, 0.25, 32, P(A), P(A), None, None, 0, None) == INVALID
     assert ev(P(A), None, 10, 720, 0.25, 32, P(A), P(A), P(A), None, 0, None) == INVALID     # exact, no ws
     assert ev(P(A), None, 10, 720, 0.25, 32, P(A), P(A), P(A), P(A), 100, None) == WORKSPACE
+    n = ctypes.c_uint64(0)
+    sink = lib.gc_ceiling_sink_bytes()
+    assert sink == 2048 * 256 * 4
+    assert lib.gc_ceiling_valu(3, 10, P(A), sink, ctypes.byref(n), None) == INVALID
+    assert lib.gc_ceiling_valu(0, 0, P(A), sink, ctypes.byref(n), None) == INVALID
+    assert lib.gc_ceiling_valu(0, 10, P(A), sink - 1, ctypes.byref(n), None) == WORKSPACE
+    assert lib.gc_ceiling_lds_atomic(0, 0, 10, P(A), sink, ctypes.byref(n), None) == INVALID
+    assert lib.gc_ceiling_lds_atomic(gc.MAX_BINS + 1, 0, 10, P(A), sink, ctypes.byref(n), None) == INVALID
+    assert lib.gc_ceiling_lds_atomic(720, 0, 10, None, sink, ctypes.byref(n), None) == INVALID

@@ -28,6 +28,7 @@ from dataclasses import dataclass
 
 __all__ = ["GCError", "Tuning", "library_path", "load", "prepared_bytes", "workspace_bytes",
            "prepare", "histogram_dd_dr_rr", "histogram_totals", "omega", "eval_angle_core",
+           "ceiling_valu", "ceiling_lds_atomic",
            "MAX_BINS", "MAX_GALAXIES", "ALIGNMENT"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -101,6 +102,9 @@ def load():
         "gc_histogram_totals": (i32, [vp, vp, vp, i32, vp, vp]),
         "gc_omega": (i32, [vp, vp, vp, i32, i64, i64, vp, vp]),
         "gc_eval_angle_core": (i32, [vp, vp, i64, i32, ctypes.c_double, i32, vp, vp, vp, vp, sz, vp]),
+        "gc_ceiling_sink_bytes": (sz, []),
+        "gc_ceiling_valu": (i32, [i32, i64, vp, sz, ctypes.POINTER(ctypes.c_uint64), vp]),
+        "gc_ceiling_lds_atomic": (i32, [i32, i32, i64, vp, sz, ctypes.POINTER(ctypes.c_uint64), vp]),
         "gc_status_string": (ctypes.c_char_p, [i32]),
         "gc_last_device_error": (ctypes.c_int, []),
         "gc_version": (ctypes.c_char_p, []),
@@ -223,3 +227,47 @@ def eval_angle_core(x, nbins: int, bin_width_deg: float, with_exact: bool = True
                                      ws.numel() if ws is not None else 0, _stream(stream)),
            "gc_eval_angle_core")
     return bins, trip, exact
+
+
+def _timed(launch, stream=None):
+    torch = _torch()
+    st = torch.cuda.current_stream() if stream is None else stream
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    n = launch(_stream(st))
+    e1.record(st)
+    e1.synchronize()
+    return n, e0.elapsed_time(e1) / 1e3
+
+
+def ceiling_valu(kind: int, iters: int = 4096, repeats: int = 3):
+    """Measured VALU rate (lane operations per second) of independent FMA chains (kind 0:
+    fp32 FMA, 1: fp32 square root, 2: fp64 FMA); best of `repeats` timed launches."""
+    torch = _torch()
+    sink = torch.empty(load().gc_ceiling_sink_bytes(), dtype=torch.uint8, device="cuda")
+    ops = ctypes.c_uint64(0)
+    best = None
+    for _ in range(repeats + 1):
+        def launch(s):
+            _check(load().gc_ceiling_valu(int(kind), int(iters), _ptr(sink), sink.numel(), ctypes.byref(ops), s),
+                   "gc_ceiling_valu")
+            return ops.value
+        n, dt = _timed(launch)
+        best = dt if best is None else min(best, dt)
+    return ops.value / best
+
+
+def ceiling_lds_atomic(nbins: int, same_bin: bool = False, iters: int = 2048, repeats: int = 3):
+    """Measured LDS atomic increments per second into per-wave histograms of nbins bins."""
+    torch = _torch()
+    sink = torch.empty(load().gc_ceiling_sink_bytes(), dtype=torch.uint8, device="cuda")
+    n_at = ctypes.c_uint64(0)
+    best = None
+    for _ in range(repeats + 1):
+        def launch(s):
+            _check(load().gc_ceiling_lds_atomic(int(nbins), int(bool(same_bin)), int(iters), _ptr(sink), sink.numel(),
+                                                ctypes.byref(n_at), s), "gc_ceiling_lds_atomic")
+            return n_at.value
+        n, dt = _timed(launch)
+        best = dt if best is None else min(best, dt)
+    return n_at.value / best
