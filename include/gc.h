@@ -150,11 +150,15 @@ gc_status gc_omega(const uint64_t *d_dd, const uint64_t *d_dr, const uint64_t *d
  *   d_exact_out: device, n int32, or null: the exact recheck's bin of the same cosine
  *                (fp32 cosines are widened exactly), found from the fast-path bin by the
  *                kernel's own edge-cosine search.  Needs d_workspace (at least
- *                gc_workspace_bytes(nbins) bytes, GC_ALIGNMENT-aligned) for the edge table. */
+ *                gc_workspace_bytes(nbins) bytes, GC_ALIGNMENT-aligned) for the edge table.
+ *   d_t_out    : device, n fp32, or null: the fast path's bin coordinate theta / width before
+ *                any clamping, for measuring the core's error.
+ * The kernel variant is the one gc_histogram_dd_dr_rr would use for these bins. */
 gc_status gc_eval_angle_core(const float *d_x32, const double *d_x64, int64_t n,
                              int32_t nbins, double bin_width_deg, int32_t dot_precision,
                              int32_t *d_bin_out, uint8_t *d_trip_out, int32_t *d_exact_out,
-                             void *d_workspace, size_t workspace_bytes, gc_stream_t stream);
+                             float *d_t_out, void *d_workspace, size_t workspace_bytes,
+                             gc_stream_t stream);
 
 /* --------------------------------------------------------------- ceilings ----
  * Microbenchmarks of the two resources the pair kernel uses, for reading its measured

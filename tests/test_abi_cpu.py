@@ -122,12 +122,12 @@ def test_totals_omega_core_validation(lib):
     assert lib.gc_omega(P(A), P(A), None, 10, 1, 1, P(A), None) == INVALID
     assert lib.gc_omega(P(A), P(A), P(A), 10, 1, 1, P(A + 4), None) == INVALID
     ev = lambda *a: lib.gc_eval_angle_core(*a)  # noqa: E731
-    assert ev(P(A), None, 10, 720, 0.25, 16, P(A), P(A), None, None, 0, None) == INVALID
-    assert ev(None, None, 10, 720, 0.25, 32, P(A), P(A), None, None, 0, None) == INVALID
-    assert ev(P(A), None, 0, 720, 0.25, 32, P(A), P(A), None, None, 0, None) == OK
-    assert ev(P(A), None, 10, 0, 0.25, 32, P(A), P(A), None, None, 0, None) == INVALID
-    assert ev(P(A), None, 10, 720, 0.25, 32, P(A), P(A), P(A), None, 0, None) == INVALID     # exact, no ws
-    assert ev(P(A), None, 10, 720, 0.25, 32, P(A), P(A), P(A), P(A), 100, None) == WORKSPACE
+    assert ev(P(A), None, 10, 720, 0.25, 16, P(A), P(A), None, None, None, 0, None) == INVALID
+    assert ev(None, None, 10, 720, 0.25, 32, P(A), P(A), None, None, None, 0, None) == INVALID
+    assert ev(P(A), None, 0, 720, 0.25, 32, P(A), P(A), None, None, None, 0, None) == OK
+    assert ev(P(A), None, 10, 0, 0.25, 32, P(A), P(A), None, None, None, 0, None) == INVALID
+    assert ev(P(A), None, 10, 720, 0.25, 32, P(A), P(A), P(A), None, None, 0, None) == INVALID  # exact, no ws
+    assert ev(P(A), None, 10, 720, 0.25, 32, P(A), P(A), P(A), None, P(A), 100, None) == WORKSPACE
     n = ctypes.c_uint64(0)
     sink = lib.gc_ceiling_sink_bytes()
     assert sink == 2048 * 256 * 4

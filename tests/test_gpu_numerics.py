@@ -40,7 +40,7 @@ def true_bins(x, nbins, w_deg):
 def run_core(gc, x, nbins, w):
     import torch
     xt = torch.from_numpy(x).to("cuda")
-    b, trip, exact = gc.eval_angle_core(xt, nbins, w)
+    b, trip, exact, _ = gc.eval_angle_core(xt, nbins, w)
     torch.cuda.synchronize()
     return b.cpu().numpy().astype(np.int64), trip.cpu().numpy().astype(bool), exact.cpu().numpy().astype(np.int64)
 
@@ -103,3 +103,62 @@ def test_fp64_core_sound_near_edges(gc, nbins, w):
     assert np.all((exact == tb) | near)
     r = trip[len(th): len(th) + 2_000_000].mean()
     assert r < 1.5e-2, r
+
+
+def _header_constant(name):
+    import os
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                        "two_point_angular_amd", "csrc", "gc_acos_poly.h")
+    for line in open(path):
+        parts = line.split()
+        if len(parts) >= 3 and parts[0] == "#define" and parts[1] == name:
+            return float(parts[2])
+    raise KeyError(name)
+
+
+def _core_t(gc, x, nbins, w):
+    import torch
+    xt = torch.from_numpy(x).to("cuda")
+    _, trip, _, t = gc.eval_angle_core(xt, nbins, w, with_exact=False, with_t=True)
+    torch.cuda.synchronize()
+    return t.cpu().numpy().astype(np.float64), trip.cpu().numpy().astype(bool)
+
+
+@pytest.mark.parametrize("nbins,w", [(720, 0.25), (3600, 0.05), (1500, 0.001)])
+def test_fp32_core_error_within_model(gc, nbins, w):
+    """The fp32 core's bin coordinate t against the exact acos(x)/w for the same fp32 cosine,
+    over every 64th fp32 value in [-1, 1].  The guard assumes |t~ - t| <= C(t) with
+    C(t) = E_core / w + 2^-24 (t + 2h) (core error with a 1-ulp square root, plus the
+    roundings that form t); the measured error must stay within it."""
+    print(f"[gpu] fp32 core error model nbins={nbins}", flush=True)
+    pos = np.arange(0, np.float32(1.0).view(np.uint32) + 1, 64, dtype=np.uint32).view(np.float32)
+    x = np.concatenate([pos, -pos[1:]]).astype(np.float32)
+    t, _ = _core_t(gc, x, nbins, w)
+    w_rad = np.radians(w)
+    t_exact = np.arccos(x.astype(np.float64)) / w_rad
+    err = np.abs(t - t_exact)
+    e_core = (_header_constant("GC_ACOS_CORE_ERR") + 2.0 ** -24 * (np.pi / 2)) * 1.25
+    h = (np.pi / 2) / w_rad
+    bound = e_core / w_rad + 2.0 ** -24 * (t_exact + 2 * h) * 1.01
+    ratio = err / bound
+    print(f"  max |t~ - t| = {err.max():.3e} bins; max ratio to the guard's bound {ratio.max():.3f}", flush=True)
+    assert ratio.max() <= 1.0
+    # the margin the guard keeps over what the hardware actually does
+    assert ratio.max() <= 0.9
+
+
+@pytest.mark.parametrize("nbins,w", [(720, 0.25), (1500, 0.001)])
+def test_fp64_core_error_within_model(gc, nbins, w):
+    """The fp64-dot core's t against acos(x)/w: the guard assumes a relative error rho."""
+    print(f"[gpu] fp64 core error model nbins={nbins}", flush=True)
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.uniform(-1, 1, 4_000_000), np.cos(rng.uniform(0, 0.05, 2_000_000)),
+                        1 - rng.random(100_000) * 1e-12])
+    t, _ = _core_t(gc, x, nbins, w)
+    t_exact = np.arccos(np.clip(x, -1, 1)) / np.radians(w)
+    rho = ((_header_constant("GC_ACOS_FIT_ERR") + 4 * 2.0 ** -24 * (np.pi / 2)) / 1.41 + 8 * 2.0 ** -24) * 1.25
+    sel = t_exact > 1e-3
+    rel = np.abs(t[sel] - t_exact[sel]) / t_exact[sel]
+    print(f"  max relative error {rel.max():.3e}; rho {rho:.3e}; ratio {rel.max() / rho:.3f}", flush=True)
+    assert rel.max() <= rho
+    assert np.all(np.abs(t[~sel] - t_exact[~sel]) < 1e-3 * rho + 1e-6)

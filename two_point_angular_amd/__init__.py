@@ -101,7 +101,7 @@ def load():
                                               ctypes.POINTER(_Tuning), vp]),
         "gc_histogram_totals": (i32, [vp, vp, vp, i32, vp, vp]),
         "gc_omega": (i32, [vp, vp, vp, i32, i64, i64, vp, vp]),
-        "gc_eval_angle_core": (i32, [vp, vp, i64, i32, ctypes.c_double, i32, vp, vp, vp, vp, sz, vp]),
+        "gc_eval_angle_core": (i32, [vp, vp, i64, i32, ctypes.c_double, i32, vp, vp, vp, vp, vp, sz, vp]),
         "gc_ceiling_sink_bytes": (sz, []),
         "gc_ceiling_valu": (i32, [i32, i64, vp, sz, ctypes.POINTER(ctypes.c_uint64), vp]),
         "gc_ceiling_lds_atomic": (i32, [i32, i32, i64, vp, sz, ctypes.POINTER(ctypes.c_uint64), vp]),
@@ -210,23 +210,25 @@ def omega(dd, dr, rr, n_d: int, n_r: int, out=None, stream=None):
     return out
 
 
-def eval_angle_core(x, nbins: int, bin_width_deg: float, with_exact: bool = True, stream=None):
+def eval_angle_core(x, nbins: int, bin_width_deg: float, with_exact: bool = True, with_t: bool = False,
+                    stream=None):
     """The pair kernel's angle-to-bin core on cosines x (fp32 -> fp32-dot core, fp64 ->
-    fp64-dot core).  Returns (bin, trip, exact_bin) device tensors."""
+    fp64-dot core).  Returns (bin, trip, exact_bin, t) device tensors (None where not asked)."""
     torch = _torch()
     n = x.numel()
     dot = 64 if x.dtype == torch.float64 else 32
     bins = torch.empty(n, dtype=torch.int32, device=x.device)
     trip = torch.empty(n, dtype=torch.uint8, device=x.device)
     exact = torch.empty(n, dtype=torch.int32, device=x.device) if with_exact else None
+    t = torch.empty(n, dtype=torch.float32, device=x.device) if with_t else None
     x32 = x if dot == 32 else None
     x64 = x if dot == 64 else None
     ws = torch.empty(workspace_bytes(nbins), dtype=torch.uint8, device=x.device) if with_exact else None
     _check(load().gc_eval_angle_core(_ptr(x32), _ptr(x64), n, int(nbins), float(bin_width_deg), dot,
-                                     _ptr(bins), _ptr(trip), _ptr(exact), _ptr(ws),
+                                     _ptr(bins), _ptr(trip), _ptr(exact), _ptr(t), _ptr(ws),
                                      ws.numel() if ws is not None else 0, _stream(stream)),
            "gc_eval_angle_core")
-    return bins, trip, exact
+    return bins, trip, exact, t
 
 
 def _timed(launch, stream=None):

@@ -341,7 +341,7 @@ gc_status gc_omega(const uint64_t *dd, const uint64_t *dr, const uint64_t *rr, i
 
 gc_status gc_eval_angle_core(const float *x32, const double *x64, int64_t n, int32_t nbins, double w_deg,
                              int32_t dot_precision, int32_t *bin_out, uint8_t *trip_out, int32_t *exact_out,
-                             void *workspace, size_t ws_bytes, gc_stream_t stream) {
+                             float *t_out, void *workspace, size_t ws_bytes, gc_stream_t stream) {
   gc_status st;
   if ((st = check_bins(nbins, w_deg)) != GC_OK) return st;
   if (n < 0 || (dot_precision != 32 && dot_precision != 64)) return GC_ERR_INVALID_ARGUMENT;
@@ -351,12 +351,15 @@ gc_status gc_eval_angle_core(const float *x32, const double *x64, int64_t n, int
   if (exact_out && ws_bytes < edge_table_bytes(nbins)) return GC_ERR_WORKSPACE;
   if (n == 0) return GC_OK;
   const BinParams bp = make_bins(nbins, w_deg);
+  // the same kernel variant the histogram call would use for these bins
+  const bool full_span = !d64 && (static_cast<double>(nbins) + 0.5) * w_deg >= 180.0;
   const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   double *edge_cos = static_cast<double *>(workspace);
   hipError_t e = hipSuccess;
   if (exact_out) e = launch_edges(nbins, w_deg, edge_cos, hs);
   if (e == hipSuccess)
-    e = launch_eval_core(x32, x64, n, bp, d64, exact_out ? edge_cos : nullptr, bin_out, trip_out, exact_out, hs);
+    e = launch_eval_core(x32, x64, n, bp, d64, full_span, exact_out ? edge_cos : nullptr, bin_out, trip_out,
+                         exact_out, t_out, hs);
   return e == hipSuccess ? GC_OK : device_error(e);
 }
 

@@ -102,8 +102,8 @@ hipError_t launch_omega(const uint64_t *dd, const uint64_t *dr, const uint64_t *
                         int64_t n_d, int64_t n_r, double *omega, hipStream_t s);
 hipError_t launch_edges(int32_t nbins, double w_deg, double *edge_cos, hipStream_t s);
 hipError_t launch_eval_core(const float *x32, const double *x64, int64_t n, const BinParams &bp,
-                            bool dot64, const double *edge_cos, int32_t *bin_out, uint8_t *trip_out,
-                            int32_t *exact_out, hipStream_t s);
+                            bool dot64, bool full_span, const double *edge_cos, int32_t *bin_out,
+                            uint8_t *trip_out, int32_t *exact_out, float *t_out, hipStream_t s);
 
 // Workspace layout: the edge-cosine table, then the per-workgroup 64-bit partial histograms.
 inline size_t edge_table_bytes(int32_t nbins) {

@@ -75,11 +75,13 @@ __device__ __forceinline__ float in_vgpr(float v) {
 // t = nbins, where no inner edge lies), never less.
 // h_v is (pi/2)/w held in a VGPR (see in_vgpr).
 template <bool FULL_SPAN>
-__device__ __forceinline__ void core32(float x, const BinParams &bp, float h_v, uint32_t &k, bool &trip) {
+__device__ __forceinline__ void core32(float x, const BinParams &bp, float h_v, uint32_t &k, bool &trip,
+                                       float &t_raw) {
   const float a = fabsf(x);
   const float s = __builtin_amdgcn_sqrtf(__builtin_amdgcn_fmed3f(1.0f - a, 0.0f, 1.0f));
   const float q = fmaf(-s, acos_poly(a), kHalfPiF);
   const float t = fmaf(copysignf(q, x), -bp.invw, h_v);
+  t_raw = t;
   const float tc = FULL_SPAN ? t : __builtin_amdgcn_fmed3f(t, 0.5f, bp.tmax);
   k = static_cast<uint32_t>(tc);
   trip = fabsf(tc - __builtin_rintf(tc)) * s < bp.g32;
@@ -89,7 +91,7 @@ __device__ __forceinline__ void core32(float x, const BinParams &bp, float h_v, 
 // in fp64 before narrowing, so small angles keep full relative precision.
 //   r = sqrt(1 - |x|) P(|x|) = acos(|x|);  t = r / w (x >= 0) or (pi - r) / w (x < 0).
 //   recheck iff |tc - round(tc)| * s < g64k1 * s + g64k2.
-__device__ __forceinline__ void core64(double x, const BinParams &bp, uint32_t &k, bool &trip) {
+__device__ __forceinline__ void core64(double x, const BinParams &bp, uint32_t &k, bool &trip, float &t_raw) {
   const double ax = fabs(x);
   const float y = static_cast<float>(fmax(1.0 - ax, 0.0));
   const float a = static_cast<float>(ax);
@@ -99,6 +101,7 @@ __device__ __forceinline__ void core64(double x, const BinParams &bp, uint32_t &
   const float cr = copysignf(r, __int_as_float(hi));
   const float off = __int_as_float((hi >> 31) & __float_as_int(bp.pinvw));
   const float t = fmaf(cr, bp.invw, off);
+  t_raw = t;
   const float tc = __builtin_amdgcn_fmed3f(t, 0.5f, bp.tmax);
   k = static_cast<uint32_t>(tc);
   trip = fabsf(tc - __builtin_rintf(tc)) * s < fmaf(s, bp.g64k1, bp.g64k2);
@@ -282,8 +285,9 @@ pairs_kernel(const PairArgs A) {
       uint32_t kk;
       bool tp;
       const real x = fma(ix[k], xj, fma(iy[k], yj, iz[k] * zj));
-      if constexpr (D64) core64(x, bp, kk, tp);
-      else core32<FULL_SPAN>(x, bp, h_v, kk, tp);
+      float t_unused;
+      if constexpr (D64) core64(x, bp, kk, tp, t_unused);
+      else core32<FULL_SPAN>(x, bp, h_v, kk, tp, t_unused);
       if constexpr (GENERIC) {
         const int64_t ig = i0 + lane + kWave * k;
         const bool valid = ig < F.n_i && (!F.sym || jg >= ig);
@@ -477,26 +481,31 @@ __global__ void __launch_bounds__(256) omega_kernel(const uint64_t *dd, const ui
 }
 
 // -------------------------------------------------------------------------- eval core
+template <bool FULL_SPAN>
 __global__ void __launch_bounds__(256) eval_core_kernel(const float *x32, const double *x64,
                                                         int64_t n, const BinParams bp, int dot64,
                                                         const double *edge_cos, int32_t *bin_out,
-                                                        uint8_t *trip_out, int32_t *exact_out) {
+                                                        uint8_t *trip_out, int32_t *exact_out, float *t_out) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (idx >= n) return;
   uint32_t k;
   bool trip;
   double xe;
+  float t;
   if (dot64) {
     xe = x64[idx];
-    core64(xe, bp, k, trip);
+    core64(xe, bp, k, trip, t);
   } else {
     const float xf = x32[idx];
     xe = static_cast<double>(xf);
-    core32<false>(xf, bp, bp.h, k, trip);
+    core32<FULL_SPAN>(xf, bp, bp.h, k, trip, t);
   }
-  bin_out[idx] = static_cast<int32_t>(k);
+  // k == nbins is the full-span kernel's spare bin, which the flush folds into bin nbins - 1
+  const uint32_t last = static_cast<uint32_t>(bp.nbins - 1);
+  bin_out[idx] = static_cast<int32_t>(k < last ? k : last);
   trip_out[idx] = trip ? 1 : 0;
   if (exact_out) exact_out[idx] = static_cast<int32_t>(exact_bin(xe, k, edge_cos, bp.nbins));
+  if (t_out) t_out[idx] = t;
 }
 
 }  // namespace
@@ -567,11 +576,15 @@ hipError_t launch_edges(int32_t nbins, double w_deg, double *edge_cos, hipStream
 }
 
 hipError_t launch_eval_core(const float *x32, const double *x64, int64_t n, const BinParams &bp,
-                            bool dot64, const double *edge_cos, int32_t *bin_out, uint8_t *trip_out,
-                            int32_t *exact_out, hipStream_t st) {
+                            bool dot64, bool full_span, const double *edge_cos, int32_t *bin_out,
+                            uint8_t *trip_out, int32_t *exact_out, float *t_out, hipStream_t st) {
   const int64_t blocks = (n + 255) / 256;
-  hipLaunchKernelGGL(eval_core_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, x32, x64, n,
-                     bp, dot64 ? 1 : 0, edge_cos, bin_out, trip_out, exact_out);
+  if (full_span)
+    hipLaunchKernelGGL(eval_core_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, x32, x64, n,
+                       bp, dot64 ? 1 : 0, edge_cos, bin_out, trip_out, exact_out, t_out);
+  else
+    hipLaunchKernelGGL(eval_core_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, x32, x64, n,
+                       bp, dot64 ? 1 : 0, edge_cos, bin_out, trip_out, exact_out, t_out);
   return hipGetLastError();
 }
 
