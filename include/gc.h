@@ -111,8 +111,10 @@ typedef struct {
     int32_t blocks_per_cu;   /* 0 auto (occupancy), else 1..8 workgroups per compute unit */
     int32_t shared_histogram; /* 0 auto; 1: one private LDS histogram per wavefront;
                                  2: one LDS histogram per workgroup, shared by its wavefronts */
-    int32_t full_span;       /* 0 auto; 1: always clamp the bin coordinate; 2: use the unclamped
-                                kernel (only valid when (nbins + 1/2) * width >= 180 deg) */
+    int32_t span_kernel;     /* 0 auto; 1: the generic core; 2: the core specialised to the
+                                bins' span - fp32 dot: no clamp of the bin coordinate (only
+                                valid when (nbins + 1/2) * width >= 180 deg); fp64 dot: no
+                                sign handling (only valid when nbins * width <= 90 deg) */
     int32_t reserved;        /* must be 0 */
     int64_t flush_interval;  /* 0 auto; else j-steps between flushes of the 32-bit LDS
                                 histograms into 64-bit totals (>= 1) */

@@ -96,13 +96,15 @@ def test_histogram_validation(lib):
     assert _hist(lib, ws=None) == INVALID
     assert _hist(lib, ws=P(A + 128)) == INVALID
     assert _hist(lib, wsb=gc.workspace_bytes(720) - 1) == WORKSPACE
-    T = gc._Tuning  # dot, K, blocks/CU, shared histogram, full span, reserved, flush interval
+    T = gc._Tuning  # dot, K, blocks/CU, shared histogram, span kernel, reserved, flush interval
     for bad in (T(33, 0, 0, 0, 0, 0, 0), T(0, 5, 0, 0, 0, 0, 0), T(0, 0, 9, 0, 0, 0, 0),
                 T(0, 0, -1, 0, 0, 0, 0), T(0, 0, 0, 3, 0, 0, 0), T(0, 0, 0, -1, 0, 0, 0),
                 T(0, 0, 0, 0, 3, 0, 0), T(0, 0, 0, 0, 0, 1, 0), T(0, 0, 0, 0, 0, 0, -3),
-                T(64, 0, 0, 0, 2, 0, 0)):                      # full span needs the fp32 kernel
+                T(64, 0, 0, 0, 2, 0, 0)):                      # fp64 narrow core: 180 deg > 90 deg
         assert _hist(lib, tuning=bad) == INVALID
     assert _hist(lib, nbins=700, tuning=T(0, 0, 0, 0, 2, 0, 0)) == INVALID  # 700 x 0.25 < 180 deg
+    assert _hist(lib, nbins=361, tuning=T(64, 0, 0, 0, 2, 0, 0)) == INVALID  # 361 x 0.25 > 90 deg
+    assert _hist(lib, nbins=1500, w=0.001, tuning=T(32, 0, 0, 0, 2, 0, 0)) == INVALID  # 1.5 < 180 deg
 
 
 @pytest.mark.skipif(not NO_GPU, reason="exercises the no-device error path; only without a GPU")

@@ -93,6 +93,26 @@ def test_small_and_ragged(gc, n_d, n_r):
                       budget=1.0 if n_d * n_r < 10**6 else MOVED_BUDGET)
 
 
+@pytest.mark.parametrize("nbins,w,tuning", [
+    (8192, 180.0 / 8192, {}),                        # the largest histogram, full span
+    (8192, 180.0 / 8192, dict(shared_histogram=1)),  # 8192-bin private histograms: 1 workgroup per CU
+    (8192, 180.0 / 8192, dict(shared_histogram=2)),
+    (8192, 0.0005, {}),                              # fp64 narrow core, 4.1 deg of bins
+    (1, 1.0, {}),                                    # a single bin takes every pair
+    (1, 1.0, dict(dot_precision=64)),
+    (2, 90.0, {}),                                   # two bins: one per hemisphere of separations
+    (2, 90.0, dict(dot_precision=64)),
+])
+def test_bin_count_extremes(gc, nbins, w, tuning):
+    print(f"[gpu] bin extremes nbins={nbins} w={w} tuning={tuning}", flush=True)
+    D = catalogs.clustered(1500, 21)
+    R = catalogs.uniform_sphere(1300, 22)
+    dd, dr, rr, tot, om = run_gpu(gc, D, R, nbins, w, tuning=gc.Tuning(**tuning))
+    assert list(tot) == [1500 * 1500, 1500 * 1300, 1300 * 1300]
+    check_against(f"bins={nbins} w={w} {tuning}", (dd, dr, rr), oracle_fams(D, R, nbins, w), 1500, 1300,
+                  budget=1.0)
+
+
 def test_empty_catalogs(gc):
     print("[gpu] empty catalogs", flush=True)
     D = catalogs.clustered(300, 8)
@@ -189,7 +209,7 @@ def test_outputs_overwritten_and_self_pairs(gc):
                                     dict(flush_interval=17, i_per_lane=4, dot_precision=64),
                                     dict(shared_histogram=1), dict(shared_histogram=2),
                                     dict(shared_histogram=2, flush_interval=5),
-                                    dict(full_span=1), dict(full_span=2, i_per_lane=4)])
+                                    dict(span_kernel=1), dict(span_kernel=2, i_per_lane=4)])
 def test_tuning_does_not_change_results(gc, tuning):
     print(f"[gpu] tuning {tuning}", flush=True)
     D, R = catalogs.WORKLOADS["clustered100k_720"].catalogs(n=6000)
@@ -197,6 +217,28 @@ def test_tuning_does_not_change_results(gc, tuning):
     base = run_gpu(gc, D, R, 720, 0.25)
     t = run_gpu(gc, D, R, 720, 0.25, tuning=gc.Tuning(**tuning))
     check_against(f"tuning {tuning}", t[:3], fams, len(D), len(R), t[4])
+    for x, y in zip(base[:3], t[:3]):
+        np.testing.assert_array_equal(x, y)
+
+
+@pytest.mark.parametrize("case", [
+    ("patch100k_1500", 1500, 0.001, dict(span_kernel=1)),
+    ("patch100k_1500", 1500, 0.001, dict(span_kernel=2, i_per_lane=4)),
+    ("patch100k_1500", 1500, 0.001, dict(dot_precision=32)),
+    ("patch100k_1500", 1500, 0.001, dict(shared_histogram=2, flush_interval=7)),
+    # bins ending exactly at 90 deg: every pair past 90 deg goes through the narrow core's
+    # x < 0 branch into the last bin
+    ("uniform10k_720", 360, 0.25, dict(dot_precision=64, span_kernel=2)),
+    ("uniform10k_720", 360, 0.25, dict(dot_precision=64, span_kernel=1)),
+])
+def test_fp64_span_variants(gc, case):
+    name, nbins, w, tuning = case
+    print(f"[gpu] {name} nbins={nbins} w={w} tuning {tuning}", flush=True)
+    D, R = catalogs.WORKLOADS[name].catalogs(n=6000)
+    fams = oracle_fams(D, R, nbins, w)
+    t = run_gpu(gc, D, R, nbins, w, tuning=gc.Tuning(**tuning))
+    check_against(f"{name} {tuning}", t[:3], fams, len(D), len(R), t[4])
+    base = run_gpu(gc, D, R, nbins, w, tuning=gc.Tuning(dot_precision=64))
     for x, y in zip(base[:3], t[:3]):
         np.testing.assert_array_equal(x, y)
 

@@ -56,7 +56,7 @@ class GCError(RuntimeError):
 class _Tuning(ctypes.Structure):
     _fields_ = [("dot_precision", ctypes.c_int32), ("i_per_lane", ctypes.c_int32),
                 ("blocks_per_cu", ctypes.c_int32), ("shared_histogram", ctypes.c_int32),
-                ("full_span", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("span_kernel", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("flush_interval", ctypes.c_int64)]
 
 
@@ -69,11 +69,11 @@ class Tuning:
     blocks_per_cu: int = 0
     flush_interval: int = 0
     shared_histogram: int = 0
-    full_span: int = 0
+    span_kernel: int = 0
 
     def _c(self) -> _Tuning:
         return _Tuning(self.dot_precision, self.i_per_lane, self.blocks_per_cu, self.shared_histogram,
-                       self.full_span, 0, self.flush_interval)
+                       self.span_kernel, 0, self.flush_interval)
 
 
 _lib = None

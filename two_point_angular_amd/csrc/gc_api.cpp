@@ -25,7 +25,7 @@ bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 struct DeviceInfo {
   bool valid = false;
   int cus = 0;
-  // occupancy per (kernel variant, lds bytes); variant = dot64 * 4 + full_span * 2 + (k == 8)
+  // occupancy per (kernel variant, lds bytes); variant = dot64 * 4 + span * 2 + (k == 8)
   struct Occ { size_t lds; int blocks; };
   Occ occ[8][8];
   int nocc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -34,7 +34,7 @@ constexpr int kMaxDevices = 64;
 std::mutex g_mu;
 DeviceInfo g_dev[kMaxDevices];
 
-hipError_t device_info(int *cus, bool dot64, int k, bool full_span, size_t lds, int *blocks_per_cu) {
+hipError_t device_info(int *cus, bool dot64, int k, bool span, size_t lds, int *blocks_per_cu) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -50,14 +50,14 @@ hipError_t device_info(int *cus, bool dot64, int k, bool full_span, size_t lds, 
   }
   *cus = d.cus;
   if (!blocks_per_cu) return hipSuccess;
-  const int vi = (dot64 ? 4 : 0) + (full_span ? 2 : 0) + (k == 8 ? 1 : 0);
+  const int vi = (dot64 ? 4 : 0) + (span ? 2 : 0) + (k == 8 ? 1 : 0);
   for (int q = 0; q < d.nocc[vi]; ++q)
     if (d.occ[vi][q].lds == lds) {
       *blocks_per_cu = d.occ[vi][q].blocks;
       return hipSuccess;
     }
   int blocks = 0;
-  e = pairs_occupancy(dot64, k, full_span, lds, &blocks);
+  e = pairs_occupancy(dot64, k, span, lds, &blocks);
   if (e != hipSuccess) return e;
   if (d.nocc[vi] < 8) d.occ[vi][d.nocc[vi]++] = {lds, blocks};
   *blocks_per_cu = blocks;
@@ -75,7 +75,9 @@ hipError_t device_info(int *cus, bool dot64, int k, bool full_span, size_t lds, 
 //    rechecks iff |t - round(t)| * s < g32 = 2.02 g_x / w + C, C = E_core / w + 2^-24 (nbins
 //    + 1 + 2h), which is implied by |t - round(t)| < 2.02 g_x / (s w) + C because s <= 1.
 //  fp64 dot: the cosine error is ~1e-15, so the dominant error is the fp32 core, relative
-//    to t: |t~ - t| <= rho t with rho covering sqrt, polynomial, narrowing and t roundings.
+//    to t: |t~ - t| <= rho t with rho covering sqrt, polynomial, narrowing and t roundings
+//    (two more units of 2^-24 for the narrow-range core, whose coefficients are rounded
+//    after scaling by 1 / w: sum |C_i| / P_min = 1.39 units).
 //    Recheck iff |t - round(t)| * s < g64k1 * s + g64k2, g64k1 = rho (nbins + 1),
 //    g64k2 = 2.02 g64 / w.
 constexpr double kTwoM24 = 5.9604644775390625e-08;  // 2^-24
@@ -98,12 +100,19 @@ BinParams make_bins(int32_t nbins, double w_deg) {
   const double c = e_core / w_rad + kTwoM24 * (static_cast<double>(nbins) + 1.0 + 2.0 * h) * 1.01;
   bp.g32 = static_cast<float>((2.02 * g_x / w_rad + c) * (1.0 + 1e-6));
   // fp64-dot guard
-  const double rho = ((GC_ACOS_FIT_ERR + 4.0 * kTwoM24 * (kPi / 2.0)) / 1.41 + 8.0 * kTwoM24) * 1.25;
+  const double rho = ((GC_ACOS_FIT_ERR + 4.0 * kTwoM24 * (kPi / 2.0)) / 1.41 + 10.0 * kTwoM24) * 1.25;
   const double g64 = 1e-14;
   bp.g64k1 = static_cast<float>(rho * (static_cast<double>(nbins) + 1.0) * (1.0 + 1e-6));
   bp.g64k2 = static_cast<float>(2.02 * g64 / w_rad * (1.0 + 1e-6));
+  const double coef[7] = {GC_ACOS_C0, GC_ACOS_C1, GC_ACOS_C2, GC_ACOS_C3, GC_ACOS_C4, GC_ACOS_C5, GC_ACOS_C6};
+  for (int q = 0; q < 7; ++q) bp.pw[q] = static_cast<float>(static_cast<double>(coef[q]) / w_rad);
   return bp;
 }
+
+// Spans the specialised cores accept: the fp32 core without a clamp needs nbins w to reach
+// 180 deg within half a bin; the fp64 core without sign handling needs nbins w <= 90 deg.
+bool span_full(int32_t nbins, double w_deg) { return (static_cast<double>(nbins) + 0.5) * w_deg >= 180.0; }
+bool span_narrow(int32_t nbins, double w_deg) { return static_cast<double>(nbins) * w_deg <= 90.0; }
 
 // ---- validation ------------------------------------------------------------------------------
 gc_status check_bins(int32_t nbins, double w) {
@@ -193,25 +202,28 @@ gc_status gc_histogram_dd_dr_rr_tuned(const void *prep_d, int64_t n_d, const voi
   if ((tu.dot_precision != 0 && tu.dot_precision != 32 && tu.dot_precision != 64) ||
       (tu.i_per_lane != 0 && tu.i_per_lane != 4 && tu.i_per_lane != 8) || tu.blocks_per_cu < 0 ||
       tu.blocks_per_cu > kMaxBlocksPerCU || tu.shared_histogram < 0 || tu.shared_histogram > 2 ||
-      tu.full_span < 0 || tu.full_span > 2 || tu.reserved != 0 || tu.flush_interval < 0)
+      tu.span_kernel < 0 || tu.span_kernel > 2 || tu.reserved != 0 || tu.flush_interval < 0)
     return GC_ERR_INVALID_ARGUMENT;
 
   // Plan.  Bins narrower than 0.01 deg put most pairs where the fp32 dot product cannot
   // certify the bin; those use the fp64 dot-product instantiation.
   const bool dot64 = tu.dot_precision == 64 || (tu.dot_precision == 0 && w_deg < 0.01);
-  const int k = tu.i_per_lane ? tu.i_per_lane : 8;
-  // When the bins reach 180 deg (up to half a bin), t cannot exceed nbins + 1 and the fp32
-  // kernel needs no clamp of t (a spare bin takes t = nbins).
-  const bool span_ok = (static_cast<double>(nbins) + 0.5) * w_deg >= 180.0;
-  if (tu.full_span == 2 && (dot64 || !span_ok)) return GC_ERR_INVALID_ARGUMENT;
-  const bool full_span = !dot64 && span_ok && tu.full_span != 1;
+  // Galaxies per lane: 8 for the fp32 kernel; 4 for the fp64 kernel, whose fp64 i-galaxies
+  // at K = 8 leave room for only three waves per SIMD.
+  const int k = tu.i_per_lane ? tu.i_per_lane : (dot64 ? 4 : 8);
+  // Span-specialised cores: when the bins reach 180 deg (up to half a bin), t cannot exceed
+  // nbins + 1 and the fp32 kernel needs no clamp of t (a spare bin takes t = nbins); when they
+  // end by 90 deg, the fp64 kernel needs no sign handling (x < 0 is the last bin).
+  const bool span_ok = dot64 ? span_narrow(nbins, w_deg) : span_full(nbins, w_deg);
+  if (tu.span_kernel == 2 && !span_ok) return GC_ERR_INVALID_ARGUMENT;
+  const bool span = span_ok && tu.span_kernel != 1;
   const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
 
   PairArgs a;
   memset(&a, 0, sizeof(a));
   a.nbins = nbins;
   a.hist_words = (nbins + 1 + 63) / 64 * 64;  // bin nbins: spare bin of the full-span kernel
-  a.wave_lds_words = a.hist_words + kQueueWords;
+  a.wave_lds_words = a.hist_words + queue_words(k);
   a.bp = make_bins(nbins, w_deg);
   double *edge_cos = static_cast<double *>(workspace);
   a.edge_cos = edge_cos;
@@ -240,9 +252,9 @@ gc_status gc_histogram_dd_dr_rr_tuned(const void *prep_d, int64_t n_d, const voi
     // Histogram placement: one private histogram per wave unless sharing one per workgroup
     // lets more workgroups fit in LDS.
     int cus = 0, occ = 0, occ_shared = 0;
-    hipError_t e = device_info(&cus, dot64, k, full_span, pairs_lds_bytes(a.hist_words, false), &occ);
+    hipError_t e = device_info(&cus, dot64, k, span, pairs_lds_bytes(a.hist_words, false, k), &occ);
     if (e != hipSuccess) return device_error(e);
-    e = device_info(&cus, dot64, k, full_span, pairs_lds_bytes(a.hist_words, true), &occ_shared);
+    e = device_info(&cus, dot64, k, span, pairs_lds_bytes(a.hist_words, true, k), &occ_shared);
     if (e != hipSuccess) return device_error(e);
     bool shared = tu.shared_histogram == 2 || (tu.shared_histogram == 0 && occ_shared > occ);
     if (shared) occ = occ_shared;
@@ -301,7 +313,7 @@ gc_status gc_histogram_dd_dr_rr_tuned(const void *prep_d, int64_t n_d, const voi
     num_wg = cur;
     e = launch_edges(nbins, w_deg, edge_cos, hs);
     if (e != hipSuccess) return device_error(e);
-    e = launch_pairs(a, num_wg, dot64, k, full_span, hs);
+    e = launch_pairs(a, num_wg, dot64, k, span, hs);
     if (e != hipSuccess) return device_error(e);
   }
   uint64_t *outs[3] = {dd, dr, rr};
@@ -351,14 +363,14 @@ gc_status gc_eval_angle_core(const float *x32, const double *x64, int64_t n, int
   if (exact_out && ws_bytes < edge_table_bytes(nbins)) return GC_ERR_WORKSPACE;
   if (n == 0) return GC_OK;
   const BinParams bp = make_bins(nbins, w_deg);
-  // the same kernel variant the histogram call would use for these bins
-  const bool full_span = !d64 && (static_cast<double>(nbins) + 0.5) * w_deg >= 180.0;
+  // the same core the histogram call would use for these bins
+  const bool span = d64 ? span_narrow(nbins, w_deg) : span_full(nbins, w_deg);
   const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   double *edge_cos = static_cast<double *>(workspace);
   hipError_t e = hipSuccess;
   if (exact_out) e = launch_edges(nbins, w_deg, edge_cos, hs);
   if (e == hipSuccess)
-    e = launch_eval_core(x32, x64, n, bp, d64, full_span, exact_out ? edge_cos : nullptr, bin_out, trip_out,
+    e = launch_eval_core(x32, x64, n, bp, d64, span, exact_out ? edge_cos : nullptr, bin_out, trip_out,
                          exact_out, t_out, hs);
   return e == hipSuccess ? GC_OK : device_error(e);
 }

@@ -11,8 +11,9 @@ namespace gc {
 constexpr int kWave = 64;            // CDNA wavefront width
 constexpr int kWavesPerWG = 4;       // pair-kernel workgroup = 4 independent wavefronts
 constexpr int kWGThreads = kWave * kWavesPerWG;
-constexpr int kMaxK = 8;             // largest i galaxies per lane
-constexpr int kQueueWords = 2 * kWave * (kMaxK + 1);  // per-wave recheck queue (8-byte entries)
+// Per-wave recheck queue, 8-byte entries: a j-step appends at most 64 K entries to fewer
+// than 64 pending ones, so 64 (K + 1) entries suffice.
+constexpr int queue_words(int k) { return 2 * kWave * (k + 1); }
 constexpr int kMaxWorkgroups = 2048; // partial-histogram slots held by the workspace
 constexpr int kMaxBlocksPerCU = 8;
 
@@ -51,6 +52,7 @@ struct BinParams {
   float g32;     // fp32-dot guard: recheck iff |t - round(t)| * s < g32
   float g64k1;   // fp64-dot guard: recheck iff |t - round(t)| * s < g64k1 * s + g64k2
   float g64k2;
+  float pw[7];   // acos polynomial coefficients times 1 / w_rad (fp32): narrow-range fp64 core
   int32_t nbins;
 };
 
@@ -77,23 +79,25 @@ struct PairArgs {
   int64_t flush_interval;      // j-steps between flushes of the 32-bit LDS histograms
   int32_t nbins;
   int32_t hist_words;          // LDS words of one histogram (>= nbins + 1: bin nbins is a spare)
-  int32_t wave_lds_words;      // hist_words + kQueueWords
+  int32_t wave_lds_words;      // hist_words + queue_words(K)
   int32_t shared_hist;         // 0: one histogram per wave; 1: one per workgroup (4 waves)
 };
 
 // LDS bytes of one pair-kernel workgroup.
-inline size_t pairs_lds_bytes(int32_t hist_words, bool shared_hist) {
-  const size_t words = shared_hist ? hist_words + static_cast<size_t>(kWavesPerWG) * kQueueWords
-                                   : static_cast<size_t>(kWavesPerWG) * (hist_words + kQueueWords);
+inline size_t pairs_lds_bytes(int32_t hist_words, bool shared_hist, int k) {
+  const size_t qw = static_cast<size_t>(queue_words(k));
+  const size_t words = shared_hist ? hist_words + static_cast<size_t>(kWavesPerWG) * qw
+                                   : static_cast<size_t>(kWavesPerWG) * (hist_words + qw);
   return words * sizeof(uint32_t);
 }
 
 // ---- launchers (gc_kernels.hip) ----------------------------------------------------------
 hipError_t launch_prepare(const float *ra, const float *dec, int64_t n, void *blob, hipStream_t s);
-// dot64: fp64 dot-product variant; k: galaxies per lane (4 or 8); full_span: nbins w covers
-// 180 deg (fp32 variant only: no clamp of t, spare bin instead)
-hipError_t launch_pairs(const PairArgs &a, int num_wg, bool dot64, int k, bool full_span, hipStream_t s);
-hipError_t pairs_occupancy(bool dot64, int k, bool full_span, size_t lds_bytes, int *blocks_per_cu);
+// dot64: fp64 dot-product variant; k: galaxies per lane (4 or 8); span: the variant
+// specialised to the bins' span - fp32 dot: nbins w covers 180 deg (no clamp of t, spare bin
+// instead); fp64 dot: nbins w <= 90 deg (no sign handling)
+hipError_t launch_pairs(const PairArgs &a, int num_wg, bool dot64, int k, bool span, hipStream_t s);
+hipError_t pairs_occupancy(bool dot64, int k, bool span, size_t lds_bytes, int *blocks_per_cu);
 hipError_t launch_merge(const unsigned long long *slots, int32_t nbins, const int32_t wg_begin[3],
                         const int32_t wg_end[3], uint64_t *out[3], hipStream_t s);
 hipError_t launch_totals(const uint64_t *dd, const uint64_t *dr, const uint64_t *rr, int32_t nbins,
@@ -102,7 +106,7 @@ hipError_t launch_omega(const uint64_t *dd, const uint64_t *dr, const uint64_t *
                         int64_t n_d, int64_t n_r, double *omega, hipStream_t s);
 hipError_t launch_edges(int32_t nbins, double w_deg, double *edge_cos, hipStream_t s);
 hipError_t launch_eval_core(const float *x32, const double *x64, int64_t n, const BinParams &bp,
-                            bool dot64, bool full_span, const double *edge_cos, int32_t *bin_out,
+                            bool dot64, bool span, const double *edge_cos, int32_t *bin_out,
                             uint8_t *trip_out, int32_t *exact_out, float *t_out, hipStream_t s);
 
 // Workspace layout: the edge-cosine table, then the per-workgroup 64-bit partial histograms.

@@ -91,20 +91,44 @@ __device__ __forceinline__ void core32(float x, const BinParams &bp, float h_v, 
 // in fp64 before narrowing, so small angles keep full relative precision.
 //   r = sqrt(1 - |x|) P(|x|) = acos(|x|);  t = r / w (x >= 0) or (pi - r) / w (x < 0).
 //   recheck iff |tc - round(tc)| * s < g64k1 * s + g64k2.
-__device__ __forceinline__ void core64(double x, const BinParams &bp, uint32_t &k, bool &trip, float &t_raw) {
-  const double ax = fabs(x);
-  const float y = static_cast<float>(fmax(1.0 - ax, 0.0));
-  const float a = static_cast<float>(ax);
-  const float s = __builtin_amdgcn_sqrtf(y);
-  const float r = s * acos_poly(a);
-  const int hi = __double2hiint(x);
-  const float cr = copysignf(r, __int_as_float(hi));
-  const float off = __int_as_float((hi >> 31) & __float_as_int(bp.pinvw));
-  const float t = fmaf(cr, bp.invw, off);
+// NARROW (nbins w <= 90 deg): a pair with x < 0 is past 90 degrees and belongs to the last
+// bin, so no sign handling is needed.  The signed x goes through the same expression with
+// 1 - x clamped to [0, 1]: for a in [-1, 0] every term of P(a) is positive (the
+// coefficients alternate in sign), so P(a) >= P(0) ~ pi/2 (1 - 1.3e-7) and, with s = 1,
+// t >= nbins (1 - 1e-6) > nbins - 1/2.  Such t clamps to the last bin and |tc - round(tc)|
+// = 1/2 keeps the guard quiet.  The coefficients come pre-scaled by 1 / w (bp.pw; the
+// highest one in a VGPR, pw6_v), so t = s P'(x) without a final multiply.
+template <bool NARROW>
+__device__ __forceinline__ void core64(double x, const BinParams &bp, float pw6_v, uint32_t &k, bool &trip,
+                                       float &t_raw) {
+  float s, t;
+  if constexpr (NARROW) {
+    s = __builtin_amdgcn_sqrtf(__builtin_amdgcn_fmed3f(static_cast<float>(1.0 - x), 0.0f, 1.0f));
+    const float a = static_cast<float>(x);
+    float p = fmaf(pw6_v, a, bp.pw[5]);
+    p = fmaf(p, a, bp.pw[4]);
+    p = fmaf(p, a, bp.pw[3]);
+    p = fmaf(p, a, bp.pw[2]);
+    p = fmaf(p, a, bp.pw[1]);
+    p = fmaf(p, a, bp.pw[0]);
+    t = s * p;
+  } else {
+    const double ax = fabs(x);
+    const float y = static_cast<float>(fmax(1.0 - ax, 0.0));
+    const float a = static_cast<float>(ax);
+    s = __builtin_amdgcn_sqrtf(y);
+    const float r = s * acos_poly(a);
+    const int hi = __double2hiint(x);
+    const float cr = copysignf(r, __int_as_float(hi));
+    const float off = __int_as_float((hi >> 31) & __float_as_int(bp.pinvw));
+    t = fmaf(cr, bp.invw, off);
+  }
   t_raw = t;
   const float tc = __builtin_amdgcn_fmed3f(t, 0.5f, bp.tmax);
   k = static_cast<uint32_t>(tc);
-  trip = fabsf(tc - __builtin_rintf(tc)) * s < fmaf(s, bp.g64k1, bp.g64k2);
+  // |tc - round(tc)| * s < g64k1 * s + g64k2, arranged so that each instruction reads one
+  // scalar constant
+  trip = (fabsf(tc - __builtin_rintf(tc)) - bp.g64k1) * s < bp.g64k2;
 }
 
 // Exact recheck in the cosine domain.  theta >= e w  <=>  x <= cos(e w), so bin k holds x
@@ -180,8 +204,10 @@ __device__ __forceinline__ void drain_queue(uint32_t *hist, const uint32_t *queu
   __builtin_amdgcn_wave_barrier();
 }
 
-template <int K, bool D64, bool FULL_SPAN>
-__global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu(D64 ? 3 : 4)))
+// SPAN selects the core specialised to the bins' span: fp32 dot, the full-span core;
+// fp64 dot, the narrow-range core.
+template <int K, bool D64, bool SPAN>
+__global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu((D64 && K == 8) ? 3 : 4)))
 pairs_kernel(const PairArgs A) {
   typedef typename Real<D64>::T real;
   constexpr int BI = kWave * K;       // i-block: galaxies per wave
@@ -192,14 +218,16 @@ pairs_kernel(const PairArgs A) {
   const int wv = threadIdx.x / kWave;
   // LDS: private mode, per wave [histogram | queue]; shared mode, [histogram | 4 queues].
   const bool shared_hist = A.shared_hist != 0;
-  uint32_t *const hist = shared_hist ? lds : lds + wv * (A.hist_words + kQueueWords);
-  uint32_t *const queue = shared_hist ? lds + A.hist_words + wv * kQueueWords : hist + A.hist_words;
+  constexpr int QW = queue_words(K);
+  uint32_t *const hist = shared_hist ? lds : lds + wv * (A.hist_words + QW);
+  uint32_t *const queue = shared_hist ? lds + A.hist_words + wv * QW : hist + A.hist_words;
   const int g = blockIdx.x;
   const int fi = g < A.fam[0].wg_end ? 0 : (g < A.fam[1].wg_end ? 1 : 2);
   const FamilyWork &F = A.fam[fi];
   const BinParams &bp = A.bp;
   const uint32_t W = F.sym ? 2u : 1u;
-  const float h_v = in_vgpr(bp.h);
+  // the one wave-uniform constant each core needs in a VGPR
+  const float c_v = in_vgpr(D64 ? bp.pw[6] : bp.h);
 
   unsigned long long *const slot = A.slots + static_cast<size_t>(g) * A.nbins;
   for (int b = threadIdx.x; b < A.nbins; b += kWGThreads) slot[b] = 0ull;
@@ -243,9 +271,8 @@ pairs_kernel(const PairArgs A) {
   int64_t i0 = 0;
   real ix[K], iy[K], iz[K];
 
-  // A j-step appends at most 64 K entries to fewer than 64 pending ones, and the queue is
-  // drained (64 at a time, from the top) after every j-step: 64 (K + 1) entries suffice.
-  static_assert(2 * kWave * (K + 1) <= kQueueWords, "recheck queue too small");
+  // The queue is drained (64 at a time, from the top) after every j-step, so it never holds
+  // more than 64 (K + 1) entries.
   auto drain = [&](int c) __attribute__((always_inline)) {
     drain_queue(hist, queue, qcount - c, c, F.ci, F.cj, i0, W, A.edge_cos, A.nbins);
     qcount -= c;
@@ -286,8 +313,8 @@ pairs_kernel(const PairArgs A) {
       bool tp;
       const real x = fma(ix[k], xj, fma(iy[k], yj, iz[k] * zj));
       float t_unused;
-      if constexpr (D64) core64(x, bp, kk, tp, t_unused);
-      else core32<FULL_SPAN>(x, bp, h_v, kk, tp, t_unused);
+      if constexpr (D64) core64<SPAN>(x, bp, c_v, kk, tp, t_unused);
+      else core32<SPAN>(x, bp, c_v, kk, tp, t_unused);
       if constexpr (GENERIC) {
         const int64_t ig = i0 + lane + kWave * k;
         const bool valid = ig < F.n_i && (!F.sym || jg >= ig);
@@ -481,7 +508,7 @@ __global__ void __launch_bounds__(256) omega_kernel(const uint64_t *dd, const ui
 }
 
 // -------------------------------------------------------------------------- eval core
-template <bool FULL_SPAN>
+template <bool SPAN>
 __global__ void __launch_bounds__(256) eval_core_kernel(const float *x32, const double *x64,
                                                         int64_t n, const BinParams bp, int dot64,
                                                         const double *edge_cos, int32_t *bin_out,
@@ -494,11 +521,11 @@ __global__ void __launch_bounds__(256) eval_core_kernel(const float *x32, const 
   float t;
   if (dot64) {
     xe = x64[idx];
-    core64(xe, bp, k, trip, t);
+    core64<SPAN>(xe, bp, bp.pw[6], k, trip, t);
   } else {
     const float xf = x32[idx];
     xe = static_cast<double>(xf);
-    core32<FULL_SPAN>(xf, bp, bp.h, k, trip, t);
+    core32<SPAN>(xf, bp, bp.h, k, trip, t);
   }
   // k == nbins is the full-span kernel's spare bin, which the flush folds into bin nbins - 1
   const uint32_t last = static_cast<uint32_t>(bp.nbins - 1);
@@ -526,25 +553,27 @@ template <int K, bool D64, bool FS> static const void *pairs_fn() {
   return reinterpret_cast<const void *>(&pairs_kernel<K, D64, FS>);
 }
 
-// Instantiations: K in {4, 8}; fp32 dot with and without the full-span specialisation;
-// fp64 dot (always clamped).
-static const void *select_pairs(bool dot64, int k, bool full_span) {
-  if (dot64) return k == 4 ? pairs_fn<4, true, false>() : pairs_fn<8, true, false>();
-  if (full_span) return k == 4 ? pairs_fn<4, false, true>() : pairs_fn<8, false, true>();
+// Instantiations: K in {4, 8} x {fp32, fp64 dot} x {generic, span-specialised core}.
+static const void *select_pairs(bool dot64, int k, bool span) {
+  if (dot64) {
+    if (span) return k == 4 ? pairs_fn<4, true, true>() : pairs_fn<8, true, true>();
+    return k == 4 ? pairs_fn<4, true, false>() : pairs_fn<8, true, false>();
+  }
+  if (span) return k == 4 ? pairs_fn<4, false, true>() : pairs_fn<8, false, true>();
   return k == 4 ? pairs_fn<4, false, false>() : pairs_fn<8, false, false>();
 }
 
-hipError_t pairs_occupancy(bool dot64, int k, bool full_span, size_t lds_bytes, int *blocks_per_cu) {
-  const void *fn = select_pairs(dot64, k, full_span);
+hipError_t pairs_occupancy(bool dot64, int k, bool span, size_t lds_bytes, int *blocks_per_cu) {
+  const void *fn = select_pairs(dot64, k, span);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      static_cast<int>(lds_bytes));
   if (e != hipSuccess) return e;
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, fn, kWGThreads, lds_bytes);
 }
 
-hipError_t launch_pairs(const PairArgs &a, int num_wg, bool dot64, int k, bool full_span, hipStream_t st) {
-  const size_t lds = pairs_lds_bytes(a.hist_words, a.shared_hist != 0);
-  const void *fn = select_pairs(dot64, k, full_span);
+hipError_t launch_pairs(const PairArgs &a, int num_wg, bool dot64, int k, bool span, hipStream_t st) {
+  const size_t lds = pairs_lds_bytes(a.hist_words, a.shared_hist != 0, k);
+  const void *fn = select_pairs(dot64, k, span);
   void *args[] = {const_cast<PairArgs *>(&a)};
   return hipLaunchKernel(fn, dim3(num_wg), dim3(kWGThreads), args, lds, st);
 }
@@ -576,10 +605,10 @@ hipError_t launch_edges(int32_t nbins, double w_deg, double *edge_cos, hipStream
 }
 
 hipError_t launch_eval_core(const float *x32, const double *x64, int64_t n, const BinParams &bp,
-                            bool dot64, bool full_span, const double *edge_cos, int32_t *bin_out,
+                            bool dot64, bool span, const double *edge_cos, int32_t *bin_out,
                             uint8_t *trip_out, int32_t *exact_out, float *t_out, hipStream_t st) {
   const int64_t blocks = (n + 255) / 256;
-  if (full_span)
+  if (span)
     hipLaunchKernelGGL(eval_core_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, x32, x64, n,
                        bp, dot64 ? 1 : 0, edge_cos, bin_out, trip_out, exact_out, t_out);
   else
