@@ -222,7 +222,7 @@ gc_status gc_histogram_dd_dr_rr_tuned(const void *prep_d, int64_t n_d, const voi
   PairArgs a;
   memset(&a, 0, sizeof(a));
   a.nbins = nbins;
-  a.hist_words = (nbins + 1 + 63) / 64 * 64;  // bin nbins: spare bin of the full-span kernel
+  a.hist_words = (nbins + kWave + 63) / 64 * 64;  // 64 spare bins past the last (see core32)
   a.wave_lds_words = a.hist_words + queue_words(k);
   a.bp = make_bins(nbins, w_deg);
   double *edge_cos = static_cast<double *>(workspace);

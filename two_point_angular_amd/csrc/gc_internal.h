@@ -48,7 +48,7 @@ struct BinParams {
   float invw;    // 1 / w_rad                       (fp32)
   float h;       // (pi/2) / w_rad                   (fp32)
   float pinvw;   // pi / w_rad                       (fp32)
-  float tmax;    // nbins - 0.5: clamp of t before truncation
+  float tmax;    // nbins - 0.5: clamp of t before truncation (plus the lane index in the pair kernel)
   float g32;     // fp32-dot guard: recheck iff |t - round(t)| * s < g32
   float g64k1;   // fp64-dot guard: recheck iff |t - round(t)| * s < g64k1 * s + g64k2
   float g64k2;
@@ -78,7 +78,7 @@ struct PairArgs {
   const double *edge_cos;      // [nbins + 1] cos(e w) in fp64, for the exact recheck
   int64_t flush_interval;      // j-steps between flushes of the 32-bit LDS histograms
   int32_t nbins;
-  int32_t hist_words;          // LDS words of one histogram (>= nbins + 1: bin nbins is a spare)
+  int32_t hist_words;          // LDS words of one histogram (>= nbins + 64: 64 spare bins)
   int32_t wave_lds_words;      // hist_words + queue_words(K)
   int32_t shared_hist;         // 0: one histogram per wave; 1: one per workgroup (4 waves)
 };

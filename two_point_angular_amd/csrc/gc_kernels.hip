@@ -66,23 +66,28 @@ __device__ __forceinline__ float in_vgpr(float v) {
 
 // fp32-dot core.  x is the fp32 dot product of the two fp32 unit vectors.
 //   s  = sqrt(1 - |x|) (clamped at 0),  q = pi/2 - s P(|x|) = pi/2 - acos(|x|)
-//   theta = pi/2 - sign(x) q,  t = theta / w,  tc = clamp(t, 0.5, nbins - 0.5)
+//   theta = pi/2 - sign(x) q,  t = theta / w,  tc = clamp(t, 0.5, tmax_v)
 //   k = trunc(tc); recheck iff |tc - round(tc)| * s < g32, i.e. iff an inner bin edge
 //   lies within the certified error bound 2.02 g_x / (s w) + C of t.
+// tmax_v = nbins - 1/2 + lane: past the last bin each lane clamps into a spare bin of its
+// own (bins nbins .. nbins + 63, folded into bin nbins - 1 by the flush), so a wave whose
+// pairs all lie beyond the binned range adds to 64 different LDS words instead of one.
+// The integers nbins .. nbins + 63 are edges of spare bins only; a pair the guard flags
+// near one is rechecked into bin nbins - 1, where it already counts.
 // FULL_SPAN (nbins w >= 180 deg - w/2): t stays below nbins + 1, so the clamp is dropped;
-// t = nbins lands in a spare bin that the flush folds into bin nbins - 1, and t in (-1, 0)
-// truncates to 0.  Without the clamp the guard can only trip more often (near t = 0 and
-// t = nbins, where no inner edge lies), never less.
+// t = nbins lands in spare bin nbins, and t in (-1, 0) truncates to 0.  Without the clamp
+// the guard can only trip more often (near t = 0 and t = nbins, where no inner edge lies),
+// never less.
 // h_v is (pi/2)/w held in a VGPR (see in_vgpr).
 template <bool FULL_SPAN>
-__device__ __forceinline__ void core32(float x, const BinParams &bp, float h_v, uint32_t &k, bool &trip,
-                                       float &t_raw) {
+__device__ __forceinline__ void core32(float x, const BinParams &bp, float h_v, float tmax_v, uint32_t &k,
+                                       bool &trip, float &t_raw) {
   const float a = fabsf(x);
   const float s = __builtin_amdgcn_sqrtf(__builtin_amdgcn_fmed3f(1.0f - a, 0.0f, 1.0f));
   const float q = fmaf(-s, acos_poly(a), kHalfPiF);
   const float t = fmaf(copysignf(q, x), -bp.invw, h_v);
   t_raw = t;
-  const float tc = FULL_SPAN ? t : __builtin_amdgcn_fmed3f(t, 0.5f, bp.tmax);
+  const float tc = FULL_SPAN ? t : __builtin_amdgcn_fmed3f(t, 0.5f, tmax_v);
   k = static_cast<uint32_t>(tc);
   trip = fabsf(tc - __builtin_rintf(tc)) * s < bp.g32;
 }
@@ -95,12 +100,13 @@ __device__ __forceinline__ void core32(float x, const BinParams &bp, float h_v, 
 // bin, so no sign handling is needed.  The signed x goes through the same expression with
 // 1 - x clamped to [0, 1]: for a in [-1, 0] every term of P(a) is positive (the
 // coefficients alternate in sign), so P(a) >= P(0) ~ pi/2 (1 - 1.3e-7) and, with s = 1,
-// t >= nbins (1 - 1e-6) > nbins - 1/2.  Such t clamps to the last bin and |tc - round(tc)|
-// = 1/2 keeps the guard quiet.  The coefficients come pre-scaled by 1 / w (bp.pw; the
-// highest one in a VGPR, pw6_v), so t = s P'(x) without a final multiply.
+// t >= nbins (1 - 1e-6) > nbins - 1/2, which truncates to the last bin or a spare bin past
+// it (the guard may flag it near a spare bin's edge; the recheck keeps it in the last bin).  The coefficients come pre-scaled by 1 / w (bp.pw; the
+// highest one in a VGPR, pw6_v), so t = s P'(x) without a final multiply.  tmax_v: as in
+// core32, each lane's own spare bin past the last bin.
 template <bool NARROW>
-__device__ __forceinline__ void core64(double x, const BinParams &bp, float pw6_v, uint32_t &k, bool &trip,
-                                       float &t_raw) {
+__device__ __forceinline__ void core64(double x, const BinParams &bp, float pw6_v, float tmax_v, uint32_t &k,
+                                       bool &trip, float &t_raw) {
   float s, t;
   if constexpr (NARROW) {
     s = __builtin_amdgcn_sqrtf(__builtin_amdgcn_fmed3f(static_cast<float>(1.0 - x), 0.0f, 1.0f));
@@ -124,7 +130,7 @@ __device__ __forceinline__ void core64(double x, const BinParams &bp, float pw6_
     t = fmaf(cr, bp.invw, off);
   }
   t_raw = t;
-  const float tc = __builtin_amdgcn_fmed3f(t, 0.5f, bp.tmax);
+  const float tc = __builtin_amdgcn_fmed3f(t, 0.5f, tmax_v);
   k = static_cast<uint32_t>(tc);
   // |tc - round(tc)| * s < g64k1 * s + g64k2, arranged so that each instruction reads one
   // scalar constant
@@ -184,7 +190,8 @@ template <> struct Real<true> { typedef double T; };
 
 // Re-bin the c <= 64 queued pairs in entries [first, first + c) exactly in fp64 (one pair
 // per lane) and move their counts from the fast-path bin to the exact bin.  Entry e: word
-// 2e = j, word 2e+1 = (i - i0) << 16 | fast-path bin.
+// 2e = j, word 2e+1 = (i - i0) << 16 | fast-path bin.  A fast-path bin >= nbins is a spare
+// bin standing for bin nbins - 1.
 __device__ __forceinline__ void drain_queue(uint32_t *hist, const uint32_t *queue, int first, int c,
                                             const Prepared &ci, const Prepared &cj, int64_t i0, uint32_t w,
                                             const double *edge_cos, int32_t nbins) {
@@ -195,8 +202,10 @@ __device__ __forceinline__ void drain_queue(uint32_t *hist, const uint32_t *queu
     const uint32_t jj = queue[2 * e];
     const uint32_t p = queue[2 * e + 1];
     const uint32_t kf = p & 0xffffu;
-    const uint32_t ke = exact_bin(dot64(ci, i0 + (p >> 16), cj, jj), kf, edge_cos, nbins);
-    if (ke != kf) {
+    const uint32_t last = static_cast<uint32_t>(nbins - 1);
+    const uint32_t kr = kf < last ? kf : last;
+    const uint32_t ke = exact_bin(dot64(ci, i0 + (p >> 16), cj, jj), kr, edge_cos, nbins);
+    if (ke != kr) {
       atomicSub(hist + kf, w);
       atomicAdd(hist + ke, w);
     }
@@ -205,9 +214,13 @@ __device__ __forceinline__ void drain_queue(uint32_t *hist, const uint32_t *queu
 }
 
 // SPAN selects the core specialised to the bins' span: fp32 dot, the full-span core;
-// fp64 dot, the narrow-range core.
+// fp64 dot, the narrow-range core.  Register budgets: K = 4 builds for six waves per SIMD
+// (<= 80 VGPRs), fp32 K = 8 for five (<= 96; its 24 fp32 i-coordinates), fp64 K = 8 for four
+// (48 VGPRs of fp64 i-coordinates).  Measured on the 100k workloads, each step up in waves
+// per SIMD outweighed the few spills it costs outside the pair loop.
 template <int K, bool D64, bool SPAN>
-__global__ void __launch_bounds__(kWGThreads) __attribute__((amdgpu_waves_per_eu((D64 && K == 8) ? 3 : 4)))
+__global__ void __launch_bounds__(kWGThreads)
+__attribute__((amdgpu_waves_per_eu(K == 4 ? 6 : (D64 ? 4 : 5))))
 pairs_kernel(const PairArgs A) {
   typedef typename Real<D64>::T real;
   constexpr int BI = kWave * K;       // i-block: galaxies per wave
@@ -215,7 +228,10 @@ pairs_kernel(const PairArgs A) {
   extern __shared__ uint32_t lds[];
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int wv = threadIdx.x / kWave;
+  // The wave index is the same in every lane; readfirstlane tells the compiler so, which keeps
+  // the step range, the loop counters and every j index in SGPRs (scalar loads of j, scalar
+  // branches).
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   // LDS: private mode, per wave [histogram | queue]; shared mode, [histogram | 4 queues].
   const bool shared_hist = A.shared_hist != 0;
   constexpr int QW = queue_words(K);
@@ -226,8 +242,9 @@ pairs_kernel(const PairArgs A) {
   const FamilyWork &F = A.fam[fi];
   const BinParams &bp = A.bp;
   const uint32_t W = F.sym ? 2u : 1u;
-  // the one wave-uniform constant each core needs in a VGPR
+  // the one wave-uniform constant each core needs in a VGPR, and this lane's clamp
   const float c_v = in_vgpr(D64 ? bp.pw[6] : bp.h);
+  const float tmax_v = bp.tmax + static_cast<float>(lane);
 
   unsigned long long *const slot = A.slots + static_cast<size_t>(g) * A.nbins;
   for (int b = threadIdx.x; b < A.nbins; b += kWGThreads) slot[b] = 0ull;
@@ -283,15 +300,18 @@ pairs_kernel(const PairArgs A) {
   // Move the LDS histogram into the workgroup's 64-bit slot.  Each bin is taken with an
   // atomic exchange, so in shared mode other waves may keep adding meanwhile; the value is
   // read as signed because a pending recheck may have moved a count out of a bin that an
-  // earlier flush already emptied (the flush interval keeps every bin within +-2^31).
+  // earlier flush already emptied (the flush interval keeps every bin within +-2^31).  The
+  // 64 spare bins past nbins are summed across the wave and added to bin nbins - 1.
   auto flush = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_wave_barrier();
-    for (int bb = lane; bb <= A.nbins; bb += kWave) {  // bin nbins is the spare bin
+    for (int bb = lane; bb < A.nbins; bb += kWave) {
       const uint32_t c = atomicExch(hist + bb, 0u);
-      if (c)
-        atomicAdd(slot + (bb < A.nbins ? bb : A.nbins - 1),
-                  static_cast<unsigned long long>(static_cast<long long>(static_cast<int>(c))));
+      if (c) atomicAdd(slot + bb, static_cast<unsigned long long>(static_cast<long long>(static_cast<int>(c))));
     }
+    long long spare = static_cast<int>(atomicExch(hist + A.nbins + lane, 0u));
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) spare += __shfl_xor(spare, off, kWave);
+    if (lane == 0 && spare) atomicAdd(slot + (A.nbins - 1), static_cast<unsigned long long>(spare));
     __builtin_amdgcn_wave_barrier();
   };
   auto load_j = [&](int64_t jj, real &x, real &y, real &z) __attribute__((always_inline)) {
@@ -313,8 +333,8 @@ pairs_kernel(const PairArgs A) {
       bool tp;
       const real x = fma(ix[k], xj, fma(iy[k], yj, iz[k] * zj));
       float t_unused;
-      if constexpr (D64) core64<SPAN>(x, bp, c_v, kk, tp, t_unused);
-      else core32<SPAN>(x, bp, c_v, kk, tp, t_unused);
+      if constexpr (D64) core64<SPAN>(x, bp, c_v, tmax_v, kk, tp, t_unused);
+      else core32<SPAN>(x, bp, c_v, tmax_v, kk, tp, t_unused);
       if constexpr (GENERIC) {
         const int64_t ig = i0 + lane + kWave * k;
         const bool valid = ig < F.n_i && (!F.sym || jg >= ig);
@@ -521,11 +541,11 @@ __global__ void __launch_bounds__(256) eval_core_kernel(const float *x32, const 
   float t;
   if (dot64) {
     xe = x64[idx];
-    core64<SPAN>(xe, bp, bp.pw[6], k, trip, t);
+    core64<SPAN>(xe, bp, bp.pw[6], bp.tmax, k, trip, t);
   } else {
     const float xf = x32[idx];
     xe = static_cast<double>(xf);
-    core32<SPAN>(xf, bp, bp.h, k, trip, t);
+    core32<SPAN>(xf, bp, bp.h, bp.tmax, k, trip, t);
   }
   // k == nbins is the full-span kernel's spare bin, which the flush folds into bin nbins - 1
   const uint32_t last = static_cast<uint32_t>(bp.nbins - 1);
