@@ -72,6 +72,89 @@ def cpu_baseline(D, R, nbins, w, target_s=12.0):
                       f"{dt2:.1f} s on {threads} threads)"}
 
 
+LADDER_VARIANTS = [
+    # label, rung, arccos, tile, bin stride (0: nbins)
+    ("L0 one thread per pair, per-pair sin/cos, acosf", 0, "rung", 0, 0),
+    ("L1 + DD/RR symmetry", 1, "rung", 0, 0),
+    ("L2 + per-galaxy sin/cos prepass", 2, "rung", 0, 0),
+    ("L3 + LDS j-tile (512)", 3, "rung", 512, 0),
+    ("L4 + handbook polynomial acos", 4, "rung", 512, 0),
+    ("L5 + unroll 8, launch bounds, diagonal skip", 5, "rung", 512, 0),
+    ("L5 with acosf", 5, "libm", 512, 0),
+    ("L5 with the degree-6 fit (no guard)", 5, "fit6", 512, 0),
+    ("L5 tile 64", 5, "rung", 64, 0),
+    ("L5 tile 128", 5, "rung", 128, 0),
+    ("L5 tile 256", 5, "rung", 256, 0),
+    ("L5 tile 1024", 5, "rung", 1024, 0),
+    ("L5 bins padded to a multiple of 64", 5, "rung", 512, -64),
+    ("L5 bin stride nbins + 1", 5, "rung", 512, -1),
+]
+
+
+def run_ladder(gc, wl, D, R, ra_d, dec_d, ra_r, dec_r, pd, pr, out, ws, reps, warmup):
+    """Time each ladder variant (HIP events around the call, median of `reps`) and compare its
+    counts with the certified path's: moved pairs = sum over edges of |net flow|, the number of
+    bins that differ, and the largest omega change where RR >= 1000."""
+    import numpy as np
+    import torch
+
+    n_d, n_r, nbins, w = len(D), len(R), wl.nbins, wl.bin_width_deg
+    ordered = float(n_d * n_d + n_d * n_r + n_r * n_r)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts)), float(np.min(ts))
+
+    def omega(h):
+        dd, dr, rr = (x.astype(np.float64) for x in h)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            return (dd / n_d**2 - 2 * dr / (n_d * n_r) + rr / n_r**2) / (rr / n_r**2)
+
+    gc.prepare(ra_d, dec_d, out=pd)
+    gc.prepare(ra_r, dec_r, out=pr)
+    ms, mn = timed(lambda: gc.histogram_dd_dr_rr(pd, n_d, pr, n_r, nbins, w, out=out, workspace=ws))
+    ref = [x.cpu().numpy().astype(np.int64) for x in out]
+    ref_om = omega(ref)
+    rows = [{"variant": "certified path (gc.h pair kernel)", "ms": ms, "min_ms": mn, "moved_pairs": 0,
+             "bins_differing": 0, "max_abs_domega": 0.0}]
+    lws = torch.empty(gc.ladder_workspace_bytes(n_d, n_r), dtype=torch.uint8, device=out.device)
+    lout = torch.empty_like(out)
+    for label, rung, acos, tile, stride in LADDER_VARIANTS:
+        st = stride if stride >= 0 else (((nbins + 63) // 64) * 64 if stride == -64 else nbins + 1)
+
+        def call():
+            gc.ladder_histogram(rung, ra_d, dec_d, ra_r, dec_r, nbins, w, acos=acos, tile=tile, bin_stride=st,
+                                out=lout, workspace=lws)
+        ms, mn = timed(call)
+        h = [x.cpu().numpy().astype(np.int64) for x in lout]
+        for x, want in zip(h, (n_d * n_d, n_d * n_r, n_r * n_r)):
+            if int(x.sum()) != want:
+                print(f"{label}: total {int(x.sum())} != {want}", file=sys.stderr)
+                sys.exit(1)
+        moved = int(sum(np.abs(np.cumsum(a - b)[:-1]).sum() for a, b in zip(h, ref)))
+        differing = int(np.any(np.stack([a != b for a, b in zip(h, ref)]), axis=0).sum())
+        ok = ref[2] >= 1000
+        dom = float(np.max(np.abs(omega(h)[ok] - ref_om[ok]))) if ok.any() else 0.0
+        rows.append({"variant": label, "rung": rung, "acos": acos, "tile": tile, "bin_stride": st, "ms": ms,
+                     "min_ms": mn, "moved_pairs": moved, "bins_differing": differing, "max_abs_domega": dom})
+    for r in rows:
+        print(f"# {r['variant']:50s} {r['ms']:10.3f} ms  {ordered / (r['ms'] / 1e3):.3e} pairs/s  "
+              f"moved {r['moved_pairs']:9d}  bins differing {r['bins_differing']:4d}  "
+              f"max|d omega| {r['max_abs_domega']:.2e}", flush=True)
+    print(json.dumps({"ladder": rows, "workload": wl.name, "ordered_pairs": ordered, "reps": reps,
+                      "what": "median of HIP-event-timed calls; counts compared with the certified path"}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -83,6 +166,9 @@ def main():
     ap.add_argument("--dot", type=int, default=0, help="tuning: dot-product precision (0 auto, 32, 64)")
     ap.add_argument("--k", type=int, default=0, help="tuning: i galaxies per lane (0 auto, 4, 8)")
     ap.add_argument("--blocks-per-cu", type=int, default=0)
+    ap.add_argument("--ladder", action="store_true",
+                    help="instead of the bench line: time every rung of the page's ablation ladder "
+                         "(include/gc_ladder.h) on the workload and compare its counts with the exact path")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after timing, copy this many bytes device-to-device with a plain copy kernel "
                          "(reference dispatch for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -113,6 +199,9 @@ def main():
     ws = torch.empty(gc.workspace_bytes(nbins), dtype=torch.uint8, device=dev)
     om = torch.empty(nbins, dtype=torch.float64, device=dev)
     totals = torch.empty((args.steps + args.warmup, 3), dtype=torch.int64, device=dev)
+    if args.ladder:
+        run_ladder(gc, wl, D, R, ra_d, dec_d, ra_r, dec_r, pd, pr, out, ws, max(args.steps, 1), args.warmup)
+        return
     tuning = None
     if args.dot or args.k or args.blocks_per_cu:
         tuning = gc.Tuning(dot_precision=args.dot, i_per_lane=args.k, blocks_per_cu=args.blocks_per_cu)

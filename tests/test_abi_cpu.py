@@ -10,7 +10,8 @@ import pytest
 import two_point_angular_amd as gc
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "gc.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 OK, INVALID, UNSUPPORTED, WORKSPACE, DEVICE = 0, 1, 2, 3, 4
 A = 4096  # a 256-aligned fake device address; never dereferenced
@@ -25,15 +26,16 @@ def lib():
     return gc.load()
 
 
-def header_functions():
-    text = open(HEADER).read()
+def header_functions(path):
+    text = open(path).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(gc_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_function(lib):
-    names = header_functions()
-    assert len(names) >= 11
+    assert [os.path.basename(h) for h in HEADERS] == ["gc.h", "gc_ladder.h"]
+    names = [n for h in HEADERS for n in header_functions(h)]
+    assert len(names) >= 13
     for name in names:
         assert hasattr(lib, name), name
 
@@ -139,3 +141,35 @@ def test_totals_omega_core_validation(lib):
     assert lib.gc_ceiling_lds_atomic(0, 0, 10, P(A), sink, ctypes.byref(n), None) == INVALID
     assert lib.gc_ceiling_lds_atomic(gc.MAX_BINS + 1, 0, 10, P(A), sink, ctypes.byref(n), None) == INVALID
     assert lib.gc_ceiling_lds_atomic(720, 0, 10, None, sink, ctypes.byref(n), None) == INVALID
+
+
+def test_ladder_validation(lib):
+    P = ctypes.c_void_p
+    assert lib.gc_ladder_workspace_bytes(-1, 0) == 0
+    assert lib.gc_ladder_workspace_bytes(0, gc_ladder_max() + 1) == 0
+    assert lib.gc_ladder_workspace_bytes(10, 100) == 3 * (256 + 512)
+
+    def lad(rung=3, acos=-1, tile=0, stride=0, nd=10, nr=10, nbins=720, w=0.25, ws=P(A), wsb=1 << 30, **kw):
+        p = dict(rad=P(A), decd=P(A), rar=P(A), decr=P(A), dd=P(A), dr=P(A + 8192), rr=P(A + 16384))
+        p.update(kw)
+        return lib.gc_ladder_histogram(rung, acos, tile, stride, p["rad"], p["decd"], nd, p["rar"], p["decr"], nr,
+                                       nbins, w, p["dd"], p["dr"], p["rr"], ws, wsb, None)
+
+    for bad in (dict(rung=-1), dict(rung=6), dict(acos=-2), dict(acos=3), dict(rung=0, tile=64),
+                dict(tile=32), dict(tile=100), dict(tile=2048), dict(stride=719), dict(nbins=0), dict(w=0.0),
+                dict(w=float("nan")), dict(nd=-1), dict(rad=None), dict(decr=P(A + 2)), dict(dd=None),
+                dict(rr=P(A + 4)), dict(ws=None), dict(ws=P(A + 8))):
+        assert lad(**bad) == INVALID, bad
+    assert lad(nbins=gc.MAX_BINS + 1) == UNSUPPORTED
+    assert lad(nd=gc_ladder_max() + 1) == UNSUPPORTED
+    assert lad(stride=40000) == UNSUPPORTED                       # LDS footprint above 160 KiB
+    assert lad(rung=2, wsb=lib.gc_ladder_workspace_bytes(10, 10) - 1) == WORKSPACE
+    if NO_GPU:  # valid arguments (rungs 0-1 need no workspace); the launch then fails without a device
+        assert lad(rung=1, ws=None, wsb=0) == DEVICE
+
+
+def gc_ladder_max():
+    for line in open(os.path.join(ROOT, "include", "gc_ladder.h")):
+        if line.startswith("#define GC_LADDER_MAX_GALAXIES"):
+            return int(line.split()[2].rstrip("LL"))
+    raise KeyError

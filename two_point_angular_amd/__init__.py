@@ -102,6 +102,9 @@ def load():
         "gc_histogram_totals": (i32, [vp, vp, vp, i32, vp, vp]),
         "gc_omega": (i32, [vp, vp, vp, i32, i64, i64, vp, vp]),
         "gc_eval_angle_core": (i32, [vp, vp, i64, i32, ctypes.c_double, i32, vp, vp, vp, vp, vp, sz, vp]),
+        "gc_ladder_workspace_bytes": (sz, [i64, i64]),
+        "gc_ladder_histogram": (i32, [i32, i32, i32, i32, vp, vp, i64, vp, vp, i64, i32, ctypes.c_double, vp, vp,
+                                      vp, vp, sz, vp]),
         "gc_ceiling_sink_bytes": (sz, []),
         "gc_ceiling_valu": (i32, [i32, i64, vp, sz, ctypes.POINTER(ctypes.c_uint64), vp]),
         "gc_ceiling_lds_atomic": (i32, [i32, i32, i64, vp, sz, ctypes.POINTER(ctypes.c_uint64), vp]),
@@ -229,6 +232,37 @@ def eval_angle_core(x, nbins: int, bin_width_deg: float, with_exact: bool = True
                                      ws.numel() if ws is not None else 0, _stream(stream)),
            "gc_eval_angle_core")
     return bins, trip, exact, t
+
+
+LADDER_RUNGS = 6
+LADDER_ACOS = {"rung": -1, "libm": 0, "handbook": 1, "fit6": 2}
+
+
+def ladder_workspace_bytes(n_d: int, n_r: int) -> int:
+    return int(load().gc_ladder_workspace_bytes(int(n_d), int(n_r)))
+
+
+def ladder_histogram(rung: int, ra_d, dec_d, ra_r, dec_r, nbins: int, bin_width_deg: float, acos: str = "rung",
+                     tile: int = 0, bin_stride: int = 0, out=None, workspace=None, stream=None):
+    """(DD, DR, RR) of one rung of the page's ablation ladder (fp32 arithmetic, no guard; see
+    include/gc_ladder.h) from fp32 arcmin device tensors."""
+    torch = _torch()
+    for t, nm in ((ra_d, "ra_d"), (dec_d, "dec_d"), (ra_r, "ra_r"), (dec_r, "dec_r")):
+        _need(t, torch.float32, nm)
+    n_d, n_r = ra_d.numel(), ra_r.numel()
+    if dec_d.numel() != n_d or dec_r.numel() != n_r:
+        raise ValueError("ra and dec must have the same length")
+    dev = ra_d.device
+    if out is None:
+        out = torch.empty((3, nbins), dtype=torch.int64, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(ladder_workspace_bytes(n_d, n_r), 1), dtype=torch.uint8, device=dev)
+    _check(load().gc_ladder_histogram(int(rung), LADDER_ACOS[acos], int(tile), int(bin_stride), _ptr(ra_d),
+                                      _ptr(dec_d), n_d, _ptr(ra_r), _ptr(dec_r), n_r, int(nbins),
+                                      float(bin_width_deg), _ptr(out[0]), _ptr(out[1]), _ptr(out[2]),
+                                      _ptr(workspace), workspace.numel(), _stream(stream)),
+           "gc_ladder_histogram")
+    return out[0], out[1], out[2]
 
 
 def _timed(launch, stream=None):

@@ -21,7 +21,7 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-I", os.path.join(ROOT, "include")]
 
-SOURCES = ["gc_kernels.hip", "gc_api.cpp", "gc_ceilings.hip"]
+SOURCES = ["gc_kernels.hip", "gc_api.cpp", "gc_ceilings.hip", "gc_ladder.hip"]
 
 
 def hipcc() -> str:

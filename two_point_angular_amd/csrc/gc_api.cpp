@@ -19,6 +19,12 @@ gc_status device_error(hipError_t e) {
   return GC_ERR_DEVICE;
 }
 
+}  // namespace
+
+void record_hip_error(hipError_t e) { t_last_hip_error = static_cast<int>(e); }
+
+namespace {
+
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // ---- per-device cache: CU count and pair-kernel occupancy -----------------------------

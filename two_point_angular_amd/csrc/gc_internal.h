@@ -91,6 +91,9 @@ inline size_t pairs_lds_bytes(int32_t hist_words, bool shared_hist, int k) {
   return words * sizeof(uint32_t);
 }
 
+// Records a failed HIP call for gc_last_device_error() (gc_api.cpp).
+void record_hip_error(hipError_t e);
+
 // ---- launchers (gc_kernels.hip) ----------------------------------------------------------
 hipError_t launch_prepare(const float *ra, const float *dec, int64_t n, void *blob, hipStream_t s);
 // dot64: fp64 dot-product variant; k: galaxies per lane (4 or 8); span: the variant
