@@ -48,7 +48,8 @@ typedef enum {
                                     finite, misaligned buffer, bad tuning field */
     GC_ERR_UNSUPPORTED = 2,      /* nbins above GC_MAX_BINS, n above GC_MAX_GALAXIES */
     GC_ERR_WORKSPACE = 3,        /* workspace smaller than gc_workspace_bytes() */
-    GC_ERR_DEVICE = 4            /* a HIP call or kernel launch failed; see gc_last_device_error() */
+    GC_ERR_DEVICE = 4,           /* a HIP call or kernel launch failed; see gc_last_device_error() */
+    GC_ERR_IO = 5                /* a file could not be opened, mapped, parsed or written (gc_io.h) */
 } gc_status;
 
 #define GC_MAX_BINS 8192                 /* bins per histogram (LDS-resident per wavefront) */

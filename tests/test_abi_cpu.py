@@ -33,9 +33,9 @@ def header_functions(path):
 
 
 def test_exports_every_declared_function(lib):
-    assert [os.path.basename(h) for h in HEADERS] == ["gc.h", "gc_ladder.h"]
+    assert [os.path.basename(h) for h in HEADERS] == ["gc.h", "gc_io.h", "gc_ladder.h"]
     names = [n for h in HEADERS for n in header_functions(h)]
-    assert len(names) >= 13
+    assert len(names) >= 16
     for name in names:
         assert hasattr(lib, name), name
 
@@ -54,6 +54,7 @@ def test_sizes(lib):
 def test_status_strings(lib):
     assert lib.gc_status_string(0) == b"ok"
     assert lib.gc_status_string(3) == b"workspace too small"
+    assert lib.gc_status_string(5) == b"file input/output error"
     assert lib.gc_status_string(99) == b"unknown status"
     assert lib.gc_version().startswith(b"gc ")
     assert lib.gc_last_device_error() == 0

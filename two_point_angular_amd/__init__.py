@@ -40,7 +40,7 @@ ALIGNMENT = 256
 
 GC_OK = 0
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported size", 3: "workspace too small",
-           4: "device error"}
+           4: "device error", 5: "file input/output error"}
 
 
 class GCError(RuntimeError):
@@ -105,6 +105,9 @@ def load():
         "gc_ladder_workspace_bytes": (sz, [i64, i64]),
         "gc_ladder_histogram": (i32, [i32, i32, i32, i32, vp, vp, i64, vp, vp, i64, i32, ctypes.c_double, vp, vp,
                                       vp, vp, sz, vp]),
+        "gc_catalog_count": (i32, [ctypes.c_char_p, ctypes.POINTER(i64)]),
+        "gc_catalog_read": (i32, [ctypes.c_char_p, vp, vp, i64, ctypes.POINTER(i64)]),
+        "gc_omega_write": (i32, [ctypes.c_char_p, vp, vp, vp, vp, i32, ctypes.c_double]),
         "gc_ceiling_sink_bytes": (sz, []),
         "gc_ceiling_valu": (i32, [i32, i64, vp, sz, ctypes.POINTER(ctypes.c_uint64), vp]),
         "gc_ceiling_lds_atomic": (i32, [i32, i32, i64, vp, sz, ctypes.POINTER(ctypes.c_uint64), vp]),
@@ -232,6 +235,41 @@ def eval_angle_core(x, nbins: int, bin_width_deg: float, with_exact: bool = True
                                      ws.numel() if ws is not None else 0, _stream(stream)),
            "gc_eval_angle_core")
     return bins, trip, exact, t
+
+
+CLI_PATH = os.path.join(_PKG, "bin", "galaxy_gc")
+
+
+def catalog_count(path: str) -> int:
+    """Galaxy count of a catalog text file (its first token)."""
+    n = ctypes.c_int64(0)
+    _check(load().gc_catalog_count(os.fsencode(path), ctypes.byref(n)), "gc_catalog_count")
+    return n.value
+
+
+def read_catalog(path: str):
+    """(alpha, delta) fp32 host arrays in arcminutes from a catalog text file."""
+    import numpy as np
+    n = catalog_count(path)
+    ra = np.empty(n, dtype=np.float32)
+    dec = np.empty(n, dtype=np.float32)
+    got = ctypes.c_int64(0)
+    _check(load().gc_catalog_read(os.fsencode(path), ra.ctypes.data_as(ctypes.c_void_p),
+                                  dec.ctypes.data_as(ctypes.c_void_p), n, ctypes.byref(got)), "gc_catalog_read")
+    return ra, dec
+
+
+def write_omega(path: str, dd, dr, rr, omega_values, bin_width_deg: float) -> None:
+    """Write the result file (the page's omega.out layout) from host arrays."""
+    import numpy as np
+    arrs = [np.ascontiguousarray(np.asarray(x), dtype=np.uint64) for x in (dd, dr, rr)]
+    om = np.ascontiguousarray(np.asarray(omega_values), dtype=np.float64)
+    nb = om.size
+    if any(a.size != nb for a in arrs):
+        raise ValueError("dd, dr, rr and omega must have the same length")
+    vp = ctypes.c_void_p
+    _check(load().gc_omega_write(os.fsencode(path), *[a.ctypes.data_as(vp) for a in arrs], om.ctypes.data_as(vp),
+                                 nb, float(bin_width_deg)), "gc_omega_write")
 
 
 LADDER_RUNGS = 6

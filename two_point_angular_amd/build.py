@@ -14,6 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libgc.so")
+BINDIR = os.path.join(PKG, "bin")
+CLI = os.path.join(BINDIR, "galaxy_gc")
 ARCH = "gfx950"
 
 # -packed-fp32-ops: no packed FP32 (v_pk_*_f32) instructions anywhere in the device code.
@@ -21,7 +23,8 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-I", os.path.join(ROOT, "include")]
 
-SOURCES = ["gc_kernels.hip", "gc_api.cpp", "gc_ceilings.hip", "gc_ladder.hip"]
+SOURCES = ["gc_kernels.hip", "gc_api.cpp", "gc_ceilings.hip", "gc_ladder.hip", "gc_io.cpp"]
+CLI_SOURCE = "galaxy_gc.cpp"   # the end-to-end program, linked against libgc.so
 
 
 def hipcc() -> str:
@@ -53,7 +56,24 @@ def build(verbose: bool = False) -> str:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("link of libgc.so failed")
     os.replace(tmp, LIB)
+    build_cli(verbose)
     return LIB
+
+
+def build_cli(verbose: bool = False) -> str:
+    """galaxy_gc (bin/), linked against lib/libgc.so through an $ORIGIN-relative rpath."""
+    os.makedirs(BINDIR, exist_ok=True)
+    tmp = CLI + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), *HIP_FLAGS, "-x", "hip", os.path.join(CSRC, CLI_SOURCE), "-o", tmp, "-L", LIBDIR, "-lgc",
+           "-Wl,-rpath,$ORIGIN/../lib"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("build of galaxy_gc failed")
+    os.replace(tmp, CLI)
+    return CLI
 
 
 if __name__ == "__main__":

@@ -138,3 +138,30 @@ WORKLOADS = {
     "clustered1m_720": Workload("clustered1m_720", 1_000_000, 720, 0.25, "clustered"),
     "patch100k_1500": Workload("patch100k_1500", 100_000, 1500, 0.001, "patch"),
 }
+
+
+def write_text(cat: Catalog, path: str) -> None:
+    """Write a catalog in the page's input format: the galaxy count, then one "alpha delta"
+    line per galaxy in arcminutes.  Nine significant digits identify every fp32 value, so
+    a reader that rounds correctly gets the same fp32 catalog back."""
+    with open(path, "w") as f:
+        f.write(f"{len(cat)}\n")
+        f.write("".join(f"{a:.9g} {d:.9g}\n" for a, d in zip(cat.ra.tolist(), cat.dec.tolist())))
+
+
+def _main(argv=None) -> int:
+    import argparse
+    ap = argparse.ArgumentParser(description="Write a workload's D and R catalogs as text files.")
+    ap.add_argument("workload", choices=sorted(WORKLOADS))
+    ap.add_argument("d_path")
+    ap.add_argument("r_path")
+    ap.add_argument("-n", type=int, default=None, help="first n galaxies only")
+    a = ap.parse_args(argv)
+    D, R = WORKLOADS[a.workload].catalogs(n=a.n)
+    write_text(D, a.d_path)
+    write_text(R, a.r_path)
+    return 0
+
+
+if __name__ == "__main__":
+    raise SystemExit(_main())

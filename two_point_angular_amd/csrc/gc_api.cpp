@@ -164,6 +164,7 @@ const char *gc_status_string(gc_status s) {
     case GC_ERR_UNSUPPORTED: return "unsupported size";
     case GC_ERR_WORKSPACE: return "workspace too small";
     case GC_ERR_DEVICE: return "device error";
+    case GC_ERR_IO: return "file input/output error";
   }
   return "unknown status";
 }
