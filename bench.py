@@ -166,6 +166,8 @@ def main():
     ap.add_argument("--dot", type=int, default=0, help="tuning: dot-product precision (0 auto, 32, 64)")
     ap.add_argument("--k", type=int, default=0, help="tuning: i galaxies per lane (0 auto, 4, 8)")
     ap.add_argument("--blocks-per-cu", type=int, default=0)
+    ap.add_argument("--parts", type=int, default=1,
+                    help="run each step's histogram job as this many additive parts (gc_histogram_part)")
     ap.add_argument("--ladder", action="store_true",
                     help="instead of the bench line: time every rung of the page's ablation ladder "
                          "(include/gc_ladder.h) on the workload and compare its counts with the exact path")
@@ -211,7 +213,13 @@ def main():
         gc.prepare(ra_r, dec_r, out=pr)
         if ev is not None:
             ev[0].record()
-        dd, dr, rr = gc.histogram_dd_dr_rr(pd, n_d, pr, n_r, nbins, w, out=out, workspace=ws, tuning=tuning)
+        if args.parts == 1:
+            dd, dr, rr = gc.histogram_dd_dr_rr(pd, n_d, pr, n_r, nbins, w, out=out, workspace=ws, tuning=tuning)
+        else:
+            out.zero_()
+            for p in range(args.parts):
+                gc.histogram_part(pd, n_d, pr, n_r, nbins, w, p, args.parts, out, workspace=ws, tuning=tuning)
+            dd, dr, rr = out[0], out[1], out[2]
         if ev is not None:
             ev[1].record()
         gc.histogram_totals(dd, dr, rr, out=totals[idx])
@@ -266,9 +274,10 @@ def main():
                    "catalogs": f"D {wl.kind} seed 1, R uniform seed 2" if wl.kind == "clustered" else
                    f"D {wl.kind} seed 1, R {wl.kind} seed 2",
                    "ordered_pairs_per_step": ordered, "evaluated_pairs_per_step": evaluated,
-                   "parallelism": "1 GPU"},
+                   "parallelism": "1 GPU", **({"parts": args.parts} if args.parts != 1 else {})},
         "kernel_ms": {"mean": float(np.mean(kern_ms)), "median": float(np.median(kern_ms)),
-                      "min": float(np.min(kern_ms)), "what": "pair kernel + merge, HIP events"},
+                      "min": float(np.min(kern_ms)),
+                      "what": "pair kernel + merge, HIP events" + (f" ({args.parts} parts)" if args.parts != 1 else "")},
         "roofline": {"bound": "alu", "achieved": achieved, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / FP32_PEAK_TFLOPS, "traffic": measured_traffic(wl.name),
                      "note": f"{FLOPS_PER_PAIR:.0f} algorithmic FP32 flops per evaluated pair"},

@@ -128,6 +128,33 @@ gc_status gc_histogram_dd_dr_rr_tuned(const void *d_prepared_d, int64_t n_d,
                                       void *d_workspace, size_t workspace_bytes,
                                       const gc_tuning *tuning, gc_stream_t stream);
 
+/* ------------------------------------------------------------------ parts ----
+ * One part of the histogram job, for catalogs too large to process in one call
+ * (N >> 10^6), for checkpointing, or for spreading the job over several devices or
+ * processes.  The histograms are additive over any partition of the pairs (section
+ * "L1: DD/RR symmetry" sums weighted pairs; nothing else couples them), so the job is
+ * cut into `parts` pieces: part p takes, in each of DD, DR and RR, the work units
+ * floor(T p / parts) .. floor(T (p+1) / parts) of the T units the single call uses.
+ * Each pair's bin depends on that pair alone, so the parts of one job, in any order
+ * and on any device, sum exactly to gc_histogram_dd_dr_rr's result.
+ *
+ * Unlike gc_histogram_dd_dr_rr this call ACCUMULATES: it adds the part's counts to
+ * d_dd, d_dr, d_rr (zero them before part 0).  Arguments are those of
+ * gc_histogram_dd_dr_rr_tuned (tuning may be null), plus:
+ *   part, parts : 1 <= parts <= GC_MAX_PARTS, 0 <= part < parts.  Every part of one
+ *                 job must use the same catalogs, bins and tuning.
+ * A part that holds no work for a family adds nothing to it.  Calls that add into the
+ * same outputs must be ordered (the same stream, or synchronised).
+ */
+#define GC_MAX_PARTS (1LL << 40)
+gc_status gc_histogram_part(const void *d_prepared_d, int64_t n_d,
+                            const void *d_prepared_r, int64_t n_r,
+                            int32_t nbins, double bin_width_deg,
+                            int64_t part, int64_t parts,
+                            uint64_t *d_dd, uint64_t *d_dr, uint64_t *d_rr,
+                            void *d_workspace, size_t workspace_bytes,
+                            const gc_tuning *tuning, gc_stream_t stream);
+
 /* ----------------------------------------------------------------- totals ----
  * The three histogram sums, for the exact-total check of section "The problem"
  * (each family must sum to N_a * N_b).  d_totals: device, 3 uint64 (DD, DR, RR

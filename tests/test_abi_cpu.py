@@ -174,3 +174,36 @@ def gc_ladder_max():
         if line.startswith("#define GC_LADDER_MAX_GALAXIES"):
             return int(line.split()[2].rstrip("LL"))
     raise KeyError
+
+
+def test_part_validation(lib):
+    P = ctypes.c_void_p
+
+    def part(p, n, **kw):
+        a = dict(pd=P(A), nd=10, pr=P(A), nr=10, nbins=720, w=0.25)
+        a.update(kw)
+        return lib.gc_histogram_part(a["pd"], a["nd"], a["pr"], a["nr"], a["nbins"], a["w"], p, n, P(A),
+                                     P(A + 8192), P(A + 16384), P(A), gc.workspace_bytes(720), None, None)
+
+    for p, n in ((0, 0), (-1, 4), (4, 4), (5, 4), (0, gc.MAX_PARTS + 1)):
+        assert part(p, n) == INVALID, (p, n)
+    assert part(0, 2, nbins=0) == INVALID
+    assert part(0, 2, pd=P(A + 4)) == INVALID
+    if NO_GPU:
+        assert part(1, 2) == DEVICE
+
+
+def test_checkpoint_files(tmp_path):
+    from two_point_angular_amd import parts
+    import numpy as np
+    meta = parts._meta(10, 12, 720, 0.25, 7, "k", None)
+    path = str(tmp_path / "ck.npz")
+    assert parts.load_checkpoint(path, meta) is None
+    h = np.arange(3 * 720, dtype=np.uint64).reshape(3, 720) * np.uint64(1 << 40)
+    parts.save_checkpoint(path, meta, 3, h)
+    nxt, back = parts.load_checkpoint(path, meta)
+    assert nxt == 3 and np.array_equal(back, h)
+    other = parts._meta(10, 12, 720, 0.25, 8, "k", None)
+    with pytest.raises(ValueError, match="another job"):
+        parts.load_checkpoint(path, other)
+    assert sorted(os.listdir(tmp_path)) == ["ck.npz"]          # the temporary file was renamed

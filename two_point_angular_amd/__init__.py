@@ -99,6 +99,8 @@ def load():
         "gc_histogram_dd_dr_rr": (i32, [vp, i64, vp, i64, i32, ctypes.c_double, vp, vp, vp, vp, sz, vp]),
         "gc_histogram_dd_dr_rr_tuned": (i32, [vp, i64, vp, i64, i32, ctypes.c_double, vp, vp, vp, vp, sz,
                                               ctypes.POINTER(_Tuning), vp]),
+        "gc_histogram_part": (i32, [vp, i64, vp, i64, i32, ctypes.c_double, i64, i64, vp, vp, vp, vp, sz,
+                                    ctypes.POINTER(_Tuning), vp]),
         "gc_histogram_totals": (i32, [vp, vp, vp, i32, vp, vp]),
         "gc_omega": (i32, [vp, vp, vp, i32, i64, i64, vp, vp]),
         "gc_eval_angle_core": (i32, [vp, vp, i64, i32, ctypes.c_double, i32, vp, vp, vp, vp, vp, sz, vp]),
@@ -196,6 +198,26 @@ def histogram_dd_dr_rr(prep_d, n_d: int, prep_r, n_r: int, nbins: int, bin_width
         st = lib.gc_histogram_dd_dr_rr_tuned(*args, ctypes.byref(tc), _stream(stream))
     _check(st, "gc_histogram_dd_dr_rr")
     return dd, dr, rr
+
+
+MAX_PARTS = 1 << 40
+
+
+def histogram_part(prep_d, n_d: int, prep_r, n_r: int, nbins: int, bin_width_deg: float, part: int, parts: int,
+                   out, workspace=None, tuning: Tuning | None = None, stream=None):
+    """ADD part `part` of `parts` of the (DD, DR, RR) job into `out` ((3, nbins) int64 device
+    tensor); the parts of one job sum exactly to histogram_dd_dr_rr's result."""
+    torch = _torch()
+    dev = out.device
+    if workspace is None:
+        workspace = torch.empty(max(workspace_bytes(nbins), 1), dtype=torch.uint8, device=dev)
+    tc = tuning._c() if tuning is not None else None
+    _check(load().gc_histogram_part(_ptr(prep_d), int(n_d), _ptr(prep_r), int(n_r), int(nbins),
+                                    float(bin_width_deg), int(part), int(parts), _ptr(out[0]), _ptr(out[1]),
+                                    _ptr(out[2]), _ptr(workspace), workspace.numel(),
+                                    ctypes.byref(tc) if tc is not None else None, _stream(stream)),
+           "gc_histogram_part")
+    return out
 
 
 def histogram_totals(dd, dr, rr, out=None, stream=None):

@@ -191,10 +191,18 @@ size_t gc_workspace_bytes(int32_t nbins) {
   return workspace_bytes(nbins);
 }
 
-gc_status gc_histogram_dd_dr_rr_tuned(const void *prep_d, int64_t n_d, const void *prep_r, int64_t n_r,
-                                      int32_t nbins, double w_deg, uint64_t *dd, uint64_t *dr,
-                                      uint64_t *rr, void *workspace, size_t ws_bytes,
-                                      const gc_tuning *tuning, gc_stream_t stream) {
+}  // extern "C"
+
+namespace gc {
+namespace {
+
+// The histogram call and its parts.  Part p of P takes, in every family, the j-steps
+// floor(T p / P) .. floor(T (p+1) / P) of the same decomposition; with accumulate the merge adds
+// to the outputs.  Every pair's bin is fixed by the pair alone (the lane always holds the lower
+// index of a self pair, and the recheck is exact), so the parts sum to the single call's result.
+gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, int64_t n_r, int32_t nbins,
+                         double w_deg, uint64_t *dd, uint64_t *dr, uint64_t *rr, void *workspace, size_t ws_bytes,
+                         const gc_tuning *tuning, int64_t part, int64_t parts, bool accumulate, gc_stream_t stream) {
   gc_status st;
   if ((st = check_bins(nbins, w_deg)) != GC_OK) return st;
   if ((st = check_catalog(prep_d, n_d)) != GC_OK) return st;
@@ -242,13 +250,17 @@ gc_status gc_histogram_dd_dr_rr_tuned(const void *prep_d, int64_t n_d, const voi
   int64_t steps[3], total = 0;
   for (int f = 0; f < 3; ++f) {
     const bool sym = f != 1;
-    steps[f] = family_steps(nn[f][0], nn[f][1], sym, k);
+    const int64_t all = family_steps(nn[f][0], nn[f][1], sym, k);
+    const int64_t s0 = static_cast<int64_t>(static_cast<__int128>(all) * part / parts);
+    const int64_t s1 = static_cast<int64_t>(static_cast<__int128>(all) * (part + 1) / parts);
+    steps[f] = s1 - s0;
     total += steps[f];
     FamilyWork &fw = a.fam[f];
     fw.ci = cc[f][0];
     fw.cj = cc[f][1];
     fw.n_i = nn[f][0];
     fw.n_j = nn[f][1];
+    fw.step_begin = s0;
     fw.total_steps = steps[f];
     fw.sym = sym ? 1 : 0;
   }
@@ -324,9 +336,30 @@ gc_status gc_histogram_dd_dr_rr_tuned(const void *prep_d, int64_t n_d, const voi
     if (e != hipSuccess) return device_error(e);
   }
   uint64_t *outs[3] = {dd, dr, rr};
-  hipError_t e = launch_merge(a.slots, nbins, wb, we, outs, hs);
+  hipError_t e = launch_merge(a.slots, nbins, wb, we, outs, accumulate, hs);
   if (e != hipSuccess) return device_error(e);
   return GC_OK;
+}
+
+}  // namespace
+}  // namespace gc
+
+extern "C" {
+
+gc_status gc_histogram_dd_dr_rr_tuned(const void *prep_d, int64_t n_d, const void *prep_r, int64_t n_r,
+                                      int32_t nbins, double w_deg, uint64_t *dd, uint64_t *dr,
+                                      uint64_t *rr, void *workspace, size_t ws_bytes,
+                                      const gc_tuning *tuning, gc_stream_t stream) {
+  return histogram_impl(prep_d, n_d, prep_r, n_r, nbins, w_deg, dd, dr, rr, workspace, ws_bytes, tuning, 0, 1, false,
+                        stream);
+}
+
+gc_status gc_histogram_part(const void *prep_d, int64_t n_d, const void *prep_r, int64_t n_r, int32_t nbins,
+                            double w_deg, int64_t part, int64_t parts, uint64_t *dd, uint64_t *dr, uint64_t *rr,
+                            void *workspace, size_t ws_bytes, const gc_tuning *tuning, gc_stream_t stream) {
+  if (parts < 1 || parts > GC_MAX_PARTS || part < 0 || part >= parts) return GC_ERR_INVALID_ARGUMENT;
+  return histogram_impl(prep_d, n_d, prep_r, n_r, nbins, w_deg, dd, dr, rr, workspace, ws_bytes, tuning, part, parts,
+                        true, stream);
 }
 
 gc_status gc_histogram_dd_dr_rr(const void *prep_d, int64_t n_d, const void *prep_r, int64_t n_r,

@@ -60,12 +60,13 @@ struct BinParams {
 // One family (DD, DR or RR): the i catalog is held in registers, the j catalog streamed.
 // Its work is a list of "j-steps": one j galaxy against one i-block of 64*K galaxies.
 // Block b (i in [b*BI, b*BI + BI)) has j in [0, n_j) (cross family) or [b*BI, n_j)
-// (self family, i <= j).  The family's workgroups [wg_begin, wg_end) split the j-steps
-// evenly among their wavefronts.
+// (self family, i <= j).  The family's workgroups [wg_begin, wg_end) split the launch's
+// j-steps evenly among their wavefronts.
 struct FamilyWork {
   Prepared ci, cj;
   int64_t n_i, n_j;
-  int64_t total_steps;
+  int64_t step_begin;  // first j-step of this launch (a part of the job may start past 0)
+  int64_t total_steps; // j-steps of this launch: [step_begin, step_begin + total_steps)
   int32_t sym;       // 1: self family (j >= i, weight 2 off the diagonal, 1 on it)
   int32_t wg_begin, wg_end;
   int32_t pad_;
@@ -101,8 +102,9 @@ hipError_t launch_prepare(const float *ra, const float *dec, int64_t n, void *bl
 // instead); fp64 dot: nbins w <= 90 deg (no sign handling)
 hipError_t launch_pairs(const PairArgs &a, int num_wg, bool dot64, int k, bool span, hipStream_t s);
 hipError_t pairs_occupancy(bool dot64, int k, bool span, size_t lds_bytes, int *blocks_per_cu);
+// accumulate: add the sums to the outputs instead of overwriting them
 hipError_t launch_merge(const unsigned long long *slots, int32_t nbins, const int32_t wg_begin[3],
-                        const int32_t wg_end[3], uint64_t *out[3], hipStream_t s);
+                        const int32_t wg_end[3], uint64_t *out[3], bool accumulate, hipStream_t s);
 hipError_t launch_totals(const uint64_t *dd, const uint64_t *dr, const uint64_t *rr, int32_t nbins,
                          uint64_t *totals, hipStream_t s);
 hipError_t launch_omega(const uint64_t *dd, const uint64_t *dr, const uint64_t *rr, int32_t nbins,

@@ -256,12 +256,13 @@ pairs_kernel(const PairArgs A) {
   __threadfence();
   __syncthreads();
 
-  // This wave's share [s, s_end) of the family's j-steps: floor(T v / V) .. floor(T (v+1) / V).
+  // This wave's share [s, s_end) of the launch's j-steps: step_begin + floor(T v / V) ..
+  // step_begin + floor(T (v+1) / V).
   const int64_t V = static_cast<int64_t>(F.wg_end - F.wg_begin) * kWavesPerWG;
   const int64_t v = static_cast<int64_t>(g - F.wg_begin) * kWavesPerWG + wv;
   const int64_t tq = F.total_steps / V, tr = F.total_steps % V;
-  int64_t s = tq * v + (tr * v) / V;
-  const int64_t s_end = tq * (v + 1) + (tr * (v + 1)) / V;
+  int64_t s = F.step_begin + tq * v + (tr * v) / V;
+  const int64_t s_end = F.step_begin + tq * (v + 1) + (tr * (v + 1)) / V;
 
   // Locate block b and its j: cross family L(b) = n_j; self family L(b) = n - b BI,
   // prefix P(b) = b n - BI b (b - 1) / 2.
@@ -465,12 +466,13 @@ __global__ void __launch_bounds__(256) edges_kernel(int32_t nbins, double w_deg,
 }
 
 // ------------------------------------------------------------------------------- merge
-// out_f[bin] = sum of slots of family f's workgroups.  Block: 256 threads = 4 waves over
-// the slot list, one bin per lane; grid (ceil(nbins / 64), 3).
+// out_f[bin] = sum of slots of family f's workgroups (plus out_f[bin] itself when
+// accumulating).  Block: 256 threads = 4 waves over the slot list, one bin per lane; grid
+// (ceil(nbins / 64), 3).
 __global__ void __launch_bounds__(256) merge_kernel(const unsigned long long *__restrict__ slots,
                                                     int32_t nbins, int32_t b0, int32_t b1, int32_t b2,
                                                     int32_t e0, int32_t e1, int32_t e2, uint64_t *o0,
-                                                    uint64_t *o1, uint64_t *o2) {
+                                                    uint64_t *o1, uint64_t *o2, int32_t accumulate) {
   __shared__ unsigned long long part[4][kWave];
   const int f = blockIdx.y;
   const int lane = threadIdx.x & (kWave - 1);
@@ -485,7 +487,8 @@ __global__ void __launch_bounds__(256) merge_kernel(const unsigned long long *__
   __syncthreads();
   if (wv == 0 && bin < nbins) {
     uint64_t *o = f == 0 ? o0 : (f == 1 ? o1 : o2);
-    o[bin] = part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane];
+    const uint64_t sum = part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane];
+    o[bin] = accumulate ? o[bin] + sum : sum;
   }
 }
 
@@ -599,10 +602,10 @@ hipError_t launch_pairs(const PairArgs &a, int num_wg, bool dot64, int k, bool s
 }
 
 hipError_t launch_merge(const unsigned long long *slots, int32_t nbins, const int32_t wb[3],
-                        const int32_t we[3], uint64_t *out[3], hipStream_t st) {
+                        const int32_t we[3], uint64_t *out[3], bool accumulate, hipStream_t st) {
   dim3 grid((nbins + kWave - 1) / kWave, 3);
   hipLaunchKernelGGL(merge_kernel, grid, dim3(256), 0, st, slots, nbins, wb[0], wb[1], wb[2], we[0], we[1],
-                     we[2], out[0], out[1], out[2]);
+                     we[2], out[0], out[1], out[2], accumulate ? 1 : 0);
   return hipGetLastError();
 }
 
