@@ -133,7 +133,8 @@ gc_status gc_histogram_dd_dr_rr_tuned(const void *d_prepared_d, int64_t n_d,
  * (N >> 10^6), for checkpointing, or for spreading the job over several devices or
  * processes.  The histograms are additive over any partition of the pairs (section
  * "L1: DD/RR symmetry" sums weighted pairs; nothing else couples them), so the job is
- * cut into `parts` pieces: part p takes, in each of DD, DR and RR, the work units
+ * cut into `parts` pieces: part p takes, in each of DD, DR and RR and in each of its
+ * two kinds of work unit (off-diagonal and diagonal/ragged), the units
  * floor(T p / parts) .. floor(T (p+1) / parts) of the T units the single call uses.
  * Each pair's bin depends on that pair alone, so the parts of one job, in any order
  * and on any device, sum exactly to gc_histogram_dd_dr_rr's result.

@@ -139,13 +139,21 @@ size_t workspace_bytes(int32_t nbins) {
          static_cast<size_t>(kMaxWorkgroups) * static_cast<size_t>(nbins) * sizeof(unsigned long long);
 }
 
-// j-steps of one family: cross (n_i blocks x n_j) or self (upper triangle by blocks).
-int64_t family_steps(int64_t n_i, int64_t n_j, bool sym, int k) {
-  if (n_i == 0 || n_j == 0) return 0;
+// j-steps of one family in its two segments.  Cross: fast = full blocks x n_j, generic = the
+// ragged block's n_j steps.  Self (upper triangle by blocks): fast = sum over full blocks b of
+// n - (b+1) BI, generic = n (the diagonal blocks, ragged block included, tile [0, n)).
+void family_steps(int64_t n_i, int64_t n_j, bool sym, int k, int64_t *fast, int64_t *generic) {
+  *fast = *generic = 0;
+  if (n_i == 0 || n_j == 0) return;
   const int64_t bi = static_cast<int64_t>(kWave) * k;
-  const int64_t nb = (n_i + bi - 1) / bi;
-  if (!sym) return nb * n_j;
-  return nb * n_j - bi * nb * (nb - 1) / 2;
+  const int64_t nbf = n_i / bi;
+  if (!sym) {
+    *fast = nbf * n_j;
+    *generic = (n_i % bi) ? n_j : 0;
+  } else {
+    *fast = nbf * n_j - bi * nbf * (nbf + 1) / 2;
+    *generic = n_j;
+  }
 }
 
 }  // namespace
@@ -196,9 +204,9 @@ size_t gc_workspace_bytes(int32_t nbins) {
 namespace gc {
 namespace {
 
-// The histogram call and its parts.  Part p of P takes, in every family, the j-steps
-// floor(T p / P) .. floor(T (p+1) / P) of the same decomposition; with accumulate the merge adds
-// to the outputs.  Every pair's bin is fixed by the pair alone (the lane always holds the lower
+// The histogram call and its parts.  Part p of P takes, in each segment of every family, the
+// j-steps floor(T p / P) .. floor(T (p+1) / P) of the same decomposition; with accumulate the
+// merge adds to the outputs.  Every pair's bin is fixed by the pair alone (the lane always holds the lower
 // index of a self pair, and the recheck is exact), so the parts sum to the single call's result.
 gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, int64_t n_r, int32_t nbins,
                          double w_deg, uint64_t *dd, uint64_t *dr, uint64_t *rr, void *workspace, size_t ws_bytes,
@@ -250,18 +258,22 @@ gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, in
   int64_t steps[3], total = 0;
   for (int f = 0; f < 3; ++f) {
     const bool sym = f != 1;
-    const int64_t all = family_steps(nn[f][0], nn[f][1], sym, k);
-    const int64_t s0 = static_cast<int64_t>(static_cast<__int128>(all) * part / parts);
-    const int64_t s1 = static_cast<int64_t>(static_cast<__int128>(all) * (part + 1) / parts);
-    steps[f] = s1 - s0;
-    total += steps[f];
+    int64_t all_fast = 0, all_gen = 0;
+    family_steps(nn[f][0], nn[f][1], sym, k, &all_fast, &all_gen);
+    auto cut = [&](int64_t all, int64_t q) {
+      return static_cast<int64_t>(static_cast<__int128>(all) * q / parts);
+    };
     FamilyWork &fw = a.fam[f];
+    fw.fast_begin = cut(all_fast, part);
+    fw.fast_steps = cut(all_fast, part + 1) - fw.fast_begin;
+    fw.gen_begin = cut(all_gen, part);
+    fw.gen_steps = cut(all_gen, part + 1) - fw.gen_begin;
+    steps[f] = fw.fast_steps + fw.gen_steps;
+    total += steps[f];
     fw.ci = cc[f][0];
     fw.cj = cc[f][1];
     fw.n_i = nn[f][0];
     fw.n_j = nn[f][1];
-    fw.step_begin = s0;
-    fw.total_steps = steps[f];
     fw.sym = sym ? 1 : 0;
   }
 

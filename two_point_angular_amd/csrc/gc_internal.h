@@ -60,13 +60,18 @@ struct BinParams {
 // One family (DD, DR or RR): the i catalog is held in registers, the j catalog streamed.
 // Its work is a list of "j-steps": one j galaxy against one i-block of 64*K galaxies.
 // Block b (i in [b*BI, b*BI + BI)) has j in [0, n_j) (cross family) or [b*BI, n_j)
-// (self family, i <= j).  The family's workgroups [wg_begin, wg_end) split the launch's
-// j-steps evenly among their wavefronts.
+// (self family, i <= j).  The steps fall into a fast segment (off-diagonal steps of full
+// blocks) and a generic one (the diagonal steps of a self family, all steps of a ragged
+// block); the family's workgroups [wg_begin, wg_end) split each segment evenly among their
+// wavefronts.
 struct FamilyWork {
   Prepared ci, cj;
   int64_t n_i, n_j;
-  int64_t step_begin;  // first j-step of this launch (a part of the job may start past 0)
-  int64_t total_steps; // j-steps of this launch: [step_begin, step_begin + total_steps)
+  // This launch's j-steps in the family's two segments (a part of the job may start past 0):
+  // fast steps [fast_begin, fast_begin + fast_steps) - off-diagonal steps of full i-blocks;
+  // generic steps [gen_begin, gen_begin + gen_steps) - diagonal steps and the ragged block.
+  int64_t fast_begin, fast_steps;
+  int64_t gen_begin, gen_steps;
   int32_t sym;       // 1: self family (j >= i, weight 2 off the diagonal, 1 on it)
   int32_t wg_begin, wg_end;
   int32_t pad_;

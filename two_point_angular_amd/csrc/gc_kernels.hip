@@ -256,32 +256,24 @@ pairs_kernel(const PairArgs A) {
   __threadfence();
   __syncthreads();
 
-  // This wave's share [s, s_end) of the launch's j-steps: step_begin + floor(T v / V) ..
-  // step_begin + floor(T (v+1) / V).
+  // The family's j-steps form two segments, each split evenly among the family's waves (V of
+  // them; this is wave v), so every wave gets the same share of both kinds of work:
+  //   fast    - the off-diagonal steps of full i-blocks: batched, unrolled, no per-pair checks;
+  //   generic - the diagonal steps j in [i0, i0 + BI) of a self family and every step of a
+  //             ragged last i-block: per-pair weights and validity, a rolled loop, slower.
+  // (Giving each wave one contiguous range of all steps left the generic-heavy tail of the
+  // triangle, and the ragged block, to the last few waves, which then finished late.)
   const int64_t V = static_cast<int64_t>(F.wg_end - F.wg_begin) * kWavesPerWG;
   const int64_t v = static_cast<int64_t>(g - F.wg_begin) * kWavesPerWG + wv;
-  const int64_t tq = F.total_steps / V, tr = F.total_steps % V;
-  int64_t s = F.step_begin + tq * v + (tr * v) / V;
-  const int64_t s_end = F.step_begin + tq * (v + 1) + (tr * (v + 1)) / V;
-
-  // Locate block b and its j: cross family L(b) = n_j; self family L(b) = n - b BI,
-  // prefix P(b) = b n - BI b (b - 1) / 2.
-  int64_t b = 0, j = 0;
-  if (s < s_end) {
-    if (!F.sym) {
-      b = s / F.n_j;
-      j = s - b * F.n_j;
-    } else {
-      int64_t lo = 0, hi = (F.n_i + BI - 1) / BI - 1;
-      while (lo < hi) {
-        const int64_t mid = (lo + hi + 1) >> 1;
-        const int64_t pm = mid * F.n_j - static_cast<int64_t>(BI) * mid * (mid - 1) / 2;
-        if (pm <= s) lo = mid; else hi = mid - 1;
-      }
-      b = lo;
-      j = b * BI + (s - (b * F.n_j - static_cast<int64_t>(BI) * b * (b - 1) / 2));
-    }
-  }
+  auto share = [&](int64_t begin, int64_t total, int64_t &lo, int64_t &hi) __attribute__((always_inline)) {
+    const int64_t q = total / V, r = total % V;
+    lo = begin + q * v + (r * v) / V;
+    hi = begin + q * (v + 1) + (r * (v + 1)) / V;
+  };
+  int64_t fs, fe, gs, ge;
+  share(F.fast_begin, F.fast_steps, fs, fe);
+  share(F.gen_begin, F.gen_steps, gs, ge);
+  const int64_t nbf = F.n_i / BI;  // full i-blocks
 
   int64_t since_flush = 0;
   int qcount = 0;  // queue entries [0, qcount) are pending
@@ -419,9 +411,7 @@ pairs_kernel(const PairArgs A) {
     }
   };
 
-  while (s < s_end) {
-    const int64_t nsteps = (s_end - s) < (F.n_j - j) ? (s_end - s) : (F.n_j - j);
-    const int64_t j1 = j + nsteps;
+  auto load_i_block = [&](int64_t b) __attribute__((always_inline)) {
     i0 = b * BI;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
@@ -433,25 +423,54 @@ pairs_kernel(const PairArgs A) {
         ix[k] = F.ci.x[il]; iy[k] = F.ci.y[il]; iz[k] = F.ci.z[il];
       }
     }
-    const bool full = i0 + BI <= F.n_i;
-    if (F.sym) {
-      // j in [i0, i0 + BI) meets this block's own galaxies: per-pair weights there.
-      const int64_t dz = j1 < i0 + BI ? j1 : i0 + BI;
-      if (!full) {
-        run_generic(j, j1);
-      } else {
-        if (j < dz) run_generic(j, dz);
-        const int64_t jf = j > dz ? j : dz;
-        if (jf < j1) run_fast(jf, j1);
-      }
-    } else {
-      if (full) run_fast(j, j1);
-      else run_generic(j, j1);
+  };
+
+  // Generic segment.  Self family: block b holds steps [b BI, b BI + min(BI, n - b BI)), so step
+  // s is block s / BI, j = s.  Cross family: only the ragged block nbf, j = s.
+  {
+    int64_t s = gs;
+    while (s < ge) {
+      const int64_t b = F.sym ? s / BI : nbf;
+      const int64_t j = s;
+      const int64_t jend = F.sym ? ((b + 1) * BI < F.n_j ? (b + 1) * BI : F.n_j) : F.n_j;
+      const int64_t nsteps = (ge - s) < (jend - j) ? (ge - s) : (jend - j);
+      if (nsteps <= 0) break;  // unreachable for consistent step counts; keeps every wave finite
+      load_i_block(b);
+      run_generic(j, j + nsteps);
+      drain_all();
+      s += nsteps;
     }
-    drain_all();
-    s += nsteps;
-    ++b;
-    j = F.sym ? b * BI : 0;
+  }
+
+  // Fast segment over the full blocks.  Cross family: block b has steps j in [0, n_j), prefix
+  // b n_j.  Self family: block b has j in [(b+1) BI, n), prefix Pf(b) = b n - BI b (b+1) / 2.
+  {
+    int64_t s = fs, b = 0, j = 0;
+    if (s < fe) {
+      if (!F.sym) {
+        b = s / F.n_j;
+        j = s - b * F.n_j;
+      } else {
+        int64_t lo = 0, hi = nbf - 1;
+        while (lo < hi) {
+          const int64_t mid = (lo + hi + 1) >> 1;
+          const int64_t pm = mid * F.n_j - static_cast<int64_t>(BI) * mid * (mid + 1) / 2;
+          if (pm <= s) lo = mid; else hi = mid - 1;
+        }
+        b = lo;
+        j = (b + 1) * BI + (s - (b * F.n_j - static_cast<int64_t>(BI) * b * (b + 1) / 2));
+      }
+    }
+    while (s < fe) {
+      const int64_t nsteps = (fe - s) < (F.n_j - j) ? (fe - s) : (F.n_j - j);
+      if (nsteps <= 0) break;  // unreachable for consistent step counts; keeps every wave finite
+      load_i_block(b);
+      run_fast(j, j + nsteps);
+      drain_all();
+      s += nsteps;
+      ++b;
+      j = F.sym ? (b + 1) * BI : 0;
+    }
   }
   flush();
 }
