@@ -116,7 +116,10 @@ typedef struct {
                                 bins' span - fp32 dot: no clamp of the bin coordinate (only
                                 valid when (nbins + 1/2) * width >= 180 deg); fp64 dot: no
                                 sign handling (only valid when nbins * width <= 90 deg) */
-    int32_t reserved;        /* must be 0 */
+    int32_t bin_table;       /* 0 auto; 1: never bin through a table; 2: always (only valid
+                                for the fp32 dot product, bins covering 180 deg and widths
+                                where the table is sound, about >= 0.25 deg; forces one
+                                shared histogram per workgroup) */
     int64_t flush_interval;  /* 0 auto; else j-steps between flushes of the 32-bit LDS
                                 histograms into 64-bit totals (>= 1) */
 } gc_tuning;
@@ -180,11 +183,13 @@ gc_status gc_omega(const uint64_t *d_dd, const uint64_t *d_dr, const uint64_t *d
  *   d_trip_out : device, n uint8: 1 where the guard sends the pair to the exact recheck.
  *   d_exact_out: device, n int32, or null: the exact recheck's bin of the same cosine
  *                (fp32 cosines are widened exactly), found from the fast-path bin by the
- *                kernel's own edge-cosine search.  Needs d_workspace (at least
- *                gc_workspace_bytes(nbins) bytes, GC_ALIGNMENT-aligned) for the edge table.
- *   d_t_out    : device, n fp32, or null: the fast path's bin coordinate theta / width before
- *                any clamping, for measuring the core's error.
- * The kernel variant is the one gc_histogram_dd_dr_rr would use for these bins. */
+ *                kernel's own edge-cosine search.
+ *   d_t_out    : device, n fp32, or null: the fast path's coordinate before binning, for
+ *                measuring the core's error: theta / width (arccos cores), or
+ *                c = copysign(sqrt(1 - |x|), x) (the bin-table core).
+ *   d_workspace: at least gc_workspace_bytes(nbins) bytes, GC_ALIGNMENT-aligned; needed when
+ *                d_exact_out is given or the core bins through a table (may be null otherwise).
+ * The core is the one gc_histogram_dd_dr_rr would use for these bins with default tuning. */
 gc_status gc_eval_angle_core(const float *d_x32, const double *d_x64, int64_t n,
                              int32_t nbins, double bin_width_deg, int32_t dot_precision,
                              int32_t *d_bin_out, uint8_t *d_trip_out, int32_t *d_exact_out,

@@ -48,7 +48,8 @@ def test_sizes(lib):
     assert lib.gc_prepared_bytes(10**5) % gc.ALIGNMENT == 0
     assert lib.gc_workspace_bytes(0) == 0
     assert lib.gc_workspace_bytes(gc.MAX_BINS + 1) == 0
-    assert lib.gc_workspace_bytes(720) == 2048 * 720 * 8 + (721 * 8 + 255) // 256 * 256
+    # edge cosines, the bin table (2049 8-byte entries), 2048 per-workgroup partial histograms
+    assert lib.gc_workspace_bytes(720) == 2048 * 720 * 8 + (721 * 8 + 255) // 256 * 256 + (2049 * 8 + 255) // 256 * 256
 
 
 def test_status_strings(lib):
@@ -99,15 +100,21 @@ def test_histogram_validation(lib):
     assert _hist(lib, ws=None) == INVALID
     assert _hist(lib, ws=P(A + 128)) == INVALID
     assert _hist(lib, wsb=gc.workspace_bytes(720) - 1) == WORKSPACE
-    T = gc._Tuning  # dot, K, blocks/CU, shared histogram, span kernel, reserved, flush interval
+    T = gc._Tuning  # dot, K, blocks/CU, shared histogram, span kernel, bin table, flush interval
     for bad in (T(33, 0, 0, 0, 0, 0, 0), T(0, 5, 0, 0, 0, 0, 0), T(0, 0, 9, 0, 0, 0, 0),
                 T(0, 0, -1, 0, 0, 0, 0), T(0, 0, 0, 3, 0, 0, 0), T(0, 0, 0, -1, 0, 0, 0),
-                T(0, 0, 0, 0, 3, 0, 0), T(0, 0, 0, 0, 0, 1, 0), T(0, 0, 0, 0, 0, 0, -3),
+                T(0, 0, 0, 0, 3, 0, 0), T(0, 0, 0, 0, 0, 3, 0), T(0, 0, 0, 0, 0, -1, 0), T(0, 0, 0, 0, 0, 0, -3),
                 T(64, 0, 0, 0, 2, 0, 0)):                      # fp64 narrow core: 180 deg > 90 deg
         assert _hist(lib, tuning=bad) == INVALID
     assert _hist(lib, nbins=700, tuning=T(0, 0, 0, 0, 2, 0, 0)) == INVALID  # 700 x 0.25 < 180 deg
     assert _hist(lib, nbins=361, tuning=T(64, 0, 0, 0, 2, 0, 0)) == INVALID  # 361 x 0.25 > 90 deg
     assert _hist(lib, nbins=1500, w=0.001, tuning=T(32, 0, 0, 0, 2, 0, 0)) == INVALID  # 1.5 < 180 deg
+    # the bin table: fp32 dot, full span, a sound table, a shared histogram
+    assert _hist(lib, tuning=T(64, 0, 0, 0, 0, 2, 0)) == INVALID
+    assert _hist(lib, nbins=3600, w=0.05, tuning=T(0, 0, 0, 0, 0, 2, 0)) == INVALID   # too narrow
+    assert _hist(lib, nbins=700, tuning=T(0, 0, 0, 0, 0, 2, 0)) == INVALID            # not full span
+    assert _hist(lib, tuning=T(0, 0, 0, 1, 0, 2, 0)) == INVALID                       # private histograms
+    assert _hist(lib, tuning=T(0, 0, 0, 0, 1, 2, 0)) == INVALID                       # generic core
 
 
 @pytest.mark.skipif(not NO_GPU, reason="exercises the no-device error path; only without a GPU")
@@ -133,6 +140,7 @@ def test_totals_omega_core_validation(lib):
     assert ev(P(A), None, 10, 0, 0.25, 32, P(A), P(A), None, None, None, 0, None) == INVALID
     assert ev(P(A), None, 10, 720, 0.25, 32, P(A), P(A), P(A), None, None, 0, None) == INVALID  # exact, no ws
     assert ev(P(A), None, 10, 720, 0.25, 32, P(A), P(A), P(A), None, P(A), 100, None) == WORKSPACE
+    assert ev(P(A), None, 10, 720, 0.25, 32, P(A), P(A), None, None, None, 0, None) == INVALID  # table, no ws
     n = ctypes.c_uint64(0)
     sink = lib.gc_ceiling_sink_bytes()
     assert sink == 2048 * 256 * 4

@@ -65,7 +65,17 @@ def check_sound(x_exact_in, b, trip, nbins, w, g):
     assert not bad.any(), (int(bad.sum()), xk[bad][:5], b[keep][bad][:5], lo[bad][:5], hi[bad][:5])
 
 
-@pytest.mark.parametrize("nbins,w", [(720, 0.25), (3600, 0.05), (1500, 0.001)])
+# (nbins, width): 720 x 0.25 deg bins through the bin table; 1440 x 0.125 and 3600 x 0.05 deg
+# through the full-span arccos core (too narrow for the table); 1500 x 0.001 deg through the
+# clamped arccos core.
+FP32_CASES = [(720, 0.25), (1440, 0.125), (3600, 0.05), (1500, 0.001)]
+
+
+def uses_table(nbins, w):
+    return nbins * w >= 180 and w >= 0.25
+
+
+@pytest.mark.parametrize("nbins,w", FP32_CASES)
 def test_fp32_core_sound_near_edges(gc, nbins, w):
     print(f"[gpu] fp32 core near edges nbins={nbins}", flush=True)
     rng = np.random.default_rng(nbins)
@@ -124,16 +134,26 @@ def _core_t(gc, x, nbins, w):
     return t.cpu().numpy().astype(np.float64), trip.cpu().numpy().astype(bool)
 
 
-@pytest.mark.parametrize("nbins,w", [(720, 0.25), (3600, 0.05), (1500, 0.001)])
+@pytest.mark.parametrize("nbins,w", FP32_CASES)
 def test_fp32_core_error_within_model(gc, nbins, w):
-    """The fp32 core's bin coordinate t against the exact acos(x)/w for the same fp32 cosine,
-    over every 64th fp32 value in [-1, 1].  The guard assumes |t~ - t| <= C(t) with
-    C(t) = E_core / w + 2^-24 (t + 2h) (core error with a 1-ulp square root, plus the
-    roundings that form t); the measured error must stay within it."""
+    """The fp32 core's coordinate against its exact value for the same fp32 cosine, over every
+    64th fp32 value in [-1, 1].  Arccos cores: the guard assumes |t~ - t| <= C(t) with
+    C(t) = E_core / w + 2^-24 (t + 2h) (core error with a 1-ulp square root, plus the roundings
+    that form t).  Bin-table core: c = copysign(sqrt(1 - |x|), x), and the guard assumes
+    |c~ - c| s~ <= 1.5 * 2^-23 for the core's own roundings (subtraction, 1-ulp square root)."""
     print(f"[gpu] fp32 core error model nbins={nbins}", flush=True)
     pos = np.arange(0, np.float32(1.0).view(np.uint32) + 1, 64, dtype=np.uint32).view(np.float32)
     x = np.concatenate([pos, -pos[1:]]).astype(np.float32)
     t, _ = _core_t(gc, x, nbins, w)
+    if uses_table(nbins, w):
+        xd = x.astype(np.float64)
+        c_exact = np.copysign(np.sqrt(1.0 - np.abs(xd)), xd)
+        s = np.abs(t)
+        ratio = np.abs(t - c_exact) * s / (1.5 * 2.0 ** -23)
+        print(f"  max |c~ - c| s = {np.max(np.abs(t - c_exact) * s):.3e}; max ratio to the guard's core "
+              f"term {ratio.max():.3f}", flush=True)
+        assert ratio.max() <= 0.9
+        return
     w_rad = np.radians(w)
     t_exact = np.arccos(x.astype(np.float64)) / w_rad
     err = np.abs(t - t_exact)

@@ -209,7 +209,9 @@ def test_outputs_overwritten_and_self_pairs(gc):
                                     dict(flush_interval=17, i_per_lane=4, dot_precision=64),
                                     dict(shared_histogram=1), dict(shared_histogram=2),
                                     dict(shared_histogram=2, flush_interval=5),
-                                    dict(span_kernel=1), dict(span_kernel=2, i_per_lane=4)])
+                                    dict(span_kernel=1), dict(span_kernel=2, i_per_lane=4),
+                                    dict(bin_table=1), dict(bin_table=2, i_per_lane=4),
+                                    dict(bin_table=2, flush_interval=5)])
 def test_tuning_does_not_change_results(gc, tuning):
     print(f"[gpu] tuning {tuning}", flush=True)
     D, R = catalogs.WORKLOADS["clustered100k_720"].catalogs(n=6000)
@@ -264,3 +266,45 @@ def test_million_catalogs_totals_and_subproblem(gc):
     fam = oracle.family_rows(Ds.ra, Ds.dec, R.ra, R.dec, wl.nbins, wl.bin_width_deg)
     rep = oracle.flow_check(sub_dr, fam, len(Ds) * n)
     assert rep.ok, rep.message
+
+
+def test_bin_table_maps_every_entry(gc):
+    """The bin table built on the device for 720 x 0.25 deg: for every entry q (c in
+    [q/M - 1, (q+1)/M - 1)) and 65 values of c across it, bin = B - [c < e] equals the bin of
+    the angle of c, theta = 2 asin(c / sqrt2) (c >= 0) or 180 - 2 asin(-c / sqrt2) degrees."""
+    import torch
+    print("[gpu] bin table entries", flush=True)
+    nbins, w = 720, 0.25
+    ws = torch.zeros(gc.workspace_bytes(nbins), dtype=torch.uint8, device="cuda")
+    x = torch.tensor([0.5], dtype=torch.float32, device="cuda")
+    bins = torch.empty(1, dtype=torch.int32, device="cuda")
+    trip = torch.empty(1, dtype=torch.uint8, device="cuda")
+    import ctypes
+    _ptr = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    st = gc.load().gc_eval_angle_core(_ptr(x), None, 1, nbins, w, 32, _ptr(bins), _ptr(trip), None, None,
+                                      _ptr(ws), ws.numel(), None)
+    assert st == 0
+    torch.cuda.synchronize()
+    m = int(np.ceil(4 / np.radians(w)))
+    off = ((nbins + 1) * 8 + 255) // 256 * 256
+    tab = ws[off: off + (2 * m + 1) * 8].cpu().numpy().view(np.uint32).reshape(-1, 2)
+    e = tab[:, 0].view(np.float32).astype(np.float64)
+    b = tab[:, 1].astype(np.int64)
+    q = np.arange(2 * m + 1)
+    frac = np.linspace(0.0, 1.0, 65)[:-1]
+    c = (q[:, None] + frac[None, :]) / m - 1.0
+    c = np.clip(c, -1.0, 1.0)
+    th = np.where(c >= 0, 2 * np.degrees(np.arcsin(np.minimum(c, 1) / np.sqrt(2))),
+                  180 - 2 * np.degrees(np.arcsin(np.minimum(-c, 1) / np.sqrt(2))))
+    want = np.minimum(np.floor(th / w).astype(np.int64), nbins - 1)
+    got = b[:, None] - (c < e[:, None])
+    # a sample within the fp32 rounding of the stored edge may fall either way
+    near = np.abs(c - e[:, None]) < 1e-6
+    assert np.all((got == want) | near), int(((got != want) & ~near).sum())
+    # every entry that holds an edge holds the one inside it, when there is one
+    for k in range(1, nbins):
+        th_e = k * w
+        ce = np.sqrt(2) * np.sin(np.radians(th_e) / 2) if th_e <= 90 else -np.sqrt(2) * np.cos(np.radians(th_e) / 2)
+        qe = int(np.floor(m * (ce + 1)))
+        if qe <= 2 * m:
+            assert abs(e[qe] - ce) < 1e-6 and b[qe] == k, (k, qe, e[qe], ce, b[qe])

@@ -56,7 +56,7 @@ class GCError(RuntimeError):
 class _Tuning(ctypes.Structure):
     _fields_ = [("dot_precision", ctypes.c_int32), ("i_per_lane", ctypes.c_int32),
                 ("blocks_per_cu", ctypes.c_int32), ("shared_histogram", ctypes.c_int32),
-                ("span_kernel", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("span_kernel", ctypes.c_int32), ("bin_table", ctypes.c_int32),
                 ("flush_interval", ctypes.c_int64)]
 
 
@@ -70,10 +70,11 @@ class Tuning:
     flush_interval: int = 0
     shared_histogram: int = 0
     span_kernel: int = 0
+    bin_table: int = 0
 
     def _c(self) -> _Tuning:
         return _Tuning(self.dot_precision, self.i_per_lane, self.blocks_per_cu, self.shared_histogram,
-                       self.span_kernel, 0, self.flush_interval)
+                       self.span_kernel, self.bin_table, self.flush_interval)
 
 
 _lib = None
@@ -251,7 +252,7 @@ def eval_angle_core(x, nbins: int, bin_width_deg: float, with_exact: bool = True
     t = torch.empty(n, dtype=torch.float32, device=x.device) if with_t else None
     x32 = x if dot == 32 else None
     x64 = x if dot == 64 else None
-    ws = torch.empty(workspace_bytes(nbins), dtype=torch.uint8, device=x.device) if with_exact else None
+    ws = torch.empty(workspace_bytes(nbins), dtype=torch.uint8, device=x.device)
     _check(load().gc_eval_angle_core(_ptr(x32), _ptr(x64), n, int(nbins), float(bin_width_deg), dot,
                                      _ptr(bins), _ptr(trip), _ptr(exact), _ptr(t), _ptr(ws),
                                      ws.numel() if ws is not None else 0, _stream(stream)),

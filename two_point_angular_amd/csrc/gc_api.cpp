@@ -31,16 +31,16 @@ bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 struct DeviceInfo {
   bool valid = false;
   int cus = 0;
-  // occupancy per (kernel variant, lds bytes); variant = dot64 * 4 + span * 2 + (k == 8)
+  // occupancy per (kernel variant, lds bytes); variant = (dot64 * 3 + core) * 2 + (k == 8)
   struct Occ { size_t lds; int blocks; };
-  Occ occ[8][8];
-  int nocc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  Occ occ[12][8];
+  int nocc[12] = {};
 };
 constexpr int kMaxDevices = 64;
 std::mutex g_mu;
 DeviceInfo g_dev[kMaxDevices];
 
-hipError_t device_info(int *cus, bool dot64, int k, bool span, size_t lds, int *blocks_per_cu) {
+hipError_t device_info(int *cus, bool dot64, int k, int core, size_t lds, int *blocks_per_cu) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -56,14 +56,14 @@ hipError_t device_info(int *cus, bool dot64, int k, bool span, size_t lds, int *
   }
   *cus = d.cus;
   if (!blocks_per_cu) return hipSuccess;
-  const int vi = (dot64 ? 4 : 0) + (span ? 2 : 0) + (k == 8 ? 1 : 0);
+  const int vi = ((dot64 ? 3 : 0) + core) * 2 + (k == 8 ? 1 : 0);
   for (int q = 0; q < d.nocc[vi]; ++q)
     if (d.occ[vi][q].lds == lds) {
       *blocks_per_cu = d.occ[vi][q].blocks;
       return hipSuccess;
     }
   int blocks = 0;
-  e = pairs_occupancy(dot64, k, span, lds, &blocks);
+  e = pairs_occupancy(dot64, k, core, lds, &blocks);
   if (e != hipSuccess) return e;
   if (d.nocc[vi] < 8) d.occ[vi][d.nocc[vi]++] = {lds, blocks};
   *blocks_per_cu = blocks;
@@ -115,6 +115,63 @@ BinParams make_bins(int32_t nbins, double w_deg) {
   return bp;
 }
 
+// ---- bin-table core -------------------------------------------------------------------------
+// The fp32-dot core of the full span can bin through a table instead of an arccos (core_lut in
+// gc_kernels.hip): c = copysign(sqrt(1 - |x|), x) grows with the angle on each half (c =
+// sqrt2 sin(theta/2) up to 90 deg, -sqrt2 cos(theta/2) beyond), entry q covers c in
+// [q/M - 1, (q+1)/M - 1) widened by a margin, and holds the one edge in that range.
+// Guard: the computed c has |c~ - c| s~ <= g_x (1 + 2^-22) + 2^-24 + 2^-23 (dot product,
+// subtraction, 1-ulp square root); the stored edge is rounded to fp32 (2^-24); the subtraction
+// and product of the test round relatively: recheck iff |c - e| s < lut_g = 1.1 (g_x + 2^-22).
+// The table is sound when
+//  (a) no widened entry range can hold two edges: 1/M + 2 margin < the smallest gap between
+//      consecutive edges in c (M = ceil(4 / w_rad), margin = 0.45 (gap - 1/M));
+//  (b) where the error of c exceeds the margin (s < S* = lut_g / margin), it cannot reach any
+//      edge: s + lut_g / s < |c| of the first and last edges for s in [2^-12, S*] (2^-12 is
+//      the smallest non-zero s; the bound is convex in s, so its endpoints decide).
+// Then every edge within the error of c~ lies in c~'s entry, which holds it.
+struct LutPlan {
+  bool ok = false;
+  int32_t m = 0;
+  double margin = 0.0;
+  float g = 0.0f;
+};
+
+LutPlan plan_lut(int32_t nbins, double w_deg) {
+  LutPlan p;
+  if (!((static_cast<double>(nbins) + 0.5) * w_deg >= 180.0) || nbins < 2) return p;
+  const double w = w_deg * (kPi / 180.0);
+  const double md = ceil(4.0 / w);
+  if (2.0 * md + 1.0 > static_cast<double>(kLutMaxEntries)) return p;
+  const double sqrt2 = 1.41421356237309504880;
+  auto c_right = [&](int e) { return sqrt2 * sin(0.5 * e * w); };
+  auto c_left = [&](int e) { return -sqrt2 * cos(0.5 * e * w); };
+  double gap = 1e300, c_edge_min = 1e300;
+  for (int e = 1; e < nbins; ++e) {
+    const double th = e * w_deg;
+    if (th > 180.0) break;
+    if (th <= 90.0) c_edge_min = fmin(c_edge_min, fabs(c_right(e)));
+    if (th >= 90.0) c_edge_min = fmin(c_edge_min, fabs(c_left(e)));
+    if (e + 1 < nbins && (e + 1) * w_deg <= 180.0) {
+      if ((e + 1) * w_deg <= 90.0) gap = fmin(gap, c_right(e + 1) - c_right(e));
+      if (th >= 90.0) gap = fmin(gap, c_left(e + 1) - c_left(e));
+    }
+  }
+  const double margin = 0.45 * (gap - 1.0 / md);
+  if (!(margin > 0.0)) return p;
+  const double g_x = 5.0 * kTwoM24 * (1.0 + 1e-6) + 1e-12;
+  const double g = 1.1 * (g_x + 4.0 * kTwoM24);
+  const double s_min = 1.0 / 4096.0;
+  const double s_star = g / margin;
+  const double reach = fmax(s_min + g / s_min, s_star + g / s_star);
+  if (!(reach < 0.95 * c_edge_min)) return p;
+  p.ok = true;
+  p.m = static_cast<int32_t>(md);
+  p.margin = margin;
+  p.g = static_cast<float>(g * (1.0 + 1e-6));
+  return p;
+}
+
 // Spans the specialised cores accept: the fp32 core without a clamp needs nbins w to reach
 // 180 deg within half a bin; the fp64 core without sign handling needs nbins w <= 90 deg.
 bool span_full(int32_t nbins, double w_deg) { return (static_cast<double>(nbins) + 0.5) * w_deg >= 180.0; }
@@ -135,7 +192,7 @@ gc_status check_catalog(const void *prep, int64_t n) {
 }
 
 size_t workspace_bytes(int32_t nbins) {
-  return edge_table_bytes(nbins) +
+  return edge_table_bytes(nbins) + kLutBytes +
          static_cast<size_t>(kMaxWorkgroups) * static_cast<size_t>(nbins) * sizeof(unsigned long long);
 }
 
@@ -225,7 +282,8 @@ gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, in
   if ((tu.dot_precision != 0 && tu.dot_precision != 32 && tu.dot_precision != 64) ||
       (tu.i_per_lane != 0 && tu.i_per_lane != 4 && tu.i_per_lane != 8) || tu.blocks_per_cu < 0 ||
       tu.blocks_per_cu > kMaxBlocksPerCU || tu.shared_histogram < 0 || tu.shared_histogram > 2 ||
-      tu.span_kernel < 0 || tu.span_kernel > 2 || tu.reserved != 0 || tu.flush_interval < 0)
+      tu.span_kernel < 0 || tu.span_kernel > 2 || tu.bin_table < 0 || tu.bin_table > 2 ||
+      tu.flush_interval < 0)
     return GC_ERR_INVALID_ARGUMENT;
 
   // Plan.  Bins narrower than 0.01 deg put most pairs where the fp32 dot product cannot
@@ -240,6 +298,12 @@ gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, in
   const bool span_ok = dot64 ? span_narrow(nbins, w_deg) : span_full(nbins, w_deg);
   if (tu.span_kernel == 2 && !span_ok) return GC_ERR_INVALID_ARGUMENT;
   const bool span = span_ok && tu.span_kernel != 1;
+  // The bin-table core (fp32, full span, shared histogram) where its table is sound.
+  const LutPlan lp = dot64 ? LutPlan() : plan_lut(nbins, w_deg);
+  const bool lut_ok = lp.ok && span && tu.shared_histogram != 1;
+  if (tu.bin_table == 2 && !lut_ok) return GC_ERR_INVALID_ARGUMENT;
+  const bool use_lut = lut_ok && tu.bin_table != 1;
+  const int core = use_lut ? 2 : (span ? 1 : 0);
   const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
 
   PairArgs a;
@@ -248,9 +312,17 @@ gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, in
   a.hist_words = (nbins + kWave + 63) / 64 * 64;  // 64 spare bins past the last (see core32)
   a.wave_lds_words = a.hist_words + queue_words(k);
   a.bp = make_bins(nbins, w_deg);
+  if (use_lut) {
+    a.bp.lut_m = static_cast<float>(lp.m);
+    a.bp.lut_g = lp.g;
+    a.bp.lut_n = 2 * lp.m;
+  }
+  uint2 *lut_dev = reinterpret_cast<uint2 *>(static_cast<char *>(workspace) + edge_table_bytes(nbins));
+  a.lut = use_lut ? lut_dev : nullptr;
   double *edge_cos = static_cast<double *>(workspace);
   a.edge_cos = edge_cos;
-  a.slots = reinterpret_cast<unsigned long long *>(static_cast<char *>(workspace) + edge_table_bytes(nbins));
+  a.slots = reinterpret_cast<unsigned long long *>(static_cast<char *>(workspace) + edge_table_bytes(nbins) +
+                                                    kLutBytes);
 
   const Prepared pd = prepared_view(prep_d, n_d), pr = prepared_view(prep_r, n_r);
   const int64_t nn[3][2] = {{n_d, n_d}, {n_d, n_r}, {n_r, n_r}};
@@ -283,11 +355,12 @@ gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, in
     // Histogram placement: one private histogram per wave unless sharing one per workgroup
     // lets more workgroups fit in LDS.
     int cus = 0, occ = 0, occ_shared = 0;
-    hipError_t e = device_info(&cus, dot64, k, span, pairs_lds_bytes(a.hist_words, false, k), &occ);
+    hipError_t e = device_info(&cus, dot64, k, core, pairs_lds_bytes(a.hist_words, false, k), &occ);
     if (e != hipSuccess) return device_error(e);
-    e = device_info(&cus, dot64, k, span, pairs_lds_bytes(a.hist_words, true, k), &occ_shared);
+    e = device_info(&cus, dot64, k, core,
+                    pairs_lds_bytes(a.hist_words, true, k, use_lut ? a.bp.lut_n + 1 : 0), &occ_shared);
     if (e != hipSuccess) return device_error(e);
-    bool shared = tu.shared_histogram == 2 || (tu.shared_histogram == 0 && occ_shared > occ);
+    bool shared = use_lut || tu.shared_histogram == 2 || (tu.shared_histogram == 0 && occ_shared > occ);
     if (shared) occ = occ_shared;
     a.shared_hist = shared ? 1 : 0;
     // Between two flushes a bin must stay within +-2^31: each j-step adds at most 2 * 64 K
@@ -344,7 +417,11 @@ gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, in
     num_wg = cur;
     e = launch_edges(nbins, w_deg, edge_cos, hs);
     if (e != hipSuccess) return device_error(e);
-    e = launch_pairs(a, num_wg, dot64, k, span, hs);
+    if (use_lut) {
+      e = launch_lut(nbins, w_deg, lp.m, lp.margin, lut_dev, hs);
+      if (e != hipSuccess) return device_error(e);
+    }
+    e = launch_pairs(a, num_wg, dot64, k, core, hs);
     if (e != hipSuccess) return device_error(e);
   }
   uint64_t *outs[3] = {dd, dr, rr};
@@ -411,18 +488,29 @@ gc_status gc_eval_angle_core(const float *x32, const double *x64, int64_t n, int
   if (n < 0 || (dot_precision != 32 && dot_precision != 64)) return GC_ERR_INVALID_ARGUMENT;
   const bool d64 = dot_precision == 64;
   if (n > 0 && ((d64 && !x64) || (!d64 && !x32) || !bin_out || !trip_out)) return GC_ERR_INVALID_ARGUMENT;
-  if (exact_out && (!workspace || !aligned(workspace, GC_ALIGNMENT))) return GC_ERR_INVALID_ARGUMENT;
-  if (exact_out && ws_bytes < edge_table_bytes(nbins)) return GC_ERR_WORKSPACE;
-  if (n == 0) return GC_OK;
-  const BinParams bp = make_bins(nbins, w_deg);
   // the same core the histogram call would use for these bins
   const bool span = d64 ? span_narrow(nbins, w_deg) : span_full(nbins, w_deg);
+  const LutPlan lp = d64 ? LutPlan() : plan_lut(nbins, w_deg);
+  const bool use_lut = lp.ok && span;
+  const int core = use_lut ? 2 : (span ? 1 : 0);
+  if (n == 0) return GC_OK;
+  const bool need_ws = exact_out || use_lut;
+  if (need_ws && (!workspace || !aligned(workspace, GC_ALIGNMENT))) return GC_ERR_INVALID_ARGUMENT;
+  if (need_ws && ws_bytes < edge_table_bytes(nbins) + kLutBytes) return GC_ERR_WORKSPACE;
+  BinParams bp = make_bins(nbins, w_deg);
   const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   double *edge_cos = static_cast<double *>(workspace);
+  uint2 *lut = need_ws ? reinterpret_cast<uint2 *>(static_cast<char *>(workspace) + edge_table_bytes(nbins)) : nullptr;
   hipError_t e = hipSuccess;
   if (exact_out) e = launch_edges(nbins, w_deg, edge_cos, hs);
+  if (e == hipSuccess && use_lut) {
+    bp.lut_m = static_cast<float>(lp.m);
+    bp.lut_g = lp.g;
+    bp.lut_n = 2 * lp.m;
+    e = launch_lut(nbins, w_deg, lp.m, lp.margin, lut, hs);
+  }
   if (e == hipSuccess)
-    e = launch_eval_core(x32, x64, n, bp, d64, span, exact_out ? edge_cos : nullptr, bin_out, trip_out,
+    e = launch_eval_core(x32, x64, n, bp, d64, core, lut, exact_out ? edge_cos : nullptr, bin_out, trip_out,
                          exact_out, t_out, hs);
   return e == hipSuccess ? GC_OK : device_error(e);
 }

@@ -53,8 +53,15 @@ struct BinParams {
   float g64k1;   // fp64-dot guard: recheck iff |t - round(t)| * s < g64k1 * s + g64k2
   float g64k2;
   float pw[7];   // acos polynomial coefficients times 1 / w_rad (fp32): narrow-range fp64 core
+  float lut_m;   // bin-table core: entries per unit of c (M); the table has 2 M + 1 entries
+  float lut_g;   // bin-table core guard: recheck iff |c - e| * s < lut_g
+  int32_t lut_n; // 2 M (last entry index), or 0 when the bin table is not used
   int32_t nbins;
 };
+
+// Bin-table core (fp32 dot, bins covering 0..180 deg): the table lives in the workspace and is
+// copied into LDS by each workgroup; entry q = {edge e (fp32 bits), bin just below it + 1}.
+constexpr int kLutMaxEntries = 2049;
 
 // ---- pair-kernel work description ---------------------------------------------------
 // One family (DD, DR or RR): the i catalog is held in registers, the j catalog streamed.
@@ -80,6 +87,7 @@ struct FamilyWork {
 struct PairArgs {
   FamilyWork fam[3];           // DD, DR, RR
   BinParams bp;
+  const uint2 *lut;            // bin table (lut_n + 1 entries) in the workspace, or null
   unsigned long long *slots;   // [num_workgroups][nbins] 64-bit partial histograms
   const double *edge_cos;      // [nbins + 1] cos(e w) in fp64, for the exact recheck
   int64_t flush_interval;      // j-steps between flushes of the 32-bit LDS histograms
@@ -90,9 +98,12 @@ struct PairArgs {
 };
 
 // LDS bytes of one pair-kernel workgroup.
-inline size_t pairs_lds_bytes(int32_t hist_words, bool shared_hist, int k) {
+// LDS bytes of one pair-kernel workgroup: histogram(s), the bin table (lut_entries 8-byte
+// entries, shared-histogram mode only) and the four recheck queues.
+inline size_t pairs_lds_bytes(int32_t hist_words, bool shared_hist, int k, int32_t lut_entries = 0) {
   const size_t qw = static_cast<size_t>(queue_words(k));
-  const size_t words = shared_hist ? hist_words + static_cast<size_t>(kWavesPerWG) * qw
+  const size_t words = shared_hist ? hist_words + 2 * static_cast<size_t>(lut_entries) +
+                                         static_cast<size_t>(kWavesPerWG) * qw
                                    : static_cast<size_t>(kWavesPerWG) * (hist_words + qw);
   return words * sizeof(uint32_t);
 }
@@ -102,11 +113,13 @@ void record_hip_error(hipError_t e);
 
 // ---- launchers (gc_kernels.hip) ----------------------------------------------------------
 hipError_t launch_prepare(const float *ra, const float *dec, int64_t n, void *blob, hipStream_t s);
-// dot64: fp64 dot-product variant; k: galaxies per lane (4 or 8); span: the variant
-// specialised to the bins' span - fp32 dot: nbins w covers 180 deg (no clamp of t, spare bin
-// instead); fp64 dot: nbins w <= 90 deg (no sign handling)
-hipError_t launch_pairs(const PairArgs &a, int num_wg, bool dot64, int k, bool span, hipStream_t s);
-hipError_t pairs_occupancy(bool dot64, int k, bool span, size_t lds_bytes, int *blocks_per_cu);
+// dot64: fp64 dot-product variant; k: galaxies per lane (4 or 8); core: 0 the generic core;
+// 1 the one specialised to the bins' span - fp32 dot: nbins w covers 180 deg (no clamp of t,
+// spare bin instead); fp64 dot: nbins w <= 90 deg (no sign handling); 2 (fp32 only) the
+// bin-table core (full span, shared histogram)
+hipError_t launch_pairs(const PairArgs &a, int num_wg, bool dot64, int k, int core, hipStream_t s);
+hipError_t pairs_occupancy(bool dot64, int k, int core, size_t lds_bytes, int *blocks_per_cu);
+hipError_t launch_lut(int32_t nbins, double w_deg, int32_t m, double margin, uint2 *lut, hipStream_t s);
 // accumulate: add the sums to the outputs instead of overwriting them
 hipError_t launch_merge(const unsigned long long *slots, int32_t nbins, const int32_t wg_begin[3],
                         const int32_t wg_end[3], uint64_t *out[3], bool accumulate, hipStream_t s);
@@ -116,12 +129,14 @@ hipError_t launch_omega(const uint64_t *dd, const uint64_t *dr, const uint64_t *
                         int64_t n_d, int64_t n_r, double *omega, hipStream_t s);
 hipError_t launch_edges(int32_t nbins, double w_deg, double *edge_cos, hipStream_t s);
 hipError_t launch_eval_core(const float *x32, const double *x64, int64_t n, const BinParams &bp,
-                            bool dot64, bool span, const double *edge_cos, int32_t *bin_out,
+                            bool dot64, int core, const uint2 *lut, const double *edge_cos, int32_t *bin_out,
                             uint8_t *trip_out, int32_t *exact_out, float *t_out, hipStream_t s);
 
-// Workspace layout: the edge-cosine table, then the per-workgroup 64-bit partial histograms.
+// Workspace layout: the edge-cosine table, the bin table, then the per-workgroup 64-bit
+// partial histograms.
 inline size_t edge_table_bytes(int32_t nbins) {
   return ((static_cast<size_t>(nbins) + 1) * sizeof(double) + 255) / 256 * 256;
 }
+constexpr size_t kLutBytes = (static_cast<size_t>(kLutMaxEntries) * 8 + 255) / 256 * 256;
 
 }  // namespace gc

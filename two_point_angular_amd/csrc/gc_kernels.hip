@@ -137,6 +137,35 @@ __device__ __forceinline__ void core64(double x, const BinParams &bp, float pw6_
   trip = (fabsf(tc - __builtin_rintf(tc)) - bp.g64k1) * s < bp.g64k2;
 }
 
+// Bin-table core (fp32 dot, bins covering 0..180 deg).  Instead of an arccos it uses
+//   c = copysign(sqrt(1 - |x|), x),
+// which increases with the angle on each half: c in [0, 1] for 0..90 deg (c = sqrt2 sin(theta/2)),
+// c in [-1, 0) for 90..180 deg (c = -sqrt2 cos(theta/2)).  Entry q = floor(M (c + 1)) of the
+// table holds the one bin edge e within its range of c widened by a margin (or a far value) and
+// B = (bin just below e) + 1, so bin = B - [c < e].  Recheck iff |c - e| s < lut_g, which bounds
+// the error of c times s (dot-product error g_x, the subtraction, the 1-ulp square root, the
+// rounding of e): near an edge the lookup decides nothing the guard has not certified.
+// tab: the table (LDS in the pair kernel, global memory in the diagnostic kernel).
+__device__ __forceinline__ void lut_lookup(float x, const BinParams &bp, const uint2 *tab, float &c, float &s,
+                                           uint2 &ent) {
+  s = __builtin_amdgcn_sqrtf(__builtin_amdgcn_fmed3f(1.0f - fabsf(x), 0.0f, 1.0f));
+  c = copysignf(s, x);
+  ent = tab[static_cast<uint32_t>(fmaf(c, bp.lut_m, bp.lut_m))];
+}
+__device__ __forceinline__ void lut_bin(float c, float s, uint2 ent, const BinParams &bp, uint32_t &k, bool &trip) {
+  const float d = c - __uint_as_float(ent.x);
+  trip = fabsf(d) * s < bp.lut_g;
+  k = ent.y - (__float_as_uint(d) >> 31);
+}
+__device__ __forceinline__ void core_lut(float x, const BinParams &bp, const uint2 *tab, uint32_t &k, bool &trip,
+                                         float &c_raw) {
+  float c, s;
+  uint2 ent;
+  lut_lookup(x, bp, tab, c, s, ent);
+  lut_bin(c, s, ent, bp, k, trip);
+  c_raw = c;
+}
+
 // Exact recheck in the cosine domain.  theta >= e w  <=>  x <= cos(e w), so bin k holds x
 // iff c[k+1] < x <= c[k], with c[e] = cos(e w) in fp64 (c[0] = 1; c[e] = -inf past 180
 // degrees).  Starting from the fast-path bin k, walk to the bin that satisfies this.  The
@@ -213,16 +242,20 @@ __device__ __forceinline__ void drain_queue(uint32_t *hist, const uint32_t *queu
   __builtin_amdgcn_wave_barrier();
 }
 
-// SPAN selects the core specialised to the bins' span: fp32 dot, the full-span core;
-// fp64 dot, the narrow-range core.  Register budgets: K = 4 builds for six waves per SIMD
+// CORE 0: the generic core; 1: the core specialised to the bins' span (fp32 dot, full span;
+// fp64 dot, narrow range); 2 (fp32 dot): the bin-table core on the fast steps, with a shared
+// histogram and the table in LDS (the generic steps use the full-span core).  Register budgets: K = 4 builds for six waves per SIMD
 // (<= 80 VGPRs), fp32 K = 8 for five (<= 96; its 24 fp32 i-coordinates), fp64 K = 8 for four
 // (48 VGPRs of fp64 i-coordinates).  Measured on the 100k workloads, each step up in waves
 // per SIMD outweighed the few spills it costs outside the pair loop.
-template <int K, bool D64, bool SPAN>
+template <int K, bool D64, int CORE>
 __global__ void __launch_bounds__(kWGThreads)
 __attribute__((amdgpu_waves_per_eu(K == 4 ? 6 : (D64 ? 4 : 5))))
 pairs_kernel(const PairArgs A) {
   typedef typename Real<D64>::T real;
+  constexpr bool SPAN = CORE != 0;
+  constexpr bool LUT = CORE == 2;
+  static_assert(!(LUT && D64), "the bin table is an fp32-dot core");
   constexpr int BI = kWave * K;       // i-block: galaxies per wave
   constexpr int JB = D64 ? 4 : 8;     // j galaxies per scalar batch
   extern __shared__ uint32_t lds[];
@@ -232,11 +265,14 @@ pairs_kernel(const PairArgs A) {
   // the step range, the loop counters and every j index in SGPRs (scalar loads of j, scalar
   // branches).
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  // LDS: private mode, per wave [histogram | queue]; shared mode, [histogram | 4 queues].
-  const bool shared_hist = A.shared_hist != 0;
+  // LDS: private mode, per wave [histogram | queue]; shared mode, [histogram | bin table |
+  // 4 queues] (the table only with the bin-table core).
+  const bool shared_hist = LUT || A.shared_hist != 0;
   constexpr int QW = queue_words(K);
+  const int lut_words = LUT ? 2 * (A.bp.lut_n + 1) : 0;
   uint32_t *const hist = shared_hist ? lds : lds + wv * (A.hist_words + QW);
-  uint32_t *const queue = shared_hist ? lds + A.hist_words + wv * QW : hist + A.hist_words;
+  uint2 *const tab = reinterpret_cast<uint2 *>(lds + A.hist_words);
+  uint32_t *const queue = shared_hist ? lds + A.hist_words + lut_words + wv * QW : hist + A.hist_words;
   const int g = blockIdx.x;
   const int fi = g < A.fam[0].wg_end ? 0 : (g < A.fam[1].wg_end ? 1 : 2);
   const FamilyWork &F = A.fam[fi];
@@ -250,6 +286,8 @@ pairs_kernel(const PairArgs A) {
   for (int b = threadIdx.x; b < A.nbins; b += kWGThreads) slot[b] = 0ull;
   if (shared_hist) {
     for (int b = threadIdx.x; b < A.hist_words; b += kWGThreads) hist[b] = 0u;
+    if constexpr (LUT)
+      for (int q = threadIdx.x; q <= A.bp.lut_n; q += kWGThreads) tab[q] = A.lut[q];
   } else {
     for (int b = lane; b < A.hist_words; b += kWave) hist[b] = 0u;
   }
@@ -318,37 +356,59 @@ pairs_kernel(const PairArgs A) {
   // One j against this lane's K i-galaxies.  Pairs the guard flags are appended to the
   // wave's queue right after their atomic (each bin index dies at once), and the queue is
   // drained in full-wave batches after the step.
+  // Append a flagged pair (this lane's k-th i against j) to the wave's queue.
+  auto enqueue = [&](bool tp, uint32_t kk, int k, int64_t jg) __attribute__((always_inline)) {
+    const unsigned long long m = __ballot(tp);
+    if (m) {
+      if (tp) {
+        // slot = pending count + number of flagged lanes below this one
+        const uint32_t e = __builtin_amdgcn_mbcnt_hi(
+            static_cast<uint32_t>(m >> 32),
+            __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), static_cast<uint32_t>(qcount)));
+        queue[2 * e] = static_cast<uint32_t>(jg);
+        queue[2 * e + 1] = (lane_tag + (static_cast<uint32_t>(kWave * k) << 16)) | kk;
+      }
+      qcount += __popcll(m);
+    }
+  };
+
   auto step = [&](real xj, real yj, real zj, int64_t jg, auto generic_tag) __attribute__((always_inline)) {
     constexpr bool GENERIC = decltype(generic_tag)::value;
+    if constexpr (LUT && !GENERIC) {
+      // all K table reads first, so one LDS wait covers them
+      float cv[K], sv[K];
+      uint2 ev[K];
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-      uint32_t kk;
-      bool tp;
-      const real x = fma(ix[k], xj, fma(iy[k], yj, iz[k] * zj));
-      float t_unused;
-      if constexpr (D64) core64<SPAN>(x, bp, c_v, tmax_v, kk, tp, t_unused);
-      else core32<SPAN>(x, bp, c_v, tmax_v, kk, tp, t_unused);
-      if constexpr (GENERIC) {
-        const int64_t ig = i0 + lane + kWave * k;
-        const bool valid = ig < F.n_i && (!F.sym || jg >= ig);
-        const bool self = F.sym && jg == ig;  // only a self family pairs a galaxy with itself
-        if (self) kk = 0u;                     // separation 0
-        tp = tp && valid && !self;
-        if (valid) atomicAdd(hist + kk, self ? 1u : W);
-      } else {
+      for (int k = 0; k < K; ++k)
+        lut_lookup(fmaf(ix[k], xj, fmaf(iy[k], yj, iz[k] * zj)), bp, tab, cv[k], sv[k], ev[k]);
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        uint32_t kk;
+        bool tp;
+        lut_bin(cv[k], sv[k], ev[k], bp, kk, tp);
         atomicAdd(hist + kk, W);
+        enqueue(tp, kk, k, jg);
       }
-      const unsigned long long m = __ballot(tp);
-      if (m) {
-        if (tp) {
-          // slot = pending count + number of flagged lanes below this one
-          const uint32_t e = __builtin_amdgcn_mbcnt_hi(
-              static_cast<uint32_t>(m >> 32),
-              __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), static_cast<uint32_t>(qcount)));
-          queue[2 * e] = static_cast<uint32_t>(jg);
-          queue[2 * e + 1] = (lane_tag + (static_cast<uint32_t>(kWave * k) << 16)) | kk;
+    } else {
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        uint32_t kk;
+        bool tp;
+        const real x = fma(ix[k], xj, fma(iy[k], yj, iz[k] * zj));
+        float t_unused;
+        if constexpr (D64) core64<SPAN>(x, bp, c_v, tmax_v, kk, tp, t_unused);
+        else core32<SPAN>(x, bp, c_v, tmax_v, kk, tp, t_unused);
+        if constexpr (GENERIC) {
+          const int64_t ig = i0 + lane + kWave * k;
+          const bool valid = ig < F.n_i && (!F.sym || jg >= ig);
+          const bool self = F.sym && jg == ig;  // only a self family pairs a galaxy with itself
+          if (self) kk = 0u;                     // separation 0
+          tp = tp && valid && !self;
+          if (valid) atomicAdd(hist + kk, self ? 1u : W);
+        } else {
+          atomicAdd(hist + kk, W);
         }
-        qcount += __popcll(m);
+        enqueue(tp, kk, k, jg);
       }
     }
     while (qcount >= kWave) drain(kWave);
@@ -484,6 +544,70 @@ __global__ void __launch_bounds__(256) edges_kernel(int32_t nbins, double w_deg,
   c[e] = deg <= 180.0 ? cos(deg * (3.14159265358979323846 / 180.0)) : -__builtin_inf();
 }
 
+// ------------------------------------------------------------------------------ bin table
+// Entry q of the bin-table core (q = 0 .. 2M): c in [q/M - 1, (q+1)/M - 1), widened by `margin`
+// on both sides.  An edge at angle e w (e = 1 .. nbins-1) sits at c = sqrt2 sin(e w / 2) when
+// e w <= 90 deg and at c = -sqrt2 cos(e w / 2) when e w >= 90 deg (both for exactly 90).  With
+// one edge in range: {e, bin e - 1 + 1}; with none: {far, the bin of the entry's middle + 1}.
+// The host only selects this core when no widened range can hold two edges.
+__device__ __forceinline__ double lut_angle_deg(double c) {  // inverse of the map above
+  constexpr double kSqrtHalf = 0.70710678118654752440, kDeg = 57.295779513082320877;
+  return c >= 0.0 ? 2.0 * asin(fmin(c, 1.0) * kSqrtHalf) * kDeg : 180.0 - 2.0 * asin(fmin(-c, 1.0) * kSqrtHalf) * kDeg;
+}
+
+__global__ void __launch_bounds__(256) lut_kernel(int32_t nbins, double w_deg, int32_t m, double margin,
+                                                  uint2 *lut) {
+  const int q = blockIdx.x * blockDim.x + threadIdx.x;
+  if (q > 2 * m) return;
+  constexpr double kSqrt2 = 1.41421356237309504880, kRad = 3.14159265358979323846 / 180.0;
+  const double lo = static_cast<double>(q) / m - 1.0 - margin;
+  const double hi = static_cast<double>(q + 1) / m - 1.0 + margin;
+  int count = 0, edge = 0;
+  double ce = 0.0;
+  // right half (0 .. 90 deg): c in [max(lo, 0), min(hi, 1)]
+  if (hi >= 0.0 && lo <= 1.0) {
+    const int e0 = static_cast<int>(floor(lut_angle_deg(fmax(lo, 0.0)) / w_deg)) - 1;
+    const int e1 = static_cast<int>(ceil(lut_angle_deg(fmin(hi, 1.0)) / w_deg)) + 1;
+    for (int e = e0 < 1 ? 1 : e0; e <= e1 && e < nbins; ++e) {
+      const double th = static_cast<double>(e) * w_deg;
+      if (th > 90.0) break;
+      const double c = kSqrt2 * sin(0.5 * th * kRad);
+      if (c >= lo && c <= hi) {
+        ++count;
+        ce = c;
+        edge = e;
+      }
+    }
+  }
+  // left half (90 .. 180 deg): c in [max(lo, -1), min(hi, 0))
+  if (lo < 0.0 && hi >= -1.0) {
+    const int e0 = static_cast<int>(floor(lut_angle_deg(fmax(lo, -1.0)) / w_deg)) - 1;
+    const int e1 = static_cast<int>(ceil(lut_angle_deg(fmin(hi, -1e-300)) / w_deg)) + 1;
+    for (int e = e0 < 1 ? 1 : e0; e <= e1 && e < nbins; ++e) {
+      const double th = static_cast<double>(e) * w_deg;
+      if (th < 90.0) continue;
+      const double c = -kSqrt2 * cos(0.5 * th * kRad);
+      if (c >= lo && c <= hi) {
+        ++count;
+        ce = c;
+        edge = e;
+      }
+    }
+  }
+  uint2 ent;
+  if (count >= 1) {
+    ent.x = __float_as_uint(static_cast<float>(ce));
+    ent.y = static_cast<uint32_t>(edge);  // bin below the edge is edge - 1; stored + 1
+  } else {
+    const double mid = fmin(fmax((static_cast<double>(q) + 0.5) / m - 1.0, -1.0), 1.0);
+    int b = static_cast<int>(floor(lut_angle_deg(mid) / w_deg));
+    b = b < 0 ? 0 : (b > nbins - 1 ? nbins - 1 : b);
+    ent.x = __float_as_uint(1e30f);  // c < e always: bin = B - 1
+    ent.y = static_cast<uint32_t>(b + 1);
+  }
+  lut[q] = ent;
+}
+
 // ------------------------------------------------------------------------------- merge
 // out_f[bin] = sum of slots of family f's workgroups (plus out_f[bin] itself when
 // accumulating).  Block: 256 threads = 4 waves over the slot list, one bin per lane; grid
@@ -550,11 +674,12 @@ __global__ void __launch_bounds__(256) omega_kernel(const uint64_t *dd, const ui
 }
 
 // -------------------------------------------------------------------------- eval core
-template <bool SPAN>
+template <int CORE>
 __global__ void __launch_bounds__(256) eval_core_kernel(const float *x32, const double *x64,
-                                                        int64_t n, const BinParams bp, int dot64,
+                                                        int64_t n, const BinParams bp, int dot64, const uint2 *lut,
                                                         const double *edge_cos, int32_t *bin_out,
                                                         uint8_t *trip_out, int32_t *exact_out, float *t_out) {
+  constexpr bool SPAN = CORE != 0;
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (idx >= n) return;
   uint32_t k;
@@ -567,7 +692,8 @@ __global__ void __launch_bounds__(256) eval_core_kernel(const float *x32, const 
   } else {
     const float xf = x32[idx];
     xe = static_cast<double>(xf);
-    core32<SPAN>(xf, bp, bp.h, bp.tmax, k, trip, t);
+    if constexpr (CORE == 2) core_lut(xf, bp, lut, k, trip, t);
+    else core32<SPAN>(xf, bp, bp.h, bp.tmax, k, trip, t);
   }
   // k == nbins is the full-span kernel's spare bin, which the flush folds into bin nbins - 1
   const uint32_t last = static_cast<uint32_t>(bp.nbins - 1);
@@ -591,31 +717,34 @@ hipError_t launch_prepare(const float *ra, const float *dec, int64_t n, void *bl
   return hipGetLastError();
 }
 
-template <int K, bool D64, bool FS> static const void *pairs_fn() {
-  return reinterpret_cast<const void *>(&pairs_kernel<K, D64, FS>);
+template <int K, bool D64, int CORE> static const void *pairs_fn() {
+  return reinterpret_cast<const void *>(&pairs_kernel<K, D64, CORE>);
 }
 
-// Instantiations: K in {4, 8} x {fp32, fp64 dot} x {generic, span-specialised core}.
-static const void *select_pairs(bool dot64, int k, bool span) {
+// Instantiations: K in {4, 8} x {fp32, fp64 dot} x {generic, span-specialised core}, plus the
+// fp32 bin-table core.
+static const void *select_pairs(bool dot64, int k, int core) {
   if (dot64) {
-    if (span) return k == 4 ? pairs_fn<4, true, true>() : pairs_fn<8, true, true>();
-    return k == 4 ? pairs_fn<4, true, false>() : pairs_fn<8, true, false>();
+    if (core) return k == 4 ? pairs_fn<4, true, 1>() : pairs_fn<8, true, 1>();
+    return k == 4 ? pairs_fn<4, true, 0>() : pairs_fn<8, true, 0>();
   }
-  if (span) return k == 4 ? pairs_fn<4, false, true>() : pairs_fn<8, false, true>();
-  return k == 4 ? pairs_fn<4, false, false>() : pairs_fn<8, false, false>();
+  if (core == 2) return k == 4 ? pairs_fn<4, false, 2>() : pairs_fn<8, false, 2>();
+  if (core) return k == 4 ? pairs_fn<4, false, 1>() : pairs_fn<8, false, 1>();
+  return k == 4 ? pairs_fn<4, false, 0>() : pairs_fn<8, false, 0>();
 }
 
-hipError_t pairs_occupancy(bool dot64, int k, bool span, size_t lds_bytes, int *blocks_per_cu) {
-  const void *fn = select_pairs(dot64, k, span);
+hipError_t pairs_occupancy(bool dot64, int k, int core, size_t lds_bytes, int *blocks_per_cu) {
+  const void *fn = select_pairs(dot64, k, core);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      static_cast<int>(lds_bytes));
   if (e != hipSuccess) return e;
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, fn, kWGThreads, lds_bytes);
 }
 
-hipError_t launch_pairs(const PairArgs &a, int num_wg, bool dot64, int k, bool span, hipStream_t st) {
-  const size_t lds = pairs_lds_bytes(a.hist_words, a.shared_hist != 0, k);
-  const void *fn = select_pairs(dot64, k, span);
+hipError_t launch_pairs(const PairArgs &a, int num_wg, bool dot64, int k, int core, hipStream_t st) {
+  const size_t lds = pairs_lds_bytes(a.hist_words, core == 2 || a.shared_hist != 0, k,
+                                     core == 2 ? a.bp.lut_n + 1 : 0);
+  const void *fn = select_pairs(dot64, k, core);
   void *args[] = {const_cast<PairArgs *>(&a)};
   return hipLaunchKernel(fn, dim3(num_wg), dim3(kWGThreads), args, lds, st);
 }
@@ -641,21 +770,30 @@ hipError_t launch_omega(const uint64_t *dd, const uint64_t *dr, const uint64_t *
   return hipGetLastError();
 }
 
+hipError_t launch_lut(int32_t nbins, double w_deg, int32_t m, double margin, uint2 *lut, hipStream_t st) {
+  hipLaunchKernelGGL(lut_kernel, dim3((2 * m + 1 + 255) / 256), dim3(256), 0, st, nbins, w_deg, m, margin, lut);
+  return hipGetLastError();
+}
+
 hipError_t launch_edges(int32_t nbins, double w_deg, double *edge_cos, hipStream_t st) {
   hipLaunchKernelGGL(edges_kernel, dim3((nbins + 1 + 255) / 256), dim3(256), 0, st, nbins, w_deg, edge_cos);
   return hipGetLastError();
 }
 
 hipError_t launch_eval_core(const float *x32, const double *x64, int64_t n, const BinParams &bp,
-                            bool dot64, bool span, const double *edge_cos, int32_t *bin_out,
+                            bool dot64, int core, const uint2 *lut, const double *edge_cos, int32_t *bin_out,
                             uint8_t *trip_out, int32_t *exact_out, float *t_out, hipStream_t st) {
-  const int64_t blocks = (n + 255) / 256;
-  if (span)
-    hipLaunchKernelGGL(eval_core_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, x32, x64, n,
-                       bp, dot64 ? 1 : 0, edge_cos, bin_out, trip_out, exact_out, t_out);
+  const dim3 grid(static_cast<unsigned>((n + 255) / 256));
+  const int d = dot64 ? 1 : 0;
+  if (core == 2)
+    hipLaunchKernelGGL(eval_core_kernel<2>, grid, dim3(256), 0, st, x32, x64, n, bp, d, lut, edge_cos, bin_out,
+                       trip_out, exact_out, t_out);
+  else if (core == 1)
+    hipLaunchKernelGGL(eval_core_kernel<1>, grid, dim3(256), 0, st, x32, x64, n, bp, d, lut, edge_cos, bin_out,
+                       trip_out, exact_out, t_out);
   else
-    hipLaunchKernelGGL(eval_core_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, x32, x64, n,
-                       bp, dot64 ? 1 : 0, edge_cos, bin_out, trip_out, exact_out, t_out);
+    hipLaunchKernelGGL(eval_core_kernel<0>, grid, dim3(256), 0, st, x32, x64, n, bp, d, lut, edge_cos, bin_out,
+                       trip_out, exact_out, t_out);
   return hipGetLastError();
 }
 
