@@ -116,10 +116,11 @@ typedef struct {
                                 bins' span - fp32 dot: no clamp of the bin coordinate (only
                                 valid when (nbins + 1/2) * width >= 180 deg); fp64 dot: no
                                 sign handling (only valid when nbins * width <= 90 deg) */
-    int32_t bin_table;       /* 0 auto; 1: never bin through a table; 2: always (only valid
-                                for the fp32 dot product, bins covering 180 deg and widths
-                                where the table is sound, about >= 0.25 deg; forces one
-                                shared histogram per workgroup) */
+    int32_t fast_core;       /* 0 auto; 1: never use an arccos-free core; 2: always - the
+                                bin table (fp32 dot, bins covering 180 deg at widths where
+                                the table is sound, about >= 0.22 deg; one histogram shared
+                                per workgroup) or the series (fp64 dot, bins ending by about
+                                9 deg); invalid where neither applies */
     int64_t flush_interval;  /* 0 auto; else j-steps between flushes of the 32-bit LDS
                                 histograms into 64-bit totals (>= 1) */
 } gc_tuning;

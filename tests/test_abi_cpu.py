@@ -100,7 +100,7 @@ def test_histogram_validation(lib):
     assert _hist(lib, ws=None) == INVALID
     assert _hist(lib, ws=P(A + 128)) == INVALID
     assert _hist(lib, wsb=gc.workspace_bytes(720) - 1) == WORKSPACE
-    T = gc._Tuning  # dot, K, blocks/CU, shared histogram, span kernel, bin table, flush interval
+    T = gc._Tuning  # dot, K, blocks/CU, shared histogram, span kernel, fast core, flush interval
     for bad in (T(33, 0, 0, 0, 0, 0, 0), T(0, 5, 0, 0, 0, 0, 0), T(0, 0, 9, 0, 0, 0, 0),
                 T(0, 0, -1, 0, 0, 0, 0), T(0, 0, 0, 3, 0, 0, 0), T(0, 0, 0, -1, 0, 0, 0),
                 T(0, 0, 0, 0, 3, 0, 0), T(0, 0, 0, 0, 0, 3, 0), T(0, 0, 0, 0, 0, -1, 0), T(0, 0, 0, 0, 0, 0, -3),
@@ -109,8 +109,10 @@ def test_histogram_validation(lib):
     assert _hist(lib, nbins=700, tuning=T(0, 0, 0, 0, 2, 0, 0)) == INVALID  # 700 x 0.25 < 180 deg
     assert _hist(lib, nbins=361, tuning=T(64, 0, 0, 0, 2, 0, 0)) == INVALID  # 361 x 0.25 > 90 deg
     assert _hist(lib, nbins=1500, w=0.001, tuning=T(32, 0, 0, 0, 2, 0, 0)) == INVALID  # 1.5 < 180 deg
-    # the bin table: fp32 dot, full span, a sound table, a shared histogram
-    assert _hist(lib, tuning=T(64, 0, 0, 0, 0, 2, 0)) == INVALID
+    # arccos-free cores: the bin table (fp32 dot, full span, a sound table, a shared histogram)
+    # or the series (fp64 dot, bins ending by ~9 deg)
+    assert _hist(lib, tuning=T(64, 0, 0, 0, 0, 2, 0)) == INVALID                      # 180 deg, fp64
+    assert _hist(lib, nbins=100, w=0.1, tuning=T(64, 0, 0, 0, 0, 2, 0)) == INVALID     # 10 deg: series too short
     assert _hist(lib, nbins=3600, w=0.05, tuning=T(0, 0, 0, 0, 0, 2, 0)) == INVALID   # too narrow
     assert _hist(lib, nbins=700, tuning=T(0, 0, 0, 0, 0, 2, 0)) == INVALID            # not full span
     assert _hist(lib, tuning=T(0, 0, 0, 1, 0, 2, 0)) == INVALID                       # private histograms

@@ -95,7 +95,23 @@ def test_fp32_core_sound_near_edges(gc, nbins, w):
         assert r < 1.5e-2, r
 
 
-@pytest.mark.parametrize("nbins,w", [(720, 0.25), (3600, 0.05), (1500, 0.001)])
+# fp64 cores: 720 x 0.25 deg the generic core, 400 x 0.2 deg (80 deg) the narrow-range core,
+# 1500 x 0.001 deg the series core.
+FP64_CASES = [(720, 0.25), (400, 0.2), (1500, 0.001)]
+
+
+def series_rho(nbins, w):
+    """The series core's relative bound when it applies (bins ending by ~9 deg), else None."""
+    th = (nbins + 1) * np.radians(w)
+    if th >= np.pi / 2:
+        return None
+    y = 2 * np.sin(th / 2) ** 2
+    q = 2 * np.arcsin(np.sqrt(y / 2)) / np.sqrt(y)
+    r = (q - np.sqrt(2) * (1 + y / 12 + 3 * y * y / 160)) / q
+    return 1.25 * (r + 7 * 2.0 ** -24) if 0 <= r <= 2e-8 else None
+
+
+@pytest.mark.parametrize("nbins,w", FP64_CASES)
 def test_fp64_core_sound_near_edges(gc, nbins, w):
     print(f"[gpu] fp64 core near edges nbins={nbins}", flush=True)
     rng = np.random.default_rng(nbins + 1)
@@ -167,11 +183,13 @@ def test_fp32_core_error_within_model(gc, nbins, w):
     assert ratio.max() <= 0.9
 
 
-@pytest.mark.parametrize("nbins,w", [(720, 0.25), (1500, 0.001)])
+@pytest.mark.parametrize("nbins,w", FP64_CASES)
 def test_fp64_core_error_within_model(gc, nbins, w):
     """The fp64-dot core's t against acos(x)/w: the guard assumes a relative error rho.  For
     bins ending by 90 deg the narrow-range core is used; it needs t accurate only for x >= 0,
-    and for x < 0 (past 90 deg) only t >= nbins - 1/2, which clamps to the last bin."""
+    and for x < 0 (past 90 deg) only t >= nbins - 1/2, which clamps to the last bin.  For bins
+    ending by ~9 deg the series core is used: its bound rho_s holds up to one bin past the
+    range, and beyond it t only has to stay at or past the last bin."""
     print(f"[gpu] fp64 core error model nbins={nbins}", flush=True)
     rng = np.random.default_rng(5)
     x = np.concatenate([rng.uniform(-1, 1, 4_000_000), np.cos(rng.uniform(0, 0.05, 2_000_000)),
@@ -180,7 +198,12 @@ def test_fp64_core_error_within_model(gc, nbins, w):
     t_exact = np.arccos(np.clip(x, -1, 1)) / np.radians(w)
     rho = ((_header_constant("GC_ACOS_FIT_ERR") + 4 * 2.0 ** -24 * (np.pi / 2)) / 1.41 + 10 * 2.0 ** -24) * 1.25
     narrow = nbins * w <= 90.0
+    rho_s = series_rho(nbins, w)
+    if rho_s is not None:
+        rho = rho_s
     acc = x >= 0 if narrow else np.ones(len(x), bool)
+    if rho_s is not None:
+        acc = acc & (t_exact <= nbins + 1)
     if narrow:
         assert np.all(t[~acc] >= nbins - 0.5) and not trip[~acc].any()
     sel = acc & (t_exact > 1e-3)

@@ -210,8 +210,8 @@ def test_outputs_overwritten_and_self_pairs(gc):
                                     dict(shared_histogram=1), dict(shared_histogram=2),
                                     dict(shared_histogram=2, flush_interval=5),
                                     dict(span_kernel=1), dict(span_kernel=2, i_per_lane=4),
-                                    dict(bin_table=1), dict(bin_table=2, i_per_lane=4),
-                                    dict(bin_table=2, flush_interval=5)])
+                                    dict(fast_core=1), dict(fast_core=2, i_per_lane=4),
+                                    dict(fast_core=2, flush_interval=5)])
 def test_tuning_does_not_change_results(gc, tuning):
     print(f"[gpu] tuning {tuning}", flush=True)
     D, R = catalogs.WORKLOADS["clustered100k_720"].catalogs(n=6000)

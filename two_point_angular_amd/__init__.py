@@ -56,7 +56,7 @@ class GCError(RuntimeError):
 class _Tuning(ctypes.Structure):
     _fields_ = [("dot_precision", ctypes.c_int32), ("i_per_lane", ctypes.c_int32),
                 ("blocks_per_cu", ctypes.c_int32), ("shared_histogram", ctypes.c_int32),
-                ("span_kernel", ctypes.c_int32), ("bin_table", ctypes.c_int32),
+                ("span_kernel", ctypes.c_int32), ("fast_core", ctypes.c_int32),
                 ("flush_interval", ctypes.c_int64)]
 
 
@@ -70,11 +70,11 @@ class Tuning:
     flush_interval: int = 0
     shared_histogram: int = 0
     span_kernel: int = 0
-    bin_table: int = 0
+    fast_core: int = 0
 
     def _c(self) -> _Tuning:
         return _Tuning(self.dot_precision, self.i_per_lane, self.blocks_per_cu, self.shared_histogram,
-                       self.span_kernel, self.bin_table, self.flush_interval)
+                       self.span_kernel, self.fast_core, self.flush_interval)
 
 
 _lib = None

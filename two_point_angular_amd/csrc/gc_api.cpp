@@ -172,6 +172,49 @@ LutPlan plan_lut(int32_t nbins, double w_deg) {
   return p;
 }
 
+// ---- series core ---------------------------------------------------------------------------
+// fp64 dot, bins ending by about 9 deg: t = s (q0 + q1 y + q2 y^2) / w with y = 1 - x, the
+// quadratic truncation of acos(1 - y) / sqrt(y) = sqrt2 (1 + y/12 + 3y^2/160 + 5y^3/896 + ...).
+// All omitted terms are positive, so the relative truncation error R grows with y; it is taken
+// at y_max = 1 - cos((nbins + 1) w), one bin past the range (beyond it the guard never needs t:
+// the quadratic grows with y, so those pairs land at or past the last bin).  The core's
+// relative error: R plus roundings of the three scaled coefficients (1 unit of 2^-24), the two
+// fmas (2), narrowing y (half a unit through the square root), the 1-ulp square root (2) and
+// the product (1): rho_s = 1.25 (R + 7 * 2^-24).  Used when R <= 2e-8.
+struct SeriesPlan;
+void apply_series(BinParams &bp, const SeriesPlan &sp, int32_t nbins);
+
+struct SeriesPlan {
+  bool ok = false;
+  float ps[3] = {0.0f, 0.0f, 0.0f};
+  double rho = 0.0;
+};
+
+SeriesPlan plan_series(int32_t nbins, double w_deg) {
+  SeriesPlan p;
+  const double w = w_deg * (kPi / 180.0);
+  const double th = (static_cast<double>(nbins) + 1.0) * w;
+  if (!(th < kPi / 2.0)) return p;
+  const double sh = sin(0.5 * th);
+  const double y = 2.0 * sh * sh;                       // 1 - cos(th), without cancellation
+  const double q_exact = 2.0 * asin(sqrt(0.5 * y)) / sqrt(y);
+  const double sqrt2 = 1.41421356237309504880;
+  const double q_trunc = sqrt2 * (1.0 + y / 12.0 + 3.0 * y * y / 160.0);
+  const double r = (q_exact - q_trunc) / q_exact;
+  if (!(r >= 0.0 && r <= 2e-8)) return p;
+  p.ok = true;
+  p.ps[0] = static_cast<float>(sqrt2 / w);
+  p.ps[1] = static_cast<float>(sqrt2 / 12.0 / w);
+  p.ps[2] = static_cast<float>(3.0 * sqrt2 / 160.0 / w);
+  p.rho = 1.25 * (r + 7.0 * kTwoM24);
+  return p;
+}
+
+void apply_series(BinParams &bp, const SeriesPlan &sp, int32_t nbins) {
+  for (int q = 0; q < 3; ++q) bp.ps[q] = sp.ps[q];
+  bp.g64k1 = static_cast<float>(sp.rho * (static_cast<double>(nbins) + 1.0) * (1.0 + 1e-6));
+}
+
 // Spans the specialised cores accept: the fp32 core without a clamp needs nbins w to reach
 // 180 deg within half a bin; the fp64 core without sign handling needs nbins w <= 90 deg.
 bool span_full(int32_t nbins, double w_deg) { return (static_cast<double>(nbins) + 0.5) * w_deg >= 180.0; }
@@ -282,7 +325,7 @@ gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, in
   if ((tu.dot_precision != 0 && tu.dot_precision != 32 && tu.dot_precision != 64) ||
       (tu.i_per_lane != 0 && tu.i_per_lane != 4 && tu.i_per_lane != 8) || tu.blocks_per_cu < 0 ||
       tu.blocks_per_cu > kMaxBlocksPerCU || tu.shared_histogram < 0 || tu.shared_histogram > 2 ||
-      tu.span_kernel < 0 || tu.span_kernel > 2 || tu.bin_table < 0 || tu.bin_table > 2 ||
+      tu.span_kernel < 0 || tu.span_kernel > 2 || tu.fast_core < 0 || tu.fast_core > 2 ||
       tu.flush_interval < 0)
     return GC_ERR_INVALID_ARGUMENT;
 
@@ -298,12 +341,16 @@ gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, in
   const bool span_ok = dot64 ? span_narrow(nbins, w_deg) : span_full(nbins, w_deg);
   if (tu.span_kernel == 2 && !span_ok) return GC_ERR_INVALID_ARGUMENT;
   const bool span = span_ok && tu.span_kernel != 1;
-  // The bin-table core (fp32, full span, shared histogram) where its table is sound.
+  // The arccos-free cores where they are sound: the bin table (fp32 dot, full span, shared
+  // histogram) and the series (fp64 dot, bins ending by ~9 deg).
   const LutPlan lp = dot64 ? LutPlan() : plan_lut(nbins, w_deg);
+  const SeriesPlan sp = dot64 ? plan_series(nbins, w_deg) : SeriesPlan();
   const bool lut_ok = lp.ok && span && tu.shared_histogram != 1;
-  if (tu.bin_table == 2 && !lut_ok) return GC_ERR_INVALID_ARGUMENT;
-  const bool use_lut = lut_ok && tu.bin_table != 1;
-  const int core = use_lut ? 2 : (span ? 1 : 0);
+  const bool series_ok = sp.ok && span;
+  if (tu.fast_core == 2 && !lut_ok && !series_ok) return GC_ERR_INVALID_ARGUMENT;
+  const bool use_lut = lut_ok && tu.fast_core != 1;
+  const bool use_series = series_ok && tu.fast_core != 1;
+  const int core = (use_lut || use_series) ? 2 : (span ? 1 : 0);
   const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
 
   PairArgs a;
@@ -312,6 +359,7 @@ gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, in
   a.hist_words = (nbins + kWave + 63) / 64 * 64;  // 64 spare bins past the last (see core32)
   a.wave_lds_words = a.hist_words + queue_words(k);
   a.bp = make_bins(nbins, w_deg);
+  if (use_series) apply_series(a.bp, sp, nbins);
   if (use_lut) {
     a.bp.lut_m = static_cast<float>(lp.m);
     a.bp.lut_g = lp.g;
@@ -491,13 +539,16 @@ gc_status gc_eval_angle_core(const float *x32, const double *x64, int64_t n, int
   // the same core the histogram call would use for these bins
   const bool span = d64 ? span_narrow(nbins, w_deg) : span_full(nbins, w_deg);
   const LutPlan lp = d64 ? LutPlan() : plan_lut(nbins, w_deg);
+  const SeriesPlan sp = d64 ? plan_series(nbins, w_deg) : SeriesPlan();
   const bool use_lut = lp.ok && span;
-  const int core = use_lut ? 2 : (span ? 1 : 0);
+  const bool use_series = sp.ok && span;
+  const int core = (use_lut || use_series) ? 2 : (span ? 1 : 0);
   if (n == 0) return GC_OK;
   const bool need_ws = exact_out || use_lut;
   if (need_ws && (!workspace || !aligned(workspace, GC_ALIGNMENT))) return GC_ERR_INVALID_ARGUMENT;
   if (need_ws && ws_bytes < edge_table_bytes(nbins) + kLutBytes) return GC_ERR_WORKSPACE;
   BinParams bp = make_bins(nbins, w_deg);
+  if (use_series) apply_series(bp, sp, nbins);
   const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   double *edge_cos = static_cast<double *>(workspace);
   uint2 *lut = need_ws ? reinterpret_cast<uint2 *>(static_cast<char *>(workspace) + edge_table_bytes(nbins)) : nullptr;

@@ -53,6 +53,7 @@ struct BinParams {
   float g64k1;   // fp64-dot guard: recheck iff |t - round(t)| * s < g64k1 * s + g64k2
   float g64k2;
   float pw[7];   // acos polynomial coefficients times 1 / w_rad (fp32): narrow-range fp64 core
+  float ps[3];   // series core (fp64 dot, narrow bins): sqrt2 (1, 1/12, 3/160) / w_rad
   float lut_m;   // bin-table core: entries per unit of c (M); the table has 2 M + 1 entries
   float lut_g;   // bin-table core guard: recheck iff |c - e| * s < lut_g
   int32_t lut_n; // 2 M (last entry index), or 0 when the bin table is not used
@@ -115,8 +116,8 @@ void record_hip_error(hipError_t e);
 hipError_t launch_prepare(const float *ra, const float *dec, int64_t n, void *blob, hipStream_t s);
 // dot64: fp64 dot-product variant; k: galaxies per lane (4 or 8); core: 0 the generic core;
 // 1 the one specialised to the bins' span - fp32 dot: nbins w covers 180 deg (no clamp of t,
-// spare bin instead); fp64 dot: nbins w <= 90 deg (no sign handling); 2 (fp32 only) the
-// bin-table core (full span, shared histogram)
+// spare bin instead); fp64 dot: nbins w <= 90 deg (no sign handling); 2 - fp32 dot: the
+// bin-table core (full span, shared histogram); fp64 dot: the series core (bins ending by ~9 deg)
 hipError_t launch_pairs(const PairArgs &a, int num_wg, bool dot64, int k, int core, hipStream_t s);
 hipError_t pairs_occupancy(bool dot64, int k, int core, size_t lds_bytes, int *blocks_per_cu);
 hipError_t launch_lut(int32_t nbins, double w_deg, int32_t m, double margin, uint2 *lut, hipStream_t s);

@@ -104,11 +104,21 @@ __device__ __forceinline__ void core32(float x, const BinParams &bp, float h_v, 
 // it (the guard may flag it near a spare bin's edge; the recheck keeps it in the last bin).  The coefficients come pre-scaled by 1 / w (bp.pw; the
 // highest one in a VGPR, pw6_v), so t = s P'(x) without a final multiply.  tmax_v: as in
 // core32, each lane's own spare bin past the last bin.
-template <bool NARROW>
+// SERIES (bins ending by about 9 deg): with y = 1 - x formed in fp64, acos(1 - y) / sqrt(y) =
+// sqrt2 (1 + y/12 + 3 y^2/160 + 5 y^3/896 + ...), all terms positive; over the binned range
+// (y <= 1 - cos((nbins + 1) w)) the quadratic truncation is within its next term, far below the
+// guard's rho, so t = s (q0 + q1 y + q2 y^2) / w (coefficients pre-scaled, q2 in a VGPR).  The
+// quadratic grows with y, so every pair past the range, x < 0 included (y clamped to 1), lands
+// at or past the last bin.
+template <int MODE>  // 0: generic, 1: NARROW, 2: SERIES
 __device__ __forceinline__ void core64(double x, const BinParams &bp, float pw6_v, float tmax_v, uint32_t &k,
                                        bool &trip, float &t_raw) {
   float s, t;
-  if constexpr (NARROW) {
+  if constexpr (MODE == 2) {
+    const float y = __builtin_amdgcn_fmed3f(static_cast<float>(1.0 - x), 0.0f, 1.0f);
+    s = __builtin_amdgcn_sqrtf(y);
+    t = s * fmaf(fmaf(pw6_v, y, bp.ps[1]), y, bp.ps[0]);
+  } else if constexpr (MODE == 1) {
     s = __builtin_amdgcn_sqrtf(__builtin_amdgcn_fmed3f(static_cast<float>(1.0 - x), 0.0f, 1.0f));
     const float a = static_cast<float>(x);
     float p = fmaf(pw6_v, a, bp.pw[5]);
@@ -254,8 +264,7 @@ __attribute__((amdgpu_waves_per_eu(K == 4 ? 6 : (D64 ? 4 : 5))))
 pairs_kernel(const PairArgs A) {
   typedef typename Real<D64>::T real;
   constexpr bool SPAN = CORE != 0;
-  constexpr bool LUT = CORE == 2;
-  static_assert(!(LUT && D64), "the bin table is an fp32-dot core");
+  constexpr bool LUT = CORE == 2 && !D64;  // fp64 dot: CORE 2 is the series core
   constexpr int BI = kWave * K;       // i-block: galaxies per wave
   constexpr int JB = D64 ? 4 : 8;     // j galaxies per scalar batch
   extern __shared__ uint32_t lds[];
@@ -279,7 +288,7 @@ pairs_kernel(const PairArgs A) {
   const BinParams &bp = A.bp;
   const uint32_t W = F.sym ? 2u : 1u;
   // the one wave-uniform constant each core needs in a VGPR, and this lane's clamp
-  const float c_v = in_vgpr(D64 ? bp.pw[6] : bp.h);
+  const float c_v = in_vgpr(D64 ? (CORE == 2 ? bp.ps[2] : bp.pw[6]) : bp.h);
   const float tmax_v = bp.tmax + static_cast<float>(lane);
 
   unsigned long long *const slot = A.slots + static_cast<size_t>(g) * A.nbins;
@@ -396,7 +405,7 @@ pairs_kernel(const PairArgs A) {
         bool tp;
         const real x = fma(ix[k], xj, fma(iy[k], yj, iz[k] * zj));
         float t_unused;
-        if constexpr (D64) core64<SPAN>(x, bp, c_v, tmax_v, kk, tp, t_unused);
+        if constexpr (D64) core64<CORE>(x, bp, c_v, tmax_v, kk, tp, t_unused);
         else core32<SPAN>(x, bp, c_v, tmax_v, kk, tp, t_unused);
         if constexpr (GENERIC) {
           const int64_t ig = i0 + lane + kWave * k;
@@ -688,11 +697,11 @@ __global__ void __launch_bounds__(256) eval_core_kernel(const float *x32, const 
   float t;
   if (dot64) {
     xe = x64[idx];
-    core64<SPAN>(xe, bp, bp.pw[6], bp.tmax, k, trip, t);
+    core64<CORE>(xe, bp, CORE == 2 ? bp.ps[2] : bp.pw[6], bp.tmax, k, trip, t);
   } else {
     const float xf = x32[idx];
     xe = static_cast<double>(xf);
-    if constexpr (CORE == 2) core_lut(xf, bp, lut, k, trip, t);
+    if constexpr (CORE == 2) core_lut(xf, bp, lut, k, trip, t);  // (fp32 dot: CORE 2 is the table)
     else core32<SPAN>(xf, bp, bp.h, bp.tmax, k, trip, t);
   }
   // k == nbins is the full-span kernel's spare bin, which the flush folds into bin nbins - 1
@@ -722,9 +731,10 @@ template <int K, bool D64, int CORE> static const void *pairs_fn() {
 }
 
 // Instantiations: K in {4, 8} x {fp32, fp64 dot} x {generic, span-specialised core}, plus the
-// fp32 bin-table core.
+// fp32 bin-table core and the fp64 series core.
 static const void *select_pairs(bool dot64, int k, int core) {
   if (dot64) {
+    if (core == 2) return k == 4 ? pairs_fn<4, true, 2>() : pairs_fn<8, true, 2>();
     if (core) return k == 4 ? pairs_fn<4, true, 1>() : pairs_fn<8, true, 1>();
     return k == 4 ? pairs_fn<4, true, 0>() : pairs_fn<8, true, 0>();
   }
@@ -742,8 +752,8 @@ hipError_t pairs_occupancy(bool dot64, int k, int core, size_t lds_bytes, int *b
 }
 
 hipError_t launch_pairs(const PairArgs &a, int num_wg, bool dot64, int k, int core, hipStream_t st) {
-  const size_t lds = pairs_lds_bytes(a.hist_words, core == 2 || a.shared_hist != 0, k,
-                                     core == 2 ? a.bp.lut_n + 1 : 0);
+  const bool table = core == 2 && !dot64;
+  const size_t lds = pairs_lds_bytes(a.hist_words, table || a.shared_hist != 0, k, table ? a.bp.lut_n + 1 : 0);
   const void *fn = select_pairs(dot64, k, core);
   void *args[] = {const_cast<PairArgs *>(&a)};
   return hipLaunchKernel(fn, dim3(num_wg), dim3(kWGThreads), args, lds, st);
