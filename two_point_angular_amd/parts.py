@@ -28,7 +28,8 @@ from . import Tuning, histogram_part, workspace_bytes
 
 def _meta(n_d, n_r, nbins, w, parts, key, tuning):
     t = None if tuning is None else [tuning.dot_precision, tuning.i_per_lane, tuning.blocks_per_cu,
-                                     tuning.shared_histogram, tuning.span_kernel, tuning.flush_interval]
+                                     tuning.shared_histogram, tuning.span_kernel, tuning.fast_core,
+                                     tuning.flush_interval]
     return json.dumps({"n_d": int(n_d), "n_r": int(n_r), "nbins": int(nbins), "bin_width_deg": float(w),
                        "parts": int(parts), "key": str(key), "tuning": t}, sort_keys=True)
 
