@@ -270,8 +270,10 @@ def test_million_catalogs_totals_and_subproblem(gc):
 
 def test_bin_table_maps_every_entry(gc):
     """The bin table built on the device for 720 x 0.25 deg: for every entry q (c in
-    [q/M - 1, (q+1)/M - 1)) and 65 values of c across it, bin = B - [c < e] equals the bin of
-    the angle of c, theta = 2 asin(c / sqrt2) (c >= 0) or 180 - 2 asin(-c / sqrt2) degrees."""
+    [(q - 1/2)/M - 1, (q + 1/2)/M - 1]) and 64 values of c across it, bin = B - [x > e] with
+    x = cos(theta) equals the bin of the angle of c, theta = 2 asin(c / sqrt2) (c >= 0) or
+    180 - 2 asin(-c / sqrt2) degrees.  The middle entry (q = M) holds both ends of the range: its
+    words nbins + 64 and nbins + 65 count as bins 0 and nbins - 1."""
     import torch
     print("[gpu] bin table entries", flush=True)
     nbins, w = 720, 0.25
@@ -290,21 +292,23 @@ def test_bin_table_maps_every_entry(gc):
     tab = ws[off: off + (2 * m + 1) * 8].cpu().numpy().view(np.uint32).reshape(-1, 2)
     e = tab[:, 0].view(np.float32).astype(np.float64)
     b = tab[:, 1].astype(np.int64)
+    assert e[m] == 0.0 and b[m] == nbins + 65
     q = np.arange(2 * m + 1)
     frac = np.linspace(0.0, 1.0, 65)[:-1]
-    c = (q[:, None] + frac[None, :]) / m - 1.0
+    c = (q[:, None] + frac[None, :] - 0.5) / m - 1.0
     c = np.clip(c, -1.0, 1.0)
     th = np.where(c >= 0, 2 * np.degrees(np.arcsin(np.minimum(c, 1) / np.sqrt(2))),
                   180 - 2 * np.degrees(np.arcsin(np.minimum(-c, 1) / np.sqrt(2))))
+    xs = np.cos(np.radians(th))
     want = np.minimum(np.floor(th / w).astype(np.int64), nbins - 1)
-    got = b[:, None] - (c < e[:, None])
-    # a sample within the fp32 rounding of the stored edge may fall either way
-    near = np.abs(c - e[:, None]) < 1e-6
+    got = b[:, None] - (xs > e[:, None])
+    got = np.where(got == nbins + 64, 0, np.minimum(got, nbins - 1))
+    # a sample within the fp32 rounding of the stored edge cosine may fall either way
+    near = np.abs(xs - e[:, None]) < 1e-7
     assert np.all((got == want) | near), int(((got != want) & ~near).sum())
-    # every entry that holds an edge holds the one inside it, when there is one
+    # every edge is held by the entry its c rounds to
     for k in range(1, nbins):
         th_e = k * w
         ce = np.sqrt(2) * np.sin(np.radians(th_e) / 2) if th_e <= 90 else -np.sqrt(2) * np.cos(np.radians(th_e) / 2)
-        qe = int(np.floor(m * (ce + 1)))
-        if qe <= 2 * m:
-            assert abs(e[qe] - ce) < 1e-6 and b[qe] == k, (k, qe, e[qe], ce, b[qe])
+        qe = int(np.rint(m * (ce + 1)))
+        assert abs(e[qe] - np.cos(np.radians(th_e))) < 1e-7 and b[qe] == k, (k, qe, e[qe], b[qe])

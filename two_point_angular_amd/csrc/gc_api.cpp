@@ -118,17 +118,24 @@ BinParams make_bins(int32_t nbins, double w_deg) {
 // ---- bin-table core -------------------------------------------------------------------------
 // The fp32-dot core of the full span can bin through a table instead of an arccos (core_lut in
 // gc_kernels.hip): c = copysign(sqrt(1 - |x|), x) grows with the angle on each half (c =
-// sqrt2 sin(theta/2) up to 90 deg, -sqrt2 cos(theta/2) beyond), entry q covers c in
-// [q/M - 1, (q+1)/M - 1) widened by a margin, and holds the one edge in that range.
-// Guard: the computed c has |c~ - c| s~ <= g_x (1 + 2^-22) + 2^-24 + 2^-23 (dot product,
-// subtraction, 1-ulp square root); the stored edge is rounded to fp32 (2^-24); the subtraction
-// and product of the test round relatively: recheck iff |c - e| s < lut_g = 1.1 (g_x + 2^-22).
-// The table is sound when
+// sqrt2 sin(theta/2) up to 90 deg, -sqrt2 cos(theta/2) beyond), entry q = round(M (c + 1))
+// covers c in [(q - 1/2)/M - 1, (q + 1/2)/M - 1] widened by a margin, and holds the one edge in
+// that range as its cosine e (fp32); the pair's side of the edge is the sign of e - x.
+// Guard (in the cosine): |x~ - x| <= g_x (fp32 unit vectors and dot product), |e - cos| <=
+// 2^-25 (fp32 rounding of a cosine in [-1, 1]); recheck iff |e - x~| < lut_g = 1.1 (g_x +
+// 2^-25).  (The test's subtraction rounds monotonically and lut_g is an fp32 number, so a
+// computed |e - x~| >= lut_g means the exact one is too, up to the 10 % margin.)
+// Selecting the entry: |c~ - c| s~ <= g_c = 1.1 (g_x + 2^-22) (dot product, the subtraction
+// 1 - |x|, the 1-ulp square root).  The table is sound when
 //  (a) no widened entry range can hold two edges: 1/M + 2 margin < the smallest gap between
 //      consecutive edges in c (M = ceil(4 / w_rad), margin = 0.45 (gap - 1/M));
-//  (b) where the error of c exceeds the margin (s < S* = lut_g / margin), it cannot reach any
-//      edge: s + lut_g / s < |c| of the first and last edges for s in [2^-12, S*] (2^-12 is
-//      the smallest non-zero s; the bound is convex in s, so its endpoints decide).
+//  (b) where the error of c exceeds the margin (s < S* = g_c / margin), it cannot reach any
+//      edge: s + g_c / s < |c| of the first and last edges for s in [2^-12, S*] (2^-12 is
+//      the smallest non-zero s; the bound is convex in s, so its endpoints decide);
+//  (c) the middle entry (q = M: c within 1/(2M) of 0, i.e. both the smallest angles and the
+//      largest) holds no edge: 1/(2M) + margin < |c| of the first and last edges.  It stores
+//      e = 0 and sends x > 0 to a histogram word counted as bin 0 and x < 0 to one counted as
+//      bin nbins - 1 (|x~| > 1 - 1/(4 M^2) there, so it never trips).
 // Then every edge within the error of c~ lies in c~'s entry, which holds it.
 struct LutPlan {
   bool ok = false;
@@ -160,16 +167,25 @@ LutPlan plan_lut(int32_t nbins, double w_deg) {
   const double margin = 0.45 * (gap - 1.0 / md);
   if (!(margin > 0.0)) return p;
   const double g_x = 5.0 * kTwoM24 * (1.0 + 1e-6) + 1e-12;
-  const double g = 1.1 * (g_x + 4.0 * kTwoM24);
+  const double g_c = 1.1 * (g_x + 4.0 * kTwoM24);
   const double s_min = 1.0 / 4096.0;
-  const double s_star = g / margin;
-  const double reach = fmax(s_min + g / s_min, s_star + g / s_star);
+  const double s_star = g_c / margin;
+  const double reach = fmax(s_min + g_c / s_min, s_star + g_c / s_star);
   if (!(reach < 0.95 * c_edge_min)) return p;
+  if (!(0.5 / md + margin < 0.95 * c_edge_min)) return p;
   p.ok = true;
   p.m = static_cast<int32_t>(md);
   p.margin = margin;
-  p.g = static_cast<float>(g * (1.0 + 1e-6));
+  p.g = static_cast<float>(1.1 * (g_x + 0.5 * kTwoM24) * (1.0 + 1e-6));
   return p;
+}
+
+void apply_lut(BinParams &bp, const LutPlan &lp) {
+  bp.lut_m = static_cast<float>(lp.m);
+  bp.lut_mb = static_cast<float>(lp.m) + 8388608.0f;  // exact: M < 2^23
+  bp.lut_g = lp.g;
+  bp.lut_n = 2 * lp.m;
+  bp.lut_sh = 2;
 }
 
 // ---- series core ---------------------------------------------------------------------------
@@ -361,9 +377,9 @@ gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, in
   a.bp = make_bins(nbins, w_deg);
   if (use_series) apply_series(a.bp, sp, nbins);
   if (use_lut) {
-    a.bp.lut_m = static_cast<float>(lp.m);
-    a.bp.lut_g = lp.g;
-    a.bp.lut_n = 2 * lp.m;
+    a.hist_words = (nbins + kWave + kLutAliasWords + 63) / 64 * 64;
+    a.wave_lds_words = a.hist_words + queue_words(k);
+    apply_lut(a.bp, lp);
   }
   uint2 *lut_dev = reinterpret_cast<uint2 *>(static_cast<char *>(workspace) + edge_table_bytes(nbins));
   a.lut = use_lut ? lut_dev : nullptr;
@@ -555,9 +571,7 @@ gc_status gc_eval_angle_core(const float *x32, const double *x64, int64_t n, int
   hipError_t e = hipSuccess;
   if (exact_out) e = launch_edges(nbins, w_deg, edge_cos, hs);
   if (e == hipSuccess && use_lut) {
-    bp.lut_m = static_cast<float>(lp.m);
-    bp.lut_g = lp.g;
-    bp.lut_n = 2 * lp.m;
+    apply_lut(bp, lp);
     e = launch_lut(nbins, w_deg, lp.m, lp.margin, lut, hs);
   }
   if (e == hipSuccess)

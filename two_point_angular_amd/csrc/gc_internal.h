@@ -55,14 +55,23 @@ struct BinParams {
   float pw[7];   // acos polynomial coefficients times 1 / w_rad (fp32): narrow-range fp64 core
   float ps[3];   // series core (fp64 dot, narrow bins): sqrt2 (1, 1/12, 3/160) / w_rad
   float lut_m;   // bin-table core: entries per unit of c (M); the table has 2 M + 1 entries
-  float lut_g;   // bin-table core guard: recheck iff |c - e| * s < lut_g
+  float lut_mb;  // M + 2^23: fma(c, M, M + 2^23) holds round(M (c + 1)) in its low mantissa bits
+  float lut_g;   // bin-table core guard: recheck iff |cos(edge) - x| < lut_g
   int32_t lut_n; // 2 M (last entry index), or 0 when the bin table is not used
+  int32_t lut_sh;  // 2: log2 of the bytes per histogram word (an argument, so that the compiler
+                   // keeps (sign << 2) + address as one shift-and-add)
   int32_t nbins;
 };
 
 // Bin-table core (fp32 dot, bins covering 0..180 deg): the table lives in the workspace and is
-// copied into LDS by each workgroup; entry q = {edge e (fp32 bits), bin just below it + 1}.
+// copied into LDS by each workgroup; entry q = {cos(edge) (fp32 bits), the bin above the edge}.
+// In LDS the bin becomes the byte address of its histogram word.
 constexpr int kLutMaxEntries = 2049;
+// The table's middle entry (c within 1/(2M) of 0) holds both the smallest angles (x near 1)
+// and the largest (x near -1).  It stores e = 0 and bin word nbins + 65, so x > 0 lands in word
+// nbins + 64 (counted as bin 0) and x < 0 in word nbins + 65 (counted as bin nbins - 1): two
+// histogram words past the 64 spare ones.
+constexpr int kLutAliasWords = 2;
 
 // ---- pair-kernel work description ---------------------------------------------------
 // One family (DD, DR or RR): the i catalog is held in registers, the j catalog streamed.

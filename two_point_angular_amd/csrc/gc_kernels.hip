@@ -147,33 +147,55 @@ __device__ __forceinline__ void core64(double x, const BinParams &bp, float pw6_
   trip = (fabsf(tc - __builtin_rintf(tc)) - bp.g64k1) * s < bp.g64k2;
 }
 
-// Bin-table core (fp32 dot, bins covering 0..180 deg).  Instead of an arccos it uses
+// Bin-table core (fp32 dot, bins covering 0..180 deg).  The table entry is chosen by
 //   c = copysign(sqrt(1 - |x|), x),
 // which increases with the angle on each half: c in [0, 1] for 0..90 deg (c = sqrt2 sin(theta/2)),
-// c in [-1, 0) for 90..180 deg (c = -sqrt2 cos(theta/2)).  Entry q = floor(M (c + 1)) of the
-// table holds the one bin edge e within its range of c widened by a margin (or a far value) and
-// B = (bin just below e) + 1, so bin = B - [c < e].  Recheck iff |c - e| s < lut_g, which bounds
-// the error of c times s (dot-product error g_x, the subtraction, the 1-ulp square root, the
-// rounding of e): near an edge the lookup decides nothing the guard has not certified.
-// tab: the table (LDS in the pair kernel, global memory in the diagnostic kernel).
-__device__ __forceinline__ void lut_lookup(float x, const BinParams &bp, const uint2 *tab, float &c, float &s,
-                                           uint2 &ent) {
-  s = __builtin_amdgcn_sqrtf(__builtin_amdgcn_fmed3f(1.0f - fabsf(x), 0.0f, 1.0f));
+// c in [-1, 0) for 90..180 deg (c = -sqrt2 cos(theta/2)), so equal steps of c are steps of
+// comparable angle.  Entry q = round(M (c + 1)) holds the one bin edge whose c lies in the
+// entry's range widened by a margin, as e = cos(edge angle) in fp32, and B = the bin above the
+// edge; with no edge in range, e = 4 (beyond every cosine) and B = the entry's bin.  A pair lies
+// below the edge iff x > e, so bin = B - [e - x < 0], and it is rechecked iff |e - x| < lut_g,
+// which bounds the dot product's error plus the rounding of e.  The side of the edge is thus
+// decided on the cosine itself; c only selects the edge, and the host checks that the error of c
+// can never select an entry without the edge a pair is near.
+// lut_key: fma(c, M, M + 2^23) is 2^23 + q exactly (one rounding of M (c + 1) + 2^23 to an
+// integer), so q is the key's bit pattern minus that of 2^23.
+__device__ __forceinline__ float lut_key(float x, const BinParams &bp, float &c) {
+  const float s = __builtin_amdgcn_sqrtf(__builtin_amdgcn_fmed3f(1.0f - fabsf(x), 0.0f, 1.0f));
   c = copysignf(s, x);
-  ent = tab[static_cast<uint32_t>(fmaf(c, bp.lut_m, bp.lut_m))];
+  return fmaf(c, bp.lut_m, bp.lut_mb);
 }
-__device__ __forceinline__ void lut_bin(float c, float s, uint2 ent, const BinParams &bp, uint32_t &k, bool &trip) {
-  const float d = c - __uint_as_float(ent.x);
-  trip = fabsf(d) * s < bp.lut_g;
-  k = ent.y - (__float_as_uint(d) >> 31);
-}
+constexpr uint32_t kLutKeyBias = 0x4B000000u;  // bit pattern of 2^23
+
+// The core with the table in global memory (diagnostic kernel): entry = {e bits, B}.
 __device__ __forceinline__ void core_lut(float x, const BinParams &bp, const uint2 *tab, uint32_t &k, bool &trip,
                                          float &c_raw) {
-  float c, s;
-  uint2 ent;
-  lut_lookup(x, bp, tab, c, s, ent);
-  lut_bin(c, s, ent, bp, k, trip);
+  float c;
+  const uint2 ent = tab[__float_as_uint(lut_key(x, bp, c)) - kLutKeyBias];
+  const float d = __uint_as_float(ent.x) - x;
+  trip = fabsf(d) < bp.lut_g;
+  k = ent.y - (__float_as_uint(d) >> 31);
   c_raw = c;
+}
+
+// The pair kernel's form, with the table in LDS: entry = {e bits, byte address of bin B's
+// histogram word}.  Entry q sits at LDS byte tab + 8 q = (key bits << 3) + tab_bias with
+// tab_bias = tab - (bits of 2^23 << 3) (mod 2^32): one shift-and-add per lookup.  The histogram
+// word to add to is (sign of e - x, as 0 or -1) << 2 plus the entry's address: one more.
+typedef __attribute__((address_space(3))) const unsigned long long lds_entry_t;
+typedef __attribute__((address_space(3))) uint32_t lds_word_t;
+__device__ __forceinline__ uint32_t lds_address(const void *p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char *)p));
+}
+__device__ __forceinline__ uint2 lut_read_lds(float key, uint32_t tab_bias) {
+  const unsigned long long v =
+      *reinterpret_cast<lds_entry_t *>(static_cast<uintptr_t>((__float_as_uint(key) << 3) + tab_bias));
+  return make_uint2(static_cast<uint32_t>(v), static_cast<uint32_t>(v >> 32));
+}
+__device__ __forceinline__ uint32_t lut_word_address(float x, uint2 ent, const BinParams &bp, bool &trip) {
+  const float d = __uint_as_float(ent.x) - x;
+  trip = fabsf(d) < bp.lut_g;
+  return (static_cast<uint32_t>(__float_as_int(d) >> 31) << bp.lut_sh) + ent.y;
 }
 
 // Exact recheck in the cosine domain.  theta >= e w  <=>  x <= cos(e w), so bin k holds x
@@ -282,6 +304,8 @@ pairs_kernel(const PairArgs A) {
   uint32_t *const hist = shared_hist ? lds : lds + wv * (A.hist_words + QW);
   uint2 *const tab = reinterpret_cast<uint2 *>(lds + A.hist_words);
   uint32_t *const queue = shared_hist ? lds + A.hist_words + lut_words + wv * QW : hist + A.hist_words;
+  const uint32_t hist_addr = lds_address(hist);
+  const uint32_t tab_bias = lds_address(tab) - (kLutKeyBias << 3);
   const int g = blockIdx.x;
   const int fi = g < A.fam[0].wg_end ? 0 : (g < A.fam[1].wg_end ? 1 : 2);
   const FamilyWork &F = A.fam[fi];
@@ -296,7 +320,10 @@ pairs_kernel(const PairArgs A) {
   if (shared_hist) {
     for (int b = threadIdx.x; b < A.hist_words; b += kWGThreads) hist[b] = 0u;
     if constexpr (LUT)
-      for (int q = threadIdx.x; q <= A.bp.lut_n; q += kWGThreads) tab[q] = A.lut[q];
+      for (int q = threadIdx.x; q <= A.bp.lut_n; q += kWGThreads) {
+        const uint2 e = A.lut[q];
+        tab[q] = make_uint2(e.x, hist_addr + 4u * e.y);
+      }
   } else {
     for (int b = lane; b < A.hist_words; b += kWave) hist[b] = 0u;
   }
@@ -349,6 +376,14 @@ pairs_kernel(const PairArgs A) {
       if (c) atomicAdd(slot + bb, static_cast<unsigned long long>(static_cast<long long>(static_cast<int>(c))));
     }
     long long spare = static_cast<int>(atomicExch(hist + A.nbins + lane, 0u));
+    if constexpr (LUT) {
+      // the middle table entry's two words: bin 0 and bin nbins - 1
+      if (lane < kLutAliasWords) {
+        const long long a = static_cast<int>(atomicExch(hist + A.nbins + kWave + lane, 0u));
+        if (lane == 0 && a) atomicAdd(slot, static_cast<unsigned long long>(a));
+        if (lane == 1) spare += a;
+      }
+    }
 #pragma unroll
     for (int off = kWave / 2; off > 0; off >>= 1) spare += __shfl_xor(spare, off, kWave);
     if (lane == 0 && spare) atomicAdd(slot + (A.nbins - 1), static_cast<unsigned long long>(spare));
@@ -385,18 +420,21 @@ pairs_kernel(const PairArgs A) {
     constexpr bool GENERIC = decltype(generic_tag)::value;
     if constexpr (LUT && !GENERIC) {
       // all K table reads first, so one LDS wait covers them
-      float cv[K], sv[K];
+      float xv[K];
       uint2 ev[K];
 #pragma unroll
-      for (int k = 0; k < K; ++k)
-        lut_lookup(fmaf(ix[k], xj, fmaf(iy[k], yj, iz[k] * zj)), bp, tab, cv[k], sv[k], ev[k]);
+      for (int k = 0; k < K; ++k) {
+        float c_unused;
+        xv[k] = fmaf(ix[k], xj, fmaf(iy[k], yj, iz[k] * zj));
+        ev[k] = lut_read_lds(lut_key(xv[k], bp, c_unused), tab_bias);
+      }
 #pragma unroll
       for (int k = 0; k < K; ++k) {
-        uint32_t kk;
         bool tp;
-        lut_bin(cv[k], sv[k], ev[k], bp, kk, tp);
-        atomicAdd(hist + kk, W);
-        enqueue(tp, kk, k, jg);
+        const uint32_t a = lut_word_address(xv[k], ev[k], bp, tp);
+        __hip_atomic_fetch_add(reinterpret_cast<lds_word_t *>(static_cast<uintptr_t>(a)), W, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
+        enqueue(tp, (a - hist_addr) >> 2, k, jg);
       }
     } else {
 #pragma unroll
@@ -554,11 +592,12 @@ __global__ void __launch_bounds__(256) edges_kernel(int32_t nbins, double w_deg,
 }
 
 // ------------------------------------------------------------------------------ bin table
-// Entry q of the bin-table core (q = 0 .. 2M): c in [q/M - 1, (q+1)/M - 1), widened by `margin`
-// on both sides.  An edge at angle e w (e = 1 .. nbins-1) sits at c = sqrt2 sin(e w / 2) when
-// e w <= 90 deg and at c = -sqrt2 cos(e w / 2) when e w >= 90 deg (both for exactly 90).  With
-// one edge in range: {e, bin e - 1 + 1}; with none: {far, the bin of the entry's middle + 1}.
-// The host only selects this core when no widened range can hold two edges.
+// Entry q of the bin-table core (q = 0 .. 2M): c in [(q - 1/2)/M - 1, (q + 1/2)/M - 1] (the
+// index rounds), widened by `margin` on both sides.  An edge at angle e w (e = 1 .. nbins-1) sits
+// at c = sqrt2 sin(e w / 2) when e w <= 90 deg and at c = -sqrt2 cos(e w / 2) when e w >= 90 deg
+// (both for exactly 90).  With one edge in range: {cos(e w) rounded to fp32, e (the bin above the
+// edge)}; with none: {4, the bin of the entry's middle}.  The host only selects this core when
+// no widened range can hold two edges.
 __device__ __forceinline__ double lut_angle_deg(double c) {  // inverse of the map above
   constexpr double kSqrtHalf = 0.70710678118654752440, kDeg = 57.295779513082320877;
   return c >= 0.0 ? 2.0 * asin(fmin(c, 1.0) * kSqrtHalf) * kDeg : 180.0 - 2.0 * asin(fmin(-c, 1.0) * kSqrtHalf) * kDeg;
@@ -569,10 +608,9 @@ __global__ void __launch_bounds__(256) lut_kernel(int32_t nbins, double w_deg, i
   const int q = blockIdx.x * blockDim.x + threadIdx.x;
   if (q > 2 * m) return;
   constexpr double kSqrt2 = 1.41421356237309504880, kRad = 3.14159265358979323846 / 180.0;
-  const double lo = static_cast<double>(q) / m - 1.0 - margin;
-  const double hi = static_cast<double>(q + 1) / m - 1.0 + margin;
+  const double lo = (static_cast<double>(q) - 0.5) / m - 1.0 - margin;
+  const double hi = (static_cast<double>(q) + 0.5) / m - 1.0 + margin;
   int count = 0, edge = 0;
-  double ce = 0.0;
   // right half (0 .. 90 deg): c in [max(lo, 0), min(hi, 1)]
   if (hi >= 0.0 && lo <= 1.0) {
     const int e0 = static_cast<int>(floor(lut_angle_deg(fmax(lo, 0.0)) / w_deg)) - 1;
@@ -583,7 +621,6 @@ __global__ void __launch_bounds__(256) lut_kernel(int32_t nbins, double w_deg, i
       const double c = kSqrt2 * sin(0.5 * th * kRad);
       if (c >= lo && c <= hi) {
         ++count;
-        ce = c;
         edge = e;
       }
     }
@@ -598,21 +635,23 @@ __global__ void __launch_bounds__(256) lut_kernel(int32_t nbins, double w_deg, i
       const double c = -kSqrt2 * cos(0.5 * th * kRad);
       if (c >= lo && c <= hi) {
         ++count;
-        ce = c;
         edge = e;
       }
     }
   }
   uint2 ent;
-  if (count >= 1) {
-    ent.x = __float_as_uint(static_cast<float>(ce));
-    ent.y = static_cast<uint32_t>(edge);  // bin below the edge is edge - 1; stored + 1
+  if (q == m && count == 0) {
+    ent.x = __float_as_uint(0.0f);                       // the middle entry (x near +-1)
+    ent.y = static_cast<uint32_t>(nbins + kWave + 1);    // x < 0: word nbins + 65; x > 0: nbins + 64
+  } else if (count >= 1) {
+    ent.x = __float_as_uint(static_cast<float>(cos(static_cast<double>(edge) * w_deg * kRad)));
+    ent.y = static_cast<uint32_t>(edge);  // the bin above the edge; the one below is edge - 1
   } else {
-    const double mid = fmin(fmax((static_cast<double>(q) + 0.5) / m - 1.0, -1.0), 1.0);
+    const double mid = fmin(fmax(static_cast<double>(q) / m - 1.0, -1.0), 1.0);
     int b = static_cast<int>(floor(lut_angle_deg(mid) / w_deg));
     b = b < 0 ? 0 : (b > nbins - 1 ? nbins - 1 : b);
-    ent.x = __float_as_uint(1e30f);  // c < e always: bin = B - 1
-    ent.y = static_cast<uint32_t>(b + 1);
+    ent.x = __float_as_uint(4.0f);  // e - x > 0 for every cosine: bin = B
+    ent.y = static_cast<uint32_t>(b);
   }
   lut[q] = ent;
 }
@@ -704,9 +743,12 @@ __global__ void __launch_bounds__(256) eval_core_kernel(const float *x32, const 
     if constexpr (CORE == 2) core_lut(xf, bp, lut, k, trip, t);  // (fp32 dot: CORE 2 is the table)
     else core32<SPAN>(xf, bp, bp.h, bp.tmax, k, trip, t);
   }
-  // k == nbins is the full-span kernel's spare bin, which the flush folds into bin nbins - 1
+  // k >= nbins: the full-span kernel's spare bins and the table's word nbins + 65, which the
+  // flush folds into bin nbins - 1; the table's word nbins + 64 is bin 0
   const uint32_t last = static_cast<uint32_t>(bp.nbins - 1);
-  bin_out[idx] = static_cast<int32_t>(k < last ? k : last);
+  if (CORE == 2 && !dot64 && k == static_cast<uint32_t>(bp.nbins + kWave)) k = 0;
+  k = k < last ? k : last;
+  bin_out[idx] = static_cast<int32_t>(k);
   trip_out[idx] = trip ? 1 : 0;
   if (exact_out) exact_out[idx] = static_cast<int32_t>(exact_bin(xe, k, edge_cos, bp.nbins));
   if (t_out) t_out[idx] = t;
