@@ -85,9 +85,22 @@ hipError_t device_info(int *cus, bool dot64, int k, int core, size_t lds, int *b
 //    (two more units of 2^-24 for the narrow-range core, whose coefficients are rounded
 //    after scaling by 1 / w: sum |C_i| / P_min = 1.39 units).
 //    Recheck iff |t - round(t)| * s < g64k1 * s + g64k2, g64k1 = rho (nbins + 1),
-//    g64k2 = 2.02 g64 / w.
+//    g64k2 = 2.02 g64 / w.  The narrow-range and series cores bin no angle near 180 deg, and
+//    every edge lies at t >= 1, where s >= s_lo = 0.95 sqrt2 sin(w/4) (a pair with t~ < 1/2
+//    is clamped to t = 1/2, which never trips, and is more than half a bin from any edge).
+//    There g64k2 / s <= g64k2 / s_lo, so they recheck iff |t - round(t)| < g64c = g64k1 +
+//    g64k2 / s_lo: one compare instead of a subtraction, a multiply and a compare.
 constexpr double kTwoM24 = 5.9604644775390625e-08;  // 2^-24
 constexpr double kPi = 3.14159265358979323846;
+
+void set_fp64_guard(BinParams &bp, double rho, int32_t nbins, double w_rad) {
+  const double g64 = 1e-14;
+  const double k1 = rho * (static_cast<double>(nbins) + 1.0), k2 = 2.02 * g64 / w_rad;
+  const double s_lo = 0.95 * 1.41421356237309504880 * sin(0.25 * w_rad);
+  bp.g64k1 = static_cast<float>(k1 * (1.0 + 1e-6));
+  bp.g64k2 = static_cast<float>(k2 * (1.0 + 1e-6));
+  bp.g64c = static_cast<float>((k1 + k2 / s_lo) * (1.0 + 1e-6));
+}
 
 BinParams make_bins(int32_t nbins, double w_deg) {
   const double w_rad = w_deg * (kPi / 180.0);
@@ -107,9 +120,7 @@ BinParams make_bins(int32_t nbins, double w_deg) {
   bp.g32 = static_cast<float>((2.02 * g_x / w_rad + c) * (1.0 + 1e-6));
   // fp64-dot guard
   const double rho = ((GC_ACOS_FIT_ERR + 4.0 * kTwoM24 * (kPi / 2.0)) / 1.41 + 10.0 * kTwoM24) * 1.25;
-  const double g64 = 1e-14;
-  bp.g64k1 = static_cast<float>(rho * (static_cast<double>(nbins) + 1.0) * (1.0 + 1e-6));
-  bp.g64k2 = static_cast<float>(2.02 * g64 / w_rad * (1.0 + 1e-6));
+  set_fp64_guard(bp, rho, nbins, w_rad);
   const double coef[7] = {GC_ACOS_C0, GC_ACOS_C1, GC_ACOS_C2, GC_ACOS_C3, GC_ACOS_C4, GC_ACOS_C5, GC_ACOS_C6};
   for (int q = 0; q < 7; ++q) bp.pw[q] = static_cast<float>(static_cast<double>(coef[q]) / w_rad);
   return bp;
@@ -198,7 +209,7 @@ void apply_lut(BinParams &bp, const LutPlan &lp) {
 // fmas (2), narrowing y (half a unit through the square root), the 1-ulp square root (2) and
 // the product (1): rho_s = 1.25 (R + 7 * 2^-24).  Used when R <= 2e-8.
 struct SeriesPlan;
-void apply_series(BinParams &bp, const SeriesPlan &sp, int32_t nbins);
+void apply_series(BinParams &bp, const SeriesPlan &sp, int32_t nbins, double w_deg);
 
 struct SeriesPlan {
   bool ok = false;
@@ -226,9 +237,9 @@ SeriesPlan plan_series(int32_t nbins, double w_deg) {
   return p;
 }
 
-void apply_series(BinParams &bp, const SeriesPlan &sp, int32_t nbins) {
+void apply_series(BinParams &bp, const SeriesPlan &sp, int32_t nbins, double w_deg) {
   for (int q = 0; q < 3; ++q) bp.ps[q] = sp.ps[q];
-  bp.g64k1 = static_cast<float>(sp.rho * (static_cast<double>(nbins) + 1.0) * (1.0 + 1e-6));
+  set_fp64_guard(bp, sp.rho, nbins, w_deg * (kPi / 180.0));
 }
 
 // Spans the specialised cores accept: the fp32 core without a clamp needs nbins w to reach
@@ -375,7 +386,7 @@ gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, in
   a.hist_words = (nbins + kWave + 63) / 64 * 64;  // 64 spare bins past the last (see core32)
   a.wave_lds_words = a.hist_words + queue_words(k);
   a.bp = make_bins(nbins, w_deg);
-  if (use_series) apply_series(a.bp, sp, nbins);
+  if (use_series) apply_series(a.bp, sp, nbins, w_deg);
   if (use_lut) {
     a.hist_words = (nbins + kWave + kLutAliasWords + 63) / 64 * 64;
     a.wave_lds_words = a.hist_words + queue_words(k);
@@ -564,7 +575,7 @@ gc_status gc_eval_angle_core(const float *x32, const double *x64, int64_t n, int
   if (need_ws && (!workspace || !aligned(workspace, GC_ALIGNMENT))) return GC_ERR_INVALID_ARGUMENT;
   if (need_ws && ws_bytes < edge_table_bytes(nbins) + kLutBytes) return GC_ERR_WORKSPACE;
   BinParams bp = make_bins(nbins, w_deg);
-  if (use_series) apply_series(bp, sp, nbins);
+  if (use_series) apply_series(bp, sp, nbins, w_deg);
   const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   double *edge_cos = static_cast<double *>(workspace);
   uint2 *lut = need_ws ? reinterpret_cast<uint2 *>(static_cast<char *>(workspace) + edge_table_bytes(nbins)) : nullptr;

@@ -52,6 +52,7 @@ struct BinParams {
   float g32;     // fp32-dot guard: recheck iff |t - round(t)| * s < g32
   float g64k1;   // fp64-dot guard: recheck iff |t - round(t)| * s < g64k1 * s + g64k2
   float g64k2;
+  float g64c;    // fp64-dot guard of the narrow and series cores: recheck iff |t - round(t)| < g64c
   float pw[7];   // acos polynomial coefficients times 1 / w_rad (fp32): narrow-range fp64 core
   float ps[3];   // series core (fp64 dot, narrow bins): sqrt2 (1, 1/12, 3/160) / w_rad
   float lut_m;   // bin-table core: entries per unit of c (M); the table has 2 M + 1 entries

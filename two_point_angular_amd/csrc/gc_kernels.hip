@@ -95,7 +95,8 @@ __device__ __forceinline__ void core32(float x, const BinParams &bp, float h_v, 
 // fp64-dot core.  x is the fp64 dot product of the fp64 unit vectors; 1 - |x| is formed
 // in fp64 before narrowing, so small angles keep full relative precision.
 //   r = sqrt(1 - |x|) P(|x|) = acos(|x|);  t = r / w (x >= 0) or (pi - r) / w (x < 0).
-//   recheck iff |tc - round(tc)| * s < g64k1 * s + g64k2.
+//   recheck iff |tc - round(tc)| * s < g64k1 * s + g64k2 (NARROW and SERIES: iff
+//   |tc - round(tc)| < g64c, the same window where an edge can be).
 // NARROW (nbins w <= 90 deg): a pair with x < 0 is past 90 degrees and belongs to the last
 // bin, so no sign handling is needed.  The signed x goes through the same expression with
 // 1 - x clamped to [0, 1]: for a in [-1, 0] every term of P(a) is positive (the
@@ -142,9 +143,14 @@ __device__ __forceinline__ void core64(double x, const BinParams &bp, float pw6_
   t_raw = t;
   const float tc = __builtin_amdgcn_fmed3f(t, 0.5f, tmax_v);
   k = static_cast<uint32_t>(tc);
-  // |tc - round(tc)| * s < g64k1 * s + g64k2, arranged so that each instruction reads one
-  // scalar constant
-  trip = (fabsf(tc - __builtin_rintf(tc)) - bp.g64k1) * s < bp.g64k2;
+  if constexpr (MODE == 0) {
+    // |tc - round(tc)| * s < g64k1 * s + g64k2, arranged so that each instruction reads one
+    // scalar constant
+    trip = (fabsf(tc - __builtin_rintf(tc)) - bp.g64k1) * s < bp.g64k2;
+  } else {
+    // no edge near 180 deg: s is bounded below near every edge, and the window is constant
+    trip = fabsf(tc - __builtin_rintf(tc)) < bp.g64c;
+  }
 }
 
 // Bin-table core (fp32 dot, bins covering 0..180 deg).  The table entry is chosen by
