@@ -11,9 +11,13 @@ namespace gc {
 constexpr int kWave = 64;            // CDNA wavefront width
 constexpr int kWavesPerWG = 4;       // pair-kernel workgroup = 4 independent wavefronts
 constexpr int kWGThreads = kWave * kWavesPerWG;
-// Per-wave recheck queue, 8-byte entries: a j-step appends at most 64 K entries to fewer
-// than 64 pending ones, so 64 (K + 1) entries suffice.
-constexpr int queue_words(int k) { return 2 * kWave * (k + 1); }
+// Per-wave recheck queue, 8-byte entries.  Full batches of 64 are drained after every j-step,
+// and with K = 8 also after its first half, so a drain point leaves fewer than 64 pending and
+// the next appends at most 64 D entries (D = 4 pairs per lane: K = 4, or half of K = 8):
+// 64 (D + 1) entries suffice.  (Halving the queue of K = 8 lets a fifth workgroup fit in LDS
+// beside the bin table or a 3600-bin shared histogram.)
+constexpr int drain_span(int k) { return k > 4 ? k / 2 : k; }
+constexpr int queue_words(int k) { return 2 * kWave * (drain_span(k) + 1); }
 constexpr int kMaxWorkgroups = 2048; // partial-histogram slots held by the workspace
 constexpr int kMaxBlocksPerCU = 8;
 

@@ -361,14 +361,18 @@ pairs_kernel(const PairArgs A) {
   int64_t i0 = 0;
   real ix[K], iy[K], iz[K];
 
-  // The queue is drained (64 at a time, from the top) after every j-step, so it never holds
-  // more than 64 (K + 1) entries.
+  // The queue is drained (64 at a time, from the top) after every j-step and, with K = 8,
+  // after its first half, so it never holds more than 64 (drain_span(K) + 1) entries.
   auto drain = [&](int c) __attribute__((always_inline)) {
     drain_queue(hist, queue, qcount - c, c, F.ci, F.cj, i0, W, A.edge_cos, A.nbins);
     qcount -= c;
   };
   auto drain_all = [&]() __attribute__((always_inline)) {
     while (qcount > 0) drain(qcount < kWave ? qcount : kWave);
+  };
+  // Drain full-wave batches: leaves fewer than 64 entries pending.
+  auto drain_full = [&]() __attribute__((always_inline)) {
+    while (qcount >= kWave) drain(kWave);
   };
   // Move the LDS histogram into the workgroup's 64-bit slot.  Each bin is taken with an
   // atomic exchange, so in shared mode other waves may keep adding meanwhile; the value is
@@ -441,6 +445,7 @@ pairs_kernel(const PairArgs A) {
         __hip_atomic_fetch_add(reinterpret_cast<lds_word_t *>(static_cast<uintptr_t>(a)), W, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_WORKGROUP);
         enqueue(tp, (a - hist_addr) >> 2, k, jg);
+        if (k + 1 == drain_span(K) && k + 1 < K) drain_full();
       }
     } else {
 #pragma unroll
@@ -462,9 +467,10 @@ pairs_kernel(const PairArgs A) {
           atomicAdd(hist + kk, W);
         }
         enqueue(tp, kk, k, jg);
+        if (k + 1 == drain_span(K) && k + 1 < K) drain_full();
       }
     }
-    while (qcount >= kWave) drain(kWave);
+    drain_full();
   };
 
   auto check_flush = [&]() __attribute__((always_inline)) {
