@@ -109,11 +109,12 @@ def test_histogram_validation(lib):
     assert _hist(lib, nbins=700, tuning=T(0, 0, 0, 0, 2, 0, 0)) == INVALID  # 700 x 0.25 < 180 deg
     assert _hist(lib, nbins=361, tuning=T(64, 0, 0, 0, 2, 0, 0)) == INVALID  # 361 x 0.25 > 90 deg
     assert _hist(lib, nbins=1500, w=0.001, tuning=T(32, 0, 0, 0, 2, 0, 0)) == INVALID  # 1.5 < 180 deg
-    # arccos-free cores: the bin table (fp32 dot, full span, a sound table, a shared histogram)
-    # or the series (fp64 dot, bins ending by ~9 deg)
+    # fast cores: the bin table (fp32 dot, full span, a sound table, a shared histogram), the edge
+    # table (fp32 dot, full span, bins of >= ~0.02 deg whose table fits in LDS beside the
+    # histogram) or the series (fp64 dot, bins ending by ~9 deg)
     assert _hist(lib, tuning=T(64, 0, 0, 0, 0, 2, 0)) == INVALID                      # 180 deg, fp64
     assert _hist(lib, nbins=100, w=0.1, tuning=T(64, 0, 0, 0, 0, 2, 0)) == INVALID     # 10 deg: series too short
-    assert _hist(lib, nbins=3600, w=0.05, tuning=T(0, 0, 0, 0, 0, 2, 0)) == INVALID   # too narrow
+    assert _hist(lib, nbins=8192, w=0.022, tuning=T(0, 0, 0, 0, 0, 2, 0)) == INVALID  # edge table too big
     assert _hist(lib, nbins=700, tuning=T(0, 0, 0, 0, 0, 2, 0)) == INVALID            # not full span
     assert _hist(lib, tuning=T(0, 0, 0, 1, 0, 2, 0)) == INVALID                       # private histograms
     assert _hist(lib, tuning=T(0, 0, 0, 0, 1, 2, 0)) == INVALID                       # generic core

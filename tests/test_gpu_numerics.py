@@ -66,13 +66,26 @@ def check_sound(x_exact_in, b, trip, nbins, w, g):
 
 
 # (nbins, width): 720 x 0.25 deg bins through the bin table; 1440 x 0.125 and 3600 x 0.05 deg
-# through the full-span arccos core (too narrow for the table); 1500 x 0.001 deg through the
-# clamped arccos core.
+# through the edge table (too narrow for the bin table); 1500 x 0.001 deg through the clamped
+# arccos core.
 FP32_CASES = [(720, 0.25), (1440, 0.125), (3600, 0.05), (1500, 0.001)]
 
 
 def uses_table(nbins, w):
     return nbins * w >= 180 and w >= 0.25
+
+
+def etab_e3():
+    """The edge-table core's arccos error bound (rad): 1.25 (CORE_ERR + 2^-24 pi/2)."""
+    return 1.25 * (_header_constant("GC_ACOS3_CORE_ERR") + 2.0 ** -24 * np.pi / 2)
+
+
+def uses_etab(nbins, w):
+    """Full span, too fine for the bin table, arccos error <= a quarter bin, and the interleaved
+    table and histogram with four queues of 640 words within 40 KB of LDS."""
+    hist_words = (nbins + 1 + 64 + 63) // 64 * 64
+    return ((nbins + 0.5) * w >= 180 and not uses_table(nbins, w) and etab_e3() / np.radians(w) <= 0.25
+            and nbins + 2 <= 16640 // 4 and (2 * hist_words + 4 * 640) * 4 <= 40960)
 
 
 @pytest.mark.parametrize("nbins,w", FP32_CASES)
@@ -155,7 +168,8 @@ def test_fp32_core_error_within_model(gc, nbins, w):
     """The fp32 core's coordinate against its exact value for the same fp32 cosine, over every
     64th fp32 value in [-1, 1].  Arccos cores: the guard assumes |t~ - t| <= C(t) with
     C(t) = E_core / w + 2^-24 (t + 2h) (core error with a 1-ulp square root, plus the roundings
-    that form t).  Bin-table core: c = copysign(sqrt(1 - |x|), x), and the guard assumes
+    that form t); the edge table's degree-3 arccos the same with its own E_core (its table
+    assumes it when it names the edge to compare with).  Bin-table core: c = copysign(sqrt(1 - |x|), x), and the guard assumes
     |c~ - c| s~ <= 1.5 * 2^-23 for the core's own roundings (subtraction, 1-ulp square root)."""
     print(f"[gpu] fp32 core error model nbins={nbins}", flush=True)
     pos = np.arange(0, np.float32(1.0).view(np.uint32) + 1, 64, dtype=np.uint32).view(np.float32)
@@ -174,6 +188,9 @@ def test_fp32_core_error_within_model(gc, nbins, w):
     t_exact = np.arccos(x.astype(np.float64)) / w_rad
     err = np.abs(t - t_exact)
     e_core = (_header_constant("GC_ACOS_CORE_ERR") + 2.0 ** -24 * (np.pi / 2)) * 1.25
+    if uses_etab(nbins, w):
+        # the edge table's degree-3 arccos: its own bound, checked the same way
+        e_core = etab_e3()
     h = (np.pi / 2) / w_rad
     bound = e_core / w_rad + 2.0 ** -24 * (t_exact + 2 * h) * 1.01
     ratio = err / bound

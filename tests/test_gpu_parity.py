@@ -312,3 +312,34 @@ def test_bin_table_maps_every_entry(gc):
         ce = np.sqrt(2) * np.sin(np.radians(th_e) / 2) if th_e <= 90 else -np.sqrt(2) * np.cos(np.radians(th_e) / 2)
         qe = int(np.rint(m * (ce + 1)))
         assert abs(e[qe] - np.cos(np.radians(th_e))) < 1e-7 and b[qe] == k, (k, qe, e[qe], b[qe])
+
+
+def test_edge_table_entries(gc):
+    """The edge table built on the device for 3600 x 0.05 deg: e_r = cos(r w) (fp32) for every
+    entry whose pairs the degree-3 arccos places within 0.45 bins of their true angle, NaN (always
+    recheck) only in a few entries at each end of the range, -4 past 180 deg."""
+    import ctypes
+    import torch
+    print("[gpu] edge table entries", flush=True)
+    nbins, w = 3600, 0.05
+    ws = torch.zeros(gc.workspace_bytes(nbins), dtype=torch.uint8, device="cuda")
+    x = torch.tensor([0.5], dtype=torch.float32, device="cuda")
+    bins = torch.empty(1, dtype=torch.int32, device="cuda")
+    trip = torch.empty(1, dtype=torch.uint8, device="cuda")
+    _ptr = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    st = gc.load().gc_eval_angle_core(_ptr(x), None, 1, nbins, w, 32, _ptr(bins), _ptr(trip), None, None,
+                                      _ptr(ws), ws.numel(), None)
+    assert st == 0
+    torch.cuda.synchronize()
+    off = ((nbins + 1) * 8 + 255) // 256 * 256
+    e = ws[off: off + (nbins + 2) * 4].cpu().numpy().view(np.float32).astype(np.float64)
+    nan = np.isnan(e)
+    r = np.arange(nbins + 2)
+    assert nan[0] and nan[nbins] and not nan[nbins // 2]
+    # flagged entries form one run at each end, of a few entries
+    idx = np.flatnonzero(~nan)
+    lo, hi = int(idx[0]), int(idx[-1]) + 1
+    assert not nan[lo:hi].any() and lo <= 8 and nbins - hi <= 8, (lo, hi)
+    inner = ~nan & (r < nbins)
+    assert np.all(np.abs(e[inner] - np.cos(np.radians(r[inner] * w))) <= 2.0 ** -24)
+    assert np.all(e[~nan & (r >= nbins)] == -4.0)

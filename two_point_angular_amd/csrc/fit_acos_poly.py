@@ -21,6 +21,10 @@ errors that the kernel's guard relies on:
     q = fma(-sqrt(1-a), P(a), pi/2), evaluated with emulated fp32 arithmetic
     (--exhaustive; otherwise on a 2^24-point grid).
 
+A degree-3 polynomial of the same form (GC_ACOS3_*, error ~1e-4 rad) serves the edge-table
+core, which needs the angle only to within a fraction of a bin to pick the edge to compare
+with; the comparison itself is made on the cosine.
+
 Usage: python fit_acos_poly.py [--exhaustive]
 """
 import argparse
@@ -141,22 +145,22 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--exhaustive", action="store_true")
     args = ap.parse_args()
-    coef = fit()
-    coef32 = coef.astype(np.float32)
-    fit_err, core_err = measure(coef32, args.exhaustive)
-    lines = [
-        "// Generated by fit_acos_poly.py -- do not edit.",
-        "// acos(a) ~= sqrt(1 - a) * P(a) for a in [0, 1]; P minimax (degree %d)." % DEGREE,
-        "// FIT_ERR:  max |P(a) - acos(a)/sqrt(1-a)| with these fp32 coefficients = %.3e" % fit_err,
-        "// CORE_ERR: max |fma(-sqrt(1-a), P(a), pi/2) - (pi/2 - acos(a))| in fp32, %s = %.3e rad"
-        % ("every fp32 a in [0,1]" if args.exhaustive else "2^24-point grid", core_err),
-        "#pragma once",
-        "#define GC_ACOS_DEGREE %d" % DEGREE,
-        "#define GC_ACOS_FIT_ERR %.6e" % fit_err,
-        "#define GC_ACOS_CORE_ERR %.6e" % core_err,
-    ]
-    for k, ck in enumerate(coef32):
-        lines.append("#define GC_ACOS_C%d %sf  /* %.9e */" % (k, float(ck).hex(), float(ck)))
+    where = "every fp32 a in [0,1]" if args.exhaustive else "2^24-point grid"
+    lines = ["// Generated by fit_acos_poly.py -- do not edit.", "#pragma once"]
+    for degree, prefix in ((DEGREE, "GC_ACOS"), (3, "GC_ACOS3")):
+        coef32 = fit(degree).astype(np.float32)
+        fit_err, core_err = measure(coef32, args.exhaustive)
+        lines += [
+            "// acos(a) ~= sqrt(1 - a) * P(a) for a in [0, 1]; P minimax (degree %d)." % degree,
+            "// FIT_ERR:  max |P(a) - acos(a)/sqrt(1-a)| with these fp32 coefficients = %.3e" % fit_err,
+            "// CORE_ERR: max |fma(-sqrt(1-a), P(a), pi/2) - (pi/2 - acos(a))| in fp32, %s = %.3e rad"
+            % (where, core_err),
+            "#define %s_DEGREE %d" % (prefix, degree),
+            "#define %s_FIT_ERR %.6e" % (prefix, fit_err),
+            "#define %s_CORE_ERR %.6e" % (prefix, core_err),
+        ]
+        for k, ck in enumerate(coef32):
+            lines.append("#define %s_C%d %sf  /* %.9e */" % (prefix, k, float(ck).hex(), float(ck)))
     path = os.path.join(HERE, "gc_acos_poly.h")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")

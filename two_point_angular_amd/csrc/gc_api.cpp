@@ -31,10 +31,10 @@ bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 struct DeviceInfo {
   bool valid = false;
   int cus = 0;
-  // occupancy per (kernel variant, lds bytes); variant = (dot64 * 3 + core) * 2 + (k == 8)
+  // occupancy per (kernel variant, lds bytes); variant = (dot64 * 4 + core) * 2 + (k == 8)
   struct Occ { size_t lds; int blocks; };
-  Occ occ[12][8];
-  int nocc[12] = {};
+  Occ occ[16][8];
+  int nocc[16] = {};
 };
 constexpr int kMaxDevices = 64;
 std::mutex g_mu;
@@ -56,7 +56,7 @@ hipError_t device_info(int *cus, bool dot64, int k, int core, size_t lds, int *b
   }
   *cus = d.cus;
   if (!blocks_per_cu) return hipSuccess;
-  const int vi = ((dot64 ? 3 : 0) + core) * 2 + (k == 8 ? 1 : 0);
+  const int vi = ((dot64 ? 4 : 0) + core) * 2 + (k == 8 ? 1 : 0);
   for (int q = 0; q < d.nocc[vi]; ++q)
     if (d.occ[vi][q].lds == lds) {
       *blocks_per_cu = d.occ[vi][q].blocks;
@@ -197,6 +197,40 @@ void apply_lut(BinParams &bp, const LutPlan &lp) {
   bp.lut_g = lp.g;
   bp.lut_n = 2 * lp.m;
   bp.lut_sh = 2;
+}
+
+// ---- edge-table core ------------------------------------------------------------------------
+// fp32 dot, bins covering 180 deg that are too fine for the bin table (etab_kernel and etab_key
+// in gc_kernels.hip): a degree-3 arccos picks edge r = round(t~), the cosine decides the side.
+// Sound when every pair the table does not flag (NaN) has |t~ - t| < 0.45: the table builder
+// checks this per entry with the arccos error e3 = 1.25 (CORE_ERR + 2^-24 pi/2) (a 1-ulp
+// square root adds half an ulp of P <= pi/2).  The host requires e3 / w <= 0.25, so that away
+// from 0 and 180 deg the dot product's share of the budget leaves few entries flagged, and the
+// interleaved table and histogram with four queues within 40 KB of LDS (four workgroups per CU).
+struct EtabPlan {
+  bool ok = false;
+  double g_x = 0.0, e3 = 0.0;
+  float g = 0.0f;
+};
+
+EtabPlan plan_etab(int32_t nbins, double w_deg, int k) {
+  EtabPlan p;
+  const double w = w_deg * (kPi / 180.0);
+  p.e3 = 1.25 * (GC_ACOS3_CORE_ERR + kTwoM24 * (kPi / 2.0));
+  if (!(p.e3 / w <= 0.25)) return p;
+  if (static_cast<size_t>(nbins) + 2 > kLutBytes / 4) return p;
+  const int32_t hw = etab_hist_words(nbins);
+  if (pairs_lds_bytes(hw, true, k, hw) > 40960) return p;
+  p.ok = true;
+  p.g_x = 5.0 * kTwoM24 * (1.0 + 1e-6) + 1e-12;
+  p.g = static_cast<float>(1.1 * (p.g_x + 0.5 * kTwoM24) * (1.0 + 1e-6));
+  return p;
+}
+
+void apply_etab(BinParams &bp, const EtabPlan &ep, int32_t nbins) {
+  bp.lut_g = ep.g;
+  bp.lut_n = nbins + 1;  // last entry
+  bp.lut_sh = 3;         // 8 bytes per {e_r, count} pair
 }
 
 // ---- series core ---------------------------------------------------------------------------
@@ -370,14 +404,18 @@ gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, in
   const bool span = span_ok && tu.span_kernel != 1;
   // The arccos-free cores where they are sound: the bin table (fp32 dot, full span, shared
   // histogram) and the series (fp64 dot, bins ending by ~9 deg).
+  // (and the edge table: fp32 dot, full span, bins too fine for the bin table)
   const LutPlan lp = dot64 ? LutPlan() : plan_lut(nbins, w_deg);
   const SeriesPlan sp = dot64 ? plan_series(nbins, w_deg) : SeriesPlan();
+  const EtabPlan ep = dot64 ? EtabPlan() : plan_etab(nbins, w_deg, k);
   const bool lut_ok = lp.ok && span && tu.shared_histogram != 1;
   const bool series_ok = sp.ok && span;
-  if (tu.fast_core == 2 && !lut_ok && !series_ok) return GC_ERR_INVALID_ARGUMENT;
+  const bool etab_ok = !lut_ok && ep.ok && span && tu.shared_histogram != 1;
+  if (tu.fast_core == 2 && !lut_ok && !series_ok && !etab_ok) return GC_ERR_INVALID_ARGUMENT;
   const bool use_lut = lut_ok && tu.fast_core != 1;
   const bool use_series = series_ok && tu.fast_core != 1;
-  const int core = (use_lut || use_series) ? 2 : (span ? 1 : 0);
+  const bool use_etab = etab_ok && tu.fast_core != 1;
+  const int core = use_etab ? 3 : ((use_lut || use_series) ? 2 : (span ? 1 : 0));
   const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
 
   PairArgs a;
@@ -392,8 +430,13 @@ gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, in
     a.wave_lds_words = a.hist_words + queue_words(k);
     apply_lut(a.bp, lp);
   }
+  if (use_etab) {
+    a.hist_words = etab_hist_words(nbins);
+    a.wave_lds_words = a.hist_words + queue_words(k);
+    apply_etab(a.bp, ep, nbins);
+  }
   uint2 *lut_dev = reinterpret_cast<uint2 *>(static_cast<char *>(workspace) + edge_table_bytes(nbins));
-  a.lut = use_lut ? lut_dev : nullptr;
+  a.lut = (use_lut || use_etab) ? lut_dev : nullptr;
   double *edge_cos = static_cast<double *>(workspace);
   a.edge_cos = edge_cos;
   a.slots = reinterpret_cast<unsigned long long *>(static_cast<char *>(workspace) + edge_table_bytes(nbins) +
@@ -433,9 +476,9 @@ gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, in
     hipError_t e = device_info(&cus, dot64, k, core, pairs_lds_bytes(a.hist_words, false, k), &occ);
     if (e != hipSuccess) return device_error(e);
     e = device_info(&cus, dot64, k, core,
-                    pairs_lds_bytes(a.hist_words, true, k, use_lut ? a.bp.lut_n + 1 : 0), &occ_shared);
+                    pairs_lds_bytes(a.hist_words, true, k, table_words(a, dot64, core)), &occ_shared);
     if (e != hipSuccess) return device_error(e);
-    bool shared = use_lut || tu.shared_histogram == 2 || (tu.shared_histogram == 0 && occ_shared > occ);
+    bool shared = use_lut || use_etab || tu.shared_histogram == 2 || (tu.shared_histogram == 0 && occ_shared > occ);
     if (shared) occ = occ_shared;
     a.shared_hist = shared ? 1 : 0;
     // Between two flushes a bin must stay within +-2^31: each j-step adds at most 2 * 64 K
@@ -494,6 +537,10 @@ gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, in
     if (e != hipSuccess) return device_error(e);
     if (use_lut) {
       e = launch_lut(nbins, w_deg, lp.m, lp.margin, lut_dev, hs);
+      if (e != hipSuccess) return device_error(e);
+    }
+    if (use_etab) {
+      e = launch_etab(nbins, w_deg, ep.g_x, ep.e3, reinterpret_cast<uint32_t *>(lut_dev), hs);
       if (e != hipSuccess) return device_error(e);
     }
     e = launch_pairs(a, num_wg, dot64, k, core, hs);
@@ -567,11 +614,13 @@ gc_status gc_eval_angle_core(const float *x32, const double *x64, int64_t n, int
   const bool span = d64 ? span_narrow(nbins, w_deg) : span_full(nbins, w_deg);
   const LutPlan lp = d64 ? LutPlan() : plan_lut(nbins, w_deg);
   const SeriesPlan sp = d64 ? plan_series(nbins, w_deg) : SeriesPlan();
+  const EtabPlan ep = d64 ? EtabPlan() : plan_etab(nbins, w_deg, 8);
   const bool use_lut = lp.ok && span;
   const bool use_series = sp.ok && span;
-  const int core = (use_lut || use_series) ? 2 : (span ? 1 : 0);
+  const bool use_etab = !use_lut && ep.ok && span;
+  const int core = use_etab ? 3 : ((use_lut || use_series) ? 2 : (span ? 1 : 0));
   if (n == 0) return GC_OK;
-  const bool need_ws = exact_out || use_lut;
+  const bool need_ws = exact_out || use_lut || use_etab;
   if (need_ws && (!workspace || !aligned(workspace, GC_ALIGNMENT))) return GC_ERR_INVALID_ARGUMENT;
   if (need_ws && ws_bytes < edge_table_bytes(nbins) + kLutBytes) return GC_ERR_WORKSPACE;
   BinParams bp = make_bins(nbins, w_deg);
@@ -584,6 +633,10 @@ gc_status gc_eval_angle_core(const float *x32, const double *x64, int64_t n, int
   if (e == hipSuccess && use_lut) {
     apply_lut(bp, lp);
     e = launch_lut(nbins, w_deg, lp.m, lp.margin, lut, hs);
+  }
+  if (e == hipSuccess && use_etab) {
+    apply_etab(bp, ep, nbins);
+    e = launch_etab(nbins, w_deg, ep.g_x, ep.e3, reinterpret_cast<uint32_t *>(lut), hs);
   }
   if (e == hipSuccess)
     e = launch_eval_core(x32, x64, n, bp, d64, core, lut, exact_out ? edge_cos : nullptr, bin_out, trip_out,

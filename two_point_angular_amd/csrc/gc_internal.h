@@ -63,8 +63,9 @@ struct BinParams {
   float lut_mb;  // M + 2^23: fma(c, M, M + 2^23) holds round(M (c + 1)) in its low mantissa bits
   float lut_g;   // bin-table core guard: recheck iff |cos(edge) - x| < lut_g
   int32_t lut_n; // 2 M (last entry index), or 0 when the bin table is not used
-  int32_t lut_sh;  // 2: log2 of the bytes per histogram word (an argument, so that the compiler
-                   // keeps (sign << 2) + address as one shift-and-add)
+  int32_t lut_sh;  // log2 of the bytes between consecutive histogram words (4 bytes; 8 in the
+                   // edge-table core); an argument, so that the compiler keeps (sign << sh) +
+                   // address as one shift-and-add
   int32_t nbins;
 };
 
@@ -77,6 +78,11 @@ constexpr int kLutMaxEntries = 2049;
 // nbins + 64 (counted as bin 0) and x < 0 in word nbins + 65 (counted as bin nbins - 1): two
 // histogram words past the 64 spare ones.
 constexpr int kLutAliasWords = 2;
+// Edge-table core (fp32 dot, bins covering 0..180 deg, too fine for the bin table): the cosine
+// of edge r (fp32, or NaN where the pair must be rechecked) for r = 0 .. nbins + 1, built in
+// the bin table's workspace area.  In LDS it is interleaved with the shared histogram: word
+// pair r + 1 = {e_r, count of bin r}; pair 0 holds the count of a bin -1 that only rechecked
+// pairs can reach (the recheck moves them out).  One lookup address then serves both.
 
 // ---- pair-kernel work description ---------------------------------------------------
 // One family (DD, DR or RR): the i catalog is held in registers, the j catalog streamed.
@@ -115,12 +121,22 @@ struct PairArgs {
 // LDS bytes of one pair-kernel workgroup.
 // LDS bytes of one pair-kernel workgroup: histogram(s), the bin table (lut_entries 8-byte
 // entries, shared-histogram mode only) and the four recheck queues.
-inline size_t pairs_lds_bytes(int32_t hist_words, bool shared_hist, int k, int32_t lut_entries = 0) {
+inline size_t pairs_lds_bytes(int32_t hist_words, bool shared_hist, int k, int32_t table_words = 0) {
   const size_t qw = static_cast<size_t>(queue_words(k));
-  const size_t words = shared_hist ? hist_words + 2 * static_cast<size_t>(lut_entries) +
+  const size_t words = shared_hist ? hist_words + static_cast<size_t>(table_words) +
                                          static_cast<size_t>(kWavesPerWG) * qw
                                    : static_cast<size_t>(kWavesPerWG) * (hist_words + qw);
   return words * sizeof(uint32_t);
+}
+// Histogram words of the edge-table core: bins -1 .. nbins + 63 (64 spares, as in core32).
+inline int32_t etab_hist_words(int32_t nbins) { return (nbins + 1 + 64 + 63) / 64 * 64; }
+// Words of the core's table in LDS: the bin table (2 per entry), or the edge cosines, which
+// the edge-table core interleaves with the histogram (one per histogram word).
+inline int32_t table_words(const PairArgs &a, bool dot64, int core) {
+  if (dot64) return 0;
+  if (core == 2) return 2 * (a.bp.lut_n + 1);
+  if (core == 3) return a.hist_words;
+  return 0;
 }
 
 // Records a failed HIP call for gc_last_device_error() (gc_api.cpp).
@@ -135,6 +151,7 @@ hipError_t launch_prepare(const float *ra, const float *dec, int64_t n, void *bl
 hipError_t launch_pairs(const PairArgs &a, int num_wg, bool dot64, int k, int core, hipStream_t s);
 hipError_t pairs_occupancy(bool dot64, int k, int core, size_t lds_bytes, int *blocks_per_cu);
 hipError_t launch_lut(int32_t nbins, double w_deg, int32_t m, double margin, uint2 *lut, hipStream_t s);
+hipError_t launch_etab(int32_t nbins, double w_deg, double g_x, double e3, uint32_t *et, hipStream_t s);
 // accumulate: add the sums to the outputs instead of overwriting them
 hipError_t launch_merge(const unsigned long long *slots, int32_t nbins, const int32_t wg_begin[3],
                         const int32_t wg_end[3], uint64_t *out[3], bool accumulate, hipStream_t s);

@@ -204,6 +204,26 @@ __device__ __forceinline__ uint32_t lut_word_address(float x, uint2 ent, const B
   return (static_cast<uint32_t>(__float_as_int(d) >> 31) << bp.lut_sh) + ent.y;
 }
 
+// Edge-table core (fp32 dot, bins covering 0..180 deg that are too fine for the bin table).  A
+// degree-3 arccos (error 6.8e-5 rad) gives t~ = theta~ / w to a fraction of a bin, and
+// r = round(t~), read from the bits of t~ + 2^23, names the one edge that can lie between t~
+// and the pair's true t: edge r, at cos(r w) = e_r.  The side is decided on the cosine, as in
+// the bin-table core: bin = r - [x > e_r], recheck iff !(|e_r - x| >= lut_g).  Where the dot
+// product's error can move t~ by half a bin (near 0 and 180 deg, where s is small), e_r is NaN:
+// the test fails and the pair is rechecked.  Past 180 deg (r >= nbins) e_r = -4: bin r - 1.
+__device__ __forceinline__ float etab_t(float x, const BinParams &bp, float h_v) {
+  const float a = fabsf(x);
+  const float s = __builtin_amdgcn_sqrtf(__builtin_amdgcn_fmed3f(1.0f - a, 0.0f, 1.0f));
+  float p = fmaf(GC_ACOS3_C3, a, GC_ACOS3_C2);
+  p = fmaf(p, a, GC_ACOS3_C1);
+  p = fmaf(p, a, GC_ACOS3_C0);
+  const float q = fmaf(-s, p, kHalfPiF);
+  return fmaf(copysignf(q, x), -bp.invw, h_v);
+}
+__device__ __forceinline__ float etab_key(float x, const BinParams &bp, float h_v) {
+  return etab_t(x, bp, h_v) + 8388608.0f;  // 2^23 + round(t~)
+}
+
 // Exact recheck in the cosine domain.  theta >= e w  <=>  x <= cos(e w), so bin k holds x
 // iff c[k+1] < x <= c[k], with c[e] = cos(e w) in fp64 (c[0] = 1; c[e] = -inf past 180
 // degrees).  Starting from the fast-path bin k, walk to the bin that satisfies this.  The
@@ -257,9 +277,10 @@ template <> struct Real<true> { typedef double T; };
 
 // Re-bin the c <= 64 queued pairs in entries [first, first + c) exactly in fp64 (one pair
 // per lane) and move their counts from the fast-path bin to the exact bin.  Entry e: word
-// 2e = j, word 2e+1 = (i - i0) << 16 | fast-path bin.  A fast-path bin >= nbins is a spare
-// bin standing for bin nbins - 1.
-__device__ __forceinline__ void drain_queue(uint32_t *hist, const uint32_t *queue, int first, int c,
+// 2e = j, word 2e+1 = (i - i0) << 16 | (fast-path bin + 1).  A fast-path bin >= nbins is a
+// spare bin standing for bin nbins - 1; bin -1 (edge-table core) stands for nothing, so its
+// count always moves.  Bin b's count is hist[b * hs].
+__device__ __forceinline__ void drain_queue(uint32_t *hist, int hs, const uint32_t *queue, int first, int c,
                                             const Prepared &ci, const Prepared &cj, int64_t i0, uint32_t w,
                                             const double *edge_cos, int32_t nbins) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -268,13 +289,14 @@ __device__ __forceinline__ void drain_queue(uint32_t *hist, const uint32_t *queu
     const int e = first + lane;
     const uint32_t jj = queue[2 * e];
     const uint32_t p = queue[2 * e + 1];
-    const uint32_t kf = p & 0xffffu;
-    const uint32_t last = static_cast<uint32_t>(nbins - 1);
-    const uint32_t kr = kf < last ? kf : last;
-    const uint32_t ke = exact_bin(dot64(ci, i0 + (p >> 16), cj, jj), kr, edge_cos, nbins);
-    if (ke != kr) {
-      atomicSub(hist + kf, w);
-      atomicAdd(hist + ke, w);
+    const int kf = static_cast<int>(p & 0xffffu) - 1;
+    const int last = nbins - 1;
+    const int kr = kf < 0 ? 0 : (kf < last ? kf : last);
+    const int ke = static_cast<int>(exact_bin(dot64(ci, i0 + (p >> 16), cj, jj), static_cast<uint32_t>(kr),
+                                              edge_cos, nbins));
+    if (ke != kr || kf < 0) {
+      atomicSub(hist + kf * hs, w);
+      atomicAdd(hist + ke * hs, w);
     }
   }
   __builtin_amdgcn_wave_barrier();
@@ -293,6 +315,8 @@ pairs_kernel(const PairArgs A) {
   typedef typename Real<D64>::T real;
   constexpr bool SPAN = CORE != 0;
   constexpr bool LUT = CORE == 2 && !D64;  // fp64 dot: CORE 2 is the series core
+  constexpr bool ETAB = CORE == 3;          // fp32 dot only
+  constexpr int HS = ETAB ? 2 : 1;          // histogram stride in words (see kEtab layout)
   constexpr int BI = kWave * K;       // i-block: galaxies per wave
   constexpr int JB = D64 ? 4 : 8;     // j galaxies per scalar batch
   extern __shared__ uint32_t lds[];
@@ -303,15 +327,19 @@ pairs_kernel(const PairArgs A) {
   // branches).
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   // LDS: private mode, per wave [histogram | queue]; shared mode, [histogram | bin table |
-  // 4 queues] (the table only with the bin-table core).
-  const bool shared_hist = LUT || A.shared_hist != 0;
+  // 4 queues] (the table only with the bin-table core); edge-table core, [{e_r, count} pairs |
+  // 4 queues], bin b's count at word 2 b + 3.
+  const bool shared_hist = LUT || ETAB || A.shared_hist != 0;
   constexpr int QW = queue_words(K);
-  const int lut_words = LUT ? 2 * (A.bp.lut_n + 1) : 0;
-  uint32_t *const hist = shared_hist ? lds : lds + wv * (A.hist_words + QW);
+  const int tab_words = LUT ? 2 * (A.bp.lut_n + 1) : (ETAB ? A.hist_words : 0);
+  uint32_t *const hist = shared_hist ? lds + (ETAB ? 3 : 0) : lds + wv * (A.hist_words + QW);
   uint2 *const tab = reinterpret_cast<uint2 *>(lds + A.hist_words);
-  uint32_t *const queue = shared_hist ? lds + A.hist_words + lut_words + wv * QW : hist + A.hist_words;
+  uint32_t *const queue = shared_hist ? lds + A.hist_words + tab_words + wv * QW : hist + A.hist_words;
   const uint32_t hist_addr = lds_address(hist);
   const uint32_t tab_bias = lds_address(tab) - (kLutKeyBias << 3);
+  // edge-table core: pair r + 1 = {e_r, count r} sits at lds + 8 (r + 1), read from key bits
+  const uint32_t etab_base = lds_address(lds);
+  const uint32_t etab_bias = etab_base + 8u - (kLutKeyBias << 3);
   const int g = blockIdx.x;
   const int fi = g < A.fam[0].wg_end ? 0 : (g < A.fam[1].wg_end ? 1 : 2);
   const FamilyWork &F = A.fam[fi];
@@ -323,7 +351,13 @@ pairs_kernel(const PairArgs A) {
 
   unsigned long long *const slot = A.slots + static_cast<size_t>(g) * A.nbins;
   for (int b = threadIdx.x; b < A.nbins; b += kWGThreads) slot[b] = 0ull;
-  if (shared_hist) {
+  if constexpr (ETAB) {
+    // pairs {e_r, 0}: pair 0 (bin -1), pairs r + 1 for r = 0 .. lut_n, zero-count spares
+    const uint32_t *et = reinterpret_cast<const uint32_t *>(A.lut);
+    uint2 *const pairs = reinterpret_cast<uint2 *>(lds);
+    for (int q = threadIdx.x; q < A.hist_words; q += kWGThreads)
+      pairs[q] = make_uint2(q >= 1 && q <= A.bp.lut_n + 1 ? et[q - 1] : 0u, 0u);
+  } else if (shared_hist) {
     for (int b = threadIdx.x; b < A.hist_words; b += kWGThreads) hist[b] = 0u;
     if constexpr (LUT)
       for (int q = threadIdx.x; q <= A.bp.lut_n; q += kWGThreads) {
@@ -364,7 +398,7 @@ pairs_kernel(const PairArgs A) {
   // The queue is drained (64 at a time, from the top) after every j-step and, with K = 8,
   // after its first half, so it never holds more than 64 (drain_span(K) + 1) entries.
   auto drain = [&](int c) __attribute__((always_inline)) {
-    drain_queue(hist, queue, qcount - c, c, F.ci, F.cj, i0, W, A.edge_cos, A.nbins);
+    drain_queue(hist, HS, queue, qcount - c, c, F.ci, F.cj, i0, W, A.edge_cos, A.nbins);
     qcount -= c;
   };
   auto drain_all = [&]() __attribute__((always_inline)) {
@@ -382,10 +416,10 @@ pairs_kernel(const PairArgs A) {
   auto flush = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_wave_barrier();
     for (int bb = lane; bb < A.nbins; bb += kWave) {
-      const uint32_t c = atomicExch(hist + bb, 0u);
+      const uint32_t c = atomicExch(hist + bb * HS, 0u);
       if (c) atomicAdd(slot + bb, static_cast<unsigned long long>(static_cast<long long>(static_cast<int>(c))));
     }
-    long long spare = static_cast<int>(atomicExch(hist + A.nbins + lane, 0u));
+    long long spare = static_cast<int>(atomicExch(hist + (A.nbins + lane) * HS, 0u));
     if constexpr (LUT) {
       // the middle table entry's two words: bin 0 and bin nbins - 1
       if (lane < kLutAliasWords) {
@@ -410,8 +444,9 @@ pairs_kernel(const PairArgs A) {
   // One j against this lane's K i-galaxies.  Pairs the guard flags are appended to the
   // wave's queue right after their atomic (each bin index dies at once), and the queue is
   // drained in full-wave batches after the step.
-  // Append a flagged pair (this lane's k-th i against j) to the wave's queue.
-  auto enqueue = [&](bool tp, uint32_t kk, int k, int64_t jg) __attribute__((always_inline)) {
+  // Append a flagged pair (this lane's k-th i against j) to the wave's queue; kslot = its
+  // fast-path bin + 1.
+  auto enqueue = [&](bool tp, uint32_t kslot, int k, int64_t jg) __attribute__((always_inline)) {
     const unsigned long long m = __ballot(tp);
     if (m) {
       if (tp) {
@@ -420,7 +455,7 @@ pairs_kernel(const PairArgs A) {
             static_cast<uint32_t>(m >> 32),
             __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), static_cast<uint32_t>(qcount)));
         queue[2 * e] = static_cast<uint32_t>(jg);
-        queue[2 * e + 1] = (lane_tag + (static_cast<uint32_t>(kWave * k) << 16)) | kk;
+        queue[2 * e + 1] = (lane_tag + (static_cast<uint32_t>(kWave * k) << 16)) | kslot;
       }
       qcount += __popcll(m);
     }
@@ -444,7 +479,28 @@ pairs_kernel(const PairArgs A) {
         const uint32_t a = lut_word_address(xv[k], ev[k], bp, tp);
         __hip_atomic_fetch_add(reinterpret_cast<lds_word_t *>(static_cast<uintptr_t>(a)), W, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_WORKGROUP);
-        enqueue(tp, (a - hist_addr) >> 2, k, jg);
+        enqueue(tp, ((a - hist_addr) >> 2) + 1, k, jg);
+        if (k + 1 == drain_span(K) && k + 1 < K) drain_full();
+      }
+    } else if constexpr (ETAB && !GENERIC) {
+      // all K edge-cosine reads first, so one LDS wait covers them
+      float xv[K], ev[K];
+      uint32_t av[K];
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        xv[k] = fmaf(ix[k], xj, fmaf(iy[k], yj, iz[k] * zj));
+        av[k] = (__float_as_uint(etab_key(xv[k], bp, c_v)) << 3) + etab_bias;
+        ev[k] = *reinterpret_cast<__attribute__((address_space(3))) const float *>(static_cast<uintptr_t>(av[k]));
+      }
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const float d = ev[k] - xv[k];
+        const bool tp = !(fabsf(d) >= bp.lut_g);
+        // the pair of bin r - [d < 0]; its count is the pair's second word
+        const uint32_t a = (static_cast<uint32_t>(__float_as_int(d) >> 31) << bp.lut_sh) + av[k];
+        __hip_atomic_fetch_add(reinterpret_cast<lds_word_t *>(static_cast<uintptr_t>(a)) + 1, W, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
+        enqueue(tp, (a - etab_base) >> 3, k, jg);
         if (k + 1 == drain_span(K) && k + 1 < K) drain_full();
       }
     } else {
@@ -462,11 +518,11 @@ pairs_kernel(const PairArgs A) {
           const bool self = F.sym && jg == ig;  // only a self family pairs a galaxy with itself
           if (self) kk = 0u;                     // separation 0
           tp = tp && valid && !self;
-          if (valid) atomicAdd(hist + kk, self ? 1u : W);
+          if (valid) atomicAdd(hist + kk * HS, self ? 1u : W);
         } else {
-          atomicAdd(hist + kk, W);
+          atomicAdd(hist + kk * HS, W);
         }
-        enqueue(tp, kk, k, jg);
+        enqueue(tp, kk + 1, k, jg);
         if (k + 1 == drain_span(K) && k + 1 < K) drain_full();
       }
     }
@@ -668,6 +724,34 @@ __global__ void __launch_bounds__(256) lut_kernel(int32_t nbins, double w_deg, i
   lut[q] = ent;
 }
 
+// ------------------------------------------------------------------------------ edge table
+// e_r for r = 0 .. nbins + 1 (fp32 bits).  Entry r serves the pairs with t~ in [r - 1/2, r + 1/2].
+// Their true angle lies within err = (2.02 g_x / s + e3) / w + 2^-24 (t + 2h) 1.01 bins of t~,
+// where s >= the smallest sqrt(1 - |cos theta|) over the entry's angles widened by e3 (the
+// arccos error, rad): s is monotone on each side of 90 deg, so the ends decide.  When err <
+// 0.45 the true bin is r - 1 or r, and e_r = cos(r w) (edge r; -4 past 180 deg); otherwise NaN.
+__global__ void __launch_bounds__(256) etab_kernel(int32_t nbins, double w_deg, double g_x, double e3,
+                                                   uint32_t *et) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r > nbins + 1) return;
+  constexpr double kPiD = 3.14159265358979323846;
+  const double w = w_deg * (kPiD / 180.0);
+  const double lo = (r - 0.5) * w - e3, hi = (r + 0.5) * w + e3;
+  float e;
+  if (!(lo > 0.0) || !(hi < kPiD)) {
+    e = __builtin_nanf("");
+  } else {
+    const double s_lo = sqrt(1.0 - fabs(cos(lo))), s_hi = sqrt(1.0 - fabs(cos(hi)));
+    const double s = fmin(s_lo, s_hi) * 0.999;
+    const double h = 0.5 * kPiD / w;
+    const double err = (2.02 * g_x / s + e3) / w + 0x1p-24 * (r + 0.5 + 2.0 * h) * 1.01;
+    if (!(err < 0.45)) e = __builtin_nanf("");
+    else if (r >= nbins || static_cast<double>(r) * w_deg >= 180.0) e = -4.0f;
+    else e = static_cast<float>(cos(static_cast<double>(r) * w));
+  }
+  et[r] = __float_as_uint(e);
+}
+
 // ------------------------------------------------------------------------------- merge
 // out_f[bin] = sum of slots of family f's workgroups (plus out_f[bin] itself when
 // accumulating).  Block: 256 threads = 4 waves over the slot list, one bin per lane; grid
@@ -752,8 +836,19 @@ __global__ void __launch_bounds__(256) eval_core_kernel(const float *x32, const 
   } else {
     const float xf = x32[idx];
     xe = static_cast<double>(xf);
-    if constexpr (CORE == 2) core_lut(xf, bp, lut, k, trip, t);  // (fp32 dot: CORE 2 is the table)
-    else core32<SPAN>(xf, bp, bp.h, bp.tmax, k, trip, t);
+    if constexpr (CORE == 2) {
+      core_lut(xf, bp, lut, k, trip, t);  // (fp32 dot: CORE 2 is the table)
+    } else if constexpr (CORE == 3) {
+      // edge table in global memory, e_r at index r; t_out = t~ (unrounded)
+      t = etab_t(xf, bp, bp.h);
+      const uint32_t r = __float_as_uint(t + 8388608.0f) - kLutKeyBias;
+      const float d = __uint_as_float(reinterpret_cast<const uint32_t *>(lut)[r]) - xf;
+      trip = !(fabsf(d) >= bp.lut_g);
+      const int kb = static_cast<int>(r) - (__float_as_int(d) < 0 ? 1 : 0);
+      k = static_cast<uint32_t>(kb < 0 ? 0 : kb);
+    } else {
+      core32<SPAN>(xf, bp, bp.h, bp.tmax, k, trip, t);
+    }
   }
   // k >= nbins: the full-span kernel's spare bins and the table's word nbins + 65, which the
   // flush folds into bin nbins - 1; the table's word nbins + 64 is bin 0
@@ -792,6 +887,7 @@ static const void *select_pairs(bool dot64, int k, int core) {
     if (core) return k == 4 ? pairs_fn<4, true, 1>() : pairs_fn<8, true, 1>();
     return k == 4 ? pairs_fn<4, true, 0>() : pairs_fn<8, true, 0>();
   }
+  if (core == 3) return k == 4 ? pairs_fn<4, false, 3>() : pairs_fn<8, false, 3>();
   if (core == 2) return k == 4 ? pairs_fn<4, false, 2>() : pairs_fn<8, false, 2>();
   if (core) return k == 4 ? pairs_fn<4, false, 1>() : pairs_fn<8, false, 1>();
   return k == 4 ? pairs_fn<4, false, 0>() : pairs_fn<8, false, 0>();
@@ -806,8 +902,8 @@ hipError_t pairs_occupancy(bool dot64, int k, int core, size_t lds_bytes, int *b
 }
 
 hipError_t launch_pairs(const PairArgs &a, int num_wg, bool dot64, int k, int core, hipStream_t st) {
-  const bool table = core == 2 && !dot64;
-  const size_t lds = pairs_lds_bytes(a.hist_words, table || a.shared_hist != 0, k, table ? a.bp.lut_n + 1 : 0);
+  const bool table = (core == 2 || core == 3) && !dot64;
+  const size_t lds = pairs_lds_bytes(a.hist_words, table || a.shared_hist != 0, k, table_words(a, dot64, core));
   const void *fn = select_pairs(dot64, k, core);
   void *args[] = {const_cast<PairArgs *>(&a)};
   return hipLaunchKernel(fn, dim3(num_wg), dim3(kWGThreads), args, lds, st);
@@ -834,6 +930,11 @@ hipError_t launch_omega(const uint64_t *dd, const uint64_t *dr, const uint64_t *
   return hipGetLastError();
 }
 
+hipError_t launch_etab(int32_t nbins, double w_deg, double g_x, double e3, uint32_t *et, hipStream_t st) {
+  hipLaunchKernelGGL(etab_kernel, dim3((nbins + 2 + 255) / 256), dim3(256), 0, st, nbins, w_deg, g_x, e3, et);
+  return hipGetLastError();
+}
+
 hipError_t launch_lut(int32_t nbins, double w_deg, int32_t m, double margin, uint2 *lut, hipStream_t st) {
   hipLaunchKernelGGL(lut_kernel, dim3((2 * m + 1 + 255) / 256), dim3(256), 0, st, nbins, w_deg, m, margin, lut);
   return hipGetLastError();
@@ -849,7 +950,10 @@ hipError_t launch_eval_core(const float *x32, const double *x64, int64_t n, cons
                             uint8_t *trip_out, int32_t *exact_out, float *t_out, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>((n + 255) / 256));
   const int d = dot64 ? 1 : 0;
-  if (core == 2)
+  if (core == 3)
+    hipLaunchKernelGGL(eval_core_kernel<3>, grid, dim3(256), 0, st, x32, x64, n, bp, d, lut, edge_cos, bin_out,
+                       trip_out, exact_out, t_out);
+  else if (core == 2)
     hipLaunchKernelGGL(eval_core_kernel<2>, grid, dim3(256), 0, st, x32, x64, n, bp, d, lut, edge_cos, bin_out,
                        trip_out, exact_out, t_out);
   else if (core == 1)
