@@ -81,11 +81,11 @@ def etab_e3():
 
 
 def uses_etab(nbins, w):
-    """Full span, too fine for the bin table, arccos error <= a quarter bin, and the interleaved
-    table and histogram with four queues of 640 words within 40 KB of LDS."""
+    """Full span, too fine for the bin table, arccos error <= a quarter bin, and the table region
+    (4096 words), the histogram and four queues of 384 words within 40 KB of LDS."""
     hist_words = (nbins + 1 + 64 + 63) // 64 * 64
     return ((nbins + 0.5) * w >= 180 and not uses_table(nbins, w) and etab_e3() / np.radians(w) <= 0.25
-            and nbins + 2 <= 16640 // 4 and (2 * hist_words + 4 * 640) * 4 <= 40960)
+            and nbins + 2 <= 4096 and (4096 + hist_words + 4 * 384) * 4 <= 40960)
 
 
 @pytest.mark.parametrize("nbins,w", FP32_CASES)

@@ -206,7 +206,7 @@ void apply_lut(BinParams &bp, const LutPlan &lp) {
 // checks this per entry with the arccos error e3 = 1.25 (CORE_ERR + 2^-24 pi/2) (a 1-ulp
 // square root adds half an ulp of P <= pi/2).  The host requires e3 / w <= 0.25, so that away
 // from 0 and 180 deg the dot product's share of the budget leaves few entries flagged, and the
-// interleaved table and histogram with four queues within 40 KB of LDS (four workgroups per CU).
+// table region, histogram and four queues within 40 KB of LDS (four workgroups per CU).
 struct EtabPlan {
   bool ok = false;
   double g_x = 0.0, e3 = 0.0;
@@ -218,9 +218,8 @@ EtabPlan plan_etab(int32_t nbins, double w_deg, int k) {
   const double w = w_deg * (kPi / 180.0);
   p.e3 = 1.25 * (GC_ACOS3_CORE_ERR + kTwoM24 * (kPi / 2.0));
   if (!(p.e3 / w <= 0.25)) return p;
-  if (static_cast<size_t>(nbins) + 2 > kLutBytes / 4) return p;
-  const int32_t hw = etab_hist_words(nbins);
-  if (pairs_lds_bytes(hw, true, k, hw) > 40960) return p;
+  if (nbins + 2 > kEtabTableWords || static_cast<size_t>(nbins) + 2 > kLutBytes / 4) return p;
+  if (pairs_lds_bytes(etab_hist_words(nbins), true, k, 3, kEtabTableWords) > 40960) return p;
   p.ok = true;
   p.g_x = 5.0 * kTwoM24 * (1.0 + 1e-6) + 1e-12;
   p.g = static_cast<float>(1.1 * (p.g_x + 0.5 * kTwoM24) * (1.0 + 1e-6));
@@ -230,7 +229,7 @@ EtabPlan plan_etab(int32_t nbins, double w_deg, int k) {
 void apply_etab(BinParams &bp, const EtabPlan &ep, int32_t nbins) {
   bp.lut_g = ep.g;
   bp.lut_n = nbins + 1;  // last entry
-  bp.lut_sh = 3;         // 8 bytes per {e_r, count} pair
+  bp.lut_sh = 2;         // 4-byte words
 }
 
 // ---- series core ---------------------------------------------------------------------------
@@ -422,18 +421,15 @@ gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, in
   memset(&a, 0, sizeof(a));
   a.nbins = nbins;
   a.hist_words = (nbins + kWave + 63) / 64 * 64;  // 64 spare bins past the last (see core32)
-  a.wave_lds_words = a.hist_words + queue_words(k);
   a.bp = make_bins(nbins, w_deg);
   if (use_series) apply_series(a.bp, sp, nbins, w_deg);
   if (use_lut) {
     a.hist_words = (nbins + kWave + kLutAliasWords + 63) / 64 * 64;
-    a.wave_lds_words = a.hist_words + queue_words(k);
-    apply_lut(a.bp, lp);
+      apply_lut(a.bp, lp);
   }
   if (use_etab) {
     a.hist_words = etab_hist_words(nbins);
-    a.wave_lds_words = a.hist_words + queue_words(k);
-    apply_etab(a.bp, ep, nbins);
+      apply_etab(a.bp, ep, nbins);
   }
   uint2 *lut_dev = reinterpret_cast<uint2 *>(static_cast<char *>(workspace) + edge_table_bytes(nbins));
   a.lut = (use_lut || use_etab) ? lut_dev : nullptr;
@@ -473,10 +469,10 @@ gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, in
     // Histogram placement: one private histogram per wave unless sharing one per workgroup
     // lets more workgroups fit in LDS.
     int cus = 0, occ = 0, occ_shared = 0;
-    hipError_t e = device_info(&cus, dot64, k, core, pairs_lds_bytes(a.hist_words, false, k), &occ);
+    hipError_t e = device_info(&cus, dot64, k, core, pairs_lds_bytes(a.hist_words, false, k, core), &occ);
     if (e != hipSuccess) return device_error(e);
     e = device_info(&cus, dot64, k, core,
-                    pairs_lds_bytes(a.hist_words, true, k, table_words(a, dot64, core)), &occ_shared);
+                    pairs_lds_bytes(a.hist_words, true, k, core, table_words(a, dot64, core)), &occ_shared);
     if (e != hipSuccess) return device_error(e);
     bool shared = use_lut || use_etab || tu.shared_histogram == 2 || (tu.shared_histogram == 0 && occ_shared > occ);
     if (shared) occ = occ_shared;

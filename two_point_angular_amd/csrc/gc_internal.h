@@ -11,13 +11,14 @@ namespace gc {
 constexpr int kWave = 64;            // CDNA wavefront width
 constexpr int kWavesPerWG = 4;       // pair-kernel workgroup = 4 independent wavefronts
 constexpr int kWGThreads = kWave * kWavesPerWG;
-// Per-wave recheck queue, 8-byte entries.  Full batches of 64 are drained after every j-step,
-// and with K = 8 also after its first half, so a drain point leaves fewer than 64 pending and
-// the next appends at most 64 D entries (D = 4 pairs per lane: K = 4, or half of K = 8):
-// 64 (D + 1) entries suffice.  (Halving the queue of K = 8 lets a fifth workgroup fit in LDS
-// beside the bin table or a 3600-bin shared histogram.)
-constexpr int drain_span(int k) { return k > 4 ? k / 2 : k; }
-constexpr int queue_words(int k) { return 2 * kWave * (drain_span(k) + 1); }
+// Per-wave recheck queue, 8-byte entries.  Full batches of 64 are drained after every j-step
+// and, within a step, after every D pairs per lane (D = drain_span: 4, i.e. once in the middle
+// of a K = 8 step; 2 for the edge-table core, whose table leaves less LDS for queues), so a
+// drain point leaves fewer than 64 pending and the next appends at most 64 D: 64 (D + 1)
+// entries suffice.  (Halving the queue of K = 8 lets a fifth workgroup fit in LDS beside the
+// bin table or a 3600-bin shared histogram.)
+constexpr int drain_span(int k, int core) { return core == 3 ? 2 : (k > 4 ? k / 2 : k); }
+constexpr int queue_words(int k, int core) { return 2 * kWave * (drain_span(k, core) + 1); }
 constexpr int kMaxWorkgroups = 2048; // partial-histogram slots held by the workspace
 constexpr int kMaxBlocksPerCU = 8;
 
@@ -63,9 +64,8 @@ struct BinParams {
   float lut_mb;  // M + 2^23: fma(c, M, M + 2^23) holds round(M (c + 1)) in its low mantissa bits
   float lut_g;   // bin-table core guard: recheck iff |cos(edge) - x| < lut_g
   int32_t lut_n; // 2 M (last entry index), or 0 when the bin table is not used
-  int32_t lut_sh;  // log2 of the bytes between consecutive histogram words (4 bytes; 8 in the
-                   // edge-table core); an argument, so that the compiler keeps (sign << sh) +
-                   // address as one shift-and-add
+  int32_t lut_sh;  // 2, log2 of the bytes per histogram word: an argument, so that the compiler
+                   // keeps (sign << 2) + address as one shift-and-add
   int32_t nbins;
 };
 
@@ -80,9 +80,9 @@ constexpr int kLutMaxEntries = 2049;
 constexpr int kLutAliasWords = 2;
 // Edge-table core (fp32 dot, bins covering 0..180 deg, too fine for the bin table): the cosine
 // of edge r (fp32, or NaN where the pair must be rechecked) for r = 0 .. nbins + 1, built in
-// the bin table's workspace area.  In LDS it is interleaved with the shared histogram: word
-// pair r + 1 = {e_r, count of bin r}; pair 0 holds the count of a bin -1 that only rechecked
-// pairs can reach (the recheck moves them out).  One lookup address then serves both.
+// the bin table's workspace area.  In LDS: [e_r (kEtabTableWords words) | histogram of bins
+// -1 .. nbins + 63 | 4 queues]; bin -1 is reachable only by rechecked pairs (the recheck moves
+// them out).
 
 // ---- pair-kernel work description ---------------------------------------------------
 // One family (DD, DR or RR): the i catalog is held in registers, the j catalog streamed.
@@ -114,15 +114,14 @@ struct PairArgs {
   int64_t flush_interval;      // j-steps between flushes of the 32-bit LDS histograms
   int32_t nbins;
   int32_t hist_words;          // LDS words of one histogram (>= nbins + 64: 64 spare bins)
-  int32_t wave_lds_words;      // hist_words + queue_words(K)
   int32_t shared_hist;         // 0: one histogram per wave; 1: one per workgroup (4 waves)
 };
 
 // LDS bytes of one pair-kernel workgroup.
 // LDS bytes of one pair-kernel workgroup: histogram(s), the bin table (lut_entries 8-byte
 // entries, shared-histogram mode only) and the four recheck queues.
-inline size_t pairs_lds_bytes(int32_t hist_words, bool shared_hist, int k, int32_t table_words = 0) {
-  const size_t qw = static_cast<size_t>(queue_words(k));
+inline size_t pairs_lds_bytes(int32_t hist_words, bool shared_hist, int k, int core, int32_t table_words = 0) {
+  const size_t qw = static_cast<size_t>(queue_words(k, core));
   const size_t words = shared_hist ? hist_words + static_cast<size_t>(table_words) +
                                          static_cast<size_t>(kWavesPerWG) * qw
                                    : static_cast<size_t>(kWavesPerWG) * (hist_words + qw);
@@ -130,12 +129,15 @@ inline size_t pairs_lds_bytes(int32_t hist_words, bool shared_hist, int k, int32
 }
 // Histogram words of the edge-table core: bins -1 .. nbins + 63 (64 spares, as in core32).
 inline int32_t etab_hist_words(int32_t nbins) { return (nbins + 1 + 64 + 63) / 64 * 64; }
-// Words of the core's table in LDS: the bin table (2 per entry), or the edge cosines, which
-// the edge-table core interleaves with the histogram (one per histogram word).
+// The edge table's LDS region (words): e_r at word r, the histogram right after it, so that
+// the count of bin r sits a fixed 4 (kEtabTableWords + 1) bytes past e_r (bin -1 first), an
+// offset the LDS atomic carries in its instruction.
+constexpr int kEtabTableWords = 4096;
+// Words of the core's table in LDS: the bin table (2 per entry), or the edge-table region.
 inline int32_t table_words(const PairArgs &a, bool dot64, int core) {
   if (dot64) return 0;
   if (core == 2) return 2 * (a.bp.lut_n + 1);
-  if (core == 3) return a.hist_words;
+  if (core == 3) return kEtabTableWords;
   return 0;
 }
 

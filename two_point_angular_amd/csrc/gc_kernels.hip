@@ -279,8 +279,8 @@ template <> struct Real<true> { typedef double T; };
 // per lane) and move their counts from the fast-path bin to the exact bin.  Entry e: word
 // 2e = j, word 2e+1 = (i - i0) << 16 | (fast-path bin + 1).  A fast-path bin >= nbins is a
 // spare bin standing for bin nbins - 1; bin -1 (edge-table core) stands for nothing, so its
-// count always moves.  Bin b's count is hist[b * hs].
-__device__ __forceinline__ void drain_queue(uint32_t *hist, int hs, const uint32_t *queue, int first, int c,
+// count always moves.
+__device__ __forceinline__ void drain_queue(uint32_t *hist, const uint32_t *queue, int first, int c,
                                             const Prepared &ci, const Prepared &cj, int64_t i0, uint32_t w,
                                             const double *edge_cos, int32_t nbins) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -295,8 +295,8 @@ __device__ __forceinline__ void drain_queue(uint32_t *hist, int hs, const uint32
     const int ke = static_cast<int>(exact_bin(dot64(ci, i0 + (p >> 16), cj, jj), static_cast<uint32_t>(kr),
                                               edge_cos, nbins));
     if (ke != kr || kf < 0) {
-      atomicSub(hist + kf * hs, w);
-      atomicAdd(hist + ke * hs, w);
+      atomicSub(hist + kf, w);
+      atomicAdd(hist + ke, w);
     }
   }
   __builtin_amdgcn_wave_barrier();
@@ -316,7 +316,6 @@ pairs_kernel(const PairArgs A) {
   constexpr bool SPAN = CORE != 0;
   constexpr bool LUT = CORE == 2 && !D64;  // fp64 dot: CORE 2 is the series core
   constexpr bool ETAB = CORE == 3;          // fp32 dot only
-  constexpr int HS = ETAB ? 2 : 1;          // histogram stride in words (see kEtab layout)
   constexpr int BI = kWave * K;       // i-block: galaxies per wave
   constexpr int JB = D64 ? 4 : 8;     // j galaxies per scalar batch
   extern __shared__ uint32_t lds[];
@@ -327,19 +326,20 @@ pairs_kernel(const PairArgs A) {
   // branches).
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   // LDS: private mode, per wave [histogram | queue]; shared mode, [histogram | bin table |
-  // 4 queues] (the table only with the bin-table core); edge-table core, [{e_r, count} pairs |
-  // 4 queues], bin b's count at word 2 b + 3.
+  // 4 queues] (the table only with the bin-table core); edge-table core, [edge cosines
+  // (kEtabTableWords) | histogram of bins -1 .. | 4 queues].
   const bool shared_hist = LUT || ETAB || A.shared_hist != 0;
-  constexpr int QW = queue_words(K);
-  const int tab_words = LUT ? 2 * (A.bp.lut_n + 1) : (ETAB ? A.hist_words : 0);
-  uint32_t *const hist = shared_hist ? lds + (ETAB ? 3 : 0) : lds + wv * (A.hist_words + QW);
+  constexpr int QW = queue_words(K, CORE);
+  const int tab_words = LUT ? 2 * (A.bp.lut_n + 1) : 0;
+  uint32_t *const hist = ETAB ? lds + kEtabTableWords + 1 : (shared_hist ? lds : lds + wv * (A.hist_words + QW));
   uint2 *const tab = reinterpret_cast<uint2 *>(lds + A.hist_words);
-  uint32_t *const queue = shared_hist ? lds + A.hist_words + tab_words + wv * QW : hist + A.hist_words;
+  uint32_t *const queue = ETAB ? lds + kEtabTableWords + A.hist_words + wv * QW
+                               : (shared_hist ? lds + A.hist_words + tab_words + wv * QW : hist + A.hist_words);
   const uint32_t hist_addr = lds_address(hist);
   const uint32_t tab_bias = lds_address(tab) - (kLutKeyBias << 3);
-  // edge-table core: pair r + 1 = {e_r, count r} sits at lds + 8 (r + 1), read from key bits
+  // edge-table core: e_r at lds + 4 r, read from the key's bits
   const uint32_t etab_base = lds_address(lds);
-  const uint32_t etab_bias = etab_base + 8u - (kLutKeyBias << 3);
+  const uint32_t etab_bias = etab_base - (kLutKeyBias << 2);
   const int g = blockIdx.x;
   const int fi = g < A.fam[0].wg_end ? 0 : (g < A.fam[1].wg_end ? 1 : 2);
   const FamilyWork &F = A.fam[fi];
@@ -352,11 +352,9 @@ pairs_kernel(const PairArgs A) {
   unsigned long long *const slot = A.slots + static_cast<size_t>(g) * A.nbins;
   for (int b = threadIdx.x; b < A.nbins; b += kWGThreads) slot[b] = 0ull;
   if constexpr (ETAB) {
-    // pairs {e_r, 0}: pair 0 (bin -1), pairs r + 1 for r = 0 .. lut_n, zero-count spares
     const uint32_t *et = reinterpret_cast<const uint32_t *>(A.lut);
-    uint2 *const pairs = reinterpret_cast<uint2 *>(lds);
-    for (int q = threadIdx.x; q < A.hist_words; q += kWGThreads)
-      pairs[q] = make_uint2(q >= 1 && q <= A.bp.lut_n + 1 ? et[q - 1] : 0u, 0u);
+    for (int q = threadIdx.x; q <= A.bp.lut_n; q += kWGThreads) lds[q] = et[q];
+    for (int b = threadIdx.x; b < A.hist_words; b += kWGThreads) hist[b - 1] = 0u;  // bins -1 ..
   } else if (shared_hist) {
     for (int b = threadIdx.x; b < A.hist_words; b += kWGThreads) hist[b] = 0u;
     if constexpr (LUT)
@@ -395,10 +393,10 @@ pairs_kernel(const PairArgs A) {
   int64_t i0 = 0;
   real ix[K], iy[K], iz[K];
 
-  // The queue is drained (64 at a time, from the top) after every j-step and, with K = 8,
-  // after its first half, so it never holds more than 64 (drain_span(K) + 1) entries.
+  // The queue is drained (64 at a time, from the top) after every j-step and within it after
+  // every drain_span pairs per lane, so it never holds more than 64 (drain_span + 1) entries.
   auto drain = [&](int c) __attribute__((always_inline)) {
-    drain_queue(hist, HS, queue, qcount - c, c, F.ci, F.cj, i0, W, A.edge_cos, A.nbins);
+    drain_queue(hist, queue, qcount - c, c, F.ci, F.cj, i0, W, A.edge_cos, A.nbins);
     qcount -= c;
   };
   auto drain_all = [&]() __attribute__((always_inline)) {
@@ -416,10 +414,10 @@ pairs_kernel(const PairArgs A) {
   auto flush = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_wave_barrier();
     for (int bb = lane; bb < A.nbins; bb += kWave) {
-      const uint32_t c = atomicExch(hist + bb * HS, 0u);
+      const uint32_t c = atomicExch(hist + bb, 0u);
       if (c) atomicAdd(slot + bb, static_cast<unsigned long long>(static_cast<long long>(static_cast<int>(c))));
     }
-    long long spare = static_cast<int>(atomicExch(hist + (A.nbins + lane) * HS, 0u));
+    long long spare = static_cast<int>(atomicExch(hist + A.nbins + lane, 0u));
     if constexpr (LUT) {
       // the middle table entry's two words: bin 0 and bin nbins - 1
       if (lane < kLutAliasWords) {
@@ -480,7 +478,7 @@ pairs_kernel(const PairArgs A) {
         __hip_atomic_fetch_add(reinterpret_cast<lds_word_t *>(static_cast<uintptr_t>(a)), W, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_WORKGROUP);
         enqueue(tp, ((a - hist_addr) >> 2) + 1, k, jg);
-        if (k + 1 == drain_span(K) && k + 1 < K) drain_full();
+        if ((k + 1) % drain_span(K, CORE) == 0 && k + 1 < K) drain_full();
       }
     } else if constexpr (ETAB && !GENERIC) {
       // all K edge-cosine reads first, so one LDS wait covers them
@@ -489,19 +487,20 @@ pairs_kernel(const PairArgs A) {
 #pragma unroll
       for (int k = 0; k < K; ++k) {
         xv[k] = fmaf(ix[k], xj, fmaf(iy[k], yj, iz[k] * zj));
-        av[k] = (__float_as_uint(etab_key(xv[k], bp, c_v)) << 3) + etab_bias;
+        av[k] = (__float_as_uint(etab_key(xv[k], bp, c_v)) << 2) + etab_bias;
         ev[k] = *reinterpret_cast<__attribute__((address_space(3))) const float *>(static_cast<uintptr_t>(av[k]));
       }
 #pragma unroll
       for (int k = 0; k < K; ++k) {
         const float d = ev[k] - xv[k];
         const bool tp = !(fabsf(d) >= bp.lut_g);
-        // the pair of bin r - [d < 0]; its count is the pair's second word
+        // e of bin r - [d < 0]'s upper edge; the bin's count sits kEtabTableWords + 1 words on
+        // (the atomic's constant offset)
         const uint32_t a = (static_cast<uint32_t>(__float_as_int(d) >> 31) << bp.lut_sh) + av[k];
-        __hip_atomic_fetch_add(reinterpret_cast<lds_word_t *>(static_cast<uintptr_t>(a)) + 1, W, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_WORKGROUP);
-        enqueue(tp, (a - etab_base) >> 3, k, jg);
-        if (k + 1 == drain_span(K) && k + 1 < K) drain_full();
+        __hip_atomic_fetch_add(reinterpret_cast<lds_word_t *>(static_cast<uintptr_t>(a)) + (kEtabTableWords + 1), W,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        enqueue(tp, ((a - etab_base) >> 2) + 1, k, jg);
+        if ((k + 1) % drain_span(K, CORE) == 0 && k + 1 < K) drain_full();
       }
     } else {
 #pragma unroll
@@ -518,12 +517,12 @@ pairs_kernel(const PairArgs A) {
           const bool self = F.sym && jg == ig;  // only a self family pairs a galaxy with itself
           if (self) kk = 0u;                     // separation 0
           tp = tp && valid && !self;
-          if (valid) atomicAdd(hist + kk * HS, self ? 1u : W);
+          if (valid) atomicAdd(hist + kk, self ? 1u : W);
         } else {
-          atomicAdd(hist + kk * HS, W);
+          atomicAdd(hist + kk, W);
         }
         enqueue(tp, kk + 1, k, jg);
-        if (k + 1 == drain_span(K) && k + 1 < K) drain_full();
+        if ((k + 1) % drain_span(K, CORE) == 0 && k + 1 < K) drain_full();
       }
     }
     drain_full();
@@ -903,7 +902,7 @@ hipError_t pairs_occupancy(bool dot64, int k, int core, size_t lds_bytes, int *b
 
 hipError_t launch_pairs(const PairArgs &a, int num_wg, bool dot64, int k, int core, hipStream_t st) {
   const bool table = (core == 2 || core == 3) && !dot64;
-  const size_t lds = pairs_lds_bytes(a.hist_words, table || a.shared_hist != 0, k, table_words(a, dot64, core));
+  const size_t lds = pairs_lds_bytes(a.hist_words, table || a.shared_hist != 0, k, core, table_words(a, dot64, core));
   const void *fn = select_pairs(dot64, k, core);
   void *args[] = {const_cast<PairArgs *>(&a)};
   return hipLaunchKernel(fn, dim3(num_wg), dim3(kWGThreads), args, lds, st);
