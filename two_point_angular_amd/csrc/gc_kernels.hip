@@ -111,12 +111,15 @@ __device__ __forceinline__ void core32(float x, const BinParams &bp, float h_v, 
 // guard's rho, so t = s (q0 + q1 y + q2 y^2) / w (coefficients pre-scaled, q2 in a VGPR).  The
 // quadratic grows with y, so every pair past the range, x < 0 included (y clamped to 1), lands
 // at or past the last bin.
+// SERIES takes y = 1 - x itself: the pair kernel forms it inside the dot product,
+// fma(-x_i, x_j, fma(-y_i, y_j, fma(-z_i, z_j, 1))), three fp64 roundings of values in [0, 2]
+// (< 7e-16 absolute, inside the guard's 1e-14 allowance for the cosine) and no subtraction.
 template <int MODE>  // 0: generic, 1: NARROW, 2: SERIES
 __device__ __forceinline__ void core64(double x, const BinParams &bp, float pw6_v, float tmax_v, uint32_t &k,
                                        bool &trip, float &t_raw) {
   float s, t;
   if constexpr (MODE == 2) {
-    const float y = __builtin_amdgcn_fmed3f(static_cast<float>(1.0 - x), 0.0f, 1.0f);
+    const float y = __builtin_amdgcn_fmed3f(static_cast<float>(x), 0.0f, 1.0f);  // x holds y = 1 - cos
     s = __builtin_amdgcn_sqrtf(y);
     t = s * fmaf(fmaf(pw6_v, y, bp.ps[1]), y, bp.ps[0]);
   } else if constexpr (MODE == 1) {
@@ -507,7 +510,9 @@ pairs_kernel(const PairArgs A) {
       for (int k = 0; k < K; ++k) {
         uint32_t kk;
         bool tp;
-        const real x = fma(ix[k], xj, fma(iy[k], yj, iz[k] * zj));
+        real x;
+        if constexpr (D64 && CORE == 2) x = fma(-ix[k], xj, fma(-iy[k], yj, fma(-iz[k], zj, 1.0)));  // 1 - cos
+        else x = fma(ix[k], xj, fma(iy[k], yj, iz[k] * zj));
         float t_unused;
         if constexpr (D64) core64<CORE>(x, bp, c_v, tmax_v, kk, tp, t_unused);
         else core32<SPAN>(x, bp, c_v, tmax_v, kk, tp, t_unused);
@@ -831,7 +836,7 @@ __global__ void __launch_bounds__(256) eval_core_kernel(const float *x32, const 
   float t;
   if (dot64) {
     xe = x64[idx];
-    core64<CORE>(xe, bp, CORE == 2 ? bp.ps[2] : bp.pw[6], bp.tmax, k, trip, t);
+    core64<CORE>(CORE == 2 ? 1.0 - xe : xe, bp, CORE == 2 ? bp.ps[2] : bp.pw[6], bp.tmax, k, trip, t);
   } else {
     const float xf = x32[idx];
     xe = static_cast<double>(xf);
