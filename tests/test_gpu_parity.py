@@ -343,3 +343,50 @@ def test_edge_table_entries(gc):
     inner = ~nan & (r < nbins)
     assert np.all(np.abs(e[inner] - np.cos(np.radians(r[inner] * w))) <= 2.0 ** -24)
     assert np.all(e[~nan & (r >= nbins)] == -4.0)
+
+
+@pytest.mark.parametrize("nbins,w", [(720, 0.25), (3600, 0.05), (1440, 0.125), (1500, 0.001)])
+def test_duplicates_and_antipodes(gc, nbins, w):
+    """Exact duplicate galaxies (cosine 1: separation 0) and exact antipodes (cosine -1: 180 deg)
+    exercise each fast core's ends: the bin table's middle entry (both ends at once), the edge
+    table's always-rechecked end entries and its bin -1, the series core's t = 0 and x < 0."""
+    print(f"[gpu] duplicates and antipodes nbins={nbins}", flush=True)
+    rng = np.random.default_rng(nbins)
+    base = catalogs.uniform_sphere(400, seed=nbins) if nbins * w >= 180 else catalogs.Catalog(
+        rng.uniform(0, 60, 400).astype(np.float32), rng.uniform(-60, 60, 400).astype(np.float32))
+
+    def build(idx, flip):
+        ra = base.ra[idx].astype(np.float64)
+        dec = base.dec[idx].astype(np.float64)
+        ra = np.where(flip, np.mod(ra + 10800.0, 21600.0), ra)
+        dec = np.where(flip, -dec, dec)
+        return catalogs.Catalog(ra.astype(np.float32), dec.astype(np.float32))
+
+    idx_d = rng.integers(0, 400, 2200)
+    idx_r = rng.integers(0, 400, 1900)
+    D = build(idx_d, rng.random(2200) < 0.3)
+    R = build(idx_r, rng.random(1900) < 0.5)
+    fams = oracle_fams(D, R, nbins, w)
+    t = run_gpu(gc, D, R, nbins, w)
+    check_against(f"duplicates {nbins}", t[:3], fams, len(D), len(R))
+    # one point and its antipode only: DD all at 0, DR all in the last bin
+    P = build(np.zeros(700, np.int64), np.zeros(700, bool))
+    Q = build(np.zeros(600, np.int64), np.ones(600, bool))
+    dd, dr, rr, tot, _ = run_gpu(gc, P, Q, nbins, w)
+    assert dd[0] == 700 * 700 and dr[nbins - 1] == 700 * 600 and rr[0] == 600 * 600
+    assert list(tot) == [700 * 700, 700 * 600, 600 * 600]
+
+
+@pytest.mark.parametrize("tuning", [dict(fast_core=1), dict(fast_core=2, i_per_lane=4), dict(flush_interval=5),
+                                    dict(dot_precision=64)])
+def test_edge_table_tuning_invariance(gc, tuning):
+    """3600 x 0.05 deg through the edge table against the arccos core, K = 4, frequent flushes
+    and the fp64 dot: the same histograms, all within the oracle's edge flow."""
+    print(f"[gpu] edge table tuning {tuning}", flush=True)
+    D, R = catalogs.WORKLOADS["clustered100k_3600"].catalogs(n=5000)
+    fams = oracle_fams(D, R, 3600, 0.05)
+    base = run_gpu(gc, D, R, 3600, 0.05)
+    check_against("edge table", base[:3], fams, len(D), len(R), base[4])
+    t = run_gpu(gc, D, R, 3600, 0.05, tuning=gc.Tuning(**tuning))
+    for x, y in zip(base[:3], t[:3]):
+        np.testing.assert_array_equal(x, y)
