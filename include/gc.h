@@ -116,11 +116,14 @@ typedef struct {
                                 bins' span - fp32 dot: no clamp of the bin coordinate (only
                                 valid when (nbins + 1/2) * width >= 180 deg); fp64 dot: no
                                 sign handling (only valid when nbins * width <= 90 deg) */
-    int32_t fast_core;       /* 0 auto; 1: never use an arccos-free core; 2: always - the
-                                bin table (fp32 dot, bins covering 180 deg at widths where
-                                the table is sound, about >= 0.22 deg; one histogram shared
-                                per workgroup) or the series (fp64 dot, bins ending by about
-                                9 deg); invalid where neither applies */
+    int32_t fast_core;       /* 0 auto; 1: never use a fast core (the degree-6 arccos
+                                cores bin every pair); 2: always - the bin table (fp32 dot,
+                                bins covering 180 deg at widths where the table is sound,
+                                about >= 0.22 deg), else the edge table (fp32 dot, bins
+                                covering 180 deg, width >= ~0.02 deg, up to ~3800 bins),
+                                both with one histogram shared per workgroup; or the series
+                                (fp64 dot, bins ending by about 9 deg); invalid where none
+                                applies */
     int64_t flush_interval;  /* 0 auto; else j-steps between flushes of the 32-bit LDS
                                 histograms into 64-bit totals (>= 1) */
 } gc_tuning;
