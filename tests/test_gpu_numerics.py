@@ -66,9 +66,9 @@ def check_sound(x_exact_in, b, trip, nbins, w, g):
 
 
 # (nbins, width): 720 x 0.25 deg bins through the bin table; 1440 x 0.125 and 3600 x 0.05 deg
-# through the edge table (too narrow for the bin table); 1500 x 0.001 deg through the clamped
-# arccos core.
-FP32_CASES = [(720, 0.25), (1440, 0.125), (3600, 0.05), (1500, 0.001)]
+# through the edge table (too narrow for the bin table), and 3601 x 0.0499972 deg, where the
+# edges fall off the round angles; 1500 x 0.001 deg through the clamped arccos core.
+FP32_CASES = [(720, 0.25), (1440, 0.125), (3600, 0.05), (3601, 0.0499972), (1500, 0.001)]
 
 
 def uses_table(nbins, w):

@@ -377,16 +377,18 @@ def test_duplicates_and_antipodes(gc, nbins, w):
     assert list(tot) == [700 * 700, 700 * 600, 600 * 600]
 
 
-@pytest.mark.parametrize("tuning", [dict(fast_core=1), dict(fast_core=2, i_per_lane=4), dict(flush_interval=5),
-                                    dict(dot_precision=64)])
-def test_edge_table_tuning_invariance(gc, tuning):
-    """3600 x 0.05 deg through the edge table against the arccos core, K = 4, frequent flushes
-    and the fp64 dot: the same histograms, all within the oracle's edge flow."""
-    print(f"[gpu] edge table tuning {tuning}", flush=True)
+@pytest.mark.parametrize("nbins,w,tuning", [(3600, 0.05, dict(fast_core=1)), (3600, 0.05, dict(fast_core=2, i_per_lane=4)),
+                                            (3600, 0.05, dict(flush_interval=5)), (3600, 0.05, dict(dot_precision=64)),
+                                            (3601, 0.0499972, dict(fast_core=1))])
+def test_edge_table_tuning_invariance(gc, nbins, w, tuning):
+    """Bins through the edge table against the arccos core, K = 4, frequent flushes and the fp64
+    dot: the same histograms, all within the oracle's edge flow; 3601 x 0.0499972 deg puts the
+    edges off the round angles."""
+    print(f"[gpu] edge table nbins={nbins} w={w} tuning {tuning}", flush=True)
     D, R = catalogs.WORKLOADS["clustered100k_3600"].catalogs(n=5000)
-    fams = oracle_fams(D, R, 3600, 0.05)
-    base = run_gpu(gc, D, R, 3600, 0.05)
+    fams = oracle_fams(D, R, nbins, w)
+    base = run_gpu(gc, D, R, nbins, w)
     check_against("edge table", base[:3], fams, len(D), len(R), base[4])
-    t = run_gpu(gc, D, R, 3600, 0.05, tuning=gc.Tuning(**tuning))
+    t = run_gpu(gc, D, R, nbins, w, tuning=gc.Tuning(**tuning))
     for x, y in zip(base[:3], t[:3]):
         np.testing.assert_array_equal(x, y)
