@@ -69,7 +69,18 @@ def cpu_baseline(D, R, nbins, w, target_s=12.0):
     assert int(fam.hist.sum()) == pairs
     return {"value": pairs / dt2, "unit": "pairs/s", "cores": threads, "kind": "oracle",
             "sample": f"DR rows D[0:{rows2}] x R[0:{len(R)}] ({pairs:.3e} ordered pairs, fp64, "
-                      f"{dt2:.1f} s on {threads} threads)"}
+                      f"{dt2:.1f} s on {threads} threads)", "cpu": _cpu_model()}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 LADDER_VARIANTS = [
