@@ -270,7 +270,8 @@ def test_million_catalogs_totals_and_subproblem(gc):
 
 def test_bin_table_maps_every_entry(gc):
     """The bin table built on the device for 720 x 0.25 deg: for every entry q (c in
-    [(q - 1/2)/M - 1, (q + 1/2)/M - 1]) and 64 values of c across it, bin = B - [x > e] with
+    [(q - 1/2)/M - 1, (q + 1/2)/M - 1], holding e and 4 B) and 64 values of c across it,
+    bin = B - [x > e] with
     x = cos(theta) equals the bin of the angle of c, theta = 2 asin(c / sqrt2) (c >= 0) or
     180 - 2 asin(-c / sqrt2) degrees.  The middle entry (q = M) holds both ends of the range: its
     words nbins + 64 and nbins + 65 count as bins 0 and nbins - 1."""
@@ -291,7 +292,8 @@ def test_bin_table_maps_every_entry(gc):
     off = ((nbins + 1) * 8 + 255) // 256 * 256
     tab = ws[off: off + (2 * m + 1) * 8].cpu().numpy().view(np.uint32).reshape(-1, 2)
     e = tab[:, 0].view(np.float32).astype(np.float64)
-    b = tab[:, 1].astype(np.int64)
+    assert np.all(tab[:, 1] % 4 == 0)  # byte offsets of histogram words
+    b = tab[:, 1].astype(np.int64) // 4
     assert e[m] == 0.0 and b[m] == nbins + 65
     q = np.arange(2 * m + 1)
     frac = np.linspace(0.0, 1.0, 65)[:-1]

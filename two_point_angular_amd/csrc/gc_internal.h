@@ -70,8 +70,8 @@ struct BinParams {
 };
 
 // Bin-table core (fp32 dot, bins covering 0..180 deg): the table lives in the workspace and is
-// copied into LDS by each workgroup; entry q = {cos(edge) (fp32 bits), the bin above the edge}.
-// In LDS the bin becomes the byte address of its histogram word.
+// copied into LDS by each workgroup; entry q = {cos(edge) (fp32 bits), 4 x the bin above the
+// edge}.  In LDS the second word becomes the byte address of the bin's histogram word.
 constexpr int kLutMaxEntries = 2049;
 // The table's middle entry (c within 1/(2M) of 0) holds both the smallest angles (x near 1)
 // and the largest (x near -1).  It stores e = 0 and bin word nbins + 65, so x > 0 lands in word

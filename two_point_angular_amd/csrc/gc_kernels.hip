@@ -176,14 +176,14 @@ __device__ __forceinline__ float lut_key(float x, const BinParams &bp, float &c)
 }
 constexpr uint32_t kLutKeyBias = 0x4B000000u;  // bit pattern of 2^23
 
-// The core with the table in global memory (diagnostic kernel): entry = {e bits, B}.
+// The core with the table in global memory (diagnostic kernel): entry = {e bits, 4 B}.
 __device__ __forceinline__ void core_lut(float x, const BinParams &bp, const uint2 *tab, uint32_t &k, bool &trip,
                                          float &c_raw) {
   float c;
   const uint2 ent = tab[__float_as_uint(lut_key(x, bp, c)) - kLutKeyBias];
   const float d = __uint_as_float(ent.x) - x;
   trip = fabsf(d) < bp.lut_g;
-  k = ent.y - (__float_as_uint(d) >> 31);
+  k = (ent.y >> 2) - (__float_as_uint(d) >> 31);
   c_raw = c;
 }
 
@@ -363,7 +363,7 @@ pairs_kernel(const PairArgs A) {
     if constexpr (LUT)
       for (int q = threadIdx.x; q <= A.bp.lut_n; q += kWGThreads) {
         const uint2 e = A.lut[q];
-        tab[q] = make_uint2(e.x, hist_addr + 4u * e.y);
+        tab[q] = make_uint2(e.x, hist_addr + e.y);
       }
   } else {
     for (int b = lane; b < A.hist_words; b += kWave) hist[b] = 0u;
@@ -472,7 +472,16 @@ pairs_kernel(const PairArgs A) {
       for (int k = 0; k < K; ++k) {
         float c_unused;
         xv[k] = fmaf(ix[k], xj, fmaf(iy[k], yj, iz[k] * zj));
-        ev[k] = lut_read_lds(lut_key(xv[k], bp, c_unused), tab_bias);
+        const float key = lut_key(xv[k], bp, c_unused);
+        // A random 64-lane LDS read costs ~7 CU cycles, the same read through the vector L1
+        // ~36; the LDS also takes every pair's atomic.  Reading the table of 3 pairs in 8 from
+        // global memory (the workspace copy, L1-resident) balances the two paths.
+        if (k % 3 == 1) {
+          ev[k] = A.lut[__float_as_uint(key) - kLutKeyBias];
+          ev[k].y += hist_addr;  // (the LDS copy holds this sum; 0 when the histogram starts LDS)
+        } else {
+          ev[k] = lut_read_lds(key, tab_bias);
+        }
       }
 #pragma unroll
       for (int k = 0; k < K; ++k) {
@@ -667,9 +676,9 @@ __global__ void __launch_bounds__(256) edges_kernel(int32_t nbins, double w_deg,
 // Entry q of the bin-table core (q = 0 .. 2M): c in [(q - 1/2)/M - 1, (q + 1/2)/M - 1] (the
 // index rounds), widened by `margin` on both sides.  An edge at angle e w (e = 1 .. nbins-1) sits
 // at c = sqrt2 sin(e w / 2) when e w <= 90 deg and at c = -sqrt2 cos(e w / 2) when e w >= 90 deg
-// (both for exactly 90).  With one edge in range: {cos(e w) rounded to fp32, e (the bin above the
-// edge)}; with none: {4, the bin of the entry's middle}.  The host only selects this core when
-// no widened range can hold two edges.
+// (both for exactly 90).  With one edge in range: {cos(e w) rounded to fp32, 4 e (the byte offset
+// of the histogram word of the bin above the edge)}; with none: {4, 4 x the bin of the entry's
+// middle}.  The host only selects this core when no widened range can hold two edges.
 __device__ __forceinline__ double lut_angle_deg(double c) {  // inverse of the map above
   constexpr double kSqrtHalf = 0.70710678118654752440, kDeg = 57.295779513082320877;
   return c >= 0.0 ? 2.0 * asin(fmin(c, 1.0) * kSqrtHalf) * kDeg : 180.0 - 2.0 * asin(fmin(-c, 1.0) * kSqrtHalf) * kDeg;
@@ -714,16 +723,16 @@ __global__ void __launch_bounds__(256) lut_kernel(int32_t nbins, double w_deg, i
   uint2 ent;
   if (q == m && count == 0) {
     ent.x = __float_as_uint(0.0f);                       // the middle entry (x near +-1)
-    ent.y = static_cast<uint32_t>(nbins + kWave + 1);    // x < 0: word nbins + 65; x > 0: nbins + 64
+    ent.y = 4u * static_cast<uint32_t>(nbins + kWave + 1);  // x < 0: word nbins + 65; x > 0: nbins + 64
   } else if (count >= 1) {
     ent.x = __float_as_uint(static_cast<float>(cos(static_cast<double>(edge) * w_deg * kRad)));
-    ent.y = static_cast<uint32_t>(edge);  // the bin above the edge; the one below is edge - 1
+    ent.y = 4u * static_cast<uint32_t>(edge);  // the bin above the edge; the one below is edge - 1
   } else {
     const double mid = fmin(fmax(static_cast<double>(q) / m - 1.0, -1.0), 1.0);
     int b = static_cast<int>(floor(lut_angle_deg(mid) / w_deg));
     b = b < 0 ? 0 : (b > nbins - 1 ? nbins - 1 : b);
     ent.x = __float_as_uint(4.0f);  // e - x > 0 for every cosine: bin = B
-    ent.y = static_cast<uint32_t>(b);
+    ent.y = 4u * static_cast<uint32_t>(b);
   }
   lut[q] = ent;
 }
