@@ -200,6 +200,16 @@ gc_status gc_eval_angle_core(const float *d_x32, const double *d_x64, int64_t n,
                              float *d_t_out, void *d_workspace, size_t workspace_bytes,
                              gc_stream_t stream);
 
+/* The dot products of the bin-table core's fast steps, computed on the matrix cores exactly as
+ * the pair kernel computes them (v_mfma_f32_16x16x4f32, components x, y, z and 0), for
+ * measuring their error against the guard's assumption.  Tile t holds 16 a-vectors and 16
+ * b-vectors: d_ax[16 t + i], d_ay[...], d_az[...] and likewise for b (device, fp32, 16 ntiles
+ * each); d_out (device, 256 ntiles fp32) receives out[256 t + 16 i + j] = a_(16t+i) . b_(16t+j).
+ * Returns GC_ERR_INVALID_ARGUMENT for ntiles < 0 or a null pointer with ntiles > 0,
+ * GC_ERR_UNSUPPORTED for ntiles >= 2^31. */
+gc_status gc_eval_dot_mfma(const float *d_ax, const float *d_ay, const float *d_az, const float *d_bx,
+                           const float *d_by, const float *d_bz, int64_t ntiles, float *d_out, gc_stream_t stream);
+
 /* --------------------------------------------------------------- ceilings ----
  * Microbenchmarks of the two resources the pair kernel uses, for reading its measured
  * rate against what this GPU sustains (not part of the histogram computation).  Each

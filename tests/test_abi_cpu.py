@@ -144,6 +144,12 @@ def test_totals_omega_core_validation(lib):
     assert ev(P(A), None, 10, 720, 0.25, 32, P(A), P(A), P(A), None, None, 0, None) == INVALID  # exact, no ws
     assert ev(P(A), None, 10, 720, 0.25, 32, P(A), P(A), P(A), None, P(A), 100, None) == WORKSPACE
     assert ev(P(A), None, 10, 720, 0.25, 32, P(A), P(A), None, None, None, 0, None) == INVALID  # table, no ws
+    dm = lambda *a: lib.gc_eval_dot_mfma(*a)  # noqa: E731
+    assert dm(P(A), P(A), P(A), P(A), P(A), P(A), -1, P(A), None) == INVALID
+    assert dm(P(A), P(A), None, P(A), P(A), P(A), 4, P(A), None) == INVALID
+    assert dm(P(A), P(A), P(A), P(A), P(A), P(A), 4, None, None) == INVALID
+    assert dm(None, None, None, None, None, None, 0, None, None) == OK
+    assert dm(P(A), P(A), P(A), P(A), P(A), P(A), 1 << 31, P(A), None) == UNSUPPORTED
     n = ctypes.c_uint64(0)
     sink = lib.gc_ceiling_sink_bytes()
     assert sink == 2048 * 256 * 4

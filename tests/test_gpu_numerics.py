@@ -229,3 +229,37 @@ def test_fp64_core_error_within_model(gc, nbins, w):
     assert rel.max() <= rho
     small = acc & ~sel
     assert np.all(np.abs(t[small] - t_exact[small]) < 1e-3 * rho + 1e-6)
+
+
+def test_matrix_core_dot_within_bound(gc):
+    """The bin-table core's fast steps take the dot product from v_mfma_f32_16x16x4f32.  Its guard
+    assumes |x~ - x.y| <= 10 * 2^-24 for fp32 unit vectors x, y (five roundings of one ulp each:
+    three products and two sums, in any order and rounding mode).  Checked against the exact
+    (fp64) dot product of the same fp32 vectors: random pairs, nearly parallel and antiparallel
+    pairs, near-orthogonal pairs, and vectors along the axes."""
+    import torch
+    print("[gpu] matrix-core dot product error", flush=True)
+    rng = np.random.default_rng(77)
+    ntiles = 40000
+    n = 16 * ntiles
+
+    def unit(v):
+        return (v / np.linalg.norm(v, axis=0)).astype(np.float32)
+
+    a = unit(rng.normal(size=(3, n)))
+    b = unit(rng.normal(size=(3, n)))
+    q = n // 4
+    b[:, :q] = unit(a[:, :q].astype(np.float64) + 1e-4 * rng.normal(size=(3, q)))            # nearly parallel
+    b[:, q:2 * q] = unit(-a[:, q:2 * q].astype(np.float64) + 1e-4 * rng.normal(size=(3, q)))  # nearly antiparallel
+    ax = np.zeros((3, 16)); ax[0, 0:4] = 1; ax[1, 4:8] = 1; ax[2, 8:12] = 1; ax[:, 12:16] = 1 / np.sqrt(3)
+    a[:, -16:] = unit(ax)
+    out = gc.eval_dot_mfma(torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda()).cpu().numpy().astype(np.float64)
+    A = a.astype(np.float64).reshape(3, ntiles, 16)
+    B = b.astype(np.float64).reshape(3, ntiles, 16)
+    exact = np.einsum("ctI,ctJ->tIJ", A, B)
+    err = np.abs(out - exact) / 2.0 ** -24
+    # the tile's own pairs (i == j) hold the biased cases; every other (i, j) is a random pair
+    print(f"  max |mfma - exact| = {err.max():.3f} x 2^-24 (bound 10)", flush=True)
+    assert err.max() <= 10.0
+    diag = err[:, np.arange(16), np.arange(16)]
+    assert diag.max() <= 10.0

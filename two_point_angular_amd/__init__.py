@@ -105,6 +105,7 @@ def load():
         "gc_histogram_totals": (i32, [vp, vp, vp, i32, vp, vp]),
         "gc_omega": (i32, [vp, vp, vp, i32, i64, i64, vp, vp]),
         "gc_eval_angle_core": (i32, [vp, vp, i64, i32, ctypes.c_double, i32, vp, vp, vp, vp, vp, sz, vp]),
+        "gc_eval_dot_mfma": (i32, [vp, vp, vp, vp, vp, vp, i64, vp, vp]),
         "gc_ladder_workspace_bytes": (sz, [i64, i64]),
         "gc_ladder_histogram": (i32, [i32, i32, i32, i32, vp, vp, i64, vp, vp, i64, i32, ctypes.c_double, vp, vp,
                                       vp, vp, sz, vp]),
@@ -258,6 +259,19 @@ def eval_angle_core(x, nbins: int, bin_width_deg: float, with_exact: bool = True
                                      ws.numel() if ws is not None else 0, _stream(stream)),
            "gc_eval_angle_core")
     return bins, trip, exact, t
+
+
+def eval_dot_mfma(a, b, stream=None):
+    """The bin-table core's matrix-core dot products: a and b are (3, 16 ntiles) fp32 device
+    tensors (x, y, z rows); returns (ntiles, 16, 16) with [t, i, j] = a_(16t+i) . b_(16t+j)."""
+    torch = _torch()
+    ntiles = a.shape[1] // 16
+    a = a.contiguous()
+    b = b.contiguous()
+    out = torch.empty((ntiles, 16, 16), dtype=torch.float32, device=a.device)
+    _check(load().gc_eval_dot_mfma(_ptr(a[0]), _ptr(a[1]), _ptr(a[2]), _ptr(b[0]), _ptr(b[1]), _ptr(b[2]), ntiles,
+                                   _ptr(out), _stream(stream)), "gc_eval_dot_mfma")
+    return out
 
 
 CLI_PATH = os.path.join(_PKG, "bin", "galaxy_gc")

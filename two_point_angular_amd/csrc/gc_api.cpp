@@ -132,17 +132,22 @@ BinParams make_bins(int32_t nbins, double w_deg) {
 // sqrt2 sin(theta/2) up to 90 deg, -sqrt2 cos(theta/2) beyond), entry q = round(M (c + 1))
 // covers c in [(q - 1/2)/M - 1, (q + 1/2)/M - 1] widened by a margin, and holds the one edge in
 // that range as its cosine e (fp32); the pair's side of the edge is the sign of e - x.
-// Guard (in the cosine): |x~ - x| <= g_x (fp32 unit vectors and dot product), |e - cos| <=
-// 2^-25 (fp32 rounding of a cosine in [-1, 1]); recheck iff |e - x~| < lut_g = 1.1 (g_x +
-// 2^-25).  (The test's subtraction rounds monotonically and lut_g is an fp32 number, so a
-// computed |e - x~| >= lut_g means the exact one is too, up to the 10 % margin.)
-// Selecting the entry: |c~ - c| s~ <= g_c = 1.1 (g_x + 2^-22) (dot product, the subtraction
-// 1 - |x|, the 1-ulp square root).  The table is sound when
+// Guard (in the cosine): |x~ - x| <= g_x, |e - cos| <= 2^-25 (fp32 rounding of a cosine in
+// [-1, 1]); recheck iff |e - x~| < lut_g = 1.1 (g_x + 2^-25).  (The test's subtraction rounds
+// monotonically and lut_g is an fp32 number, so a computed |e - x~| >= lut_g means the exact one
+// is too, up to the 10 % margin.)  g_x = kLutDotErr 2^-24: the fp32 rounding of the unit vectors
+// (2 units) plus the dot product's arithmetic, taken as up to five roundings of one ulp each
+// (three products, two sums) for the matrix-core dot of the fast steps, whatever order and
+// rounding mode the instruction uses; the scalar fma chain of the other steps needs 3.
+// Selecting the entry: y = 1 - |x~| is exact for |x~| >= 1/2, so |c~ - c| s~ <= g_x + 2^-23 s~^2
+// (the dot product through sqrt, whose derivative is 1 / (2 sqrt); the 1-ulp square root);
+// g_c = 1.1 (g_x + 2^-23) (for |x~| < 1/2, s > 0.7 and the subtraction's 2^-25 fits the 10 %).
+// The table is sound when
 //  (a) no widened entry range can hold two edges: 1/M + 2 margin < the smallest gap between
 //      consecutive edges in c (M = ceil(4 / w_rad), margin = 0.45 (gap - 1/M));
-//  (b) where the error of c exceeds the margin (s < S* = g_c / margin), it cannot reach any
-//      edge: s + g_c / s < |c| of the first and last edges for s in [2^-12, S*] (2^-12 is
-//      the smallest non-zero s; the bound is convex in s, so its endpoints decide);
+//  (b) where the error of c may exceed the margin (s~ < S* = g_c / margin), no pair can reach an
+//      edge: 1 - |x| <= y + g_x <= s~^2 (1 + 2^-22) + g_x, so |c| <= sqrt(S*^2 (1 + 2^-22) + g_x)
+//      must stay below the |c| of the first and last edges;
 //  (c) the middle entry (q = M: c within 1/(2M) of 0, i.e. both the smallest angles and the
 //      largest) holds no edge: 1/(2M) + margin < |c| of the first and last edges.  It stores
 //      e = 0 and sends x > 0 to a histogram word counted as bin 0 and x < 0 to one counted as
@@ -177,11 +182,10 @@ LutPlan plan_lut(int32_t nbins, double w_deg) {
   }
   const double margin = 0.45 * (gap - 1.0 / md);
   if (!(margin > 0.0)) return p;
-  const double g_x = 5.0 * kTwoM24 * (1.0 + 1e-6) + 1e-12;
-  const double g_c = 1.1 * (g_x + 4.0 * kTwoM24);
-  const double s_min = 1.0 / 4096.0;
+  const double g_x = kLutDotErr * kTwoM24 * (1.0 + 1e-6) + 1e-12;
+  const double g_c = 1.1 * (g_x + 2.0 * kTwoM24);
   const double s_star = g_c / margin;
-  const double reach = fmax(s_min + g_c / s_min, s_star + g_c / s_star);
+  const double reach = sqrt(s_star * s_star * (1.0 + 4.0 * kTwoM24) + g_x);
   if (!(reach < 0.95 * c_edge_min)) return p;
   if (!(0.5 / md + margin < 0.95 * c_edge_min)) return p;
   p.ok = true;
@@ -637,6 +641,17 @@ gc_status gc_eval_angle_core(const float *x32, const double *x64, int64_t n, int
   if (e == hipSuccess)
     e = launch_eval_core(x32, x64, n, bp, d64, core, lut, exact_out ? edge_cos : nullptr, bin_out, trip_out,
                          exact_out, t_out, hs);
+  return e == hipSuccess ? GC_OK : device_error(e);
+}
+
+gc_status gc_eval_dot_mfma(const float *ax, const float *ay, const float *az, const float *bx, const float *by,
+                           const float *bz, int64_t ntiles, float *out, gc_stream_t stream) {
+  if (ntiles < 0) return GC_ERR_INVALID_ARGUMENT;
+  if (ntiles == 0) return GC_OK;
+  if (!ax || !ay || !az || !bx || !by || !bz || !out) return GC_ERR_INVALID_ARGUMENT;
+  if (ntiles > 0x7fffffff) return GC_ERR_UNSUPPORTED;
+  const hipError_t e =
+      launch_eval_dot_mfma(ax, ay, az, bx, by, bz, ntiles, out, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? GC_OK : device_error(e);
 }
 

@@ -78,6 +78,8 @@ constexpr int kLutMaxEntries = 2049;
 // nbins + 64 (counted as bin 0) and x < 0 in word nbins + 65 (counted as bin nbins - 1): two
 // histogram words past the 64 spare ones.
 constexpr int kLutAliasWords = 2;
+// The bin-table core's bound on |x~ - x| in units of 2^-24 (see plan_lut in gc_api.cpp).
+constexpr double kLutDotErr = 12.0;
 // Edge-table core (fp32 dot, bins covering 0..180 deg, too fine for the bin table): the cosine
 // of edge r (fp32, or NaN where the pair must be rechecked) for r = 0 .. nbins + 1, built in
 // the bin table's workspace area.  In LDS: [e_r (kEtabTableWords words) | histogram of bins
@@ -153,6 +155,8 @@ hipError_t launch_prepare(const float *ra, const float *dec, int64_t n, void *bl
 hipError_t launch_pairs(const PairArgs &a, int num_wg, bool dot64, int k, int core, hipStream_t s);
 hipError_t pairs_occupancy(bool dot64, int k, int core, size_t lds_bytes, int *blocks_per_cu);
 hipError_t launch_lut(int32_t nbins, double w_deg, int32_t m, double margin, uint2 *lut, hipStream_t s);
+hipError_t launch_eval_dot_mfma(const float *ax, const float *ay, const float *az, const float *bx, const float *by,
+                                const float *bz, int64_t ntiles, float *out, hipStream_t s);
 hipError_t launch_etab(int32_t nbins, double w_deg, double g_x, double e3, uint32_t *et, hipStream_t s);
 // accumulate: add the sums to the outputs instead of overwriting them
 hipError_t launch_merge(const unsigned long long *slots, int32_t nbins, const int32_t wg_begin[3],

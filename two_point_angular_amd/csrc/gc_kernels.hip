@@ -42,6 +42,7 @@ __device__ __forceinline__ double ld_uniform(const double *p, int64_t i) {
 }
 
 constexpr float kHalfPiF = 1.57079632679489661923f;
+typedef float float4v __attribute__((ext_vector_type(4)));  // an MFMA accumulator
 
 // P(a) with acos(a) ~= sqrt(1 - a) * P(a) on [0, 1] (Horner, fp32 FMA).
 __device__ __forceinline__ float acos_poly(float a) {
@@ -462,6 +463,21 @@ pairs_kernel(const PairArgs A) {
     }
   };
 
+  // The same for a pair whose j varies across the wave (the MFMA fast path): i_local = i - i0.
+  auto enqueue_ij = [&](bool tp, uint32_t kslot, uint32_t i_local, int64_t jl) __attribute__((always_inline)) {
+    const unsigned long long m = __ballot(tp);
+    if (m) {
+      if (tp) {
+        const uint32_t e = __builtin_amdgcn_mbcnt_hi(
+            static_cast<uint32_t>(m >> 32),
+            __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), static_cast<uint32_t>(qcount)));
+        queue[2 * e] = static_cast<uint32_t>(jl);
+        queue[2 * e + 1] = (i_local << 16) | kslot;
+      }
+      qcount += __popcll(m);
+    }
+  };
+
   auto step = [&](real xj, real yj, real zj, int64_t jg, auto generic_tag) __attribute__((always_inline)) {
     constexpr bool GENERIC = decltype(generic_tag)::value;
     if constexpr (LUT && !GENERIC) {
@@ -599,6 +615,63 @@ pairs_kernel(const PairArgs A) {
     }
   };
 
+  // Bin-table core, fast steps: the dot products on the matrix cores.  v_mfma_f32_16x16x4f32
+  // multiplies a 16 x 4 tile of i-galaxies (lane l: component l / 16 of galaxy i0 + 16 t + l % 16,
+  // component 3 = 0) by a 4 x 16 tile of j-galaxies (lane l: component l / 16 of j0 + l % 16);
+  // lane l receives the dot products of i = i0 + 16 t + 4 (l / 16) + r, r = 0..3, with
+  // j = j0 + l % 16.  The i-block of BI galaxies is BI / 16 such tiles, held as one VGPR each; a
+  // chunk of 16 j-galaxies takes one vector load per lane.  The matrix cores run beside the VALU,
+  // which keeps only the binning (9 instructions a pair instead of 12).
+  constexpr int NT = LUT ? BI / 16 : 1;
+  const int comp = lane >> 4, sub = lane & 15;
+  float at[NT];
+  auto load_tiles = [&](int64_t b) __attribute__((always_inline)) {
+    i0 = b * BI;
+    const float *src = comp == 0 ? F.ci.x : (comp == 1 ? F.ci.y : F.ci.z);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) at[t] = comp < 3 ? src[i0 + 16 * t + sub] : 0.0f;
+  };
+  // Full chunks of 16 j in [ja, jb) (fewer than 16 remain; the caller runs them the usual way).
+  auto run_fast_mfma = [&](int64_t ja, int64_t jb) __attribute__((always_inline)) {
+    const float *jsrc = comp == 0 ? F.cj.x : (comp == 1 ? F.cj.y : F.cj.z);
+    const float4v zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t j0 = ja; j0 + 16 <= jb; j0 += 16) {
+      const int64_t jl = j0 + sub;
+      const float bj = comp < 3 ? jsrc[jl] : 0.0f;
+      // each tile's product is requested one tile ahead, so its latency overlaps the binning
+      float4v dn = __builtin_amdgcn_mfma_f32_16x16x4f32(at[0], bj, zero, 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const float4v d = dn;
+        if (t + 1 < NT) dn = __builtin_amdgcn_mfma_f32_16x16x4f32(at[t + 1 < NT ? t + 1 : t], bj, zero, 0, 0, 0);
+        uint2 ev[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float c_unused;
+          const float key = lut_key(d[r], bp, c_unused);
+          // 3 pairs in 8 read the table through the vector L1, as in the scalar-j step
+          if (r == 1 || (r == 3 && (t & 1))) {
+            ev[r] = A.lut[__float_as_uint(key) - kLutKeyBias];
+            ev[r].y += hist_addr;
+          } else {
+            ev[r] = lut_read_lds(key, tab_bias);
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          bool tp;
+          const uint32_t a = lut_word_address(d[r], ev[r], bp, tp);
+          __hip_atomic_fetch_add(reinterpret_cast<lds_word_t *>(static_cast<uintptr_t>(a)), W, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_WORKGROUP);
+          enqueue_ij(tp, ((a - hist_addr) >> 2) + 1, static_cast<uint32_t>(16 * t + 4 * comp + r), jl);
+        }
+        drain_full();  // a tile adds at most 4 entries a lane
+      }
+      since_flush += 16;
+      check_flush();
+    }
+  };
+
   auto load_i_block = [&](int64_t b) __attribute__((always_inline)) {
     i0 = b * BI;
 #pragma unroll
@@ -652,8 +725,20 @@ pairs_kernel(const PairArgs A) {
     while (s < fe) {
       const int64_t nsteps = (fe - s) < (F.n_j - j) ? (fe - s) : (F.n_j - j);
       if (nsteps <= 0) break;  // unreachable for consistent step counts; keeps every wave finite
-      load_i_block(b);
-      run_fast(j, j + nsteps);
+      if constexpr (LUT) {
+        const int64_t full = nsteps & ~static_cast<int64_t>(15);
+        if (full > 0) {
+          load_tiles(b);
+          run_fast_mfma(j, j + full);
+        }
+        if (full < nsteps) {
+          load_i_block(b);
+          run_fast(j + full, j + nsteps);
+        }
+      } else {
+        load_i_block(b);
+        run_fast(j, j + nsteps);
+      }
       drain_all();
       s += nsteps;
       ++b;
@@ -876,6 +961,24 @@ __global__ void __launch_bounds__(256) eval_core_kernel(const float *x32, const 
 
 }  // namespace
 
+// ------------------------------------------------------------------------- eval dot (MFMA)
+// One wave per tile, the pair kernel's operand layout: lane l supplies component l / 16 of a-
+// and b-vector l % 16 (component 3 = 0) and receives a_(4 (l/16) + r) . b_(l % 16), r = 0..3.
+__global__ void __launch_bounds__(64) eval_dot_mfma_kernel(const float *ax, const float *ay, const float *az,
+                                                           const float *bx, const float *by, const float *bz,
+                                                           int64_t ntiles, float *out) {
+  const int64_t t = blockIdx.x;
+  if (t >= ntiles) return;
+  const int l = threadIdx.x, comp = l >> 4, sub = l & 15;
+  const int64_t v = 16 * t + sub;
+  const float a = comp == 0 ? ax[v] : (comp == 1 ? ay[v] : (comp == 2 ? az[v] : 0.0f));
+  const float b = comp == 0 ? bx[v] : (comp == 1 ? by[v] : (comp == 2 ? bz[v] : 0.0f));
+  const float4v zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  const float4v d = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, zero, 0, 0, 0);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) out[256 * t + 16 * (4 * comp + r) + sub] = d[r];
+}
+
 // ---------------------------------------------------------------------------- launchers
 hipError_t launch_prepare(const float *ra, const float *dec, int64_t n, void *blob, hipStream_t st) {
   const int64_t p = padded_count(n);
@@ -940,6 +1043,13 @@ hipError_t launch_omega(const uint64_t *dd, const uint64_t *dr, const uint64_t *
                         int64_t n_d, int64_t n_r, double *omega, hipStream_t st) {
   hipLaunchKernelGGL(omega_kernel, dim3((nbins + 255) / 256), dim3(256), 0, st, dd, dr, rr, nbins, n_d,
                      n_r, omega);
+  return hipGetLastError();
+}
+
+hipError_t launch_eval_dot_mfma(const float *ax, const float *ay, const float *az, const float *bx, const float *by,
+                                const float *bz, int64_t ntiles, float *out, hipStream_t st) {
+  hipLaunchKernelGGL(eval_dot_mfma_kernel, dim3(static_cast<unsigned>(ntiles)), dim3(64), 0, st, ax, ay, az, bx, by,
+                     bz, ntiles, out);
   return hipGetLastError();
 }
 
