@@ -7,15 +7,18 @@
 // Kernels:
 //   prepare_kernel - (alpha, delta) arcmin -> unit radius vector, fp64 math, stored
 //                    as SoA fp32 (correctly rounded) and fp64.
-//   pairs_kernel   - the hot loop.  Persistent grid; every wavefront owns a contiguous
-//                    range of "j-steps" (one j galaxy against an i-block of 64*K
+//   pairs_kernel   - the hot loop.  Persistent grid; every wavefront takes an even share of
+//                    its family's "j-steps" (one j galaxy against an i-block of 64*K
 //                    galaxies held K per lane in VGPRs).  j is wave-uniform, so it is
 //                    streamed through the scalar unit (s_load into SGPRs, used directly
-//                    as VALU operands) instead of being staged in LDS.  Per pair: dot
-//                    product, clamp, arccos core (sqrt times a fitted polynomial), bin
-//                    index, certified guard; ds_add_u32 into the wave's private LDS
-//                    histogram.  Pairs the guard cannot certify are queued in LDS and
-//                    re-binned in fp64, 64 at a time with all lanes busy.
+//                    as VALU operands) instead of being staged in LDS; the bin-table core
+//                    instead takes its dot products from the matrix cores, 16 i x 16 j at a
+//                    time.  Per pair: dot product, then one of the cores (an arccos of
+//                    sqrt times a fitted polynomial; the bin table; the edge table; the
+//                    series), bin index, certified guard; ds_add_u32 into an LDS histogram.
+//                    Pairs the guard cannot certify are queued in LDS and re-binned in fp64,
+//                    64 at a time with all lanes busy.
+//   lut_kernel, etab_kernel - build the bin table and the edge table (fp64).
 //   merge_kernel   - sums the per-workgroup 64-bit partial histograms into the outputs.
 //   totals_kernel  - per-family sums (wave-shuffle reduction) for the exact N^2 check.
 //   omega_kernel   - Landy-Szalay estimator in fp64.
@@ -307,11 +310,14 @@ __device__ __forceinline__ void drain_queue(uint32_t *hist, const uint32_t *queu
 }
 
 // CORE 0: the generic core; 1: the core specialised to the bins' span (fp32 dot, full span;
-// fp64 dot, narrow range); 2 (fp32 dot): the bin-table core on the fast steps, with a shared
-// histogram and the table in LDS (the generic steps use the full-span core).  Register budgets: K = 4 builds for six waves per SIMD
-// (<= 80 VGPRs), fp32 K = 8 for five (<= 96; its 24 fp32 i-coordinates), fp64 K = 8 for four
-// (48 VGPRs of fp64 i-coordinates).  Measured on the 100k workloads, each step up in waves
-// per SIMD outweighed the few spills it costs outside the pair loop.
+// fp64 dot, narrow range); 2: fp32 dot, the bin-table core on the fast steps (matrix-core dot
+// products, a shared histogram and the table in LDS), fp64 dot, the series core; 3 (fp32 dot):
+// the edge-table core on the fast steps (shared histogram after the table in LDS).  The generic
+// steps of cores 2 and 3 (fp32) use the full-span core.  Register budgets: K = 4 builds for six
+// waves per SIMD (<= 80 VGPRs), fp32 K = 8 for five (<= 96; its 24 fp32 i-coordinates, or the
+// 32 matrix-core tiles), fp64 K = 8 for four (48 VGPRs of fp64 i-coordinates).  Measured on
+// the 100k workloads, each step up in waves per SIMD outweighed the few spills it costs outside
+// the pair loop.
 template <int K, bool D64, int CORE>
 __global__ void __launch_bounds__(kWGThreads)
 __attribute__((amdgpu_waves_per_eu(K == 4 ? 6 : (D64 ? 4 : 5))))
