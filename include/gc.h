@@ -65,7 +65,9 @@ typedef enum {
  * (section "The problem"); precomputing per-galaxy trigonometry is the page's
  * section "L2: precomputed sin/cos", taken one step further.
  *
- *   d_ra_arcmin, d_dec_arcmin : device, n fp32 values each; must be finite
+ *   d_ra_arcmin, d_dec_arcmin : device-accessible, n fp32 values each (device
+ *                               memory, or pinned host memory mapped into the
+ *                               device, read once over the bus); must be finite
  *                               (non-finite values give unspecified bins but the
  *                               totals still hold).
  *   n                         : number of galaxies, 0 <= n <= GC_MAX_GALAXIES.
