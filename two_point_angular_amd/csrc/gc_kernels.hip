@@ -347,6 +347,13 @@ pairs_kernel(const PairArgs A) {
                                : (shared_hist ? lds + A.hist_words + tab_words + wv * QW : hist + A.hist_words);
   const uint32_t hist_addr = lds_address(hist);
   const uint32_t tab_bias = lds_address(tab) - (kLutKeyBias << 3);
+  // the global table's copy: entry q at byte (key bits << 3) - (bits of 2^23 << 3), a 32-bit offset
+  // (one shift-and-add) that the load adds to the table's address held in scalar registers
+  const char *const lut_l1 = reinterpret_cast<const char *>(A.lut);
+  auto lut_read_l1 = [&](float key) __attribute__((always_inline)) {
+    const uint32_t off = (__float_as_uint(key) << 3) - (kLutKeyBias << 3);
+    return *reinterpret_cast<const uint2 *>(lut_l1 + off);
+  };
   // edge-table core: e_r at lds + 4 r, read from the key's bits
   const uint32_t etab_base = lds_address(lds);
   const uint32_t etab_bias = etab_base - (kLutKeyBias << 2);
@@ -499,7 +506,7 @@ pairs_kernel(const PairArgs A) {
         // ~36; the LDS also takes every pair's atomic.  Reading the table of 3 pairs in 8 from
         // global memory (the workspace copy, L1-resident) balances the two paths.
         if (k % 3 == 1) {
-          ev[k] = A.lut[__float_as_uint(key) - kLutKeyBias];
+          ev[k] = lut_read_l1(key);
           ev[k].y += hist_addr;  // (the LDS copy holds this sum; 0 when the histogram starts LDS)
         } else {
           ev[k] = lut_read_lds(key, tab_bias);
@@ -657,7 +664,7 @@ pairs_kernel(const PairArgs A) {
           const float key = lut_key(d[r], bp, c_unused);
           // 3 pairs in 8 read the table through the vector L1, as in the scalar-j step
           if (r == 1 || (r == 3 && (t & 1))) {
-            ev[r] = A.lut[__float_as_uint(key) - kLutKeyBias];
+            ev[r] = lut_read_l1(key);
             ev[r].y += hist_addr;
           } else {
             ev[r] = lut_read_lds(key, tab_bias);
