@@ -176,7 +176,8 @@ gc_status gc_histogram_totals(const uint64_t *d_dd, const uint64_t *d_dr, const 
  * Landy-Szalay estimator per bin in fp64 (section "The problem"):
  *   omega = (DD - 2 DR + RR) / RR                       when n_d == n_r,
  *   omega = (DD/n_d^2 - 2 DR/(n_d n_r) + RR/n_r^2) / (RR/n_r^2)   otherwise,
- * and NaN where RR == 0 (the page's program skips such bins).
+ * and NaN where RR == 0 (the page's program skips such bins) and in every bin when
+ * n_d == 0 < n_r (the normalised DD and DR are then 0/0).
  *   d_dd, d_dr, d_rr : device, nbins uint64 each.   d_omega: device, nbins fp64, overwritten. */
 gc_status gc_omega(const uint64_t *d_dd, const uint64_t *d_dr, const uint64_t *d_rr,
                    int32_t nbins, int64_t n_d, int64_t n_r, double *d_omega, gc_stream_t stream);

@@ -89,3 +89,32 @@ def test_cli_end_to_end(gc, tmp_path, name, n, nbins, w):
     ora_om = oracle.omega(fams["DD"].hist, fams["DR"].hist, fams["RR"].hist, len(D), len(R))
     sel = present & (fams["RR"].hist >= 1000)
     assert np.all(np.abs(fom[sel] - ora_om[sel]) <= 1e-4 + 5e-7)
+
+
+@pytest.mark.parametrize("n_d,n_r", [(0, 500), (1, 1), (700, 0)])
+def test_cli_degenerate_catalogs(gc, tmp_path, n_d, n_r):
+    """Empty and one-galaxy catalogs: the sums N_a N_b still hold (zero for an empty family) and
+    the file equals the one written from the library path's histograms."""
+    import torch
+    print(f"[gpu] galaxy_gc degenerate n_d={n_d} n_r={n_r}", flush=True)
+    nbins, w = 720, 0.25
+    D, R = catalogs.WORKLOADS["clustered100k_720"].catalogs(n=1000)
+    D, R = D.subset(0, n_d), R.subset(0, n_r)
+    dp, rp, out = tmp_path / "D.txt", tmp_path / "R.txt", tmp_path / "omega.out"
+    catalogs.write_text(D, str(dp))
+    catalogs.write_text(R, str(rp))
+    r = subprocess.run([gc.CLI_PATH, str(dp), str(rp), str(out)], capture_output=True, text=True, timeout=120)
+    print(r.stdout, r.stderr, flush=True)
+    assert r.returncode == 0 and "(exact)" in r.stdout
+    assert f"DD {n_d * n_d}  DR {n_d * n_r}  RR {n_r * n_r} (exact)" in r.stdout
+    dev = "cuda"
+    pd = gc.prepare(torch.from_numpy(D.ra).to(dev), torch.from_numpy(D.dec).to(dev))
+    pr = gc.prepare(torch.from_numpy(R.ra).to(dev), torch.from_numpy(R.dec).to(dev))
+    dd, dr, rr = gc.histogram_dd_dr_rr(pd, n_d, pr, n_r, nbins, w)
+    om = gc.omega(dd, dr, rr, n_d, n_r)
+    torch.cuda.synchronize()
+    ref = tmp_path / "ref.out"
+    gc.write_omega(str(ref), *[x.cpu().numpy() for x in (dd, dr, rr)], om.cpu().numpy(), w)
+    assert out.read_bytes() == ref.read_bytes()
+    if n_r == 1:
+        assert out.read_text().split("\n")[1].split("\t")[-1].strip() == "1"  # the one RR pair, bin 0

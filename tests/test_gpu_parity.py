@@ -118,7 +118,7 @@ def test_empty_catalogs(gc):
     D = catalogs.clustered(300, 8)
     E = D.subset(0, 0)
     dd, dr, rr, tot, om = run_gpu(gc, E, D, 720, 0.25, prefill=-1)
-    assert dd.sum() == 0 and dr.sum() == 0 and int(rr.sum()) == 300 * 300
+    assert dd.sum() == 0 and dr.sum() == 0 and int(rr.sum()) == 300 * 300 and np.all(np.isnan(om))
     dd, dr, rr, tot, om = run_gpu(gc, D, E, 720, 0.25, prefill=-1)
     assert int(dd.sum()) == 300 * 300 and dr.sum() == 0 and rr.sum() == 0
     dd, dr, rr, tot, om = run_gpu(gc, E, E, 720, 0.25, prefill=-1)
