@@ -67,9 +67,10 @@ typedef enum {
  *
  *   d_ra_arcmin, d_dec_arcmin : device-accessible, n fp32 values each (device
  *                               memory, or pinned host memory mapped into the
- *                               device, read once over the bus); must be finite
- *                               (non-finite values give unspecified bins but the
- *                               totals still hold).
+ *                               device, read once over the bus); should be finite:
+ *                               a galaxy with a non-finite coordinate is placed at
+ *                               alpha = delta = 0 (its pairs' bins are meaningless,
+ *                               the totals still hold).
  *   n                         : number of galaxies, 0 <= n <= GC_MAX_GALAXIES.
  *   d_prepared                : device, gc_prepared_bytes(n) bytes, GC_ALIGNMENT-aligned;
  *                               its layout is private to the library.  May be null
@@ -196,7 +197,9 @@ gc_status gc_omega(const uint64_t *d_dd, const uint64_t *d_dr, const uint64_t *d
  *                c = copysign(sqrt(1 - |x|), x) (the bin-table core).
  *   d_workspace: at least gc_workspace_bytes(nbins) bytes, GC_ALIGNMENT-aligned; needed when
  *                d_exact_out is given or the core bins through a table (may be null otherwise).
- * The core is the one gc_histogram_dd_dr_rr would use for these bins with default tuning. */
+ * The core is the one gc_histogram_dd_dr_rr would use for these bins with default tuning.
+ * A non-finite cosine is evaluated as 1 (a pair kernel never sees one: gc_prepare's vectors
+ * are unit vectors). */
 gc_status gc_eval_angle_core(const float *d_x32, const double *d_x64, int64_t n,
                              int32_t nbins, double bin_width_deg, int32_t dot_precision,
                              int32_t *d_bin_out, uint8_t *d_trip_out, int32_t *d_exact_out,

@@ -263,3 +263,16 @@ def test_matrix_core_dot_within_bound(gc):
     assert err.max() <= 10.0
     diag = err[:, np.arange(16), np.arange(16)]
     assert diag.max() <= 10.0
+
+
+@pytest.mark.parametrize("nbins,w,dtype", [(720, 0.25, "float32"), (3600, 0.05, "float32"), (90, 1.0, "float32"),
+                                           (1500, 0.001, "float64"), (720, 0.25, "float64")])
+def test_non_finite_cosines_evaluate_as_one(gc, nbins, w, dtype):
+    """Every core evaluates a NaN or infinite cosine as the cosine 1 (bin 0), never indexing its
+    table with it."""
+    import torch
+    print(f"[gpu] non-finite cosines {nbins} x {w} {dtype}", flush=True)
+    x = torch.tensor([np.nan, np.inf, -np.inf, 1.0], dtype=getattr(torch, dtype), device="cuda")
+    b, trip, exact, _ = gc.eval_angle_core(x, nbins, w)
+    b, trip, exact = (v.cpu().numpy() for v in (b, trip, exact))
+    assert np.all(b == b[3]) and np.all(trip == trip[3]) and np.all(exact == exact[3]) and exact[3] == 0

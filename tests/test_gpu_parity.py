@@ -125,6 +125,32 @@ def test_empty_catalogs(gc):
     assert dd.sum() == 0 and dr.sum() == 0 and rr.sum() == 0 and np.all(np.isnan(om))
 
 
+@pytest.mark.parametrize("name,nbins,w", [("clustered100k_720", 720, 0.25), ("clustered100k_3600", 3600, 0.05),
+                                          ("patch100k_1500", 1500, 0.001)])
+def test_non_finite_coordinates(gc, name, nbins, w):
+    """A galaxy with a NaN or infinite coordinate is placed at (0, 0): the histograms equal those
+    of the same catalogs with that galaxy at (0, 0), and the totals hold."""
+    print(f"[gpu] non-finite coordinates {name}", flush=True)
+    D, R = catalogs.WORKLOADS[name].catalogs(n=2000)
+    D, R = D.subset(0, 2000), R.subset(0, 1700)
+    bad_d, bad_r = np.array([3, 700, 1999]), np.array([0, 5, 1000])
+    Dn, Rn = catalogs.Catalog(D.ra.copy(), D.dec.copy()), catalogs.Catalog(R.ra.copy(), R.dec.copy())
+    Dn.ra[bad_d] = [np.nan, np.inf, 1.0]
+    Dn.dec[bad_d] = [2.0, 3.0, -np.inf]
+    Rn.ra[bad_r] = [np.nan, -np.inf, np.nan]
+    Rn.dec[bad_r] = [np.nan, 0.5, 7.0]
+    Dz, Rz = catalogs.Catalog(D.ra.copy(), D.dec.copy()), catalogs.Catalog(R.ra.copy(), R.dec.copy())
+    Dz.ra[bad_d] = 0.0
+    Dz.dec[bad_d] = 0.0
+    Rz.ra[bad_r] = 0.0
+    Rz.dec[bad_r] = 0.0
+    got = run_gpu(gc, Dn, Rn, nbins, w)
+    want = run_gpu(gc, Dz, Rz, nbins, w)
+    for k in range(3):
+        assert np.array_equal(got[k], want[k])
+    assert [int(t) for t in got[3]] == [2000 * 2000, 2000 * 1700, 1700 * 1700]
+
+
 @pytest.mark.parametrize("nbins,w,modulus", [(720, 0.25, 960), (3600, 0.05, 192)])
 def test_equator_exact_bins(gc, nbins, w, modulus):
     """Galaxies on the equator: exact integer bins (no oracle involved)."""

@@ -257,8 +257,11 @@ __global__ void __launch_bounds__(256) prepare_kernel(const float *__restrict__ 
   double ux = 0.0, uy = 0.0, uz = 0.0;
   if (idx < n) {
     const double arcmin = 3.14159265358979323846 / 10800.0;
-    const double a = static_cast<double>(ra[idx]) * arcmin;
-    const double d = static_cast<double>(dec[idx]) * arcmin;
+    // A non-finite coordinate would make a NaN vector, whose cosines could index the pair
+    // kernels' tables anywhere; such a galaxy is placed at alpha = delta = 0 instead.
+    const bool ok = __builtin_isfinite(ra[idx]) && __builtin_isfinite(dec[idx]);
+    const double a = ok ? static_cast<double>(ra[idx]) * arcmin : 0.0;
+    const double d = ok ? static_cast<double>(dec[idx]) * arcmin : 0.0;
     double sa, ca, sd, cd;
     sincos(a, &sa, &ca);
     sincos(d, &sd, &cd);
@@ -943,9 +946,10 @@ __global__ void __launch_bounds__(256) eval_core_kernel(const float *x32, const 
   float t;
   if (dot64) {
     xe = x64[idx];
+    if (!__builtin_isfinite(xe)) xe = 1.0;  // (a dot product of unit vectors is finite)
     core64<CORE>(CORE == 2 ? 1.0 - xe : xe, bp, CORE == 2 ? bp.ps[2] : bp.pw[6], bp.tmax, k, trip, t);
   } else {
-    const float xf = x32[idx];
+    const float xf = __builtin_isfinite(x32[idx]) ? x32[idx] : 1.0f;  // never index a table with NaN
     xe = static_cast<double>(xf);
     if constexpr (CORE == 2) {
       core_lut(xf, bp, lut, k, trip, t);  // (fp32 dot: CORE 2 is the table)
