@@ -429,11 +429,11 @@ gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, in
   if (use_series) apply_series(a.bp, sp, nbins, w_deg);
   if (use_lut) {
     a.hist_words = (nbins + kWave + kLutAliasWords + 63) / 64 * 64;
-      apply_lut(a.bp, lp);
+    apply_lut(a.bp, lp);
   }
   if (use_etab) {
     a.hist_words = etab_hist_words(nbins);
-      apply_etab(a.bp, ep, nbins);
+    apply_etab(a.bp, ep, nbins);
   }
   uint2 *lut_dev = reinterpret_cast<uint2 *>(static_cast<char *>(workspace) + edge_table_bytes(nbins));
   a.lut = (use_lut || use_etab) ? lut_dev : nullptr;
