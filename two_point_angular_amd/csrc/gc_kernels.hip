@@ -870,11 +870,14 @@ __global__ void __launch_bounds__(256) etab_kernel(int32_t nbins, double w_deg, 
 // out_f[bin] = sum of slots of family f's workgroups (plus out_f[bin] itself when
 // accumulating).  Block: 256 threads = 4 waves over the slot list, one bin per lane; grid
 // (ceil(nbins / 64), 3).
-__global__ void __launch_bounds__(256) merge_kernel(const unsigned long long *__restrict__ slots,
-                                                    int32_t nbins, int32_t b0, int32_t b1, int32_t b2,
-                                                    int32_t e0, int32_t e1, int32_t e2, uint64_t *o0,
-                                                    uint64_t *o1, uint64_t *o2, int32_t accumulate) {
-  __shared__ unsigned long long part[4][kWave];
+// One block per 64 bins of a family: its 16 waves each sum every 16th workgroup's partial (several
+// loads in flight per wave), then wave 0 adds the 16 sums.
+__global__ void __launch_bounds__(1024) merge_kernel(const unsigned long long *__restrict__ slots,
+                                                     int32_t nbins, int32_t b0, int32_t b1, int32_t b2,
+                                                     int32_t e0, int32_t e1, int32_t e2, uint64_t *o0,
+                                                     uint64_t *o1, uint64_t *o2, int32_t accumulate) {
+  constexpr int kMergeWaves = 16;
+  __shared__ unsigned long long part[kMergeWaves][kWave];
   const int f = blockIdx.y;
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x / kWave;
@@ -882,18 +885,21 @@ __global__ void __launch_bounds__(256) merge_kernel(const unsigned long long *__
   const int gb = f == 0 ? b0 : (f == 1 ? b1 : b2);
   const int ge = f == 0 ? e0 : (f == 1 ? e1 : e2);
   unsigned long long acc = 0ull;
-  if (bin < nbins)
-    for (int gg = gb + wv; gg < ge; gg += 4) acc += slots[static_cast<size_t>(gg) * nbins + bin];
+  if (bin < nbins) {
+#pragma unroll 4
+    for (int gg = gb + wv; gg < ge; gg += kMergeWaves) acc += slots[static_cast<size_t>(gg) * nbins + bin];
+  }
   part[wv][lane] = acc;
   __syncthreads();
   if (wv == 0 && bin < nbins) {
     uint64_t *o = f == 0 ? o0 : (f == 1 ? o1 : o2);
-    const uint64_t sum = part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane];
+    uint64_t sum = 0;
+#pragma unroll
+    for (int q = 0; q < kMergeWaves; ++q) sum += part[q][lane];
     o[bin] = accumulate ? o[bin] + sum : sum;
   }
 }
 
-// ------------------------------------------------------------------------------ totals
 __global__ void __launch_bounds__(256) totals_kernel(const uint64_t *dd, const uint64_t *dr,
                                                      const uint64_t *rr, int32_t nbins,
                                                      uint64_t *totals) {
@@ -1045,7 +1051,7 @@ hipError_t launch_pairs(const PairArgs &a, int num_wg, bool dot64, int k, int co
 hipError_t launch_merge(const unsigned long long *slots, int32_t nbins, const int32_t wb[3],
                         const int32_t we[3], uint64_t *out[3], bool accumulate, hipStream_t st) {
   dim3 grid((nbins + kWave - 1) / kWave, 3);
-  hipLaunchKernelGGL(merge_kernel, grid, dim3(256), 0, st, slots, nbins, wb[0], wb[1], wb[2], we[0], we[1],
+  hipLaunchKernelGGL(merge_kernel, grid, dim3(1024), 0, st, slots, nbins, wb[0], wb[1], wb[2], we[0], we[1],
                      we[2], out[0], out[1], out[2], accumulate ? 1 : 0);
   return hipGetLastError();
 }
