@@ -420,3 +420,50 @@ def test_edge_table_tuning_invariance(gc, nbins, w, tuning):
     t = run_gpu(gc, D, R, nbins, w, tuning=gc.Tuning(**tuning))
     for x, y in zip(base[:3], t[:3]):
         np.testing.assert_array_equal(x, y)
+
+
+def test_concurrent_streams_and_threads(gc):
+    """Two host threads, each with its own stream, workspace and outputs, run whole jobs at once
+    (the launch planner's device cache is shared); every result equals the sequential one."""
+    import threading
+    import torch
+    print("[gpu] concurrent streams and threads", flush=True)
+    jobs = []
+    for name, nbins, w in [("clustered100k_720", 720, 0.25), ("patch100k_1500", 1500, 0.001),
+                           ("clustered100k_3600", 3600, 0.05)]:
+        D, R = catalogs.WORKLOADS[name].catalogs(n=3000)
+        jobs.append((D, R.subset(0, 2500), nbins, w))
+    want = [run_gpu(gc, D, R, nbins, w) for D, R, nbins, w in jobs]
+    got = [[None] * len(jobs) for _ in range(2)]
+    errors = []
+
+    def worker(t):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for q in range(3):  # several rounds, so the two threads overlap
+                    for k, (D, R, nbins, w) in enumerate(jobs):
+                        pd = gc.prepare(_dev(D.ra), _dev(D.dec))
+                        pr = gc.prepare(_dev(R.ra), _dev(R.dec))
+                        out = torch.empty((3, nbins), dtype=torch.int64, device="cuda")
+                        gc.histogram_dd_dr_rr(pd, len(D), pr, len(R), nbins, w, out=out)
+                        om = gc.omega(out[0], out[1], out[2], len(D), len(R))
+                        s.synchronize()
+                        got[t][k] = (out.cpu().numpy().view(np.uint64).copy(), om.cpu().numpy())
+        except Exception as e:  # reported by the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(2)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=120)
+    assert not errors, errors
+    for t in range(2):
+        for k in range(len(jobs)):
+            h, om = got[t][k]
+            for f in range(3):
+                assert np.array_equal(h[f], want[k][f]), (t, k, f)
+            assert np.array_equal(np.isnan(om), np.isnan(want[k][4]))
+            ok = ~np.isnan(om)
+            assert np.array_equal(om[ok], want[k][4][ok])
