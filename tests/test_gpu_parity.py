@@ -467,3 +467,75 @@ def test_concurrent_streams_and_threads(gc):
             assert np.array_equal(np.isnan(om), np.isnan(want[k][4]))
             ok = ~np.isnan(om)
             assert np.array_equal(om[ok], want[k][4][ok])
+
+
+@pytest.mark.parametrize("name,nbins,w", [("clustered100k_720", 720, 0.25), ("clustered100k_3600", 3600, 0.05),
+                                          ("patch100k_1500", 1500, 0.001)])
+def test_hip_graph_replay(gc, name, nbins, w):
+    """The whole job (prepare x2, histograms, totals, omega) captured once in a HIP graph: the
+    library makes no allocation, memset or synchronisation, so every call only enqueues kernels.
+    Each replay, with eager work and synchronisation between replays, equals the eager result,
+    also after the input buffers receive other catalogs."""
+    import torch
+    print(f"[gpu] HIP graph replay {name}", flush=True)
+    n_d, n_r = 3000, 2500
+    D, R = catalogs.WORKLOADS[name].catalogs(n=n_d)
+    R = R.subset(0, n_r)
+    D2, R2 = catalogs.WORKLOADS[name].catalogs(n=2 * n_d)
+    D2, R2 = D2.subset(n_d, 2 * n_d), R2.subset(n_d, n_d + n_r)
+    ra_d, dec_d, ra_r, dec_r = (_dev(a) for a in (D.ra, D.dec, R.ra, R.dec))
+    pd = torch.empty(gc.prepared_bytes(n_d), dtype=torch.uint8, device="cuda")
+    pr = torch.empty(gc.prepared_bytes(n_r), dtype=torch.uint8, device="cuda")
+    out = torch.empty((3, nbins), dtype=torch.int64, device="cuda")
+    ws = torch.empty(gc.workspace_bytes(nbins), dtype=torch.uint8, device="cuda")
+    tot = torch.empty(3, dtype=torch.int64, device="cuda")
+    om = torch.empty(nbins, dtype=torch.float64, device="cuda")
+
+    def job():
+        gc.prepare(ra_d, dec_d, out=pd)
+        gc.prepare(ra_r, dec_r, out=pr)
+        gc.histogram_dd_dr_rr(pd, n_d, pr, n_r, nbins, w, out=out, workspace=ws)
+        gc.histogram_totals(out[0], out[1], out[2], out=tot)
+        gc.omega(out[0], out[1], out[2], n_d, n_r, out=om)
+
+    def state():
+        torch.cuda.synchronize()
+        return out.cpu().numpy().copy(), tot.cpu().numpy().copy(), om.cpu().numpy().copy()
+
+    def same(a, b):
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+        assert np.array_equal(np.isnan(a[2]), np.isnan(b[2]))
+        ok = ~np.isnan(a[2])
+        assert np.array_equal(a[2][ok], b[2][ok])
+
+    job()  # eager, also fills the planner's device cache before capture
+    ref = state()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        job()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        job()
+    for rep in range(3):
+        out.fill_(-1)
+        tot.fill_(-1)
+        om.fill_(0.0)
+        torch.cuda.synchronize()
+        g.replay()
+        got = state()
+        same(got, ref)
+        assert [int(t) for t in got[1]] == [n_d * n_d, n_d * n_r, n_r * n_r], rep
+    # other catalogs in the same buffers: the replay follows them
+    for dst, src in zip((ra_d, dec_d, ra_r, dec_r), (D2.ra, D2.dec, R2.ra, R2.dec)):
+        dst.copy_(_dev(src))
+    job()
+    ref2 = state()
+    assert not np.array_equal(ref2[0], ref[0])
+    for rep in range(2):
+        out.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        same(state(), ref2)
