@@ -870,10 +870,9 @@ __global__ void __launch_bounds__(256) etab_kernel(int32_t nbins, double w_deg, 
 
 // ------------------------------------------------------------------------------- merge
 // out_f[bin] = sum of slots of family f's workgroups (plus out_f[bin] itself when
-// accumulating).  Block: 256 threads = 4 waves over the slot list, one bin per lane; grid
-// (ceil(nbins / 64), 3).
-// One block per 64 bins of a family: its 16 waves each sum every 16th workgroup's partial (several
-// loads in flight per wave), then wave 0 adds the 16 sums.
+// accumulating).  Grid (ceil(nbins / 64), 3): one block of 16 waves per 64 bins of a family,
+// one bin per lane; each wave sums every 16th workgroup's slot (several loads in flight), then
+// wave 0 adds the 16 sums.
 __global__ void __launch_bounds__(1024) merge_kernel(const unsigned long long *__restrict__ slots,
                                                      int32_t nbins, int32_t b0, int32_t b1, int32_t b2,
                                                      int32_t e0, int32_t e1, int32_t e2, uint64_t *o0,
@@ -902,6 +901,7 @@ __global__ void __launch_bounds__(1024) merge_kernel(const unsigned long long *_
   }
 }
 
+// ------------------------------------------------------------------------------ totals
 __global__ void __launch_bounds__(256) totals_kernel(const uint64_t *dd, const uint64_t *dr,
                                                      const uint64_t *rr, int32_t nbins,
                                                      uint64_t *totals) {
