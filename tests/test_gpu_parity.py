@@ -539,3 +539,20 @@ def test_hip_graph_replay(gc, name, nbins, w):
         torch.cuda.synchronize()
         g.replay()
         same(state(), ref2)
+
+
+def test_identical_galaxies_past_the_flush_interval(gc):
+    """2.4M copies of one galaxy: every DD pair lands in bin 0 (weight 2 off the diagonal), so a
+    shared histogram word grows at the largest possible rate and the automatic flush interval
+    (about 5.2e5 j-steps a wave between flushes) is crossed several times; DD[0] = N^2 exactly."""
+    import torch
+    n = 2_400_000
+    print(f"[gpu] {n} identical galaxies", flush=True)
+    ra = torch.full((n,), 1234.5, dtype=torch.float32, device="cuda")
+    dec = torch.full((n,), -321.25, dtype=torch.float32, device="cuda")
+    pd = gc.prepare(ra, dec)
+    dd, dr, rr = gc.histogram_dd_dr_rr(pd, n, None, 0, 720, 0.25)
+    torch.cuda.synchronize()
+    h = dd.cpu().numpy().view(np.uint64)
+    assert int(h[0]) == n * n and int(h[1:].sum()) == 0
+    assert int(dr.cpu().numpy().view(np.uint64).sum()) == 0 and int(rr.cpu().numpy().view(np.uint64).sum()) == 0

@@ -482,9 +482,11 @@ gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, in
     if (shared) occ = occ_shared;
     a.shared_hist = shared ? 1 : 0;
     // Between two flushes a bin must stay within +-2^31: each j-step adds at most 2 * 64 K
-    // per wave, and in shared mode four waves add to the same histogram.
+    // per wave, and in shared mode four waves add to the same histogram.  A wave tests the
+    // interval after every batch of j-steps (up to 16 with the matrix-core dot), so it may run
+    // 15 steps past it; the margin of 32 covers that.
     const int64_t max_inc = 2ll * kWave * k * (shared ? kWavesPerWG : 1);
-    const int64_t auto_flush = static_cast<int64_t>(0x7fffffffll / max_inc) - 8;
+    const int64_t auto_flush = static_cast<int64_t>(0x7fffffffll / max_inc) - 32;
     a.flush_interval = tu.flush_interval ? (tu.flush_interval < auto_flush ? tu.flush_interval : auto_flush)
                                          : auto_flush;
     int per_cu = tu.blocks_per_cu ? tu.blocks_per_cu : (occ < kMaxBlocksPerCU ? occ : kMaxBlocksPerCU);
