@@ -31,7 +31,7 @@ bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 struct DeviceInfo {
   bool valid = false;
   int cus = 0;
-  // occupancy per (kernel variant, lds bytes); variant = (dot64 * 4 + core) * 2 + (k == 8)
+  // occupancy per (kernel variant, lds bytes); variant = (dot64 * 5 + core) * 2 + (k == 8)
   struct Occ { size_t lds; int blocks; };
   Occ occ[16][8];
   int nocc[16] = {};
@@ -56,7 +56,7 @@ hipError_t device_info(int *cus, bool dot64, int k, int core, size_t lds, int *b
   }
   *cus = d.cus;
   if (!blocks_per_cu) return hipSuccess;
-  const int vi = ((dot64 ? 4 : 0) + core) * 2 + (k == 8 ? 1 : 0);
+  const int vi = ((dot64 ? 5 : 0) + core) * 2 + (k == 8 ? 1 : 0);  // fp32 cores 0..4, fp64 0..2
   for (int q = 0; q < d.nocc[vi]; ++q)
     if (d.occ[vi][q].lds == lds) {
       *blocks_per_cu = d.occ[vi][q].blocks;
@@ -234,7 +234,13 @@ void apply_etab(BinParams &bp, const EtabPlan &ep, int32_t nbins) {
   bp.lut_g = ep.g;
   bp.lut_n = nbins + 1;  // last entry
   bp.lut_sh = 2;         // 4-byte words
+  // h = (pi/2) / w in fp32 is an integer for every width that divides 90 degrees (0.05, 0.25, ...):
+  // then h + 2^23 is exact and fma(., -1/w, h + 2^23) rounds t~ to the key in one step
+  bp.etab_hk = (bp.h == floorf(bp.h) && bp.h < 4194304.0f) ? bp.h + 8388608.0f : 0.0f;
 }
+
+// The edge-table core's instantiation: 4 (one-fma key) when h is integral, else 3.
+int etab_core(const BinParams &bp) { return bp.etab_hk != 0.0f ? 4 : 3; }
 
 // ---- series core ---------------------------------------------------------------------------
 // fp64 dot, bins ending by about 9 deg: t = s (q0 + q1 y + q2 y^2) / w with y = 1 - x, the
@@ -418,7 +424,7 @@ gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, in
   const bool use_lut = lut_ok && tu.fast_core != 1;
   const bool use_series = series_ok && tu.fast_core != 1;
   const bool use_etab = etab_ok && tu.fast_core != 1;
-  const int core = use_etab ? 3 : ((use_lut || use_series) ? 2 : (span ? 1 : 0));
+  int core = use_etab ? 3 : ((use_lut || use_series) ? 2 : (span ? 1 : 0));
   const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
 
   PairArgs a;
@@ -434,6 +440,7 @@ gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, in
   if (use_etab) {
     a.hist_words = etab_hist_words(nbins);
     apply_etab(a.bp, ep, nbins);
+    core = etab_core(a.bp);
   }
   uint2 *lut_dev = reinterpret_cast<uint2 *>(static_cast<char *>(workspace) + edge_table_bytes(nbins));
   a.lut = (use_lut || use_etab) ? lut_dev : nullptr;
@@ -620,7 +627,7 @@ gc_status gc_eval_angle_core(const float *x32, const double *x64, int64_t n, int
   const bool use_lut = lp.ok && span;
   const bool use_series = sp.ok && span;
   const bool use_etab = !use_lut && ep.ok && span;
-  const int core = use_etab ? 3 : ((use_lut || use_series) ? 2 : (span ? 1 : 0));
+  int core = use_etab ? 3 : ((use_lut || use_series) ? 2 : (span ? 1 : 0));
   if (n == 0) return GC_OK;
   const bool need_ws = exact_out || use_lut || use_etab;
   if (need_ws && (!workspace || !aligned(workspace, GC_ALIGNMENT))) return GC_ERR_INVALID_ARGUMENT;
@@ -638,6 +645,7 @@ gc_status gc_eval_angle_core(const float *x32, const double *x64, int64_t n, int
   }
   if (e == hipSuccess && use_etab) {
     apply_etab(bp, ep, nbins);
+    core = etab_core(bp);
     e = launch_etab(nbins, w_deg, ep.g_x, ep.e3, reinterpret_cast<uint32_t *>(lut), hs);
   }
   if (e == hipSuccess)

@@ -17,7 +17,7 @@ constexpr int kWGThreads = kWave * kWavesPerWG;
 // drain point leaves fewer than 64 pending and the next appends at most 64 D: 64 (D + 1)
 // entries suffice.  (Halving the queue of K = 8 lets a fifth workgroup fit in LDS beside the
 // bin table or a 3600-bin shared histogram.)
-constexpr int drain_span(int k, int core) { return core == 3 ? 2 : (k > 4 ? k / 2 : k); }
+constexpr int drain_span(int k, int core) { return core >= 3 ? 2 : (k > 4 ? k / 2 : k); }
 constexpr int queue_words(int k, int core) { return 2 * kWave * (drain_span(k, core) + 1); }
 constexpr int kMaxWorkgroups = 2048; // partial-histogram slots held by the workspace
 constexpr int kMaxBlocksPerCU = 8;
@@ -63,6 +63,7 @@ struct BinParams {
   float lut_m;   // bin-table core: entries per unit of c (M); the table has 2 M + 1 entries
   float lut_mb;  // M + 2^23: fma(c, M, M + 2^23) holds round(M (c + 1)) in its low mantissa bits
   float lut_g;   // bin-table core guard: recheck iff |cos(edge) - x| < lut_g
+  float etab_hk; // edge-table core with an integral h: h + 2^23 (exact), so that one fma gives the key
   int32_t lut_n; // 2 M (last entry index), or 0 when the bin table is not used
   int32_t lut_sh;  // 2, log2 of the bytes per histogram word: an argument, so that the compiler
                    // keeps (sign << 2) + address as one shift-and-add
@@ -139,7 +140,7 @@ constexpr int kEtabTableWords = 4096;
 inline int32_t table_words(const PairArgs &a, bool dot64, int core) {
   if (dot64) return 0;
   if (core == 2) return 2 * (a.bp.lut_n + 1);
-  if (core == 3) return kEtabTableWords;
+  if (core >= 3) return kEtabTableWords;
   return 0;
 }
 

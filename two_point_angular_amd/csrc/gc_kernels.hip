@@ -315,8 +315,9 @@ __device__ __forceinline__ void drain_queue(uint32_t *hist, const uint32_t *queu
 // CORE 0: the generic core; 1: the core specialised to the bins' span (fp32 dot, full span;
 // fp64 dot, narrow range); 2: fp32 dot, the bin-table core on the fast steps (matrix-core dot
 // products, a shared histogram and the table in LDS), fp64 dot, the series core; 3 (fp32 dot):
-// the edge-table core on the fast steps (shared histogram after the table in LDS).  The generic
-// steps of cores 2 and 3 (fp32) use the full-span core.  Register budgets: K = 4 builds for six
+// the edge-table core on the fast steps (shared histogram after the table in LDS); 4: the same
+// with the key from one fma, for widths where h = (pi/2) / w is an integer.  The generic steps
+// of cores 2 to 4 (fp32) use the full-span core.  Register budgets: K = 4 builds for six
 // waves per SIMD (<= 80 VGPRs), fp32 K = 8 for five (<= 96; its 24 fp32 i-coordinates, or the
 // 32 matrix-core tiles), fp64 K = 8 for four (48 VGPRs of fp64 i-coordinates).  Measured on
 // the 100k workloads, each step up in waves per SIMD outweighed the few spills it costs outside
@@ -328,7 +329,8 @@ pairs_kernel(const PairArgs A) {
   typedef typename Real<D64>::T real;
   constexpr bool SPAN = CORE != 0;
   constexpr bool LUT = CORE == 2 && !D64;  // fp64 dot: CORE 2 is the series core
-  constexpr bool ETAB = CORE == 3;          // fp32 dot only
+  constexpr bool ETAB = CORE >= 3;          // fp32 dot only
+  constexpr bool EFOLD = CORE == 4;         // edge table, key in one fma (integral h)
   constexpr int BI = kWave * K;       // i-block: galaxies per wave
   constexpr int JB = D64 ? 4 : 8;     // j galaxies per scalar batch
   extern __shared__ uint32_t lds[];
@@ -367,6 +369,9 @@ pairs_kernel(const PairArgs A) {
   const uint32_t W = F.sym ? 2u : 1u;
   // the one wave-uniform constant each core needs in a VGPR, and this lane's clamp
   const float c_v = in_vgpr(D64 ? (CORE == 2 ? bp.ps[2] : bp.pw[6]) : bp.h);
+  // the one-fma edge-table key's addend, h + 2^23, in a VGPR of its own (c_v = h also serves the
+  // generic steps' arccos core)
+  const float hk_v = in_vgpr(EFOLD ? bp.etab_hk : 0.0f);
   const float tmax_v = bp.tmax + static_cast<float>(lane);
 
   unsigned long long *const slot = A.slots + static_cast<size_t>(g) * A.nbins;
@@ -533,7 +538,8 @@ pairs_kernel(const PairArgs A) {
 #pragma unroll
       for (int k = 0; k < K; ++k) {
         xv[k] = fmaf(ix[k], xj, fmaf(iy[k], yj, iz[k] * zj));
-        av[k] = (__float_as_uint(etab_key(xv[k], bp, c_v)) << 2) + etab_bias;
+        const float key = EFOLD ? etab_t(xv[k], bp, hk_v) : etab_key(xv[k], bp, c_v);
+        av[k] = (__float_as_uint(key) << 2) + etab_bias;
         ev[k] = *reinterpret_cast<__attribute__((address_space(3))) const float *>(static_cast<uintptr_t>(av[k]));
       }
 #pragma unroll
@@ -961,10 +967,11 @@ __global__ void __launch_bounds__(256) eval_core_kernel(const float *x32, const 
     xe = static_cast<double>(xf);
     if constexpr (CORE == 2) {
       core_lut(xf, bp, lut, k, trip, t);  // (fp32 dot: CORE 2 is the table)
-    } else if constexpr (CORE == 3) {
+    } else if constexpr (CORE >= 3) {
       // edge table in global memory, e_r at index r; t_out = t~ (unrounded)
       t = etab_t(xf, bp, bp.h);
-      const uint32_t r = __float_as_uint(t + 8388608.0f) - kLutKeyBias;
+      const float key = CORE == 4 ? etab_t(xf, bp, bp.etab_hk) : t + 8388608.0f;
+      const uint32_t r = __float_as_uint(key) - kLutKeyBias;
       const float d = __uint_as_float(reinterpret_cast<const uint32_t *>(lut)[r]) - xf;
       trip = !(fabsf(d) >= bp.lut_g);
       const int kb = static_cast<int>(r) - (__float_as_int(d) < 0 ? 1 : 0);
@@ -1028,6 +1035,7 @@ static const void *select_pairs(bool dot64, int k, int core) {
     if (core) return k == 4 ? pairs_fn<4, true, 1>() : pairs_fn<8, true, 1>();
     return k == 4 ? pairs_fn<4, true, 0>() : pairs_fn<8, true, 0>();
   }
+  if (core == 4) return k == 4 ? pairs_fn<4, false, 4>() : pairs_fn<8, false, 4>();
   if (core == 3) return k == 4 ? pairs_fn<4, false, 3>() : pairs_fn<8, false, 3>();
   if (core == 2) return k == 4 ? pairs_fn<4, false, 2>() : pairs_fn<8, false, 2>();
   if (core) return k == 4 ? pairs_fn<4, false, 1>() : pairs_fn<8, false, 1>();
@@ -1043,7 +1051,7 @@ hipError_t pairs_occupancy(bool dot64, int k, int core, size_t lds_bytes, int *b
 }
 
 hipError_t launch_pairs(const PairArgs &a, int num_wg, bool dot64, int k, int core, hipStream_t st) {
-  const bool table = (core == 2 || core == 3) && !dot64;
+  const bool table = core >= 2 && !dot64;
   const size_t lds = pairs_lds_bytes(a.hist_words, table || a.shared_hist != 0, k, core, table_words(a, dot64, core));
   const void *fn = select_pairs(dot64, k, core);
   void *args[] = {const_cast<PairArgs *>(&a)};
@@ -1098,7 +1106,10 @@ hipError_t launch_eval_core(const float *x32, const double *x64, int64_t n, cons
                             uint8_t *trip_out, int32_t *exact_out, float *t_out, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>((n + 255) / 256));
   const int d = dot64 ? 1 : 0;
-  if (core == 3)
+  if (core == 4)
+    hipLaunchKernelGGL(eval_core_kernel<4>, grid, dim3(256), 0, st, x32, x64, n, bp, d, lut, edge_cos, bin_out,
+                       trip_out, exact_out, t_out);
+  else if (core == 3)
     hipLaunchKernelGGL(eval_core_kernel<3>, grid, dim3(256), 0, st, x32, x64, n, bp, d, lut, edge_cos, bin_out,
                        trip_out, exact_out, t_out);
   else if (core == 2)
