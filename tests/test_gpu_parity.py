@@ -151,6 +151,31 @@ def test_non_finite_coordinates(gc, name, nbins, w):
     assert [int(t) for t in got[3]] == [2000 * 2000, 2000 * 1700, 1700 * 1700]
 
 
+@pytest.mark.parametrize("nbins,w", [(720, 0.25), (3600, 0.05), (1500, 0.001)])
+def test_poles_and_the_alpha_seam(gc, nbins, w):
+    """Galaxies exactly at the poles (every alpha names the same point), within 1.5 degrees of the
+    north pole (where alpha spreads fast), and on the seam alpha = 0 / 21600 (the same meridian):
+    edge-flow check against the oracle for the bin-table, edge-table and series cores."""
+    print(f"[gpu] poles and seam {nbins} x {w}", flush=True)
+    rng = np.random.default_rng(2024)
+    ra = rng.uniform(0.0, 21600.0, 1500)
+    dec = np.empty(1500)
+    dec[:200] = 5400.0
+    dec[200:300] = -5400.0
+    dec[300:1100] = 5400.0 - rng.uniform(0.0, 90.0, 800)
+    dec[1100:] = rng.uniform(-5400.0, 5400.0, 400)
+    ra[1100:1200] = 0.0
+    ra[1200:1300] = 21600.0
+    D = catalogs.Catalog(ra.astype(np.float32), dec.astype(np.float32))
+    R2 = catalogs.uniform_sphere(1200, 77)
+    rdec = R2.dec.copy()
+    rdec[:600] = (5400.0 - rng.uniform(0.0, 90.0, 600)).astype(np.float32)  # near the pole too
+    R = catalogs.Catalog(R2.ra.copy(), rdec)
+    dd, dr, rr, tot, om = run_gpu(gc, D, R, nbins, w)
+    assert list(tot) == [1500 * 1500, 1500 * 1200, 1200 * 1200]
+    check_against(f"poles {nbins} x {w}", (dd, dr, rr), oracle_fams(D, R, nbins, w), 1500, 1200, om, budget=1.0)
+
+
 @pytest.mark.parametrize("nbins,w,modulus", [(720, 0.25, 960), (3600, 0.05, 192)])
 def test_equator_exact_bins(gc, nbins, w, modulus):
     """Galaxies on the equator: exact integer bins (no oracle involved)."""
