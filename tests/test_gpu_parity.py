@@ -176,6 +176,22 @@ def test_poles_and_the_alpha_seam(gc, nbins, w):
     check_against(f"poles {nbins} x {w}", (dd, dr, rr), oracle_fams(D, R, nbins, w), 1500, 1200, om, budget=1.0)
 
 
+def test_alpha_outside_one_turn(gc):
+    """Right ascension is periodic: alpha anywhere in [-2, 3) turns (and negative zero) gives the
+    oracle's histograms up to the edge-flow tolerance."""
+    print("[gpu] alpha outside one turn", flush=True)
+    rng = np.random.default_rng(99)
+    D = catalogs.clustered(2000, 31)
+    R = catalogs.uniform_sphere(1700, 32)
+    Dk = catalogs.Catalog((D.ra + 21600.0 * rng.integers(-2, 3, 2000)).astype(np.float32), D.dec.copy())
+    Rk = catalogs.Catalog((R.ra - 21600.0 * rng.integers(0, 2, 1700)).astype(np.float32), R.dec.copy())
+    Dk.ra[:5] = np.float32(-0.0)
+    for nbins, w in ((720, 0.25), (3600, 0.05)):
+        dd, dr, rr, tot, om = run_gpu(gc, Dk, Rk, nbins, w)
+        check_against(f"alpha turns {nbins}", (dd, dr, rr), oracle_fams(Dk, Rk, nbins, w), 2000, 1700, om,
+                      budget=1.0)
+
+
 @pytest.mark.parametrize("nbins,w,modulus", [(720, 0.25, 960), (3600, 0.05, 192)])
 def test_equator_exact_bins(gc, nbins, w, modulus):
     """Galaxies on the equator: exact integer bins (no oracle involved)."""
