@@ -276,3 +276,25 @@ def test_flow_check_rules():
     tot = hist.copy(); tot[3] += 1
     assert not oracle.flow_check(tot, fam, 40, moved_budget=1.0).ok
     assert not oracle.flow_check(up, fam, 40, moved_budget=1e-6).ok
+
+
+def test_poles_antipodes_and_the_last_bin():
+    """Closed forms, with a width whose edges avoid every angle used (w = 0.35 deg, 515 bins up to
+    180.25 deg): two galaxies at the same pole are 0 deg apart whatever their alpha (bin 0); the
+    two poles are 180 deg apart, and so are (alpha, 0) and (alpha + 10800, 0) on the equator
+    (bin 514, the last); equator galaxies 170 deg apart fall in bin 485 (485.7); a galaxy at a
+    pole is 90 deg from every equator galaxy (bin 257, 257.1)."""
+    nbins, w = 515, 0.35
+    north = np.array([0.0, 5000.0, 12345.0], dtype=np.float32), np.full(3, 5400.0, np.float32)
+    fam = oracle.family_rows(north[0], north[1], north[0], north[1], nbins, w)
+    assert int(fam.hist[0]) == 9 and int(fam.hist.sum()) == 9
+    south = np.array([777.0], dtype=np.float32), np.array([-5400.0], dtype=np.float32)
+    fam = oracle.family_rows(north[0], north[1], south[0], south[1], nbins, w)
+    assert int(fam.hist[nbins - 1]) == 3 and int(fam.hist.sum()) == 3
+    eq_a = np.array([0.0, 600.0], dtype=np.float32), np.zeros(2, np.float32)
+    eq_b = np.array([10800.0, 11400.0], dtype=np.float32), np.zeros(2, np.float32)
+    fam = oracle.family_rows(eq_a[0], eq_a[1], eq_b[0], eq_b[1], nbins, w)
+    # (0, 10800) and (600, 11400) are antipodal; (0, 11400) and (600, 10800) are 170 deg apart
+    assert int(fam.hist[nbins - 1]) == 2 and int(fam.hist[485]) == 2 and int(fam.hist.sum()) == 4
+    fam = oracle.family_rows(north[0], north[1], eq_a[0], eq_a[1], nbins, w)
+    assert int(fam.hist[257]) == 6 and int(fam.hist.sum()) == 6
