@@ -1,0 +1,107 @@
+"""A seeded sweep of bin counts, widths and catalog shapes against the fp64 oracle.
+
+Each case draws a regime (bins covering 180 degrees, fine bins on a narrow range, bins covering
+part of the sky or reaching far past 180 degrees, widths that divide 90 degrees and widths just
+off them), sizes from 1 to 1500 galaxies (R may be empty) and catalogs (clustered, uniform or a
+2 x 2 degree patch), so that every core and launch plan the library chooses is met at shapes
+no other test fixes.  Every family must pass the edge-flow check (totals exact, every net move
+between bins explained by pairs within 1e-5 degrees of the edge)."""
+import numpy as np
+import pytest
+
+from oracle import oracle
+from two_point_angular_amd import catalogs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def gc():
+    import torch
+    import two_point_angular_amd as gcm
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gcm.load()
+    return gcm
+
+
+def draw_case(rng):
+    regime = int(rng.integers(0, 5))
+    if regime == 0:    # bins covering 180 degrees, 2 .. 8192 of them
+        nbins = int(rng.integers(2, 8193))
+        w = 180.0 / nbins * float(rng.uniform(1.0, 1.002))
+    elif regime == 1:  # fine bins on a narrow range (fp64 dot)
+        nbins = int(rng.integers(1, 8193))
+        w = float(10 ** rng.uniform(-4, -2))
+    elif regime == 2:  # part of the sky, or far past 180 degrees
+        nbins = int(rng.integers(1, 4000))
+        w = float(rng.uniform(0.01, 1.0))
+    elif regime == 3:  # widths that divide 90 degrees
+        w = float(rng.choice([0.05, 0.1, 0.125, 0.25, 0.5, 1.0, 2.0, 5.0]))
+        nbins = int(np.ceil(180 / w))
+    else:              # widths just off round values
+        w = float(rng.choice([0.05, 0.1, 0.25])) * float(1 + rng.uniform(-1e-4, 1e-4))
+        nbins = int(np.ceil(180 / w - 0.5))
+    nbins = max(1, min(nbins, 8192))
+    n_d, n_r = int(rng.integers(1, 1500)), int(rng.integers(0, 1500))
+    kind = int(rng.integers(0, 3))
+    if kind == 0:
+        D = catalogs.clustered(n_d, int(rng.integers(1, 1000)))
+        R = catalogs.uniform_sphere(max(n_r, 1), int(rng.integers(1, 1000))).subset(0, n_r)
+    elif kind == 1:
+        D = catalogs.uniform_sphere(n_d, int(rng.integers(1, 1000)))
+        R = catalogs.uniform_sphere(max(n_r, 1), int(rng.integers(1, 1000))).subset(0, n_r)
+    else:
+        D = catalogs.Catalog(rng.uniform(0, 120, n_d).astype(np.float32), rng.uniform(0, 120, n_d).astype(np.float32))
+        R = catalogs.Catalog(rng.uniform(0, 120, n_r).astype(np.float32), rng.uniform(0, 120, n_r).astype(np.float32))
+    return regime, kind, nbins, w, D, R
+
+
+def run_case(gc, nbins, w, D, R):
+    import torch
+    n_d, n_r = len(D), len(R)
+    pd = gc.prepare(torch.from_numpy(D.ra).cuda(), torch.from_numpy(D.dec).cuda())
+    pr = gc.prepare(torch.from_numpy(R.ra).cuda(), torch.from_numpy(R.dec).cuda()) if n_r else None
+    dd, dr, rr = gc.histogram_dd_dr_rr(pd, n_d, pr, n_r, nbins, w)
+    torch.cuda.synchronize()
+    h = [x.cpu().numpy().view(np.uint64).astype(np.int64) for x in (dd, dr, rr)]
+    res = oracle.histograms(D.ra, D.dec, R.ra, R.dec, nbins, w)
+    want = {"DD": n_d * n_d, "DR": n_d * n_r, "RR": n_r * n_r}
+    return [(f, oracle.flow_check(h[k], res.family(f), want[f], moved_budget=1.0))
+            for k, f in enumerate(oracle.FAMILIES)]
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_seeded_sweep(gc, seed):
+    rng = np.random.default_rng(seed)
+    for c in range(30):
+        regime, kind, nbins, w, D, R = draw_case(rng)
+        print(f"[gpu] sweep seed {seed} case {c}: regime {regime} kind {kind} nbins {nbins} w {w!r} "
+              f"n {len(D)},{len(R)}", flush=True)
+        for f, rep in run_case(gc, nbins, w, D, R):
+            assert rep.ok, f"seed {seed} case {c} (nbins {nbins}, w {w!r}) {f}: {rep.message}"
+
+
+@pytest.mark.parametrize("nbins,w,kind", [
+    (2994, 0.7881125095716911, "uniform"),    # x < 0 in the bin table's middle entry: the bin of 180 deg
+    (3991, 0.5715292422229417, "clustered"),  # an edge past 180 deg must not enter the bin table
+    (1735, 0.6798535794426259, "uniform"),
+    (800, 0.3, "clustered"),                  # 240 deg of bins, 180 / w an integer (no bin table)
+])
+def test_bins_reaching_past_180_degrees(gc, nbins, w, kind):
+    """Bins that reach far past 180 degrees: every pair still lands in the bin of its angle (the
+    largest angles in bin floor(180 / w), none past it)."""
+    print(f"[gpu] bins past 180 deg: {nbins} x {w}", flush=True)
+    base = catalogs.uniform_sphere(1000, 41) if kind == "uniform" else catalogs.clustered(1000, 43)
+    # near-antipodes and near-duplicates of the first 200 galaxies: pairs within a fraction of a
+    # degree of 0 and of 180 degrees, the bin table's middle entry
+    a, d = base.ra[:200].astype(np.float64), base.dec[:200].astype(np.float64)
+    anti_ra, anti_dec = (a + 10800.0 + 0.2) % 21600.0, -d
+    dup_ra, dup_dec = (a + 0.3) % 21600.0, d
+    D = catalogs.Catalog(np.concatenate([base.ra, anti_ra.astype(np.float32), dup_ra.astype(np.float32)]),
+                         np.concatenate([base.dec, anti_dec.astype(np.float32), dup_dec.astype(np.float32)]))
+    R0 = catalogs.uniform_sphere(900, 42)
+    R = catalogs.Catalog(np.concatenate([R0.ra, anti_ra.astype(np.float32)]),
+                         np.concatenate([R0.dec, anti_dec.astype(np.float32)]))
+    for f, rep in run_case(gc, nbins, w, D, R):
+        assert rep.ok, f"{f}: {rep.message}"

@@ -106,6 +106,10 @@ BinParams make_bins(int32_t nbins, double w_deg) {
   const double w_rad = w_deg * (kPi / 180.0);
   BinParams bp;
   bp.nbins = nbins;
+  {
+    const double b = floor(180.0 / w_deg);
+    bp.b180 = b < static_cast<double>(nbins - 1) ? static_cast<int32_t>(b) : nbins - 1;
+  }
   bp.invw = static_cast<float>(1.0 / w_rad);
   bp.h = static_cast<float>((kPi / 2.0) / w_rad);
   bp.pinvw = static_cast<float>(kPi / w_rad);

@@ -68,6 +68,7 @@ struct BinParams {
   int32_t lut_sh;  // 2, log2 of the bytes per histogram word: an argument, so that the compiler
                    // keeps (sign << 2) + address as one shift-and-add
   int32_t nbins;
+  int32_t b180;  // the bin of the angles just below 180 deg: min(nbins - 1, floor(180 / w))
 };
 
 // Bin-table core (fp32 dot, bins covering 0..180 deg): the table lives in the workspace and is
@@ -76,8 +77,10 @@ struct BinParams {
 constexpr int kLutMaxEntries = 2049;
 // The table's middle entry (c within 1/(2M) of 0) holds both the smallest angles (x near 1)
 // and the largest (x near -1).  It stores e = 0 and bin word nbins + 65, so x > 0 lands in word
-// nbins + 64 (counted as bin 0) and x < 0 in word nbins + 65 (counted as bin nbins - 1): two
-// histogram words past the 64 spare ones.
+// nbins + 64 (counted as bin 0) and x < 0 in word nbins + 65 (counted as bin b180, the bin of
+// the angles just below 180 deg, which is nbins - 1 unless the bins reach past 180 deg): two
+// histogram words past the 64 spare ones.  (The host admits the table only when no edge lies
+// within the middle entry's range, so each word stands for one bin.)
 constexpr int kLutAliasWords = 2;
 // The bin-table core's bound on |x~ - x| in units of 2^-24 (see plan_lut in gc_api.cpp).
 constexpr double kLutDotErr = 12.0;

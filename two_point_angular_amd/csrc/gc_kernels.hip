@@ -444,11 +444,10 @@ pairs_kernel(const PairArgs A) {
     }
     long long spare = static_cast<int>(atomicExch(hist + A.nbins + lane, 0u));
     if constexpr (LUT) {
-      // the middle table entry's two words: bin 0 and bin nbins - 1
+      // the middle table entry's two words: bin 0 and bin b180 (the angles just below 180 deg)
       if (lane < kLutAliasWords) {
         const long long a = static_cast<int>(atomicExch(hist + A.nbins + kWave + lane, 0u));
-        if (lane == 0 && a) atomicAdd(slot, static_cast<unsigned long long>(a));
-        if (lane == 1) spare += a;
+        if (a) atomicAdd(slot + (lane == 0 ? 0 : A.bp.b180), static_cast<unsigned long long>(a));
       }
     }
 #pragma unroll
@@ -822,6 +821,7 @@ __global__ void __launch_bounds__(256) lut_kernel(int32_t nbins, double w_deg, i
     for (int e = e0 < 1 ? 1 : e0; e <= e1 && e < nbins; ++e) {
       const double th = static_cast<double>(e) * w_deg;
       if (th < 90.0) continue;
+      if (th > 180.0) break;  // no angle reaches an edge past 180 deg (its c would wrap positive)
       const double c = -kSqrt2 * cos(0.5 * th * kRad);
       if (c >= lo && c <= hi) {
         ++count;
@@ -980,10 +980,11 @@ __global__ void __launch_bounds__(256) eval_core_kernel(const float *x32, const 
       core32<SPAN>(xf, bp, bp.h, bp.tmax, k, trip, t);
     }
   }
-  // k >= nbins: the full-span kernel's spare bins and the table's word nbins + 65, which the
-  // flush folds into bin nbins - 1; the table's word nbins + 64 is bin 0
+  // k >= nbins: the full-span kernel's spare bins, which the flush folds into bin nbins - 1;
+  // the table's words nbins + 64 and nbins + 65 are bins 0 and b180
   const uint32_t last = static_cast<uint32_t>(bp.nbins - 1);
   if (CORE == 2 && !dot64 && k == static_cast<uint32_t>(bp.nbins + kWave)) k = 0;
+  if (CORE == 2 && !dot64 && k == static_cast<uint32_t>(bp.nbins + kWave + 1)) k = static_cast<uint32_t>(bp.b180);
   k = k < last ? k : last;
   bin_out[idx] = static_cast<int32_t>(k);
   trip_out[idx] = trip ? 1 : 0;
