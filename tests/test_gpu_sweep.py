@@ -105,3 +105,48 @@ def test_bins_reaching_past_180_degrees(gc, nbins, w, kind):
                          np.concatenate([R0.dec, anti_dec.astype(np.float32)]))
     for f, rep in run_case(gc, nbins, w, D, R):
         assert rep.ok, f"{f}: {rep.message}"
+
+
+def test_seeded_sweep_tunings_and_parts(gc):
+    """The same draws under random launch-plan overrides (dot precision, galaxies per lane,
+    workgroups per CU, histogram placement, span core, fast core, flush interval), as one call
+    or as 2 to 40 additive parts.  An override the bins cannot take is refused with
+    GC_ERR_INVALID_ARGUMENT; every accepted case passes the edge-flow check."""
+    import torch
+    rng = np.random.default_rng(21)
+    accepted = 0
+    for c in range(30):
+        regime, kind, nbins, w, D, R = draw_case(rng)
+        tun = {}
+        if rng.random() < 0.7:
+            tun = dict(dot_precision=int(rng.choice([0, 32, 64])), i_per_lane=int(rng.choice([0, 4, 8])),
+                       blocks_per_cu=int(rng.choice([0, 0, 1, 2, 3])), shared_histogram=int(rng.choice([0, 1, 2])),
+                       span_kernel=int(rng.choice([0, 1, 2])), fast_core=int(rng.choice([0, 1, 2])),
+                       flush_interval=int(rng.choice([0, 0, 1, 7, 100])))
+        parts = int(rng.choice([1, 1, 1, 2, 3, 7, 40]))
+        print(f"[gpu] sweep+tuning case {c}: nbins {nbins} w {w!r} n {len(D)},{len(R)} parts {parts} {tun}",
+              flush=True)
+        n_d, n_r = len(D), len(R)
+        pd = gc.prepare(torch.from_numpy(D.ra).cuda(), torch.from_numpy(D.dec).cuda())
+        pr = gc.prepare(torch.from_numpy(R.ra).cuda(), torch.from_numpy(R.dec).cuda()) if n_r else None
+        t = gc.Tuning(**tun)
+        try:
+            if parts == 1:
+                out = torch.empty((3, nbins), dtype=torch.int64, device="cuda")
+                gc.histogram_dd_dr_rr(pd, n_d, pr, n_r, nbins, w, out=out, tuning=t)
+            else:
+                out = torch.zeros((3, nbins), dtype=torch.int64, device="cuda")
+                for p in range(parts):
+                    gc.histogram_part(pd, n_d, pr, n_r, nbins, w, p, parts, out=out, tuning=t)
+        except gc.GCError as e:
+            assert e.status == 1, e  # an override these bins cannot take
+            continue
+        accepted += 1
+        torch.cuda.synchronize()
+        h = [x.astype(np.int64) for x in out.cpu().numpy().view(np.uint64)]
+        res = oracle.histograms(D.ra, D.dec, R.ra, R.dec, nbins, w)
+        want = {"DD": n_d * n_d, "DR": n_d * n_r, "RR": n_r * n_r}
+        for k, f in enumerate(oracle.FAMILIES):
+            rep = oracle.flow_check(h[k], res.family(f), want[f], moved_budget=1.0)
+            assert rep.ok, f"case {c} (nbins {nbins}, w {w!r}, parts {parts}, {tun}) {f}: {rep.message}"
+    assert accepted >= 20
