@@ -597,3 +597,25 @@ def test_identical_galaxies_past_the_flush_interval(gc):
     h = dd.cpu().numpy().view(np.uint64)
     assert int(h[0]) == n * n and int(h[1:].sum()) == 0
     assert int(dr.cpu().numpy().view(np.uint64).sum()) == 0 and int(rr.cpu().numpy().view(np.uint64).sum()) == 0
+
+
+def test_library_loaded_before_torch(gc):
+    """A program that loads the library before it imports torch still runs on the GPU (the
+    binding imports torch first, so that the process holds one HIP runtime)."""
+    import subprocess
+    import sys
+    print("[gpu] load order", flush=True)
+    code = ("import numpy as np\n"
+            "import two_point_angular_amd as g\n"
+            "g.load()\n"
+            "import torch\n"
+            "ra = torch.tensor([0.0, 70.0], device='cuda'); dec = torch.zeros(2, device='cuda')\n"
+            "p = g.prepare(ra, dec)\n"
+            "dd, dr, rr = g.histogram_dd_dr_rr(p, 2, p, 2, 720, 0.25)\n"
+            "h = dd.cpu().numpy()\n"
+            "assert int(h[0]) == 2 and int(h[4]) == 2 and int(h.sum()) == 4, h\n"
+            "print('ok')\n")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120,
+                       cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    print(r.stdout, r.stderr[-2000:], flush=True)
+    assert r.returncode == 0 and "ok" in r.stdout

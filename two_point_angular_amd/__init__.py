@@ -91,6 +91,10 @@ def load():
         return _lib
     if not os.path.exists(_LIB_PATH):
         raise RuntimeError(f"libgc.so not built ({_LIB_PATH}); run python -m two_point_angular_amd.build")
+    # torch first: it ships its own HIP runtime, and libgc must bind to that one.  Loaded the
+    # other way round, the process holds two runtimes and libgc's calls fail with
+    # hipErrorNoDevice.
+    _torch()
     lib = ctypes.CDLL(_LIB_PATH)
     vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
     sig = {
