@@ -150,3 +150,39 @@ def test_seeded_sweep_tunings_and_parts(gc):
             rep = oracle.flow_check(h[k], res.family(f), want[f], moved_budget=1.0)
             assert rep.ok, f"case {c} (nbins {nbins}, w {w!r}, parts {parts}, {tun}) {f}: {rep.message}"
     assert accepted >= 20
+
+
+def test_seeded_core_sweep_on_exact_cosines(gc):
+    """For drawn bins and widths, the angle-to-bin core the planner picks, on fp32 and fp64
+    cosines within 64 units in the last place of 400 edge cosines and on uniform ones: a fast bin
+    the guard lets through equals the bin of the cosine's fp64 arccos, and so does the exact
+    recheck's bin, except within 1e-5 degrees of an edge (where either side is right)."""
+    import torch
+    rng = np.random.default_rng(51)
+    for c in range(30):
+        regime, kind, nbins, w, D, R = draw_case(rng)
+        print(f"[gpu] core sweep case {c}: nbins {nbins} w {w!r}", flush=True)
+        e = np.arange(1, nbins)
+        e = e[e * w < 180.0]
+        if len(e) > 400:
+            e = rng.choice(e, 400, replace=False)
+        ce = np.cos(np.radians(e * w))
+        offs = np.arange(-64, 65)
+        for dtype in (np.float32, np.float64):
+            base = ce.astype(dtype)
+            if dtype == np.float32:
+                bits = base.view(np.int32).astype(np.int64)
+                allb = (bits[:, None] + np.where(base[:, None] >= 0, offs[None, :], -offs[None, :])).ravel()
+                x = allb[(allb >= -2**31) & (allb < 2**31)].astype(np.int32).view(np.float32)
+            else:
+                x = (base[:, None] * (1 + offs[None, :] * 2.0**-50)).ravel()
+            x = np.concatenate([x, rng.uniform(-1, 1, 20000).astype(dtype), np.array([1, -1, 0], dtype=dtype)])
+            x = np.ascontiguousarray(x[np.isfinite(x) & (np.abs(x) <= 1.0)])
+            b, trip, exact, _ = gc.eval_angle_core(torch.from_numpy(x).cuda(), nbins, w)
+            torch.cuda.synchronize()
+            b, trip, exact = (v.cpu().numpy().astype(np.int64) for v in (b, trip, exact))
+            t = np.degrees(np.arccos(x.astype(np.float64))) / w
+            truth = np.minimum(np.floor(t), nbins - 1).astype(np.int64)
+            near = np.abs(t - np.round(t)) * w < 1e-5
+            assert not ((exact != truth) & ~near).any(), (c, nbins, w, np.dtype(dtype).name)
+            assert not ((trip == 0) & (b != truth) & ~near).any(), (c, nbins, w, np.dtype(dtype).name)
