@@ -141,3 +141,33 @@ def test_cli_usage_and_input_errors(lib, tmp_path):
     r = run(str(tmp_path / "bad.txt"), str(tmp_path / "bad.txt"), str(tmp_path / "o.out"))
     assert r.returncode == 1 and "bad.txt" in r.stderr
     assert not (tmp_path / "o.out").exists()
+
+
+def test_reader_matches_python_on_random_tokens(lib, tmp_path):
+    """Seeded random tokens of every shape the grammar allows (sign, integer and fraction digits
+    up to 30, exponent of either case and sign up to 3 digits, values up to fp32's range and
+    into its subnormals): each parses to Python's correctly rounded double narrowed to fp32."""
+    rng = np.random.default_rng(12)
+    toks = []
+    while len(toks) < 4000:
+        sign = rng.choice(["", "-", "+"])
+        ip = "".join(rng.choice(list("0123456789"), int(rng.integers(0, 16))))
+        fp = "".join(rng.choice(list("0123456789"), int(rng.integers(0, 16))))
+        if not ip and not fp:
+            continue
+        body = ip + ("." + fp if fp or rng.random() < 0.3 else "")
+        if body == ".":
+            continue
+        if rng.random() < 0.5:
+            body += rng.choice(["e", "E"]) + rng.choice(["", "-", "+"]) + str(int(rng.integers(0, 60)))
+        t = sign + body
+        v = float(t)
+        if abs(v) > 3.4e38:  # the reader refuses fp32 overflow
+            continue
+        toks.append(t)
+    p = tmp_path / "rand.txt"
+    p.write_text(f"{len(toks) // 2}\n" + "\n".join(f"{a} {b}" for a, b in zip(toks[0::2], toks[1::2])) + "\n")
+    ra, dec = gc.read_catalog(str(p))
+    want = expected(toks)
+    assert np.array_equal(ra.view(np.uint32), want[0::2].view(np.uint32))
+    assert np.array_equal(dec.view(np.uint32), want[1::2].view(np.uint32))
