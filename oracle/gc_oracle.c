@@ -33,7 +33,9 @@
  *
  * Near-edge bookkeeping: for each family the oracle also counts, per inner
  * edge e = 1..nbins-1, the ordered pairs whose fp64 angle lies within
- * EDGE_TOL_DEG = 1e-5 degrees below edge e (lo[e]) or at/above it (hi[e]).
+ * EDGE_TOL_DEG = 1e-5 degrees below edge e (lo[e]) or at/above it (hi[e]),
+ * "above" meaning that the oracle's bin is e or higher.  Bins narrower than the
+ * window put one pair within it of several edges; the pair is counted at each.
  * A GPU histogram may differ from the oracle only by pairs counted there.
  *
  * Symmetric mode evaluates only i <= j for a catalog against itself and
@@ -105,8 +107,12 @@ static void count_pair(const gco_galaxy *p, const gco_galaxy *q, double w_deg, i
     double theta = acos(c) * (180.0 / PI);
     int64_t b = gco_bin_index(theta, w_deg, nbins);
     hist[b] += weight;
-    if (b >= 1 && theta - (double)b * w_deg < EDGE_TOL_DEG) hi[b] += weight;
-    if (b + 1 < nbins && (double)(b + 1) * w_deg - theta <= EDGE_TOL_DEG) lo[b + 1] += weight;
+    /* Every inner edge within the window, on each side: the pair is above the edges
+     * 1..b and below b+1..nbins-1.  The distance to an edge grows as the edge moves
+     * away from the pair's own bin, so each walk stops at the first edge outside the
+     * window; with bins wider than the window each walk tests one edge. */
+    for (int64_t e = b; e >= 1 && theta - (double)e * w_deg < EDGE_TOL_DEG; --e) hi[e] += weight;
+    for (int64_t e = b + 1; e < nbins && (double)e * w_deg - theta <= EDGE_TOL_DEG; ++e) lo[e] += weight;
 }
 
 /*

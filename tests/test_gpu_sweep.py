@@ -107,6 +107,26 @@ def test_bins_reaching_past_180_degrees(gc, nbins, w, kind):
         assert rep.ok, f"{f}: {rep.message}"
 
 
+@pytest.mark.parametrize("nbins,w", [(3, 1e-7), (100, 1e-7), (8192, 1e-7), (100, 1e-6), (1, 1e-7)])
+def test_bins_narrower_than_the_parity_window(gc, nbins, w):
+    """Bins far narrower than the 1e-5 deg parity window, over near-duplicate galaxies (offsets
+    down to 1e-5 arcmin, most of them rounded to an fp32 neighbour or to the same value): the
+    fp64 angle itself cannot place such pairs (1 - cos is a few fp64 ulps), so the GPU may put
+    them in any bin within the window of their oracle angle, and the check counts each pair at
+    every edge within that window."""
+    print(f"[gpu] bins narrower than the window: {nbins} x {w}", flush=True)
+    rng = np.random.default_rng(nbins)
+    base = catalogs.uniform_sphere(800, 51)
+    ra, dec = base.ra.astype(np.float64), base.dec.astype(np.float64)
+    j = rng.integers(0, 100, 400)
+    ra[100:500] = ra[j] + rng.normal(0, 1, 400) * 10 ** rng.uniform(-5, 0, 400)
+    dec[100:500] = np.clip(dec[j] + rng.normal(0, 1, 400) * 10 ** rng.uniform(-5, 0, 400), -5400, 5400)
+    D = catalogs.Catalog(ra.astype(np.float32), dec.astype(np.float32))
+    R = catalogs.uniform_sphere(600, 52)
+    for f, rep in run_case(gc, nbins, w, D, R):
+        assert rep.ok, f"{f}: {rep.message}"
+
+
 def test_seeded_sweep_tunings_and_parts(gc):
     """The same draws under random launch-plan overrides (dot precision, galaxies per lane,
     workgroups per CU, histogram placement, span core, fast core, flush interval), as one call

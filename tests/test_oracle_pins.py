@@ -138,6 +138,32 @@ def test_equator_near_edge_counters():
     assert int(fam.lo.sum()) == 1 and int(fam.hi.sum()) == 1
 
 
+def test_near_edge_counters_with_bins_narrower_than_the_window():
+    """Bins of 4e-6 deg are narrower than the 1e-5 deg window, so one pair lies within the
+    window of several edges and is counted at each.  On the equator the distances are the
+    right-ascension offsets: 0, 2u and 8u with u = 2^-12' (2u = 8.14e-6 deg, 8u = 3.255e-5
+    deg); the nearest edge-to-window margin is 1.4e-7 deg, far above the acos rounding."""
+    u = 2.0 ** -12
+    base = 1000.0
+    ra = np.array([base, base + 2 * u, base + 8 * u], dtype=np.float32)
+    dec = np.zeros_like(ra)
+    assert float(ra[2]) - base == 8 * u
+    fam = oracle.family_rows(ra[:1], dec[:1], ra, dec, 20, 4e-6)
+    # the three distances fall in bins 0, 2 (8.14e-6 / 4e-6) and 8 (3.255e-5 / 4e-6)
+    assert {int(b): int(fam.hist[b]) for b in np.nonzero(fam.hist)[0]} == {0: 1, 2: 1, 8: 1}
+    # below the window's upper side: 0 -> edges 1, 2 (4e-6, 8e-6); 8.14e-6 -> 3, 4 (1.2e-5,
+    # 1.6e-5); 3.255e-5 -> 9, 10 (3.6e-5, 4e-5).  Edge 5 (2e-5) and 11 (4.4e-5) are 1.19e-5 and
+    # 1.15e-5 deg away: outside.
+    assert list(np.nonzero(fam.lo)[0]) == [1, 2, 3, 4, 9, 10]
+    # above: 8.14e-6 -> edges 2, 1; 3.255e-5 -> 8, 7, 6 (3.2e-5, 2.8e-5, 2.4e-5); edge 5 is
+    # 1.26e-5 deg below 3.255e-5: outside.
+    assert list(np.nonzero(fam.hi)[0]) == [1, 2, 6, 7, 8]
+    assert int(fam.lo.sum()) == 6 and int(fam.hi.sum()) == 5
+    # a distance past the last bin is clamped into it and counted at no edge 1e-5 deg away
+    fam5 = oracle.family_rows(ra[:1], dec[:1], ra[2:], dec[2:], 5, 4e-6)
+    assert int(fam5.hist[4]) == 1 and int(fam5.lo.sum()) == 0 and int(fam5.hi.sum()) == 0
+
+
 @pytest.mark.parametrize("n_d,n_r", [(0, 5), (5, 0), (1, 1), (37, 53), (200, 200)])
 def test_totals_are_exact(n_d, n_r):
     D = catalogs.clustered(max(n_d, 1), 3).subset(0, n_d)
