@@ -127,6 +127,31 @@ def test_bins_narrower_than_the_parity_window(gc, nbins, w):
         assert rep.ok, f"{f}: {rep.message}"
 
 
+def test_seeded_sweep_narrow_widths(gc):
+    """20 random widths, log-uniform over 1e-7 .. 0.03 deg, and 1 .. 8192 bins, over catalogs half
+    made of near-duplicates (offsets 1e-6 .. 1 arcmin around an eighth of the galaxies), R of 0 to
+    1200 galaxies: every family passes the edge-flow check."""
+    rng = np.random.default_rng(201)
+    for c in range(20):
+        w = float(10 ** rng.uniform(-7, -1.5))
+        nbins = int(rng.integers(1, 8193))
+        n = int(rng.integers(200, 1500))
+        seed = int(rng.integers(1, 10**6))
+        base = catalogs.uniform_sphere(n, seed) if rng.random() < 0.5 else catalogs.clustered(n, seed)
+        ra, dec = base.ra.astype(np.float64), base.dec.astype(np.float64)
+        m = n // 2
+        j = rng.integers(0, n // 8, m)
+        lo_exp = rng.uniform(-6, -2)
+        ra[n - m:] = ra[j] + rng.normal(0, 1, m) * 10 ** rng.uniform(lo_exp, 0, m)
+        dec[n - m:] = np.clip(dec[j] + rng.normal(0, 1, m) * 10 ** rng.uniform(lo_exp, 0, m), -5400, 5400)
+        D = catalogs.Catalog(ra.astype(np.float32), dec.astype(np.float32))
+        n_r = int(rng.integers(0, 1200))
+        R = catalogs.uniform_sphere(max(n_r, 1), int(rng.integers(1, 10**6))).subset(0, n_r)
+        print(f"[gpu] narrow sweep case {c}: nbins {nbins} w {w!r} n {n},{n_r}", flush=True)
+        for f, rep in run_case(gc, nbins, w, D, R):
+            assert rep.ok, f"case {c} (nbins {nbins}, w {w!r}) {f}: {rep.message}"
+
+
 def test_seeded_sweep_tunings_and_parts(gc):
     """The same draws under random launch-plan overrides (dot precision, galaxies per lane,
     workgroups per CU, histogram placement, span core, fast core, flush interval), as one call
