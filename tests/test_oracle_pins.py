@@ -164,6 +164,32 @@ def test_near_edge_counters_with_bins_narrower_than_the_window():
     assert int(fam5.hist[4]) == 1 and int(fam5.lo.sum()) == 0 and int(fam5.hi.sum()) == 0
 
 
+@pytest.mark.parametrize("w_deg,nbins", [(3e-6, 40), (2e-5, 40), (7e-6, 3), (0.25, 720)])
+def test_near_edge_counters_against_an_exhaustive_scan(w_deg, nbins):
+    """The counters stop each walk at the first edge outside the window; scanning every edge for
+    every pair (from the per-pair angles and bins) must give the same counts."""
+    rng = np.random.default_rng(int(w_deg * 1e7) + nbins)
+    ra = rng.uniform(0, 21600, 70)
+    dec = rng.uniform(-5400, 5400, 70)
+    ra[35:] = ra[:35] + rng.normal(0, 1, 35) * 10 ** rng.uniform(-4, 1.5, 35)   # near neighbours
+    dec[35:] = np.clip(dec[:35] + rng.normal(0, 1, 35) * 10 ** rng.uniform(-4, 1.5, 35), -5400, 5400)
+    ra, dec = ra.astype(np.float32), dec.astype(np.float32)
+    bins, theta = oracle.pair_bins(ra[:30], dec[:30], ra, dec, nbins, w_deg, with_theta=True)
+    bins, theta = bins.ravel(), theta.ravel()
+    lo = np.zeros(nbins, np.uint64)
+    hi = np.zeros(nbins, np.uint64)
+    for e in range(1, nbins):
+        edge = e * w_deg
+        lo[e] = np.count_nonzero((bins < e) & (edge - theta <= oracle.EDGE_TOL_DEG))
+        hi[e] = np.count_nonzero((bins >= e) & (theta - edge < oracle.EDGE_TOL_DEG))
+    fam = oracle.family_rows(ra[:30], dec[:30], ra, dec, nbins, w_deg)
+    np.testing.assert_array_equal(fam.hist, np.bincount(bins, minlength=nbins).astype(np.uint64))
+    np.testing.assert_array_equal(fam.lo, lo)
+    np.testing.assert_array_equal(fam.hi, hi)
+    if w_deg < oracle.EDGE_TOL_DEG:
+        assert int(lo.sum()) + int(hi.sum()) > 0
+
+
 @pytest.mark.parametrize("n_d,n_r", [(0, 5), (5, 0), (1, 1), (37, 53), (200, 200)])
 def test_totals_are_exact(n_d, n_r):
     D = catalogs.clustered(max(n_d, 1), 3).subset(0, n_d)
