@@ -680,6 +680,9 @@ pairs_kernel(const PairArgs A) {
             ev[r] = lut_read_lds(key, tab_bias);
           }
         }
+        // the atomics issue at raised wave priority, so one wave's LDS burst goes out while the
+        // others bin (7.93 -> 7.82 ms on the 720-bin workload)
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           bool tp;
@@ -688,6 +691,7 @@ pairs_kernel(const PairArgs A) {
                                  __HIP_MEMORY_SCOPE_WORKGROUP);
           enqueue_ij(tp, ((a - hist_addr) >> 2) + 1, static_cast<uint32_t>(16 * t + 4 * comp + r), jl);
         }
+        __builtin_amdgcn_s_setprio(0);
         drain_full();  // a tile adds at most 4 entries a lane
       }
       since_flush += 16;
