@@ -173,10 +173,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="clustered100k_720")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--all", action="store_true",
+                    help="one JSON line for each workload (10k, 100k at 720 and 3600 bins, 1M + 1M, the patch), "
+                         "each with its CPU baseline; the 1M + 1M run takes a tenth of --steps")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the VALU / LDS ceiling microbenchmarks")
     ap.add_argument("--dot", type=int, default=0, help="tuning: dot-product precision (0 auto, 32, 64)")
     ap.add_argument("--k", type=int, default=0, help="tuning: i galaxies per lane (0 auto, 4, 8)")
     ap.add_argument("--blocks-per-cu", type=int, default=0)
+    ap.add_argument("--tune", default="",
+                    help="launch-plan overrides as name=value[,name=value...] (fields of gc_tuning, include/gc.h)")
     ap.add_argument("--parts", type=int, default=1,
                     help="run each step's histogram job as this many additive parts (gc_histogram_part)")
     ap.add_argument("--ladder", action="store_true",
@@ -199,11 +204,55 @@ def main():
     import two_point_angular_amd as gc
     from two_point_angular_amd import catalogs
 
+    tuning = None
+    fields = dict(dot_precision=args.dot, i_per_lane=args.k, blocks_per_cu=args.blocks_per_cu)
+    fields.update((kv.split("=")[0], int(kv.split("=")[1])) for kv in args.tune.split(",") if kv)
+    if any(fields.values()):
+        tuning = gc.Tuning(**fields)
+    gc.load()
+    if args.all:
+        ceilings = None if args.no_ceilings else measure_ceilings(gc)
+        for name in ALL_WORKLOADS:
+            steps = max(2, args.steps // 10) if name == "clustered1m_720" else args.steps
+            line = measure(gc, catalogs.WORKLOADS[name], args, tuning, steps, args.warmup)
+            if ceilings:
+                line["ceilings"] = ceilings
+            print(json.dumps(line), flush=True)
+        return
     wl = catalogs.WORKLOADS[args.workload]
+    if args.ladder:
+        D, R = wl.catalogs()
+        dev = torch.device("cuda:0")
+        ra_d, dec_d = torch.from_numpy(D.ra).to(dev), torch.from_numpy(D.dec).to(dev)
+        ra_r, dec_r = torch.from_numpy(R.ra).to(dev), torch.from_numpy(R.dec).to(dev)
+        pd = torch.empty(gc.prepared_bytes(len(D)), dtype=torch.uint8, device=dev)
+        pr = torch.empty(gc.prepared_bytes(len(R)), dtype=torch.uint8, device=dev)
+        out = torch.empty((3, wl.nbins), dtype=torch.int64, device=dev)
+        ws = torch.empty(gc.workspace_bytes(wl.nbins), dtype=torch.uint8, device=dev)
+        run_ladder(gc, wl, D, R, ra_d, dec_d, ra_r, dec_r, pd, pr, out, ws, max(args.steps, 1), args.warmup)
+        return
+    line = measure(gc, wl, args, tuning, args.steps, args.warmup)
+    if not args.no_ceilings:
+        line["ceilings"] = measure_ceilings(gc)
+    print(json.dumps(line), flush=True)
+
+
+# The workloads of one --all run, in order: the small case, the headline, its 3600-bin and 1M + 1M
+# variants, the small-angle patch.
+ALL_WORKLOADS = ("uniform10k_720", "clustered100k_720", "clustered100k_3600", "clustered1m_720", "patch100k_1500")
+
+
+def measure(gc, wl, args, tuning, steps, warmup):
+    """One workload: the whole path (prepare D and R, histograms, totals, omega) on resident
+    inputs, `warmup` untimed steps then `steps` timed ones.  Every step's histogram call is also
+    timed with HIP events on the launch stream; the first step is the cold run (first launch of
+    the code), reported apart, and steps 2-9 give the page's median and minimum."""
+    import numpy as np
+    import torch
+
     D, R = wl.catalogs()
     n_d, n_r, nbins, w = len(D), len(R), wl.nbins, wl.bin_width_deg
     dev = torch.device("cuda:0")
-    gc.load()
     ra_d, dec_d = torch.from_numpy(D.ra).to(dev), torch.from_numpy(D.dec).to(dev)
     ra_r, dec_r = torch.from_numpy(R.ra).to(dev), torch.from_numpy(R.dec).to(dev)
     pd = torch.empty(gc.prepared_bytes(n_d), dtype=torch.uint8, device=dev)
@@ -211,19 +260,14 @@ def main():
     out = torch.empty((3, nbins), dtype=torch.int64, device=dev)
     ws = torch.empty(gc.workspace_bytes(nbins), dtype=torch.uint8, device=dev)
     om = torch.empty(nbins, dtype=torch.float64, device=dev)
-    totals = torch.empty((args.steps + args.warmup, 3), dtype=torch.int64, device=dev)
-    if args.ladder:
-        run_ladder(gc, wl, D, R, ra_d, dec_d, ra_r, dec_r, pd, pr, out, ws, max(args.steps, 1), args.warmup)
-        return
-    tuning = None
-    if args.dot or args.k or args.blocks_per_cu:
-        tuning = gc.Tuning(dot_precision=args.dot, i_per_lane=args.k, blocks_per_cu=args.blocks_per_cu)
+    totals = torch.empty((steps + warmup, 3), dtype=torch.int64, device=dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps + warmup)]
 
-    def step(idx, ev=None):
+    def step(idx):
         gc.prepare(ra_d, dec_d, out=pd)
         gc.prepare(ra_r, dec_r, out=pr)
-        if ev is not None:
-            ev[0].record()
+        evs[idx][0].record()
         if args.parts == 1:
             dd, dr, rr = gc.histogram_dd_dr_rr(pd, n_d, pr, n_r, nbins, w, out=out, workspace=ws, tuning=tuning)
         else:
@@ -231,20 +275,17 @@ def main():
             for p in range(args.parts):
                 gc.histogram_part(pd, n_d, pr, n_r, nbins, w, p, args.parts, out, workspace=ws, tuning=tuning)
             dd, dr, rr = out[0], out[1], out[2]
-        if ev is not None:
-            ev[1].record()
+        evs[idx][1].record()
         gc.histogram_totals(dd, dr, rr, out=totals[idx])
         gc.omega(dd, dr, rr, n_d, n_r, out=om)
 
-    for i in range(args.warmup):
+    torch.cuda.synchronize()
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+    for i in range(steps):
+        step(warmup + i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
@@ -259,22 +300,24 @@ def main():
     tot = totals.cpu().numpy().view(np.uint64)
     want = np.array([n_d * n_d, n_d * n_r, n_r * n_r], dtype=np.uint64)
     if not np.all(tot == want[None, :]):
-        print(f"totals mismatch: {tot[:3]} vs {want}", file=sys.stderr)
+        print(f"{wl.name}: totals mismatch: {tot[:3]} vs {want}", file=sys.stderr)
         sys.exit(1)
-    kern_ms = np.array([a.elapsed_time(b) for a, b in evs])
-    ms_per_step = elapsed * 1e3 / args.steps
+    all_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    kern_ms = all_ms[warmup:]
+    ms_per_step = elapsed * 1e3 / steps
     ordered = float(n_d * n_d + n_d * n_r + n_r * n_r)
     evaluated = float(n_d * n_r + n_d * (n_d + 1) // 2 + n_r * (n_r + 1) // 2)
     kernel_s = float(np.mean(kern_ms)) / 1e3
     achieved = evaluated * FLOPS_PER_PAIR / kernel_s / 1e12
+    runs_2_9 = all_ms[1:9]
 
     line = {
         "metric": "galaxy pairs/sec (DD+DR+RR, 100k×100k, 720 bins); % FP32 VALU peak",
         "value": ordered / (ms_per_step / 1e3),
         "unit": "pairs/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -288,33 +331,45 @@ def main():
                    "parallelism": "1 GPU", **({"parts": args.parts} if args.parts != 1 else {})},
         "kernel_ms": {"mean": float(np.mean(kern_ms)), "median": float(np.median(kern_ms)),
                       "min": float(np.min(kern_ms)),
-                      "what": "pair kernel + merge, HIP events" + (f" ({args.parts} parts)" if args.parts != 1 else "")},
+                      "what": "pair kernel + merge, HIP events over the timed steps" +
+                              (f" ({args.parts} parts)" if args.parts != 1 else "")},
+        "protocol": {"cold_ms": float(all_ms[0]),
+                     "runs_2_9_median_ms": float(np.median(runs_2_9)) if len(runs_2_9) else None,
+                     "runs_2_9_min_ms": float(np.min(runs_2_9)) if len(runs_2_9) else None,
+                     "what": "the histogram call's HIP-event time: run 1 cold (first launch in the process), "
+                             "median and minimum of runs 2-9 (warm-up steps included)"},
         "roofline": {"bound": "alu", "achieved": achieved, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / FP32_PEAK_TFLOPS, "traffic": measured_traffic(wl.name),
-                     "note": f"{FLOPS_PER_PAIR:.0f} algorithmic FP32 flops per evaluated pair"},
+                     "note": f"{FLOPS_PER_PAIR:.0f} algorithmic FP32 flops per evaluated pair; achieved over the "
+                             "mean event time of the timed steps"},
         "cpu_baseline": None,
+        "launch_plan": gc.launch_plan(n_d, n_r, nbins, w, tuning),
     }
-    if not args.no_ceilings:
-        fma = gc.ceiling_valu(0)
-        sqrt = gc.ceiling_valu(1, iters=2048)
-        fma64 = gc.ceiling_valu(2)
-        lds_spread = gc.ceiling_lds_atomic(nbins)
-        lds_same = gc.ceiling_lds_atomic(nbins, same_bin=True, iters=256)
-        line["ceilings"] = {
-            "what": "measured on this GPU in this run: 8 independent chains per lane (VALU) and "
-                    "pure ds_add_u32 streams into per-wave LDS histograms (LDS)",
-            "fp32_fma_lane_ops_per_s": fma,
-            "fp32_fma_frac_of_nominal_2p4ghz": fma / NOMINAL_LANE_OPS,
-            "fp32_sqrt_lane_ops_per_s": sqrt,
-            "fp64_fma_lane_ops_per_s": fma64,
-            "lds_atomic_lane_ops_per_s": {"spread_bins": lds_spread, "same_bin": lds_same},
-            "pair_kernel_fma_slots_per_pair": fma * kernel_s / evaluated,
-            "pair_kernel_lds_atomic_frac": (evaluated / kernel_s) / lds_spread,
-        }
     if not args.no_cpu:
-        sub_n = min(len(D), 100_000)
-        line["cpu_baseline"] = cpu_baseline(D, R, nbins, w) if sub_n else None
-    print(json.dumps(line), flush=True)
+        line["cpu_baseline"] = cpu_baseline(D, R, nbins, w)
+    return line
+
+
+def measure_ceilings(gc):
+    """This GPU's measured rates for the resources the pair kernel uses: VALU (independent fp32 and
+    fp64 FMA chains, fp32 square roots) and LDS (random ds_add_u32 into one histogram, into a
+    sixteen-column one, onto one word; random 8-byte reads) and random 8-byte reads through the
+    vector L1 (a 14.8 KiB table).  LDS and L1 rates are 64-lane instructions per second."""
+    fma = gc.ceiling_valu(0)
+    return {
+        "what": "measured in this run; LDS and L1 entries in 64-lane instructions per second and CU cycles "
+                "per instruction at 2.4 GHz",
+        "fp32_fma_lane_ops_per_s": fma,
+        "fp32_fma_frac_of_nominal_2p4ghz": fma / NOMINAL_LANE_OPS,
+        "fp32_sqrt_lane_ops_per_s": gc.ceiling_valu(1, iters=2048),
+        "fp64_fma_lane_ops_per_s": gc.ceiling_valu(2),
+        **{name: {"instr_per_s": r, "cu_cycles_per_instr": 256 * 2.4e9 / r}
+           for name, r in (("lds_atomic_random", gc.ceiling_lds("add", 11584, 1024)),
+                           ("lds_atomic_16_columns", gc.ceiling_lds("add", 11584, 1024, cols=16)),
+                           ("lds_atomic_one_word", gc.ceiling_lds_atomic(720, same_bin=True, iters=256) / 64),
+                           ("lds_read64_random", gc.ceiling_lds("read64", 3712, 256)),
+                           ("l1_read64_random", gc.ceiling_l1(3712, 256)))},
+    }
 
 
 if __name__ == "__main__":

@@ -111,7 +111,7 @@ gc_status gc_histogram_dd_dr_rr(const void *d_prepared_d, int64_t n_d,
  * The result does not depend on these fields (only speed does). */
 typedef struct {
     int32_t dot_precision;   /* 0 auto, 32: fp32 dot product, 64: fp64 dot product */
-    int32_t i_per_lane;      /* 0 auto, or 4 or 8 galaxies held per lane */
+    int32_t i_per_lane;      /* 0 auto, or 4 or 8 galaxies held per lane (2 as well for the bin table) */
     int32_t blocks_per_cu;   /* 0 auto (occupancy), else 1..8 workgroups per compute unit */
     int32_t shared_histogram; /* 0 auto; 1: one private LDS histogram per wavefront;
                                  2: one LDS histogram per workgroup, shared by its wavefronts */
@@ -121,14 +121,19 @@ typedef struct {
                                 sign handling (only valid when nbins * width <= 90 deg) */
     int32_t fast_core;       /* 0 auto; 1: never use a fast core (the degree-6 arccos
                                 cores bin every pair); 2: always - the bin table (fp32 dot,
-                                bins covering 180 deg at widths where the table is sound,
-                                about >= 0.22 deg), else the edge table (fp32 dot, bins
-                                covering 180 deg, width >= ~0.02 deg, up to ~3800 bins),
-                                both with one histogram shared per workgroup; or the series
-                                (fp64 dot, bins ending by about 9 deg); invalid where none
+                                bins covering 180 deg, width >= ~0.032 deg; one histogram
+                                shared per workgroup of up to 16 wavefronts) or the series
+                                (fp64 dot, bins ending by about 9 deg); invalid where neither
                                 applies */
     int64_t flush_interval;  /* 0 auto; else j-steps between flushes of the 32-bit LDS
                                 histograms into 64-bit totals (>= 1) */
+    int32_t hist_columns;    /* bin-table core: 0 auto; 1 or 16 LDS histogram columns (16: one
+                                word per bin for each lane mod 16, so an atomic's 16-lane group
+                                never shares a bank; invalid where it does not fit in LDS) */
+    int32_t waves_per_group; /* bin-table core: 0 auto, else 4..16 wavefronts per workgroup */
+    int32_t l1_share;        /* bin-table core: 0 auto; share of table reads made through the
+                                vector L1 instead of LDS: 1 none, 2 a quarter, 3 three eighths */
+    int32_t reserved_;       /* must be 0 */
 } gc_tuning;
 
 gc_status gc_histogram_dd_dr_rr_tuned(const void *d_prepared_d, int64_t n_d,
@@ -183,58 +188,10 @@ gc_status gc_histogram_totals(const uint64_t *d_dd, const uint64_t *d_dr, const 
 gc_status gc_omega(const uint64_t *d_dd, const uint64_t *d_dr, const uint64_t *d_rr,
                    int32_t nbins, int64_t n_d, int64_t n_r, double *d_omega, gc_stream_t stream);
 
-/* ------------------------------------------------------------ diagnostics ----
- * Evaluate the pair kernel's per-pair angle-to-bin core on given cosines, exactly as
- * the pair kernel does, for numerical verification of its guard.
- *   dot_precision 32: reads d_x32 (n fp32 cosines); 64: reads d_x64 (n fp64 cosines).
- *   d_bin_out  : device, n int32: the fast-path bin.
- *   d_trip_out : device, n uint8: 1 where the guard sends the pair to the exact recheck.
- *   d_exact_out: device, n int32, or null: the exact recheck's bin of the same cosine
- *                (fp32 cosines are widened exactly), found from the fast-path bin by the
- *                kernel's own edge-cosine search.
- *   d_t_out    : device, n fp32, or null: the fast path's coordinate before binning, for
- *                measuring the core's error: theta / width (arccos cores), or
- *                c = copysign(sqrt(1 - |x|), x) (the bin-table core).
- *   d_workspace: at least gc_workspace_bytes(nbins) bytes, GC_ALIGNMENT-aligned; needed when
- *                d_exact_out is given or the core bins through a table (may be null otherwise).
- * The core is the one gc_histogram_dd_dr_rr would use for these bins with default tuning.
- * A non-finite cosine is evaluated as 1 (a pair kernel never sees one: gc_prepare's vectors
- * are unit vectors). */
-gc_status gc_eval_angle_core(const float *d_x32, const double *d_x64, int64_t n,
-                             int32_t nbins, double bin_width_deg, int32_t dot_precision,
-                             int32_t *d_bin_out, uint8_t *d_trip_out, int32_t *d_exact_out,
-                             float *d_t_out, void *d_workspace, size_t workspace_bytes,
-                             gc_stream_t stream);
-
-/* The dot products of the bin-table core's fast steps, computed on the matrix cores exactly as
- * the pair kernel computes them (v_mfma_f32_16x16x4f32, components x, y, z and 0), for
- * measuring their error against the guard's assumption.  Tile t holds 16 a-vectors and 16
- * b-vectors: d_ax[16 t + i], d_ay[...], d_az[...] and likewise for b (device, fp32, 16 ntiles
- * each); d_out (device, 256 ntiles fp32) receives out[256 t + 16 i + j] = a_(16t+i) . b_(16t+j).
- * Returns GC_ERR_INVALID_ARGUMENT for ntiles < 0 or a null pointer with ntiles > 0,
- * GC_ERR_UNSUPPORTED for ntiles >= 2^31. */
-gc_status gc_eval_dot_mfma(const float *d_ax, const float *d_ay, const float *d_az, const float *d_bx,
-                           const float *d_by, const float *d_bz, int64_t ntiles, float *d_out, gc_stream_t stream);
-
-/* --------------------------------------------------------------- ceilings ----
- * Microbenchmarks of the two resources the pair kernel uses, for reading its measured
- * rate against what this GPU sustains (not part of the histogram computation).  Each
- * launches 2048 workgroups of 256 threads on `stream`; the caller times the launch (HIP
- * events on the same stream) and divides *ops_out / *atomics_out by the time.
- *   gc_ceiling_valu: kind 0 = fp32 FMA, 1 = fp32 square root, 2 = fp64 FMA; 8 independent
- *     chains per lane, `iters` iterations; *ops_out = lane operations executed.
- *   gc_ceiling_lds_atomic: every lane adds 1 to its wavefront's private LDS histogram of
- *     nbins words, 16 x iters times, at 16 pseudo-random bins (same_bin = 0) or always bin 0;
- *     *atomics_out = lane atomics executed.
- *   d_sink: device scratch of gc_ceiling_sink_bytes() bytes (results are discarded).
- *   ops_out, atomics_out: host pointers. */
-size_t gc_ceiling_sink_bytes(void);
-gc_status gc_ceiling_valu(int32_t kind, int64_t iters, void *d_sink, size_t sink_bytes,
-                          uint64_t *ops_out, gc_stream_t stream);
-gc_status gc_ceiling_lds_atomic(int32_t nbins, int32_t same_bin, int64_t iters, void *d_sink,
-                                size_t sink_bytes, uint64_t *atomics_out, gc_stream_t stream);
-
-/* ----------------------------------------------------------------- status ---- */
+/* ----------------------------------------------------------------- status ----
+ * The kernels' diagnostics (the angle-to-bin core on given cosines, the matrix-core dot
+ * products) and the measured ceilings of the resources the pair kernel uses are declared in
+ * gc_diag.h; they are not part of the histogram computation. */
 const char *gc_status_string(gc_status status);
 int gc_last_device_error(void); /* last hipError_t seen by this thread (0 if none) */
 const char *gc_version(void);

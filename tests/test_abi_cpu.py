@@ -33,7 +33,7 @@ def header_functions(path):
 
 
 def test_exports_every_declared_function(lib):
-    assert [os.path.basename(h) for h in HEADERS] == ["gc.h", "gc_io.h", "gc_ladder.h"]
+    assert [os.path.basename(h) for h in HEADERS] == ["gc.h", "gc_diag.h", "gc_io.h", "gc_ladder.h"]
     names = [n for h in HEADERS for n in header_functions(h)]
     assert len(names) >= 16
     for name in names:
@@ -48,8 +48,8 @@ def test_sizes(lib):
     assert lib.gc_prepared_bytes(10**5) % gc.ALIGNMENT == 0
     assert lib.gc_workspace_bytes(0) == 0
     assert lib.gc_workspace_bytes(gc.MAX_BINS + 1) == 0
-    # edge cosines, the bin table (2049 8-byte entries), 2048 per-workgroup partial histograms
-    assert lib.gc_workspace_bytes(720) == 2048 * 720 * 8 + (721 * 8 + 255) // 256 * 256 + (2049 * 8 + 255) // 256 * 256
+    # edge cosines, the bin table (up to 14337 8-byte entries), 2048 per-workgroup partial histograms
+    assert lib.gc_workspace_bytes(720) == 2048 * 720 * 8 + (721 * 8 + 255) // 256 * 256 + (14337 * 8 + 255) // 256 * 256
 
 
 def test_status_strings(lib):
@@ -100,21 +100,29 @@ def test_histogram_validation(lib):
     assert _hist(lib, ws=None) == INVALID
     assert _hist(lib, ws=P(A + 128)) == INVALID
     assert _hist(lib, wsb=gc.workspace_bytes(720) - 1) == WORKSPACE
-    T = gc._Tuning  # dot, K, blocks/CU, shared histogram, span kernel, fast core, flush interval
+    # dot, K, blocks/CU, shared histogram, span kernel, fast core, flush interval, histogram columns,
+    # waves per workgroup, L1 share, reserved
+    T = gc._Tuning
     for bad in (T(33, 0, 0, 0, 0, 0, 0), T(0, 5, 0, 0, 0, 0, 0), T(0, 0, 9, 0, 0, 0, 0),
                 T(0, 0, -1, 0, 0, 0, 0), T(0, 0, 0, 3, 0, 0, 0), T(0, 0, 0, -1, 0, 0, 0),
-                T(0, 0, 0, 0, 3, 0, 0), T(0, 0, 0, 0, 0, 3, 0), T(0, 0, 0, 0, 0, -1, 0), T(0, 0, 0, 0, 0, 0, -3),
+                T(0, 0, 0, 0, 3, 0, 0), T(0, 0, 0, 0, 0, 4, 0), T(0, 0, 0, 0, 0, -1, 0), T(0, 0, 0, 0, 0, 0, -3),
+                T(0, 0, 0, 0, 0, 0, 0, 2), T(0, 0, 0, 0, 0, 0, 0, 8), T(0, 0, 0, 0, 0, 0, 0, 0, 3),
+                T(0, 0, 0, 0, 0, 0, 0, 0, 17), T(0, 0, 0, 0, 0, 0, 0, 0, 0, 4), T(0, 0, 0, 0, 0, 0, 0, 0, 0, -1),
+                T(0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 1),
                 T(64, 0, 0, 0, 2, 0, 0)):                      # fp64 narrow core: 180 deg > 90 deg
         assert _hist(lib, tuning=bad) == INVALID
+    # sixteen histogram columns of 3600 bins (230 KiB) do not fit in LDS
+    assert _hist(lib, nbins=3600, w=0.05, tuning=T(0, 0, 0, 0, 0, 0, 0, 16)) == INVALID
+    assert _hist(lib, nbins=720, tuning=T(0, 0, 0, 0, 0, 3, 0)) == INVALID         # no fast core 3
+    assert _hist(lib, nbins=1500, w=0.001, tuning=T(32, 2, 0, 0, 0, 0, 0)) == INVALID  # K = 2: bin table only
     assert _hist(lib, nbins=700, tuning=T(0, 0, 0, 0, 2, 0, 0)) == INVALID  # 700 x 0.25 < 180 deg
     assert _hist(lib, nbins=361, tuning=T(64, 0, 0, 0, 2, 0, 0)) == INVALID  # 361 x 0.25 > 90 deg
     assert _hist(lib, nbins=1500, w=0.001, tuning=T(32, 0, 0, 0, 2, 0, 0)) == INVALID  # 1.5 < 180 deg
-    # fast cores: the bin table (fp32 dot, full span, a sound table, a shared histogram), the edge
-    # table (fp32 dot, full span, bins of >= ~0.02 deg whose table fits in LDS beside the
-    # histogram) or the series (fp64 dot, bins ending by ~9 deg)
+    # fast cores: the bin table (fp32 dot, full span, a table of at most 14337 entries: widths of
+    # >= ~0.032 deg, a shared histogram) or the series (fp64 dot, bins ending by ~9 deg)
     assert _hist(lib, tuning=T(64, 0, 0, 0, 0, 2, 0)) == INVALID                      # 180 deg, fp64
     assert _hist(lib, nbins=100, w=0.1, tuning=T(64, 0, 0, 0, 0, 2, 0)) == INVALID     # 10 deg: series too short
-    assert _hist(lib, nbins=8192, w=0.022, tuning=T(0, 0, 0, 0, 0, 2, 0)) == INVALID  # edge table too big
+    assert _hist(lib, nbins=8192, w=0.022, tuning=T(0, 0, 0, 0, 0, 2, 0)) == INVALID  # both tables too big
     assert _hist(lib, nbins=700, tuning=T(0, 0, 0, 0, 0, 2, 0)) == INVALID            # not full span
     assert _hist(lib, tuning=T(0, 0, 0, 1, 0, 2, 0)) == INVALID                       # private histograms
     assert _hist(lib, tuning=T(0, 0, 0, 0, 1, 2, 0)) == INVALID                       # generic core
@@ -152,13 +160,27 @@ def test_totals_omega_core_validation(lib):
     assert dm(P(A), P(A), P(A), P(A), P(A), P(A), 1 << 31, P(A), None) == UNSUPPORTED
     n = ctypes.c_uint64(0)
     sink = lib.gc_ceiling_sink_bytes()
-    assert sink == 2048 * 256 * 4
+    assert sink == 2048 * 1024 * 4
     assert lib.gc_ceiling_valu(3, 10, P(A), sink, ctypes.byref(n), None) == INVALID
     assert lib.gc_ceiling_valu(0, 0, P(A), sink, ctypes.byref(n), None) == INVALID
     assert lib.gc_ceiling_valu(0, 10, P(A), sink - 1, ctypes.byref(n), None) == WORKSPACE
     assert lib.gc_ceiling_lds_atomic(0, 0, 10, P(A), sink, ctypes.byref(n), None) == INVALID
     assert lib.gc_ceiling_lds_atomic(gc.MAX_BINS + 1, 0, 10, P(A), sink, ctypes.byref(n), None) == INVALID
     assert lib.gc_ceiling_lds_atomic(720, 0, 10, None, sink, ctypes.byref(n), None) == INVALID
+    # LDS probes: kind, words, threads, sparse, cols, iters
+    lds = lambda *a: lib.gc_ceiling_lds(*a, P(A), sink, ctypes.byref(n), None)  # noqa: E731
+    assert lds(8, 1024, 256, 1, 0, 10) == INVALID          # no such kind
+    assert lds(0, 1000, 256, 1, 0, 10) == INVALID          # words not a multiple of 128
+    assert lds(0, 1024, 128, 1, 0, 10) == INVALID          # threads
+    assert lds(7, 1024, 256, 0, 0, 10) == INVALID          # sparse < 1
+    assert lds(0, 1024, 256, 1, 3, 10) == INVALID          # columns not a power of two
+    assert lds(0, 1024, 256, 1, 128, 10) == INVALID        # more columns than lanes
+    assert lds(0, 1024, 256, 1, 0, 0) == INVALID           # iters
+    assert lds(6, 40960, 256, 1, 0, 10) == UNSUPPORTED     # 160 KiB + the 4 KiB histogram
+    assert lib.gc_ceiling_lds(0, 1024, 256, 1, 0, 10, P(A), sink - 1, ctypes.byref(n), None) == WORKSPACE
+    assert lib.gc_ceiling_l1(1000, 256, 10, P(A), sink, ctypes.byref(n), None) == INVALID
+    assert lib.gc_ceiling_l1(1024, 256, 0, P(A), sink, ctypes.byref(n), None) == INVALID
+    assert lib.gc_ceiling_l1(1024, 256, 10, P(A), sink, ctypes.byref(n), None) == WORKSPACE  # table + sink
 
 
 def test_ladder_validation(lib):

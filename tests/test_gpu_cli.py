@@ -80,7 +80,7 @@ def test_cli_end_to_end(gc, tmp_path, name, n, nbins, w):
     fams = {f: res.family(f) for f in oracle.FAMILIES}
     want = {"DD": len(D) ** 2, "DR": len(D) * len(R), "RR": len(R) ** 2}
     for k, f in enumerate(oracle.FAMILIES):
-        rep = oracle.flow_check(h[k].astype(np.int64), fams[f], want[f], moved_budget=1.0)
+        rep = oracle.flow_check(h[k].astype(np.int64), fams[f], want[f])
         assert rep.ok, f"{f}: {rep.message}"
     fh, fom, present = parse_result(str(out), nbins, w)
     assert np.array_equal(present, h[2] > 0)

@@ -14,6 +14,10 @@ import pytest
 pytestmark = pytest.mark.gpu
 
 G32 = 5.0 * 2.0 ** -24 * (1 + 1e-6) + 1e-12
+# The bin-table core's fast steps take x~ from the matrix cores (v_mfma_f32_16x16x4f32), whose
+# rounding is undocumented; its guard assumes |x~ - x| <= 12 * 2^-24 (five one-ulp roundings plus
+# the fp32 rounding of both unit vectors), so its soundness is checked at that radius too.
+G_LUT = 12.0 * 2.0 ** -24 * (1 + 1e-6) + 1e-12
 G64 = 1e-14
 # The exact recheck compares the fp64 cosine with fp64 edge cosines cos(e w).  Rounding
 # cos(e w) to fp64 moves the edge by at most 2^-54 / sin(e w) rad (1.8e-10 deg at the first
@@ -66,26 +70,15 @@ def check_sound(x_exact_in, b, trip, nbins, w, g):
 
 
 # (nbins, width): 720 x 0.25 deg bins through the bin table; 1440 x 0.125 and 3600 x 0.05 deg
-# through the edge table (too narrow for the bin table), and 3601 x 0.0499972 deg, where the
-# edges fall off the round angles; 1500 x 0.001 deg through the clamped arccos core.
+# through the bin table with always-recheck entries near 0 and 180 deg, and 3601 x 0.0499972 deg,
+# where the edges fall off the round angles; 1500 x 0.001 deg through the clamped arccos core.
 FP32_CASES = [(720, 0.25), (1440, 0.125), (3600, 0.05), (3601, 0.0499972), (1500, 0.001)]
 
 
 def uses_table(nbins, w):
-    return nbins * w >= 180 and w >= 0.25
-
-
-def etab_e3():
-    """The edge-table core's arccos error bound (rad): 1.25 (CORE_ERR + 2^-24 pi/2)."""
-    return 1.25 * (_header_constant("GC_ACOS3_CORE_ERR") + 2.0 ** -24 * np.pi / 2)
-
-
-def uses_etab(nbins, w):
-    """Full span, too fine for the bin table, arccos error <= a quarter bin, and the table region
-    (4096 words), the histogram and four queues of 384 words within 40 KB of LDS."""
-    hist_words = (nbins + 1 + 64 + 63) // 64 * 64
-    return ((nbins + 0.5) * w >= 180 and not uses_table(nbins, w) and etab_e3() / np.radians(w) <= 0.25
-            and nbins + 2 <= 4096 and (4096 + hist_words + 4 * 384) * 4 <= 40960)
+    """The bin table serves fp32 bins covering 180 deg whose table (2 ceil(4 / w_rad) + 1 entries)
+    fits its 14337-entry limit: widths down to about 0.032 deg."""
+    return (nbins + 0.5) * w >= 180 and 2 * np.ceil(4 / np.radians(w)) + 1 <= 14337
 
 
 @pytest.mark.parametrize("nbins,w", FP32_CASES)
@@ -100,6 +93,9 @@ def test_fp32_core_sound_near_edges(gc, nbins, w):
     xd = x.astype(np.float64)
     assert b.min() >= 0 and b.max() <= nbins - 1
     check_sound(xd, b, trip, nbins, w, G32)
+    if uses_table(nbins, w):
+        # every cosine within 4096 ulps of an edge (>= 4096 * 2^-25, far past 12 * 2^-24) is in x
+        check_sound(xd, b, trip, nbins, w, G_LUT)
     tb, t = true_bins(xd, nbins, w)
     near = np.abs(t - np.round(t)) * w < NEAR_DEG
     assert np.all((exact == tb) | near)
@@ -168,8 +164,7 @@ def test_fp32_core_error_within_model(gc, nbins, w):
     """The fp32 core's coordinate against its exact value for the same fp32 cosine, over every
     64th fp32 value in [-1, 1].  Arccos cores: the guard assumes |t~ - t| <= C(t) with
     C(t) = E_core / w + 2^-24 (t + 2h) (core error with a 1-ulp square root, plus the roundings
-    that form t); the edge table's degree-3 arccos the same with its own E_core (its table
-    assumes it when it names the edge to compare with).  Bin-table core: c = copysign(sqrt(1 - |x|), x), and the guard assumes
+    that form t).  Bin-table core: c = copysign(sqrt(1 - |x|), x), and the guard assumes
     |c~ - c| s~ <= 1.5 * 2^-23 for the core's own roundings (subtraction, 1-ulp square root)."""
     print(f"[gpu] fp32 core error model nbins={nbins}", flush=True)
     pos = np.arange(0, np.float32(1.0).view(np.uint32) + 1, 64, dtype=np.uint32).view(np.float32)
@@ -188,9 +183,6 @@ def test_fp32_core_error_within_model(gc, nbins, w):
     t_exact = np.arccos(x.astype(np.float64)) / w_rad
     err = np.abs(t - t_exact)
     e_core = (_header_constant("GC_ACOS_CORE_ERR") + 2.0 ** -24 * (np.pi / 2)) * 1.25
-    if uses_etab(nbins, w):
-        # the edge table's degree-3 arccos: its own bound, checked the same way
-        e_core = etab_e3()
     h = (np.pi / 2) / w_rad
     bound = e_core / w_rad + 2.0 ** -24 * (t_exact + 2 * h) * 1.01
     ratio = err / bound

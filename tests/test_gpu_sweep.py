@@ -5,7 +5,9 @@ part of the sky or reaching far past 180 degrees, widths that divide 90 degrees 
 off them), sizes from 1 to 1500 galaxies (R may be empty) and catalogs (clustered, uniform or a
 2 x 2 degree patch), so that every core and launch plan the library chooses is met at shapes
 no other test fixes.  Every family must pass the edge-flow check (totals exact, every net move
-between bins explained by pairs within 1e-5 degrees of the edge)."""
+between bins explained by pairs within 1e-5 degrees of the edge, at most 1e-6 N_a N_b moved pairs).
+Only the two tests of bins narrower than the window, over near-duplicate galaxies, waive the
+moved-pair budget, for the reason their docstrings give."""
 import numpy as np
 import pytest
 
@@ -57,7 +59,10 @@ def draw_case(rng):
     return regime, kind, nbins, w, D, R
 
 
-def run_case(gc, nbins, w, D, R):
+MOVED_BUDGET = 1e-6
+
+
+def run_case(gc, nbins, w, D, R, budget=MOVED_BUDGET):
     import torch
     n_d, n_r = len(D), len(R)
     pd = gc.prepare(torch.from_numpy(D.ra).cuda(), torch.from_numpy(D.dec).cuda())
@@ -67,7 +72,7 @@ def run_case(gc, nbins, w, D, R):
     h = [x.cpu().numpy().view(np.uint64).astype(np.int64) for x in (dd, dr, rr)]
     res = oracle.histograms(D.ra, D.dec, R.ra, R.dec, nbins, w)
     want = {"DD": n_d * n_d, "DR": n_d * n_r, "RR": n_r * n_r}
-    return [(f, oracle.flow_check(h[k], res.family(f), want[f], moved_budget=1.0))
+    return [(f, oracle.flow_check(h[k], res.family(f), want[f], moved_budget=budget))
             for k, f in enumerate(oracle.FAMILIES)]
 
 
@@ -113,7 +118,10 @@ def test_bins_narrower_than_the_parity_window(gc, nbins, w):
     down to 1e-5 arcmin, most of them rounded to an fp32 neighbour or to the same value): the
     fp64 angle itself cannot place such pairs (1 - cos is a few fp64 ulps), so the GPU may put
     them in any bin within the window of their oracle angle, and the check counts each pair at
-    every edge within that window."""
+    every edge within that window.  For the same reason the 1e-6 N_a N_b budget on moved pairs is
+    waived here: the fp64 angle of a near-duplicate pair is itself uncertain by more than a bin, so
+    how many of them land across an edge is not fixed by the definition (every move must still be
+    explained by pairs within 1e-5 deg of that edge)."""
     print(f"[gpu] bins narrower than the window: {nbins} x {w}", flush=True)
     rng = np.random.default_rng(nbins)
     base = catalogs.uniform_sphere(800, 51)
@@ -123,14 +131,17 @@ def test_bins_narrower_than_the_parity_window(gc, nbins, w):
     dec[100:500] = np.clip(dec[j] + rng.normal(0, 1, 400) * 10 ** rng.uniform(-5, 0, 400), -5400, 5400)
     D = catalogs.Catalog(ra.astype(np.float32), dec.astype(np.float32))
     R = catalogs.uniform_sphere(600, 52)
-    for f, rep in run_case(gc, nbins, w, D, R):
+    for f, rep in run_case(gc, nbins, w, D, R, budget=1.0):
         assert rep.ok, f"{f}: {rep.message}"
 
 
 def test_seeded_sweep_narrow_widths(gc):
     """20 random widths, log-uniform over 1e-7 .. 0.03 deg, and 1 .. 8192 bins, over catalogs half
     made of near-duplicates (offsets 1e-6 .. 1 arcmin around an eighth of the galaxies), R of 0 to
-    1200 galaxies: every family passes the edge-flow check."""
+    1200 galaxies: every family passes the edge-flow check.  The moved-pair budget is waived as in
+    the test above: half of each catalog is near-duplicates, whose fp64 angles are uncertain by
+    more than the narrowest bins (the check still requires every move to lie within 1e-5 deg of
+    its edge)."""
     rng = np.random.default_rng(201)
     for c in range(20):
         w = float(10 ** rng.uniform(-7, -1.5))
@@ -148,13 +159,14 @@ def test_seeded_sweep_narrow_widths(gc):
         n_r = int(rng.integers(0, 1200))
         R = catalogs.uniform_sphere(max(n_r, 1), int(rng.integers(1, 10**6))).subset(0, n_r)
         print(f"[gpu] narrow sweep case {c}: nbins {nbins} w {w!r} n {n},{n_r}", flush=True)
-        for f, rep in run_case(gc, nbins, w, D, R):
+        for f, rep in run_case(gc, nbins, w, D, R, budget=1.0):
             assert rep.ok, f"case {c} (nbins {nbins}, w {w!r}) {f}: {rep.message}"
 
 
 def test_seeded_sweep_tunings_and_parts(gc):
     """The same draws under random launch-plan overrides (dot precision, galaxies per lane,
-    workgroups per CU, histogram placement, span core, fast core, flush interval), as one call
+    workgroups per CU, histogram placement, span core, fast core, flush interval, and the bin
+    table's histogram columns, workgroup size and L1 share), as one call
     or as 2 to 40 additive parts.  An override the bins cannot take is refused with
     GC_ERR_INVALID_ARGUMENT; every accepted case passes the edge-flow check."""
     import torch
@@ -164,10 +176,12 @@ def test_seeded_sweep_tunings_and_parts(gc):
         regime, kind, nbins, w, D, R = draw_case(rng)
         tun = {}
         if rng.random() < 0.7:
-            tun = dict(dot_precision=int(rng.choice([0, 32, 64])), i_per_lane=int(rng.choice([0, 4, 8])),
+            tun = dict(dot_precision=int(rng.choice([0, 32, 64])), i_per_lane=int(rng.choice([0, 2, 4, 8])),
                        blocks_per_cu=int(rng.choice([0, 0, 1, 2, 3])), shared_histogram=int(rng.choice([0, 1, 2])),
                        span_kernel=int(rng.choice([0, 1, 2])), fast_core=int(rng.choice([0, 1, 2])),
-                       flush_interval=int(rng.choice([0, 0, 1, 7, 100])))
+                       flush_interval=int(rng.choice([0, 0, 1, 7, 100])),
+                       hist_columns=int(rng.choice([0, 0, 1, 16])), waves_per_group=int(rng.choice([0, 0, 4, 8, 16])),
+                       l1_share=int(rng.choice([0, 1, 2, 3])))
         parts = int(rng.choice([1, 1, 1, 2, 3, 7, 40]))
         print(f"[gpu] sweep+tuning case {c}: nbins {nbins} w {w!r} n {len(D)},{len(R)} parts {parts} {tun}",
               flush=True)
@@ -192,7 +206,7 @@ def test_seeded_sweep_tunings_and_parts(gc):
         res = oracle.histograms(D.ra, D.dec, R.ra, R.dec, nbins, w)
         want = {"DD": n_d * n_d, "DR": n_d * n_r, "RR": n_r * n_r}
         for k, f in enumerate(oracle.FAMILIES):
-            rep = oracle.flow_check(h[k], res.family(f), want[f], moved_budget=1.0)
+            rep = oracle.flow_check(h[k], res.family(f), want[f], moved_budget=MOVED_BUDGET)
             assert rep.ok, f"case {c} (nbins {nbins}, w {w!r}, parts {parts}, {tun}) {f}: {rep.message}"
     assert accepted >= 20
 

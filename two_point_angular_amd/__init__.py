@@ -57,7 +57,16 @@ class _Tuning(ctypes.Structure):
     _fields_ = [("dot_precision", ctypes.c_int32), ("i_per_lane", ctypes.c_int32),
                 ("blocks_per_cu", ctypes.c_int32), ("shared_histogram", ctypes.c_int32),
                 ("span_kernel", ctypes.c_int32), ("fast_core", ctypes.c_int32),
-                ("flush_interval", ctypes.c_int64)]
+                ("flush_interval", ctypes.c_int64), ("hist_columns", ctypes.c_int32),
+                ("waves_per_group", ctypes.c_int32), ("l1_share", ctypes.c_int32),
+                ("reserved_", ctypes.c_int32)]
+
+
+class _Plan(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("core", "dot_precision", "i_per_lane", "hist_columns", "waves_per_group",
+                                              "l1_share", "shared_histogram", "blocks_per_cu", "workgroups",
+                                              "lds_bytes")] + \
+               [("flush_interval", ctypes.c_int64), ("always_recheck", ctypes.c_int32), ("reserved_", ctypes.c_int32)]
 
 
 @dataclass
@@ -71,10 +80,14 @@ class Tuning:
     shared_histogram: int = 0
     span_kernel: int = 0
     fast_core: int = 0
+    hist_columns: int = 0
+    waves_per_group: int = 0
+    l1_share: int = 0
 
     def _c(self) -> _Tuning:
         return _Tuning(self.dot_precision, self.i_per_lane, self.blocks_per_cu, self.shared_histogram,
-                       self.span_kernel, self.fast_core, self.flush_interval)
+                       self.span_kernel, self.fast_core, self.flush_interval, self.hist_columns,
+                       self.waves_per_group, self.l1_share, 0)
 
 
 _lib = None
@@ -119,6 +132,9 @@ def load():
         "gc_ceiling_sink_bytes": (sz, []),
         "gc_ceiling_valu": (i32, [i32, i64, vp, sz, ctypes.POINTER(ctypes.c_uint64), vp]),
         "gc_ceiling_lds_atomic": (i32, [i32, i32, i64, vp, sz, ctypes.POINTER(ctypes.c_uint64), vp]),
+        "gc_launch_plan": (i32, [i64, i64, i32, ctypes.c_double, ctypes.POINTER(_Tuning), ctypes.POINTER(_Plan)]),
+        "gc_ceiling_l1": (i32, [i32, i32, i64, vp, sz, ctypes.POINTER(ctypes.c_uint64), vp]),
+        "gc_ceiling_lds": (i32, [i32, i32, i32, i32, i32, i64, vp, sz, ctypes.POINTER(ctypes.c_uint64), vp]),
         "gc_status_string": (ctypes.c_char_p, [i32]),
         "gc_last_device_error": (ctypes.c_int, []),
         "gc_version": (ctypes.c_char_p, []),
@@ -152,10 +168,47 @@ def _ptr(t) -> ctypes.c_void_p:
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
-def _need(t, dtype, name, device=None):
+def _buf(t, name, dtype, min_numel=0, device=None, optional=False, shape=None):
+    """Check one tensor argument before its address goes to the library, which cannot see sizes:
+    dtype and contiguity (TypeError), then element count or shape (ValueError).  Returns the
+    tensor; None passes only when optional.  Where the tensors live is checked for all of a
+    call's arguments at once, after these (_on_gpu), so these checks run on any machine."""
     torch = _torch()
-    if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
-        raise TypeError(f"{name} must be a contiguous {dtype} CUDA tensor")
+    if t is None:
+        if optional:
+            return None
+        raise TypeError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be a {dtype} tensor, got {t.dtype}")
+    if not t.is_contiguous():
+        raise TypeError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.numel() < min_numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs at least {min_numel}")
+    return t
+
+
+def _on_gpu(**tensors):
+    """Every given tensor (None skipped) is a GPU tensor (TypeError), all on one device
+    (ValueError)."""
+    dev = None
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise TypeError(f"{name} must be a CUDA (HIP) device tensor")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other arguments on {dev}")
+
+
+def _need(t, dtype, name, device=None):
+    _buf(t, name, dtype)
+    _on_gpu(**{name: t})
     return t
 
 
@@ -167,34 +220,66 @@ def workspace_bytes(nbins: int) -> int:
     return int(load().gc_workspace_bytes(int(nbins)))
 
 
+def _count(v, name, limit):
+    v = int(v)
+    if v < 0 or v > limit:
+        raise ValueError(f"{name} = {v} outside [0, {limit}]")
+    return v
+
+
+def _bins(nbins):
+    nbins = int(nbins)
+    if nbins < 1 or nbins > MAX_BINS:
+        raise ValueError(f"nbins = {nbins} outside [1, {MAX_BINS}]")
+    return nbins
+
+
 def prepare(ra_arcmin, dec_arcmin, out=None, stream=None):
     """Prepared (unit-vector) form of one catalog, as an opaque uint8 device tensor."""
     torch = _torch()
-    _need(ra_arcmin, torch.float32, "ra_arcmin")
-    _need(dec_arcmin, torch.float32, "dec_arcmin")
-    n = ra_arcmin.numel()
+    _buf(ra_arcmin, "ra_arcmin", torch.float32)
+    n = _count(ra_arcmin.numel(), "n", MAX_GALAXIES)
+    _buf(dec_arcmin, "dec_arcmin", torch.float32)
     if dec_arcmin.numel() != n:
         raise ValueError("ra and dec must have the same length")
     nbytes = prepared_bytes(n)
+    _buf(out, "out", torch.uint8, nbytes, optional=True)
+    _on_gpu(ra_arcmin=ra_arcmin, dec_arcmin=dec_arcmin, out=out)
     if out is None:
         out = torch.empty(nbytes, dtype=torch.uint8, device=ra_arcmin.device)
-    elif out.numel() < nbytes:
-        raise ValueError("prepared buffer too small")
     _check(load().gc_prepare(_ptr(ra_arcmin), _ptr(dec_arcmin), n, _ptr(out), _stream(stream)), "gc_prepare")
     return out
 
 
+def _job_args(prep_d, n_d, prep_r, n_r, nbins, out, workspace, out_required):
+    """Checked arguments of a histogram call: the prepared catalogs hold prepared_bytes(n) bytes
+    (either may be absent when its n is 0), out is a (3, nbins) int64 tensor, the workspace holds
+    workspace_bytes(nbins) bytes, all on one device."""
+    torch = _torch()
+    n_d = _count(n_d, "n_d", MAX_GALAXIES)
+    n_r = _count(n_r, "n_r", MAX_GALAXIES)
+    nbins = _bins(nbins)
+    _buf(prep_d, "prep_d", torch.uint8, prepared_bytes(n_d), optional=n_d == 0)
+    _buf(prep_r, "prep_r", torch.uint8, prepared_bytes(n_r), optional=n_r == 0)
+    _buf(out, "out", torch.int64, shape=(3, nbins), optional=not out_required)
+    _buf(workspace, "workspace", torch.uint8, workspace_bytes(nbins), optional=True)
+    _on_gpu(prep_d=prep_d, prep_r=prep_r, out=out, workspace=workspace)
+    ref = next((t for t in (prep_d, prep_r, out, workspace) if t is not None), None)
+    if ref is None:
+        raise TypeError("no device tensor given (prepared catalogs, out or workspace)")
+    if out is None:
+        out = torch.empty((3, nbins), dtype=torch.int64, device=ref.device)
+    if workspace is None:
+        workspace = torch.empty(workspace_bytes(nbins), dtype=torch.uint8, device=ref.device)
+    return n_d, n_r, nbins, out, workspace
+
+
 def histogram_dd_dr_rr(prep_d, n_d: int, prep_r, n_r: int, nbins: int, bin_width_deg: float,
                        out=None, workspace=None, tuning: Tuning | None = None, stream=None):
-    """(DD, DR, RR) int64 device tensors of nbins counts each."""
-    torch = _torch()
-    dev = prep_d.device if prep_d is not None else prep_r.device
-    if out is None:
-        out = torch.empty((3, nbins), dtype=torch.int64, device=dev)
-    if workspace is None:
-        workspace = torch.empty(max(workspace_bytes(nbins), 1), dtype=torch.uint8, device=dev)
+    """(DD, DR, RR) int64 device tensors of nbins counts each (rows of `out`)."""
+    n_d, n_r, nbins, out, workspace = _job_args(prep_d, n_d, prep_r, n_r, nbins, out, workspace, False)
     dd, dr, rr = out[0], out[1], out[2]
-    args = [_ptr(prep_d), int(n_d), _ptr(prep_r), int(n_r), int(nbins), float(bin_width_deg),
+    args = [_ptr(prep_d), n_d, _ptr(prep_r), n_r, nbins, float(bin_width_deg),
             _ptr(dd), _ptr(dr), _ptr(rr), _ptr(workspace), workspace.numel()]
     lib = load()
     if tuning is None:
@@ -213,12 +298,9 @@ def histogram_part(prep_d, n_d: int, prep_r, n_r: int, nbins: int, bin_width_deg
                    out, workspace=None, tuning: Tuning | None = None, stream=None):
     """ADD part `part` of `parts` of the (DD, DR, RR) job into `out` ((3, nbins) int64 device
     tensor); the parts of one job sum exactly to histogram_dd_dr_rr's result."""
-    torch = _torch()
-    dev = out.device
-    if workspace is None:
-        workspace = torch.empty(max(workspace_bytes(nbins), 1), dtype=torch.uint8, device=dev)
+    n_d, n_r, nbins, out, workspace = _job_args(prep_d, n_d, prep_r, n_r, nbins, out, workspace, True)
     tc = tuning._c() if tuning is not None else None
-    _check(load().gc_histogram_part(_ptr(prep_d), int(n_d), _ptr(prep_r), int(n_r), int(nbins),
+    _check(load().gc_histogram_part(_ptr(prep_d), n_d, _ptr(prep_r), n_r, nbins,
                                     float(bin_width_deg), int(part), int(parts), _ptr(out[0]), _ptr(out[1]),
                                     _ptr(out[2]), _ptr(workspace), workspace.numel(),
                                     ctypes.byref(tc) if tc is not None else None, _stream(stream)),
@@ -226,21 +308,36 @@ def histogram_part(prep_d, n_d: int, prep_r, n_r: int, nbins: int, bin_width_deg
     return out
 
 
+def _families(dd, dr, rr):
+    torch = _torch()
+    _buf(dd, "dd", torch.int64)
+    nbins = _bins(dd.numel())
+    _buf(dr, "dr", torch.int64, shape=tuple(dd.shape))
+    _buf(rr, "rr", torch.int64, shape=tuple(dd.shape))
+    return nbins
+
+
 def histogram_totals(dd, dr, rr, out=None, stream=None):
     torch = _torch()
+    nbins = _families(dd, dr, rr)
+    _buf(out, "out", torch.int64, 3, optional=True)
+    _on_gpu(dd=dd, dr=dr, rr=rr, out=out)
     if out is None:
         out = torch.empty(3, dtype=torch.int64, device=dd.device)
-    _check(load().gc_histogram_totals(_ptr(dd), _ptr(dr), _ptr(rr), dd.numel(), _ptr(out), _stream(stream)),
+    _check(load().gc_histogram_totals(_ptr(dd), _ptr(dr), _ptr(rr), nbins, _ptr(out), _stream(stream)),
            "gc_histogram_totals")
     return out
 
 
 def omega(dd, dr, rr, n_d: int, n_r: int, out=None, stream=None):
     torch = _torch()
+    nbins = _families(dd, dr, rr)
+    n_d, n_r = _count(n_d, "n_d", MAX_GALAXIES), _count(n_r, "n_r", MAX_GALAXIES)
+    _buf(out, "out", torch.float64, nbins, optional=True)
+    _on_gpu(dd=dd, dr=dr, rr=rr, out=out)
     if out is None:
-        out = torch.empty(dd.numel(), dtype=torch.float64, device=dd.device)
-    _check(load().gc_omega(_ptr(dd), _ptr(dr), _ptr(rr), dd.numel(), int(n_d), int(n_r), _ptr(out),
-                           _stream(stream)), "gc_omega")
+        out = torch.empty(nbins, dtype=torch.float64, device=dd.device)
+    _check(load().gc_omega(_ptr(dd), _ptr(dr), _ptr(rr), nbins, n_d, n_r, _ptr(out), _stream(stream)), "gc_omega")
     return out
 
 
@@ -249,6 +346,11 @@ def eval_angle_core(x, nbins: int, bin_width_deg: float, with_exact: bool = True
     """The pair kernel's angle-to-bin core on cosines x (fp32 -> fp32-dot core, fp64 ->
     fp64-dot core).  Returns (bin, trip, exact_bin, t) device tensors (None where not asked)."""
     torch = _torch()
+    if not isinstance(x, torch.Tensor) or x.dtype not in (torch.float32, torch.float64):
+        raise TypeError("x must be a float32 or float64 tensor")
+    _buf(x, "x", x.dtype)
+    nbins = _bins(nbins)
+    _on_gpu(x=x)
     n = x.numel()
     dot = 64 if x.dtype == torch.float64 else 32
     bins = torch.empty(n, dtype=torch.int32, device=x.device)
@@ -258,9 +360,9 @@ def eval_angle_core(x, nbins: int, bin_width_deg: float, with_exact: bool = True
     x32 = x if dot == 32 else None
     x64 = x if dot == 64 else None
     ws = torch.empty(workspace_bytes(nbins), dtype=torch.uint8, device=x.device)
-    _check(load().gc_eval_angle_core(_ptr(x32), _ptr(x64), n, int(nbins), float(bin_width_deg), dot,
+    _check(load().gc_eval_angle_core(_ptr(x32), _ptr(x64), n, nbins, float(bin_width_deg), dot,
                                      _ptr(bins), _ptr(trip), _ptr(exact), _ptr(t), _ptr(ws),
-                                     ws.numel() if ws is not None else 0, _stream(stream)),
+                                     ws.numel(), _stream(stream)),
            "gc_eval_angle_core")
     return bins, trip, exact, t
 
@@ -269,9 +371,12 @@ def eval_dot_mfma(a, b, stream=None):
     """The bin-table core's matrix-core dot products: a and b are (3, 16 ntiles) fp32 device
     tensors (x, y, z rows); returns (ntiles, 16, 16) with [t, i, j] = a_(16t+i) . b_(16t+j)."""
     torch = _torch()
+    if not isinstance(a, torch.Tensor) or a.dim() != 2 or a.shape[0] != 3 or a.shape[1] % 16:
+        raise ValueError("a must have shape (3, 16 ntiles)")
     ntiles = a.shape[1] // 16
-    a = a.contiguous()
-    b = b.contiguous()
+    a = _buf(a.contiguous(), "a", torch.float32)
+    b = _buf(b.contiguous() if isinstance(b, torch.Tensor) else b, "b", torch.float32, shape=tuple(a.shape))
+    _on_gpu(a=a, b=b)
     out = torch.empty((ntiles, 16, 16), dtype=torch.float32, device=a.device)
     _check(load().gc_eval_dot_mfma(_ptr(a[0]), _ptr(a[1]), _ptr(a[2]), _ptr(b[0]), _ptr(b[1]), _ptr(b[2]), ntiles,
                                    _ptr(out), _stream(stream)), "gc_eval_dot_mfma")
@@ -327,10 +432,14 @@ def ladder_histogram(rung: int, ra_d, dec_d, ra_r, dec_r, nbins: int, bin_width_
     include/gc_ladder.h) from fp32 arcmin device tensors."""
     torch = _torch()
     for t, nm in ((ra_d, "ra_d"), (dec_d, "dec_d"), (ra_r, "ra_r"), (dec_r, "dec_r")):
-        _need(t, torch.float32, nm)
+        _buf(t, nm, torch.float32)
     n_d, n_r = ra_d.numel(), ra_r.numel()
     if dec_d.numel() != n_d or dec_r.numel() != n_r:
         raise ValueError("ra and dec must have the same length")
+    nbins = _bins(nbins)
+    _buf(out, "out", torch.int64, shape=(3, nbins), optional=True)
+    _buf(workspace, "workspace", torch.uint8, ladder_workspace_bytes(n_d, n_r), optional=True)
+    _on_gpu(ra_d=ra_d, dec_d=dec_d, ra_r=ra_r, dec_r=dec_r, out=out, workspace=workspace)
     dev = ra_d.device
     if out is None:
         out = torch.empty((3, nbins), dtype=torch.int64, device=dev)
@@ -386,3 +495,55 @@ def ceiling_lds_atomic(nbins: int, same_bin: bool = False, iters: int = 2048, re
         n, dt = _timed(launch)
         best = dt if best is None else min(best, dt)
     return n_at.value / best
+
+
+LDS_PROBES = {"add": 0, "add_rtn": 1, "add64": 2, "add64_rtn": 3, "read32": 4, "read64": 5,
+              "read64_then_add": 6, "add_sparse": 7}
+
+
+def ceiling_lds(kind: str, words: int, threads: int = 256, sparse: int = 1, cols: int = 0, iters: int = 512,
+                repeats: int = 3):
+    """Measured rate of one kind of random-address LDS operation (64-lane instructions per
+    second) into a table of `words` words shared by each workgroup (gc_ceiling_lds); cols > 0:
+    a table of that many columns, one per lane group (lane mod cols)."""
+    torch = _torch()
+    sink = torch.empty(load().gc_ceiling_sink_bytes(), dtype=torch.uint8, device="cuda")
+    n = ctypes.c_uint64(0)
+    best = None
+    for _ in range(repeats + 1):
+        def launch(s):
+            _check(load().gc_ceiling_lds(LDS_PROBES[kind], int(words), int(threads), int(sparse), int(cols), int(iters),
+                                         _ptr(sink), sink.numel(), ctypes.byref(n), s), "gc_ceiling_lds")
+            return n.value
+        _, dt = _timed(launch)
+        best = dt if best is None else min(best, dt)
+    return n.value / best
+
+
+def ceiling_l1(words: int, threads: int = 256, iters: int = 256, repeats: int = 3):
+    """Measured rate of random 8-byte loads (64-lane instructions per second) from a table of
+    `words` words in global memory (gc_ceiling_l1)."""
+    torch = _torch()
+    tab_bytes = (words * 4 + 255) // 256 * 256
+    sink = torch.zeros(tab_bytes + load().gc_ceiling_sink_bytes(), dtype=torch.uint8, device="cuda")
+    n = ctypes.c_uint64(0)
+    best = None
+    for _ in range(repeats + 1):
+        def launch(s):
+            _check(load().gc_ceiling_l1(int(words), int(threads), int(iters), _ptr(sink), sink.numel(),
+                                        ctypes.byref(n), s), "gc_ceiling_l1")
+            return n.value
+        _, dt = _timed(launch)
+        best = dt if best is None else min(best, dt)
+    return n.value / best
+
+
+def launch_plan(n_d: int, n_r: int, nbins: int, bin_width_deg: float, tuning: Tuning | None = None) -> dict:
+    """The launch plan of a histogram call with these sizes, bins and overrides (gc_launch_plan):
+    core, dot precision, galaxies per lane, histogram columns, waves per workgroup, L1 share,
+    occupancy, grid and LDS per workgroup.  Enqueues nothing."""
+    p = _Plan()
+    tc = tuning._c() if tuning is not None else None
+    _check(load().gc_launch_plan(int(n_d), int(n_r), int(nbins), float(bin_width_deg),
+                                 ctypes.byref(tc) if tc is not None else None, ctypes.byref(p)), "gc_launch_plan")
+    return {n: getattr(p, n) for n, _ in _Plan._fields_ if n != "reserved_"}

@@ -19,8 +19,11 @@ CLI = os.path.join(BINDIR, "galaxy_gc")
 ARCH = "gfx950"
 
 # -packed-fp32-ops: no packed FP32 (v_pk_*_f32) instructions anywhere in the device code.
+# pragma-unroll-threshold: the bin-table kernel's matrix-core loop (32 tiles, each with its rare
+# drain paths) must unroll fully, which the default size threshold refuses.
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-mllvm", "-pragma-unroll-threshold=100000",
              "-I", os.path.join(ROOT, "include")]
 
 SOURCES = ["gc_kernels.hip", "gc_api.cpp", "gc_ceilings.hip", "gc_ladder.hip", "gc_io.cpp"]

@@ -21,10 +21,6 @@ errors that the kernel's guard relies on:
     q = fma(-sqrt(1-a), P(a), pi/2), evaluated with emulated fp32 arithmetic
     (--exhaustive; otherwise on a 2^24-point grid).
 
-A degree-3 polynomial of the same form (GC_ACOS3_*, error ~1e-4 rad) serves the edge-table
-core, which needs the angle only to within a fraction of a bin to pick the edge to compare
-with; the comparison itself is made on the cosine.
-
 Usage: python fit_acos_poly.py [--exhaustive]
 """
 import argparse
@@ -147,7 +143,7 @@ def main():
     args = ap.parse_args()
     where = "every fp32 a in [0,1]" if args.exhaustive else "2^24-point grid"
     lines = ["// Generated by fit_acos_poly.py -- do not edit.", "#pragma once"]
-    for degree, prefix in ((DEGREE, "GC_ACOS"), (3, "GC_ACOS3")):
+    for degree, prefix in ((DEGREE, "GC_ACOS"),):
         coef32 = fit(degree).astype(np.float32)
         fit_err, core_err = measure(coef32, args.exhaustive)
         lines += [

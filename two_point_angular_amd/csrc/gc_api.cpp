@@ -5,9 +5,11 @@
 #include <mutex>
 #include <string.h>
 
-#include "../../include/gc.h"
+#include "../../include/gc_diag.h"
 #include "gc_acos_poly.h"
 #include "gc_internal.h"
+
+static_assert(GC_MAX_BINS == gc::kMaxBins, "the kernels' bin limit is GC_MAX_BINS");
 
 namespace gc {
 namespace {
@@ -31,16 +33,18 @@ bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 struct DeviceInfo {
   bool valid = false;
   int cus = 0;
-  // occupancy per (kernel variant, lds bytes); variant = (dot64 * 5 + core) * 2 + (k == 8)
-  struct Occ { size_t lds; int blocks; };
-  Occ occ[16][8];
-  int nocc[16] = {};
+  // occupancy per (kernel variant, bin-table variant, lds bytes, threads)
+  struct Occ { int vi, cols, l1; size_t lds; int threads, blocks; };
+  static constexpr int kSlots = 96;
+  Occ occ[kSlots];
+  int nocc = 0;
 };
 constexpr int kMaxDevices = 64;
 std::mutex g_mu;
 DeviceInfo g_dev[kMaxDevices];
 
-hipError_t device_info(int *cus, bool dot64, int k, int core, size_t lds, int *blocks_per_cu) {
+hipError_t device_info(int *cus, bool dot64, int k, int core, LutVariant lv, size_t lds, int threads,
+                       int *blocks_per_cu) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -56,16 +60,20 @@ hipError_t device_info(int *cus, bool dot64, int k, int core, size_t lds, int *b
   }
   *cus = d.cus;
   if (!blocks_per_cu) return hipSuccess;
-  const int vi = ((dot64 ? 5 : 0) + core) * 2 + (k == 8 ? 1 : 0);  // fp32 cores 0..4, fp64 0..2
-  for (int q = 0; q < d.nocc[vi]; ++q)
-    if (d.occ[vi][q].lds == lds) {
-      *blocks_per_cu = d.occ[vi][q].blocks;
+  const int vi = ((dot64 ? 5 : 0) + core) * 3 + (k == 8 ? 2 : (k == 4 ? 1 : 0));  // fp32 cores 0..4, fp64 0..2
+  const bool lut = core == 2 && !dot64;
+  const int cols = lut ? lv.cols : 1, l1 = lut ? lv.l1 : 2;
+  for (int q = 0; q < d.nocc; ++q) {
+    const DeviceInfo::Occ &o = d.occ[q];
+    if (o.vi == vi && o.cols == cols && o.l1 == l1 && o.lds == lds && o.threads == threads) {
+      *blocks_per_cu = o.blocks;
       return hipSuccess;
     }
+  }
   int blocks = 0;
-  e = pairs_occupancy(dot64, k, core, lds, &blocks);
+  e = pairs_occupancy(dot64, k, core, lv, lds, threads, &blocks);
   if (e != hipSuccess) return e;
-  if (d.nocc[vi] < 8) d.occ[vi][d.nocc[vi]++] = {lds, blocks};
+  if (d.nocc < DeviceInfo::kSlots) d.occ[d.nocc++] = {vi, cols, l1, lds, threads, blocks};
   *blocks_per_cu = blocks;
   return hipSuccess;
 }
@@ -109,6 +117,8 @@ BinParams make_bins(int32_t nbins, double w_deg) {
   {
     const double b = floor(180.0 / w_deg);
     bp.b180 = b < static_cast<double>(nbins - 1) ? static_cast<int32_t>(b) : nbins - 1;
+    const double b9 = floor(90.0 / w_deg);
+    bp.b90 = b9 < static_cast<double>(nbins - 1) ? static_cast<int32_t>(b9) : nbins - 1;
   }
   bp.invw = static_cast<float>(1.0 / w_rad);
   bp.h = static_cast<float>((kPi / 2.0) / w_rad);
@@ -161,9 +171,16 @@ struct LutPlan {
   bool ok = false;
   int32_t m = 0;
   double margin = 0.0;
+  double s_star = 0.0;  // > 0: entries whose |c| may lie below s_star hold NaN (always recheck)
   float g = 0.0f;
 };
 
+// Where (b) or (c) fails (bins narrower than about 0.22 deg), the table still serves every pair
+// whose c~ the error bound pins within the margin: an entry whose smallest |c| is at least
+// S* = g_c / margin has |c~ - c| <= g_c / s~ <= margin for every pair in it, so (a) alone makes its
+// edge the only one the pair can be near.  Entries closer to c = 0 (angles within about
+// 2 asin(S* / sqrt2) of 0 or 180 deg, the middle entry among them) hold NaN, and their pairs are
+// rechecked; S* is kept at or below 0.05 (about 4 deg), so the rechecked share stays small.
 LutPlan plan_lut(int32_t nbins, double w_deg) {
   LutPlan p;
   if (!((static_cast<double>(nbins) + 0.5) * w_deg >= 180.0) || nbins < 2) return p;
@@ -190,8 +207,10 @@ LutPlan plan_lut(int32_t nbins, double w_deg) {
   const double g_c = 1.1 * (g_x + 2.0 * kTwoM24);
   const double s_star = g_c / margin;
   const double reach = sqrt(s_star * s_star * (1.0 + 4.0 * kTwoM24) + g_x);
-  if (!(reach < 0.95 * c_edge_min)) return p;
-  if (!(0.5 / md + margin < 0.95 * c_edge_min)) return p;
+  if (!(reach < 0.95 * c_edge_min) || !(0.5 / md + margin < 0.95 * c_edge_min)) {
+    if (!(s_star <= 0.05)) return p;
+    p.s_star = s_star * (1.0 + 1e-6);
+  }
   p.ok = true;
   p.m = static_cast<int32_t>(md);
   p.margin = margin;
@@ -199,52 +218,57 @@ LutPlan plan_lut(int32_t nbins, double w_deg) {
   return p;
 }
 
-void apply_lut(BinParams &bp, const LutPlan &lp) {
+// The bin-table kernel's histogram rows: cols 16 keeps one spare row (nbins) and the alias rows
+// nbins + 1, nbins + 2; one column keeps 64 spare words and the alias words nbins + 64, nbins + 65.
+void apply_lut(BinParams &bp, const LutPlan &lp, int cols, int32_t nbins) {
   bp.lut_m = static_cast<float>(lp.m);
   bp.lut_mb = static_cast<float>(lp.m) + 8388608.0f;  // exact: M < 2^23
   bp.lut_g = lp.g;
   bp.lut_n = 2 * lp.m;
-  bp.lut_sh = 2;
+  bp.lut_sh = cols == kHistCols ? 6 : 2;
+  bp.lut_alias = cols == kHistCols ? nbins + 2 : nbins + kWave + 1;
 }
 
-// ---- edge-table core ------------------------------------------------------------------------
-// fp32 dot, bins covering 180 deg that are too fine for the bin table (etab_kernel and etab_key
-// in gc_kernels.hip): a degree-3 arccos picks edge r = round(t~), the cosine decides the side.
-// Sound when every pair the table does not flag (NaN) has |t~ - t| < 0.45: the table builder
-// checks this per entry with the arccos error e3 = 1.25 (CORE_ERR + 2^-24 pi/2) (a 1-ulp
-// square root adds half an ulp of P <= pi/2).  The host requires e3 / w <= 0.25, so that away
-// from 0 and 180 deg the dot product's share of the budget leaves few entries flagged, and the
-// table region, histogram and four queues within 40 KB of LDS (four workgroups per CU).
-struct EtabPlan {
-  bool ok = false;
-  double g_x = 0.0, e3 = 0.0;
-  float g = 0.0f;
-};
+bool lut_layout(const LutPlan &lp, int32_t nbins, int k, const gc_tuning &tu, LutVariant *lv, int *waves);
 
-EtabPlan plan_etab(int32_t nbins, double w_deg, int k) {
-  EtabPlan p;
-  const double w = w_deg * (kPi / 180.0);
-  p.e3 = 1.25 * (GC_ACOS3_CORE_ERR + kTwoM24 * (kPi / 2.0));
-  if (!(p.e3 / w <= 0.25)) return p;
-  if (nbins + 2 > kEtabTableWords || static_cast<size_t>(nbins) + 2 > kLutBytes / 4) return p;
-  if (pairs_lds_bytes(etab_hist_words(nbins), true, k, 3, kEtabTableWords) > 40960) return p;
-  p.ok = true;
-  p.g_x = 5.0 * kTwoM24 * (1.0 + 1e-6) + 1e-12;
-  p.g = static_cast<float>(1.1 * (p.g_x + 0.5 * kTwoM24) * (1.0 + 1e-6));
-  return p;
+// The bin-table kernel's K and layout: K = 8 unless overridden; where the sixteen-column histogram
+// fits, K = 4 (two workgroups of 12 waves: six per SIMD, measured faster than K = 8 with 8 and
+// K = 2 with 16).  *k receives the K chosen.
+bool lut_choose(const LutPlan &lp, int32_t nbins, const gc_tuning &tu, int *k, LutVariant *lv, int *waves) {
+  if (tu.i_per_lane) {
+    *k = tu.i_per_lane;
+    return lut_layout(lp, nbins, *k, tu, lv, waves);
+  }
+  *k = 4;
+  if (lut_layout(lp, nbins, 4, tu, lv, waves) && lv->cols == kHistCols) return true;
+  *k = 8;
+  return lut_layout(lp, nbins, 8, tu, lv, waves);
 }
 
-void apply_etab(BinParams &bp, const EtabPlan &ep, int32_t nbins) {
-  bp.lut_g = ep.g;
-  bp.lut_n = nbins + 1;  // last entry
-  bp.lut_sh = 2;         // 4-byte words
-  // h = (pi/2) / w in fp32 is an integer for every width that divides 90 degrees (0.05, 0.25, ...):
-  // then h + 2^23 is exact and fma(., -1/w, h + 2^23) rounds t~ to the key in one step
-  bp.etab_hk = (bp.h == floorf(bp.h) && bp.h < 4194304.0f) ? bp.h + 8388608.0f : 0.0f;
-}
+// LDS of one compute unit on gfx950.
+constexpr size_t kLdsPerCU = 160 * 1024;
 
-// The edge-table core's instantiation: 4 (one-fma key) when h is integral, else 3.
-int etab_core(const BinParams &bp) { return bp.etab_hk != 0.0f ? 4 : 3; }
+// The bin-table kernel's layout: sixteen histogram columns when two workgroups of 10 waves (12 at
+// K = 4) fit in a compute unit's LDS beside their tables and queues, with a quarter of the table
+// reads through the vector L1; else one column in one workgroup of 16 waves, every read from LDS
+// (the large tables of fine bins do not stay in the vector L1).  Overrides may pick any layout
+// that fits.  Returns false when none fits.
+bool lut_layout(const LutPlan &lp, int32_t nbins, int k, const gc_tuning &tu, LutVariant *lv, int *waves) {
+  const int32_t tw = 2 * (2 * lp.m + 1);
+  auto lds = [&](int cols, int nw) { return pairs_lds_bytes(lut_hist_words(nbins, cols), true, k, 2, false, nw, tw); };
+  // two workgroups per compute unit, each a whole number of waves per SIMD, as many as the
+  // registers allow: 8 waves at K = 8 (<= 96 VGPRs: five per SIMD, four used), 12 at K = 4
+  // (<= 80: six), 16 at K = 2 (<= 64: eight)
+  const int nw2 = k == 2 ? 16 : (k == 4 ? 12 : 8);
+  int cols = tu.hist_columns, nw = tu.waves_per_group;
+  if (cols == 0) cols = 2 * lds(kHistCols, nw ? nw : nw2) <= kLdsPerCU ? kHistCols : 1;
+  if (nw == 0) nw = cols == kHistCols ? nw2 : kMaxWavesPerWG;
+  if (lds(cols, nw) > kLdsPerCU) return false;
+  lv->cols = cols;
+  lv->l1 = tu.l1_share ? tu.l1_share - 1 : (cols == kHistCols ? 1 : 0);
+  *waves = nw;
+  return true;
+}
 
 // ---- series core ---------------------------------------------------------------------------
 // fp64 dot, bins ending by about 9 deg: t = s (q0 + q1 y + q2 y^2) / w with y = 1 - x, the
@@ -382,33 +406,44 @@ namespace {
 // j-steps floor(T p / P) .. floor(T (p+1) / P) of the same decomposition; with accumulate the
 // merge adds to the outputs.  Every pair's bin is fixed by the pair alone (the lane always holds the lower
 // index of a self pair, and the recheck is exact), so the parts sum to the single call's result.
+// plan_out non-null: only plan (sizes and tuning are checked; the pointers may be null) and
+// describe the launch in *plan_out; nothing is enqueued.
 gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, int64_t n_r, int32_t nbins,
                          double w_deg, uint64_t *dd, uint64_t *dr, uint64_t *rr, void *workspace, size_t ws_bytes,
-                         const gc_tuning *tuning, int64_t part, int64_t parts, bool accumulate, gc_stream_t stream) {
+                         const gc_tuning *tuning, int64_t part, int64_t parts, bool accumulate, gc_stream_t stream,
+                         gc_plan *plan_out = nullptr) {
   gc_status st;
   if ((st = check_bins(nbins, w_deg)) != GC_OK) return st;
-  if ((st = check_catalog(prep_d, n_d)) != GC_OK) return st;
-  if ((st = check_catalog(prep_r, n_r)) != GC_OK) return st;
-  if (!dd || !dr || !rr || !aligned(dd, 8) || !aligned(dr, 8) || !aligned(rr, 8))
-    return GC_ERR_INVALID_ARGUMENT;
-  if (!workspace || !aligned(workspace, GC_ALIGNMENT)) return GC_ERR_INVALID_ARGUMENT;
-  if (ws_bytes < workspace_bytes(nbins)) return GC_ERR_WORKSPACE;
+  if (plan_out) {
+    if (n_d < 0 || n_r < 0) return GC_ERR_INVALID_ARGUMENT;
+    if (n_d > GC_MAX_GALAXIES || n_r > GC_MAX_GALAXIES) return GC_ERR_UNSUPPORTED;
+  } else {
+    if ((st = check_catalog(prep_d, n_d)) != GC_OK) return st;
+    if ((st = check_catalog(prep_r, n_r)) != GC_OK) return st;
+    if (!dd || !dr || !rr || !aligned(dd, 8) || !aligned(dr, 8) || !aligned(rr, 8))
+      return GC_ERR_INVALID_ARGUMENT;
+    if (!workspace || !aligned(workspace, GC_ALIGNMENT)) return GC_ERR_INVALID_ARGUMENT;
+    if (ws_bytes < workspace_bytes(nbins)) return GC_ERR_WORKSPACE;
+  }
   gc_tuning tu;
   memset(&tu, 0, sizeof(tu));
   if (tuning) tu = *tuning;
   if ((tu.dot_precision != 0 && tu.dot_precision != 32 && tu.dot_precision != 64) ||
-      (tu.i_per_lane != 0 && tu.i_per_lane != 4 && tu.i_per_lane != 8) || tu.blocks_per_cu < 0 ||
+      (tu.i_per_lane != 0 && tu.i_per_lane != 2 && tu.i_per_lane != 4 && tu.i_per_lane != 8) || tu.blocks_per_cu < 0 ||
       tu.blocks_per_cu > kMaxBlocksPerCU || tu.shared_histogram < 0 || tu.shared_histogram > 2 ||
       tu.span_kernel < 0 || tu.span_kernel > 2 || tu.fast_core < 0 || tu.fast_core > 2 ||
-      tu.flush_interval < 0)
+      tu.flush_interval < 0 || (tu.hist_columns != 0 && tu.hist_columns != 1 && tu.hist_columns != kHistCols) ||
+      (tu.waves_per_group != 0 && (tu.waves_per_group < kWavesPerWG || tu.waves_per_group > kMaxWavesPerWG)) ||
+      tu.l1_share < 0 || tu.l1_share > 3 || tu.reserved_ != 0)
     return GC_ERR_INVALID_ARGUMENT;
 
   // Plan.  Bins narrower than 0.01 deg put most pairs where the fp32 dot product cannot
   // certify the bin; those use the fp64 dot-product instantiation.
   const bool dot64 = tu.dot_precision == 64 || (tu.dot_precision == 0 && w_deg < 0.01);
   // Galaxies per lane: 8 for the fp32 kernel; 4 for the fp64 kernel, whose fp64 i-galaxies
-  // at K = 8 leave room for only three waves per SIMD.
-  const int k = tu.i_per_lane ? tu.i_per_lane : (dot64 ? 4 : 8);
+  // at K = 8 leave room for only three waves per SIMD; 4 for the bin-table core with a sixteen-
+  // column histogram (below), whose two workgroups of 12 waves then fill six waves per SIMD.
+  int k = tu.i_per_lane ? tu.i_per_lane : (dot64 ? 4 : 8);
   // Span-specialised cores: when the bins reach 180 deg (up to half a bin), t cannot exceed
   // nbins + 1 and the fp32 kernel needs no clamp of t (a spare bin takes t = nbins); when they
   // end by 90 deg, the fp64 kernel needs no sign handling (x < 0 is the last bin).
@@ -417,37 +452,36 @@ gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, in
   const bool span = span_ok && tu.span_kernel != 1;
   // The arccos-free cores where they are sound: the bin table (fp32 dot, full span, shared
   // histogram) and the series (fp64 dot, bins ending by ~9 deg).
-  // (and the edge table: fp32 dot, full span, bins too fine for the bin table)
   const LutPlan lp = dot64 ? LutPlan() : plan_lut(nbins, w_deg);
   const SeriesPlan sp = dot64 ? plan_series(nbins, w_deg) : SeriesPlan();
-  const EtabPlan ep = dot64 ? EtabPlan() : plan_etab(nbins, w_deg, k);
-  const bool lut_ok = lp.ok && span && tu.shared_histogram != 1;
+  LutVariant lv;
+  int lut_waves = kWavesPerWG;
+  int k_lut = k;
+  const bool lut_fits = lp.ok && lut_choose(lp, nbins, tu, &k_lut, &lv, &lut_waves);
+  if (lp.ok && !lut_fits && (tu.hist_columns || tu.waves_per_group)) return GC_ERR_INVALID_ARGUMENT;
+  const bool lut_ok = lut_fits && span && tu.shared_histogram != 1;
   const bool series_ok = sp.ok && span;
-  const bool etab_ok = !lut_ok && ep.ok && span && tu.shared_histogram != 1;
-  if (tu.fast_core == 2 && !lut_ok && !series_ok && !etab_ok) return GC_ERR_INVALID_ARGUMENT;
+  if (tu.fast_core == 2 && !lut_ok && !series_ok) return GC_ERR_INVALID_ARGUMENT;
   const bool use_lut = lut_ok && tu.fast_core != 1;
   const bool use_series = series_ok && tu.fast_core != 1;
-  const bool use_etab = etab_ok && tu.fast_core != 1;
-  int core = use_etab ? 3 : ((use_lut || use_series) ? 2 : (span ? 1 : 0));
+  const int core = (use_lut || use_series) ? 2 : (span ? 1 : 0);
+  if (use_lut) k = k_lut;
+  if (k == 2 && !use_lut) return GC_ERR_INVALID_ARGUMENT;  // K = 2 is built for the bin-table core only
   const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
 
   PairArgs a;
   memset(&a, 0, sizeof(a));
   a.nbins = nbins;
+  a.waves = use_lut ? lut_waves : kWavesPerWG;
   a.hist_words = (nbins + kWave + 63) / 64 * 64;  // 64 spare bins past the last (see core32)
   a.bp = make_bins(nbins, w_deg);
   if (use_series) apply_series(a.bp, sp, nbins, w_deg);
   if (use_lut) {
-    a.hist_words = (nbins + kWave + kLutAliasWords + 63) / 64 * 64;
-    apply_lut(a.bp, lp);
-  }
-  if (use_etab) {
-    a.hist_words = etab_hist_words(nbins);
-    apply_etab(a.bp, ep, nbins);
-    core = etab_core(a.bp);
+    a.hist_words = lut_hist_words(nbins, lv.cols);
+    apply_lut(a.bp, lp, lv.cols, nbins);
   }
   uint2 *lut_dev = reinterpret_cast<uint2 *>(static_cast<char *>(workspace) + edge_table_bytes(nbins));
-  a.lut = (use_lut || use_etab) ? lut_dev : nullptr;
+  a.lut = use_lut ? lut_dev : nullptr;
   double *edge_cos = static_cast<double *>(workspace);
   a.edge_cos = edge_cos;
   a.slots = reinterpret_cast<unsigned long long *>(static_cast<char *>(workspace) + edge_table_bytes(nbins) +
@@ -484,19 +518,30 @@ gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, in
     // Histogram placement: one private histogram per wave unless sharing one per workgroup
     // lets more workgroups fit in LDS.
     int cus = 0, occ = 0, occ_shared = 0;
-    hipError_t e = device_info(&cus, dot64, k, core, pairs_lds_bytes(a.hist_words, false, k, core), &occ);
+    const int threads = a.waves * kWave;
+    const int32_t tw = table_words(a.bp.lut_n, dot64, core);
+    // (a layout that exceeds the compute unit's LDS has occupancy 0 and is not asked about)
+    const bool must_share = use_lut || tu.shared_histogram == 2;
+    const size_t lds_private = pairs_lds_bytes(a.hist_words, false, k, core, dot64, a.waves);
+    const size_t lds_shared = pairs_lds_bytes(a.hist_words, true, k, core, dot64, a.waves, tw);
+    hipError_t e = device_info(&cus, dot64, k, core, lv, 0, threads, nullptr);
     if (e != hipSuccess) return device_error(e);
-    e = device_info(&cus, dot64, k, core,
-                    pairs_lds_bytes(a.hist_words, true, k, core, table_words(a, dot64, core)), &occ_shared);
-    if (e != hipSuccess) return device_error(e);
-    bool shared = use_lut || use_etab || tu.shared_histogram == 2 || (tu.shared_histogram == 0 && occ_shared > occ);
+    if (!must_share && lds_private <= kLdsPerCU) {
+      e = device_info(&cus, dot64, k, core, lv, lds_private, threads, &occ);
+      if (e != hipSuccess) return device_error(e);
+    }
+    if (tu.shared_histogram != 1 && lds_shared <= kLdsPerCU) {
+      e = device_info(&cus, dot64, k, core, lv, lds_shared, threads, &occ_shared);
+      if (e != hipSuccess) return device_error(e);
+    }
+    bool shared = must_share || (tu.shared_histogram == 0 && occ_shared > occ);
     if (shared) occ = occ_shared;
     a.shared_hist = shared ? 1 : 0;
     // Between two flushes a bin must stay within +-2^31: each j-step adds at most 2 * 64 K
-    // per wave, and in shared mode four waves add to the same histogram.  A wave tests the
-    // interval after every batch of j-steps (up to 16 with the matrix-core dot), so it may run
-    // 15 steps past it; the margin of 32 covers that.
-    const int64_t max_inc = 2ll * kWave * k * (shared ? kWavesPerWG : 1);
+    // per wave, and in shared mode every wave of the workgroup adds to the same histogram.  A
+    // wave tests the interval after every batch of j-steps (up to 16 with the matrix-core dot),
+    // so it may run 15 steps past it; the margin of 32 covers that.
+    const int64_t max_inc = 2ll * kWave * k * (shared ? a.waves : 1);
     const int64_t auto_flush = static_cast<int64_t>(0x7fffffffll / max_inc) - 32;
     a.flush_interval = tu.flush_interval ? (tu.flush_interval < auto_flush ? tu.flush_interval : auto_flush)
                                          : auto_flush;
@@ -505,7 +550,7 @@ gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, in
     int64_t g = static_cast<int64_t>(per_cu) * cus;
     if (g > kMaxWorkgroups) g = kMaxWorkgroups;
     // at least ~32 j-steps per wave
-    const int64_t want = (total + 32 * kWavesPerWG - 1) / (32 * kWavesPerWG);
+    const int64_t want = (total + 32 * a.waves - 1) / (32 * a.waves);
     if (g > want) g = want;
     int nonzero = 0;
     for (int f = 0; f < 3; ++f) nonzero += steps[f] > 0;
@@ -546,18 +591,36 @@ gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, in
       a.fam[f].wg_end = we[f];
     }
     num_wg = cur;
+    if (plan_out) {
+      plan_out->core = core;
+      plan_out->dot_precision = dot64 ? 64 : 32;
+      plan_out->i_per_lane = k;
+      plan_out->hist_columns = use_lut ? lv.cols : 1;
+      plan_out->waves_per_group = a.waves;
+      plan_out->l1_share = use_lut ? lv.l1 + 1 : 0;
+      plan_out->shared_histogram = a.shared_hist;
+      plan_out->blocks_per_cu = per_cu;
+      plan_out->workgroups = num_wg;
+      plan_out->lds_bytes = static_cast<int32_t>(shared ? lds_shared : lds_private);
+      plan_out->flush_interval = a.flush_interval;
+      plan_out->always_recheck = use_lut && lp.s_star > 0.0 ? 1 : 0;
+      return GC_OK;
+    }
     e = launch_edges(nbins, w_deg, edge_cos, hs);
     if (e != hipSuccess) return device_error(e);
     if (use_lut) {
-      e = launch_lut(nbins, w_deg, lp.m, lp.margin, lut_dev, hs);
+      e = launch_lut(nbins, w_deg, lp.m, lp.margin, lv.cols, a.bp.lut_alias, lp.s_star, lut_dev, hs);
       if (e != hipSuccess) return device_error(e);
     }
-    if (use_etab) {
-      e = launch_etab(nbins, w_deg, ep.g_x, ep.e3, reinterpret_cast<uint32_t *>(lut_dev), hs);
-      if (e != hipSuccess) return device_error(e);
-    }
-    e = launch_pairs(a, num_wg, dot64, k, core, hs);
+    e = launch_pairs(a, num_wg, dot64, k, core, lv, hs);
     if (e != hipSuccess) return device_error(e);
+  }
+  if (plan_out) {  // no work: nothing to launch but the merge
+    memset(plan_out, 0, sizeof(*plan_out));
+    plan_out->core = core;
+    plan_out->dot_precision = dot64 ? 64 : 32;
+    plan_out->i_per_lane = k;
+    return GC_OK;
   }
   uint64_t *outs[3] = {dd, dr, rr};
   hipError_t e = launch_merge(a.slots, nbins, wb, we, outs, accumulate, hs);
@@ -584,6 +647,13 @@ gc_status gc_histogram_part(const void *prep_d, int64_t n_d, const void *prep_r,
   if (parts < 1 || parts > GC_MAX_PARTS || part < 0 || part >= parts) return GC_ERR_INVALID_ARGUMENT;
   return histogram_impl(prep_d, n_d, prep_r, n_r, nbins, w_deg, dd, dr, rr, workspace, ws_bytes, tuning, part, parts,
                         true, stream);
+}
+
+gc_status gc_launch_plan(int64_t n_d, int64_t n_r, int32_t nbins, double w_deg, const gc_tuning *tuning,
+                         gc_plan *plan) {
+  if (!plan) return GC_ERR_INVALID_ARGUMENT;
+  return histogram_impl(nullptr, n_d, nullptr, n_r, nbins, w_deg, nullptr, nullptr, nullptr, nullptr, 0, tuning, 0, 1,
+                        false, nullptr, plan);
 }
 
 gc_status gc_histogram_dd_dr_rr(const void *prep_d, int64_t n_d, const void *prep_r, int64_t n_r,
@@ -627,13 +697,15 @@ gc_status gc_eval_angle_core(const float *x32, const double *x64, int64_t n, int
   const bool span = d64 ? span_narrow(nbins, w_deg) : span_full(nbins, w_deg);
   const LutPlan lp = d64 ? LutPlan() : plan_lut(nbins, w_deg);
   const SeriesPlan sp = d64 ? plan_series(nbins, w_deg) : SeriesPlan();
-  const EtabPlan ep = d64 ? EtabPlan() : plan_etab(nbins, w_deg, 8);
-  const bool use_lut = lp.ok && span;
+  gc_tuning tu0;
+  memset(&tu0, 0, sizeof(tu0));
+  LutVariant lv;
+  int lut_waves = 0, lut_k = 0;
+  const bool use_lut = lp.ok && span && lut_choose(lp, nbins, tu0, &lut_k, &lv, &lut_waves);
   const bool use_series = sp.ok && span;
-  const bool use_etab = !use_lut && ep.ok && span;
-  int core = use_etab ? 3 : ((use_lut || use_series) ? 2 : (span ? 1 : 0));
+  const int core = (use_lut || use_series) ? 2 : (span ? 1 : 0);
   if (n == 0) return GC_OK;
-  const bool need_ws = exact_out || use_lut || use_etab;
+  const bool need_ws = exact_out || use_lut;
   if (need_ws && (!workspace || !aligned(workspace, GC_ALIGNMENT))) return GC_ERR_INVALID_ARGUMENT;
   if (need_ws && ws_bytes < edge_table_bytes(nbins) + kLutBytes) return GC_ERR_WORKSPACE;
   BinParams bp = make_bins(nbins, w_deg);
@@ -644,13 +716,8 @@ gc_status gc_eval_angle_core(const float *x32, const double *x64, int64_t n, int
   hipError_t e = hipSuccess;
   if (exact_out) e = launch_edges(nbins, w_deg, edge_cos, hs);
   if (e == hipSuccess && use_lut) {
-    apply_lut(bp, lp);
-    e = launch_lut(nbins, w_deg, lp.m, lp.margin, lut, hs);
-  }
-  if (e == hipSuccess && use_etab) {
-    apply_etab(bp, ep, nbins);
-    core = etab_core(bp);
-    e = launch_etab(nbins, w_deg, ep.g_x, ep.e3, reinterpret_cast<uint32_t *>(lut), hs);
+    apply_lut(bp, lp, lv.cols, nbins);
+    e = launch_lut(nbins, w_deg, lp.m, lp.margin, lv.cols, bp.lut_alias, lp.s_star, lut, hs);
   }
   if (e == hipSuccess)
     e = launch_eval_core(x32, x64, n, bp, d64, core, lut, exact_out ? edge_cos : nullptr, bin_out, trip_out,

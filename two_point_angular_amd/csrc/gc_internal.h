@@ -9,17 +9,21 @@
 namespace gc {
 
 constexpr int kWave = 64;            // CDNA wavefront width
-constexpr int kWavesPerWG = 4;       // pair-kernel workgroup = 4 independent wavefronts
+constexpr int kWavesPerWG = 4;       // pair-kernel workgroup of the arccos and fp64 cores
 constexpr int kWGThreads = kWave * kWavesPerWG;
+constexpr int kMaxWavesPerWG = 16;   // the bin-table core's workgroups: up to 16 waves sharing one table
 // Per-wave recheck queue, 8-byte entries.  Full batches of 64 are drained after every j-step
-// and, within a step, after every D pairs per lane (D = drain_span: 4, i.e. once in the middle
-// of a K = 8 step; 2 for the edge-table core, whose table leaves less LDS for queues), so a
-// drain point leaves fewer than 64 pending and the next appends at most 64 D: 64 (D + 1)
-// entries suffice.  (Halving the queue of K = 8 lets a fifth workgroup fit in LDS beside the
-// bin table or a 3600-bin shared histogram.)
-constexpr int drain_span(int k, int core) { return core >= 3 ? 2 : (k > 4 ? k / 2 : k); }
-constexpr int queue_words(int k, int core) { return 2 * kWave * (drain_span(k, core) + 1); }
+// and, within a step, after every D pairs per lane (D = drain_span), so a drain point leaves
+// fewer than 64 pending and the next appends at most 64 D: 64 (D + 1) entries suffice.  D = 2
+// for the bin-table core (its queues share the LDS with the table and the histogram; the
+// matrix-core steps drain after every two of a lane's four pairs), D = 1 for it at K = 2 (sixteen
+// waves' queues beside its table and histogram), else half a K = 8 step or a whole K = 4 step.
+constexpr int drain_span(int k, int core, bool d64) {
+  return (core == 2 && !d64) ? (k == 2 ? 1 : 2) : (k > 4 ? k / 2 : k);
+}
+constexpr int queue_words(int k, int core, bool d64) { return 2 * kWave * (drain_span(k, core, d64) + 1); }
 constexpr int kMaxWorkgroups = 2048; // partial-histogram slots held by the workspace
+constexpr int kMaxBins = 8192;       // GC_MAX_BINS (include/gc.h; gc_api.cpp checks they agree)
 constexpr int kMaxBlocksPerCU = 8;
 
 // ---- prepared catalog layout ---------------------------------------------------
@@ -63,33 +67,36 @@ struct BinParams {
   float lut_m;   // bin-table core: entries per unit of c (M); the table has 2 M + 1 entries
   float lut_mb;  // M + 2^23: fma(c, M, M + 2^23) holds round(M (c + 1)) in its low mantissa bits
   float lut_g;   // bin-table core guard: recheck iff |cos(edge) - x| < lut_g
-  float etab_hk; // edge-table core with an integral h: h + 2^23 (exact), so that one fma gives the key
   int32_t lut_n; // 2 M (last entry index), or 0 when the bin table is not used
-  int32_t lut_sh;  // 2, log2 of the bytes per histogram word: an argument, so that the compiler
-                   // keeps (sign << 2) + address as one shift-and-add
+  int32_t lut_sh;  // log2 of the bytes per histogram row (2; 6 with sixteen columns): an argument, so
+                   // that the compiler keeps (sign << lut_sh) + address as one shift-and-add
+  int32_t lut_alias;  // bin-table core: the middle entry's row for x < 0 (x > 0: the row before)
   int32_t nbins;
   int32_t b180;  // the bin of the angles just below 180 deg: min(nbins - 1, floor(180 / w))
+  int32_t b90;   // the bin holding 90 deg: min(nbins - 1, floor(90 / w))
 };
 
 // Bin-table core (fp32 dot, bins covering 0..180 deg): the table lives in the workspace and is
-// copied into LDS by each workgroup; entry q = {cos(edge) (fp32 bits), 4 x the bin above the
-// edge}.  In LDS the second word becomes the byte address of the bin's histogram word.
-constexpr int kLutMaxEntries = 2049;
+// copied into LDS by each workgroup; entry q = {cos(edge) (fp32 bits, or NaN: always recheck),
+// byte offset of the histogram row of the bin above the edge}.  In LDS the second word becomes the
+// byte address of that row.  Up to 14337 entries (112 KiB): M = ceil(4 / w_rad) <= 7168, widths
+// down to about 0.032 deg.
+constexpr int kLutMaxEntries = 14337;
 // The table's middle entry (c within 1/(2M) of 0) holds both the smallest angles (x near 1)
-// and the largest (x near -1).  It stores e = 0 and bin word nbins + 65, so x > 0 lands in word
-// nbins + 64 (counted as bin 0) and x < 0 in word nbins + 65 (counted as bin b180, the bin of
-// the angles just below 180 deg, which is nbins - 1 unless the bins reach past 180 deg): two
-// histogram words past the 64 spare ones.  (The host admits the table only when no edge lies
-// within the middle entry's range, so each word stands for one bin.)
+// and the largest (x near -1).  When the table needs no always-recheck entries it stores e = 0 and
+// the row lut_alias (BinParams), so x > 0 lands in row lut_alias - 1 (counted as bin 0) and x < 0
+// in row lut_alias (counted as bin b180, the bin of the angles just below 180 deg, which is
+// nbins - 1 unless the bins reach past 180 deg).  (The host admits that form only when no edge
+// lies within the middle entry's reach, so each row stands for one bin.)  One-column histograms
+// keep 64 spare rows past the last bin, so the alias rows are nbins + 64 and nbins + 65; the
+// sixteen-column histogram of the bin-table core has one spare row (nbins) and the alias rows
+// nbins + 1 and nbins + 2.
 constexpr int kLutAliasWords = 2;
+// Histogram columns of the bin-table core: one, or sixteen - row b holds one word per lane mod 16,
+// so the 16 lanes an LDS atomic serves together always hit 16 different banks.
+constexpr int kHistCols = 16;
 // The bin-table core's bound on |x~ - x| in units of 2^-24 (see plan_lut in gc_api.cpp).
 constexpr double kLutDotErr = 12.0;
-// Edge-table core (fp32 dot, bins covering 0..180 deg, too fine for the bin table): the cosine
-// of edge r (fp32, or NaN where the pair must be rechecked) for r = 0 .. nbins + 1, built in
-// the bin table's workspace area.  In LDS: [e_r (kEtabTableWords words) | histogram of bins
-// -1 .. nbins + 63 | 4 queues]; bin -1 is reachable only by rechecked pairs (the recheck moves
-// them out).
-
 // ---- pair-kernel work description ---------------------------------------------------
 // One family (DD, DR or RR): the i catalog is held in registers, the j catalog streamed.
 // Its work is a list of "j-steps": one j galaxy against one i-block of 64*K galaxies.
@@ -119,33 +126,34 @@ struct PairArgs {
   const double *edge_cos;      // [nbins + 1] cos(e w) in fp64, for the exact recheck
   int64_t flush_interval;      // j-steps between flushes of the 32-bit LDS histograms
   int32_t nbins;
-  int32_t hist_words;          // LDS words of one histogram (>= nbins + 64: 64 spare bins)
-  int32_t shared_hist;         // 0: one histogram per wave; 1: one per workgroup (4 waves)
+  int32_t hist_words;          // LDS words of one histogram (rows x columns, rounded up to 64)
+  int32_t shared_hist;         // 0: one histogram per wave; 1: one per workgroup
+  int32_t waves;               // waves per workgroup (kWavesPerWG, or up to kMaxWavesPerWG for the bin table)
 };
 
-// LDS bytes of one pair-kernel workgroup.
-// LDS bytes of one pair-kernel workgroup: histogram(s), the bin table (lut_entries 8-byte
-// entries, shared-histogram mode only) and the four recheck queues.
-inline size_t pairs_lds_bytes(int32_t hist_words, bool shared_hist, int k, int core, int32_t table_words = 0) {
-  const size_t qw = static_cast<size_t>(queue_words(k, core));
-  const size_t words = shared_hist ? hist_words + static_cast<size_t>(table_words) +
-                                         static_cast<size_t>(kWavesPerWG) * qw
-                                   : static_cast<size_t>(kWavesPerWG) * (hist_words + qw);
+// The bin-table kernel's variants: histogram columns (1 or kHistCols) and the share of table
+// reads made through the vector L1 instead of LDS (0: none; 1: a quarter; 2: three eighths).
+struct LutVariant {
+  int cols = 1;
+  int l1 = 2;
+};
+
+// LDS bytes of one pair-kernel workgroup: histogram(s), the core's table (table_words, shared-
+// histogram mode only) and one recheck queue per wave.
+inline size_t pairs_lds_bytes(int32_t hist_words, bool shared_hist, int k, int core, bool d64, int waves,
+                              int32_t table_words = 0) {
+  const size_t qw = static_cast<size_t>(queue_words(k, core, d64));
+  const size_t words = shared_hist ? hist_words + static_cast<size_t>(table_words) + static_cast<size_t>(waves) * qw
+                                   : static_cast<size_t>(waves) * (hist_words + qw);
   return words * sizeof(uint32_t);
 }
-// Histogram words of the edge-table core: bins -1 .. nbins + 63 (64 spares, as in core32).
-inline int32_t etab_hist_words(int32_t nbins) { return (nbins + 1 + 64 + 63) / 64 * 64; }
-// The edge table's LDS region (words): e_r at word r, the histogram right after it, so that
-// the count of bin r sits a fixed 4 (kEtabTableWords + 1) bytes past e_r (bin -1 first), an
-// offset the LDS atomic carries in its instruction.
-constexpr int kEtabTableWords = 4096;
-// Words of the core's table in LDS: the bin table (2 per entry), or the edge-table region.
-inline int32_t table_words(const PairArgs &a, bool dot64, int core) {
-  if (dot64) return 0;
-  if (core == 2) return 2 * (a.bp.lut_n + 1);
-  if (core >= 3) return kEtabTableWords;
-  return 0;
+// Histogram words of the bin-table core: one column with 64 spare rows and the two alias rows, or
+// kHistCols columns of nbins + 3 rows (one spare row, two alias rows).
+inline int32_t lut_hist_words(int32_t nbins, int cols) {
+  return cols == 1 ? (nbins + kWave + kLutAliasWords + 63) / 64 * 64 : (cols * (nbins + 3) + 63) / 64 * 64;
 }
+// Words of the core's table in LDS: the bin table (2 per entry).
+inline int32_t table_words(int32_t lut_n, bool dot64, int core) { return (!dot64 && core == 2) ? 2 * (lut_n + 1) : 0; }
 
 // Records a failed HIP call for gc_last_device_error() (gc_api.cpp).
 void record_hip_error(hipError_t e);
@@ -156,12 +164,17 @@ hipError_t launch_prepare(const float *ra, const float *dec, int64_t n, void *bl
 // 1 the one specialised to the bins' span - fp32 dot: nbins w covers 180 deg (no clamp of t,
 // spare bin instead); fp64 dot: nbins w <= 90 deg (no sign handling); 2 - fp32 dot: the
 // bin-table core (full span, shared histogram); fp64 dot: the series core (bins ending by ~9 deg)
-hipError_t launch_pairs(const PairArgs &a, int num_wg, bool dot64, int k, int core, hipStream_t s);
-hipError_t pairs_occupancy(bool dot64, int k, int core, size_t lds_bytes, int *blocks_per_cu);
-hipError_t launch_lut(int32_t nbins, double w_deg, int32_t m, double margin, uint2 *lut, hipStream_t s);
+// lv: the bin-table kernel's variant (core 2, fp32 dot only).
+hipError_t launch_pairs(const PairArgs &a, int num_wg, bool dot64, int k, int core, LutVariant lv, hipStream_t s);
+hipError_t pairs_occupancy(bool dot64, int k, int core, LutVariant lv, size_t lds_bytes, int threads,
+                           int *blocks_per_cu);
+// The bin table: 2 m + 1 entries; cols: the histogram's columns (scales the row offsets);
+// alias: the middle entry's row when it holds no recheck zone; s_star > 0: entries whose |c| may
+// lie below s_star hold NaN (always recheck).
+hipError_t launch_lut(int32_t nbins, double w_deg, int32_t m, double margin, int cols, int32_t alias, double s_star,
+                      uint2 *lut, hipStream_t s);
 hipError_t launch_eval_dot_mfma(const float *ax, const float *ay, const float *az, const float *bx, const float *by,
                                 const float *bz, int64_t ntiles, float *out, hipStream_t s);
-hipError_t launch_etab(int32_t nbins, double w_deg, double g_x, double e3, uint32_t *et, hipStream_t s);
 // accumulate: add the sums to the outputs instead of overwriting them
 hipError_t launch_merge(const unsigned long long *slots, int32_t nbins, const int32_t wg_begin[3],
                         const int32_t wg_end[3], uint64_t *out[3], bool accumulate, hipStream_t s);

@@ -14,11 +14,11 @@
 //                    as VALU operands) instead of being staged in LDS; the bin-table core
 //                    instead takes its dot products from the matrix cores, 16 i x 16 j at a
 //                    time.  Per pair: dot product, then one of the cores (an arccos of
-//                    sqrt times a fitted polynomial; the bin table; the edge table; the
-//                    series), bin index, certified guard; ds_add_u32 into an LDS histogram.
+//                    sqrt times a fitted polynomial; the bin table; the series), bin index,
+//                    certified guard; ds_add_u32 into an LDS histogram.
 //                    Pairs the guard cannot certify are queued in LDS and re-binned in fp64,
 //                    64 at a time with all lanes busy.
-//   lut_kernel, etab_kernel - build the bin table and the edge table (fp64).
+//   lut_kernel     - builds the bin table (fp64).
 //   merge_kernel   - sums the per-workgroup 64-bit partial histograms into the outputs.
 //   totals_kernel  - per-family sums (wave-shuffle reduction) for the exact N^2 check.
 //   omega_kernel   - Landy-Szalay estimator in fp64.
@@ -173,21 +173,23 @@ __device__ __forceinline__ void core64(double x, const BinParams &bp, float pw6_
 // can never select an entry without the edge a pair is near.
 // lut_key: fma(c, M, M + 2^23) is 2^23 + q exactly (one rounding of M (c + 1) + 2^23 to an
 // integer), so q is the key's bit pattern minus that of 2^23.
-__device__ __forceinline__ float lut_key(float x, const BinParams &bp, float &c) {
+// mb: M + 2^23 (bp.lut_mb); the pair kernel passes it held in a VGPR.
+__device__ __forceinline__ float lut_key(float x, const BinParams &bp, float mb, float &c) {
   const float s = __builtin_amdgcn_sqrtf(__builtin_amdgcn_fmed3f(1.0f - fabsf(x), 0.0f, 1.0f));
   c = copysignf(s, x);
-  return fmaf(c, bp.lut_m, bp.lut_mb);
+  return fmaf(c, bp.lut_m, mb);
 }
 constexpr uint32_t kLutKeyBias = 0x4B000000u;  // bit pattern of 2^23
 
-// The core with the table in global memory (diagnostic kernel): entry = {e bits, 4 B}.
+// The core with the table in global memory (diagnostic kernel): entry = {e bits, row offset of B}.
+// A NaN e (an always-recheck entry) fails the guard's comparison, so the pair trips.
 __device__ __forceinline__ void core_lut(float x, const BinParams &bp, const uint2 *tab, uint32_t &k, bool &trip,
                                          float &c_raw) {
   float c;
-  const uint2 ent = tab[__float_as_uint(lut_key(x, bp, c)) - kLutKeyBias];
+  const uint2 ent = tab[__float_as_uint(lut_key(x, bp, bp.lut_mb, c)) - kLutKeyBias];
   const float d = __uint_as_float(ent.x) - x;
-  trip = fabsf(d) < bp.lut_g;
-  k = (ent.y >> 2) - (__float_as_uint(d) >> 31);
+  trip = !(fabsf(d) >= bp.lut_g);
+  k = (ent.y >> bp.lut_sh) - (__float_as_uint(d) >> 31);
   c_raw = c;
 }
 
@@ -207,28 +209,8 @@ __device__ __forceinline__ uint2 lut_read_lds(float key, uint32_t tab_bias) {
 }
 __device__ __forceinline__ uint32_t lut_word_address(float x, uint2 ent, const BinParams &bp, bool &trip) {
   const float d = __uint_as_float(ent.x) - x;
-  trip = fabsf(d) < bp.lut_g;
+  trip = !(fabsf(d) >= bp.lut_g);  // NaN e (always-recheck entry): trips
   return (static_cast<uint32_t>(__float_as_int(d) >> 31) << bp.lut_sh) + ent.y;
-}
-
-// Edge-table core (fp32 dot, bins covering 0..180 deg that are too fine for the bin table).  A
-// degree-3 arccos (error 6.8e-5 rad) gives t~ = theta~ / w to a fraction of a bin, and
-// r = round(t~), read from the bits of t~ + 2^23, names the one edge that can lie between t~
-// and the pair's true t: edge r, at cos(r w) = e_r.  The side is decided on the cosine, as in
-// the bin-table core: bin = r - [x > e_r], recheck iff !(|e_r - x| >= lut_g).  Where the dot
-// product's error can move t~ by half a bin (near 0 and 180 deg, where s is small), e_r is NaN:
-// the test fails and the pair is rechecked.  Past 180 deg (r >= nbins) e_r = -4: bin r - 1.
-__device__ __forceinline__ float etab_t(float x, const BinParams &bp, float h_v) {
-  const float a = fabsf(x);
-  const float s = __builtin_amdgcn_sqrtf(__builtin_amdgcn_fmed3f(1.0f - a, 0.0f, 1.0f));
-  float p = fmaf(GC_ACOS3_C3, a, GC_ACOS3_C2);
-  p = fmaf(p, a, GC_ACOS3_C1);
-  p = fmaf(p, a, GC_ACOS3_C0);
-  const float q = fmaf(-s, p, kHalfPiF);
-  return fmaf(copysignf(q, x), -bp.invw, h_v);
-}
-__device__ __forceinline__ float etab_key(float x, const BinParams &bp, float h_v) {
-  return etab_t(x, bp, h_v) + 8388608.0f;  // 2^23 + round(t~)
 }
 
 // Exact recheck in the cosine domain.  theta >= e w  <=>  x <= cos(e w), so bin k holds x
@@ -286,27 +268,42 @@ template <> struct Real<false> { typedef float T; };
 template <> struct Real<true> { typedef double T; };
 
 // Re-bin the c <= 64 queued pairs in entries [first, first + c) exactly in fp64 (one pair
-// per lane) and move their counts from the fast-path bin to the exact bin.  Entry e: word
-// 2e = j, word 2e+1 = (i - i0) << 16 | (fast-path bin + 1).  A fast-path bin >= nbins is a
-// spare bin standing for bin nbins - 1; bin -1 (edge-table core) stands for nothing, so its
-// count always moves.
+// per lane) and move their counts from the fast-path row to the exact bin's row.  Entry e:
+// word 2e = j, word 2e+1 = (i - i0) << 16 | (fast-path row + 1); both fields fit in 16 bits
+// (i - i0 < 64 K <= 512 and rows < kMaxBins + 66, checked at compile time).
+// A fast-path row >= nbins is a spare row standing for bin nbins - 1.  The counts move in the lane's own column of a
+// multi-column histogram (any column serves: the flush sums them).  The walk to the exact bin
+// starts from the fast-path row, or, when that row lies on the other side of 90 deg from the pair
+// (an always-recheck table entry near 0 or 180 deg), from the end of the range on the pair's side.
+// The rows of i and j are clamped into their catalogs and the fast-path row into the histogram's
+// rows, so even a corrupted entry cannot read or write past them.
+template <int COLS>
 __device__ __forceinline__ void drain_queue(uint32_t *hist, const uint32_t *queue, int first, int c,
-                                            const Prepared &ci, const Prepared &cj, int64_t i0, uint32_t w,
-                                            const double *edge_cos, int32_t nbins) {
+                                            const Prepared &ci, const Prepared &cj, int64_t i0, int64_t n_i,
+                                            int64_t n_j, uint32_t w, const double *edge_cos, int32_t nbins, int32_t b90,
+                                            int32_t b180, int32_t rows) {
   const int lane = threadIdx.x & (kWave - 1);
   __builtin_amdgcn_wave_barrier();
   if (lane < c) {
     const int e = first + lane;
-    const uint32_t jj = queue[2 * e];
+    const int64_t jq = queue[2 * e];
+    const int64_t jj = jq < n_j ? jq : n_j - 1;
     const uint32_t p = queue[2 * e + 1];
-    const int kf = static_cast<int>(p & 0xffffu) - 1;
+    int kf = static_cast<int>(p & 0xffffu) - 1;
+    kf = kf < rows ? kf : rows - 1;
     const int last = nbins - 1;
-    const int kr = kf < 0 ? 0 : (kf < last ? kf : last);
-    const int ke = static_cast<int>(exact_bin(dot64(ci, i0 + (p >> 16), cj, jj), static_cast<uint32_t>(kr),
-                                              edge_cos, nbins));
-    if (ke != kr || kf < 0) {
-      atomicSub(hist + kf, w);
-      atomicAdd(hist + ke, w);
+    int kr = kf < 0 ? 0 : (kf < last ? kf : last);
+    int64_t ig = i0 + static_cast<int64_t>(p >> 16);
+    ig = ig < n_i ? ig : n_i - 1;
+    const double x = dot64(ci, ig, cj, jj);
+    // a start on the wrong side of 90 deg (b90: the bin holding 90 deg) jumps to that side's end
+    if (x < 0.0 && kr < b90) kr = b180;
+    if (x > 0.0 && kr > b90) kr = 0;
+    const int ke = static_cast<int>(exact_bin(x, static_cast<uint32_t>(kr), edge_cos, nbins));
+    if (ke != kf) {
+      const int col = COLS > 1 ? (lane & (COLS - 1)) : 0;
+      atomicSub(hist + kf * COLS + col, w);
+      atomicAdd(hist + ke * COLS + col, w);
     }
   }
   __builtin_amdgcn_wave_barrier();
@@ -314,25 +311,29 @@ __device__ __forceinline__ void drain_queue(uint32_t *hist, const uint32_t *queu
 
 // CORE 0: the generic core; 1: the core specialised to the bins' span (fp32 dot, full span;
 // fp64 dot, narrow range); 2: fp32 dot, the bin-table core on the fast steps (matrix-core dot
-// products, a shared histogram and the table in LDS), fp64 dot, the series core; 3 (fp32 dot):
-// the edge-table core on the fast steps (shared histogram after the table in LDS); 4: the same
-// with the key from one fma, for widths where h = (pi/2) / w is an integer.  The generic steps
-// of cores 2 to 4 (fp32) use the full-span core.  Register budgets: K = 4 builds for six
+// products, a shared histogram and the table in LDS), fp64 dot, the series core.  The generic
+// steps of the bin-table core use the full-span core.  Register budgets: K = 4 builds for six
 // waves per SIMD (<= 80 VGPRs), fp32 K = 8 for five (<= 96; its 24 fp32 i-coordinates, or the
 // 32 matrix-core tiles), fp64 K = 8 for four (48 VGPRs of fp64 i-coordinates).  Measured on
 // the 100k workloads, each step up in waves per SIMD outweighed the few spills it costs outside
-// the pair loop.
-template <int K, bool D64, int CORE>
-__global__ void __launch_bounds__(kWGThreads)
-__attribute__((amdgpu_waves_per_eu(K == 4 ? 6 : (D64 ? 4 : 5))))
+// the pair loop.  The bin-table core also builds at K = 2 for eight waves per SIMD (<= 64 VGPRs).
+// The bin-table core (CORE 2, fp32 dot) also takes COLS, its histogram's columns (1 or
+// kHistCols), and L1S, the share of its table reads made through the vector L1 (0 none, 1 a
+// quarter, 2 three eighths); its workgroups hold up to kMaxWavesPerWG waves (A.waves), all sharing
+// one table and one histogram.  The other cores run kWavesPerWG waves per workgroup.
+template <int K, bool D64, int CORE, int COLS = 1, int L1S = 2>
+__global__ void __launch_bounds__((CORE == 2 && !D64) ? kMaxWavesPerWG * kWave : kWGThreads)
+__attribute__((amdgpu_waves_per_eu(K == 2 ? 8 : (K == 4 ? 6 : (D64 ? 4 : 5)))))
 pairs_kernel(const PairArgs A) {
   typedef typename Real<D64>::T real;
   constexpr bool SPAN = CORE != 0;
   constexpr bool LUT = CORE == 2 && !D64;  // fp64 dot: CORE 2 is the series core
-  constexpr bool ETAB = CORE >= 3;          // fp32 dot only
-  constexpr bool EFOLD = CORE == 4;         // edge table, key in one fma (integral h)
   constexpr int BI = kWave * K;       // i-block: galaxies per wave
   constexpr int JB = D64 ? 4 : 8;     // j galaxies per scalar batch
+  static_assert(COLS == 1 || (LUT && COLS == kHistCols), "multi-column histograms belong to the bin-table core");
+  static_assert(L1S == 2 || LUT, "the L1 share is a bin-table core variant");
+  // queue entries pack (i - i0) and the fast-path row + 1 into 16 bits each
+  static_assert(BI <= 0x10000 && kMaxBins + kWave + kLutAliasWords + 1 < 0x10000, "queue fields overflow");
   extern __shared__ uint32_t lds[];
 
   const int lane = threadIdx.x & (kWave - 1);
@@ -340,17 +341,20 @@ pairs_kernel(const PairArgs A) {
   // the step range, the loop counters and every j index in SGPRs (scalar loads of j, scalar
   // branches).
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int nw = A.waves;  // waves per workgroup (blockDim.x / 64)
+  const int nthreads = nw * kWave;
   // LDS: private mode, per wave [histogram | queue]; shared mode, [histogram | bin table |
-  // 4 queues] (the table only with the bin-table core); edge-table core, [edge cosines
-  // (kEtabTableWords) | histogram of bins -1 .. | 4 queues].
-  const bool shared_hist = LUT || ETAB || A.shared_hist != 0;
-  constexpr int QW = queue_words(K, CORE);
+  // one queue per wave] (the table only with the bin-table core).
+  const bool shared_hist = LUT || A.shared_hist != 0;
+  constexpr int QW = queue_words(K, CORE, D64);
   const int tab_words = LUT ? 2 * (A.bp.lut_n + 1) : 0;
-  uint32_t *const hist = ETAB ? lds + kEtabTableWords + 1 : (shared_hist ? lds : lds + wv * (A.hist_words + QW));
+  uint32_t *const hist = shared_hist ? lds : lds + wv * (A.hist_words + QW);
   uint2 *const tab = reinterpret_cast<uint2 *>(lds + A.hist_words);
-  uint32_t *const queue = ETAB ? lds + kEtabTableWords + A.hist_words + wv * QW
-                               : (shared_hist ? lds + A.hist_words + tab_words + wv * QW : hist + A.hist_words);
+  uint32_t *const queue = shared_hist ? lds + A.hist_words + tab_words + wv * QW : hist + A.hist_words;
   const uint32_t hist_addr = lds_address(hist);
+  // a multi-column histogram: this lane's column, and its byte offset within a row
+  const int colw = COLS > 1 ? (lane & (COLS - 1)) : 0;
+  const uint32_t col4 = static_cast<uint32_t>(4 * colw);
   const uint32_t tab_bias = lds_address(tab) - (kLutKeyBias << 3);
   // the global table's copy: entry q at byte (key bits << 3) - (bits of 2^23 << 3), a 32-bit offset
   // (one shift-and-add) that the load adds to the table's address held in scalar registers
@@ -359,9 +363,6 @@ pairs_kernel(const PairArgs A) {
     const uint32_t off = (__float_as_uint(key) << 3) - (kLutKeyBias << 3);
     return *reinterpret_cast<const uint2 *>(lut_l1 + off);
   };
-  // edge-table core: e_r at lds + 4 r, read from the key's bits
-  const uint32_t etab_base = lds_address(lds);
-  const uint32_t etab_bias = etab_base - (kLutKeyBias << 2);
   const int g = blockIdx.x;
   const int fi = g < A.fam[0].wg_end ? 0 : (g < A.fam[1].wg_end ? 1 : 2);
   const FamilyWork &F = A.fam[fi];
@@ -369,21 +370,17 @@ pairs_kernel(const PairArgs A) {
   const uint32_t W = F.sym ? 2u : 1u;
   // the one wave-uniform constant each core needs in a VGPR, and this lane's clamp
   const float c_v = in_vgpr(D64 ? (CORE == 2 ? bp.ps[2] : bp.pw[6]) : bp.h);
-  // the one-fma edge-table key's addend, h + 2^23, in a VGPR of its own (c_v = h also serves the
-  // generic steps' arccos core)
-  const float hk_v = in_vgpr(EFOLD ? bp.etab_hk : 0.0f);
+  // the bin table's key addend M + 2^23, in a VGPR of its own (a VALU fma reads one scalar operand;
+  // c_v = h serves the generic steps' arccos core)
+  const float mb_v = in_vgpr(LUT ? bp.lut_mb : 0.0f);
   const float tmax_v = bp.tmax + static_cast<float>(lane);
 
   unsigned long long *const slot = A.slots + static_cast<size_t>(g) * A.nbins;
-  for (int b = threadIdx.x; b < A.nbins; b += kWGThreads) slot[b] = 0ull;
-  if constexpr (ETAB) {
-    const uint32_t *et = reinterpret_cast<const uint32_t *>(A.lut);
-    for (int q = threadIdx.x; q <= A.bp.lut_n; q += kWGThreads) lds[q] = et[q];
-    for (int b = threadIdx.x; b < A.hist_words; b += kWGThreads) hist[b - 1] = 0u;  // bins -1 ..
-  } else if (shared_hist) {
-    for (int b = threadIdx.x; b < A.hist_words; b += kWGThreads) hist[b] = 0u;
+  for (int b = threadIdx.x; b < A.nbins; b += nthreads) slot[b] = 0ull;
+  if (shared_hist) {
+    for (int b = threadIdx.x; b < A.hist_words; b += nthreads) hist[b] = 0u;
     if constexpr (LUT)
-      for (int q = threadIdx.x; q <= A.bp.lut_n; q += kWGThreads) {
+      for (int q = threadIdx.x; q <= A.bp.lut_n; q += nthreads) {
         const uint2 e = A.lut[q];
         tab[q] = make_uint2(e.x, hist_addr + e.y);
       }
@@ -400,8 +397,8 @@ pairs_kernel(const PairArgs A) {
   //             ragged last i-block: per-pair weights and validity, a rolled loop, slower.
   // (Giving each wave one contiguous range of all steps left the generic-heavy tail of the
   // triangle, and the ragged block, to the last few waves, which then finished late.)
-  const int64_t V = static_cast<int64_t>(F.wg_end - F.wg_begin) * kWavesPerWG;
-  const int64_t v = static_cast<int64_t>(g - F.wg_begin) * kWavesPerWG + wv;
+  const int64_t V = static_cast<int64_t>(F.wg_end - F.wg_begin) * nw;
+  const int64_t v = static_cast<int64_t>(g - F.wg_begin) * nw + wv;
   auto share = [&](int64_t begin, int64_t total, int64_t &lo, int64_t &hi) __attribute__((always_inline)) {
     const int64_t q = total / V, r = total % V;
     lo = begin + q * v + (r * v) / V;
@@ -414,6 +411,8 @@ pairs_kernel(const PairArgs A) {
 
   int64_t since_flush = 0;
   int qcount = 0;  // queue entries [0, qcount) are pending
+  // histogram rows: bins, spare rows and the bin table's alias rows
+  const int hist_rows = COLS > 1 ? A.nbins + 3 : A.hist_words;
   const uint32_t lane_tag = static_cast<uint32_t>(lane) << 16;
   int64_t i0 = 0;
   real ix[K], iy[K], iz[K];
@@ -421,7 +420,8 @@ pairs_kernel(const PairArgs A) {
   // The queue is drained (64 at a time, from the top) after every j-step and within it after
   // every drain_span pairs per lane, so it never holds more than 64 (drain_span + 1) entries.
   auto drain = [&](int c) __attribute__((always_inline)) {
-    drain_queue(hist, queue, qcount - c, c, F.ci, F.cj, i0, W, A.edge_cos, A.nbins);
+    drain_queue<COLS>(hist, queue, qcount - c, c, F.ci, F.cj, i0, F.n_i, F.n_j, W, A.edge_cos, A.nbins, A.bp.b90,
+                      A.bp.b180, hist_rows);
     qcount -= c;
   };
   auto drain_all = [&]() __attribute__((always_inline)) {
@@ -431,29 +431,62 @@ pairs_kernel(const PairArgs A) {
   auto drain_full = [&]() __attribute__((always_inline)) {
     while (__builtin_expect(qcount >= kWave, 0)) drain(kWave);
   };
-  // Move the LDS histogram into the workgroup's 64-bit slot.  Each bin is taken with an
+  // The bin a histogram row counts for: bins 0 .. nbins - 1 themselves; the spare rows past the
+  // last bin count for bin nbins - 1; the bin table's two alias rows for bins 0 and b180.
+  auto row_bin = [&](int row) __attribute__((always_inline)) {
+    if (row < A.nbins) return row;
+    if (LUT && row == A.bp.lut_alias - 1) return 0;
+    if (LUT && row == A.bp.lut_alias) return static_cast<int>(A.bp.b180);
+    return A.nbins - 1;
+  };
+  // Move the LDS histogram into the workgroup's 64-bit slot.  Each word is taken with an
   // atomic exchange, so in shared mode other waves may keep adding meanwhile; the value is
   // read as signed because a pending recheck may have moved a count out of a bin that an
-  // earlier flush already emptied (the flush interval keeps every bin within +-2^31).  The
-  // 64 spare bins past nbins are summed across the wave and added to bin nbins - 1.
+  // earlier flush already emptied (the flush interval keeps every word within +-2^31).  The
+  // rows past nbins are added to the bins they stand for.
   auto flush = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_wave_barrier();
-    for (int bb = lane; bb < A.nbins; bb += kWave) {
-      const uint32_t c = atomicExch(hist + bb, 0u);
-      if (c) atomicAdd(slot + bb, static_cast<unsigned long long>(static_cast<long long>(static_cast<int>(c))));
-    }
-    long long spare = static_cast<int>(atomicExch(hist + A.nbins + lane, 0u));
-    if constexpr (LUT) {
-      // the middle table entry's two words: bin 0 and bin b180 (the angles just below 180 deg)
-      if (lane < kLutAliasWords) {
-        const long long a = static_cast<int>(atomicExch(hist + A.nbins + kWave + lane, 0u));
-        if (a) atomicAdd(slot + (lane == 0 ? 0 : A.bp.b180), static_cast<unsigned long long>(a));
-      }
-    }
+    if constexpr (COLS > 1) {
+      for (int row = lane; row < hist_rows; row += kWave) {
+        long long c = 0;
 #pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) spare += __shfl_xor(spare, off, kWave);
-    if (lane == 0 && spare) atomicAdd(slot + (A.nbins - 1), static_cast<unsigned long long>(spare));
+        for (int q = 0; q < COLS; ++q) c += static_cast<int>(atomicExch(hist + row * COLS + q, 0u));
+        if (c) atomicAdd(slot + row_bin(row), static_cast<unsigned long long>(c));
+      }
+    } else {
+      for (int bb = lane; bb < A.nbins; bb += kWave) {
+        const uint32_t c = atomicExch(hist + bb, 0u);
+        if (c) atomicAdd(slot + bb, static_cast<unsigned long long>(static_cast<long long>(static_cast<int>(c))));
+      }
+      long long spare = static_cast<int>(atomicExch(hist + A.nbins + lane, 0u));
+      if constexpr (LUT) {
+        // the middle table entry's two words: bin 0 and bin b180 (the angles just below 180 deg)
+        if (lane < kLutAliasWords) {
+          const long long a = static_cast<int>(atomicExch(hist + A.nbins + kWave + lane, 0u));
+          if (a) atomicAdd(slot + (lane == 0 ? 0 : A.bp.b180), static_cast<unsigned long long>(a));
+        }
+      }
+#pragma unroll
+      for (int off = kWave / 2; off > 0; off >>= 1) spare += __shfl_xor(spare, off, kWave);
+      if (lane == 0 && spare) atomicAdd(slot + (A.nbins - 1), static_cast<unsigned long long>(spare));
+    }
     __builtin_amdgcn_wave_barrier();
+  };
+  // The last flush of a shared histogram: once every wave of the workgroup is done adding, the
+  // rows are split among all of its threads (each row read once) instead of each wave taking the
+  // whole histogram in turn.
+  auto final_flush = [&]() __attribute__((always_inline)) {
+    if (!shared_hist) {
+      flush();
+      return;
+    }
+    __syncthreads();
+    for (int row = threadIdx.x; row < hist_rows; row += nthreads) {
+      long long c = 0;
+#pragma unroll
+      for (int q = 0; q < COLS; ++q) c += static_cast<int>(hist[row * COLS + q]);
+      if (c) atomicAdd(slot + row_bin(row), static_cast<unsigned long long>(c));
+    }
   };
   auto load_j = [&](int64_t jj, real &x, real &y, real &z) __attribute__((always_inline)) {
     if constexpr (D64) {
@@ -467,7 +500,7 @@ pairs_kernel(const PairArgs A) {
   // wave's queue right after their atomic (each bin index dies at once), and the queue is
   // drained in full-wave batches after the step.
   // Append a flagged pair (this lane's k-th i against j) to the wave's queue; kslot = its
-  // fast-path bin + 1.
+  // fast-path row + 1.
   // (The flag, drain and flush tests are marked unlikely, so that the common path falls through
   // them instead of taking a branch a pair: 1-3 % on every core.)
   auto enqueue = [&](bool tp, uint32_t kslot, int k, int64_t jg) __attribute__((always_inline)) {
@@ -500,6 +533,22 @@ pairs_kernel(const PairArgs A) {
     }
   };
 
+  // Which of a lane's table reads go through the vector L1 (the rest read the LDS copy): a random
+  // 64-lane LDS read costs ~7 CU cycles, the same read through the vector L1 ~37, and the LDS also
+  // takes every pair's atomic, so a share of the reads goes to the L1.  Scalar-j steps: pairs
+  // k = 1, 4, 7 of 8 (three eighths) or k = 1, 5 (a quarter); matrix-core tiles: result r = 1, and
+  // r = 3 of odd tiles (three eighths), or r = 1 (a quarter).
+  auto l1_scalar = [](int k) constexpr { return L1S == 2 ? k % 3 == 1 : (L1S == 1 ? k % 4 == 1 : false); };
+  auto l1_tile = [](int r, int t) constexpr {
+    return L1S == 2 ? (r == 1 || (r == 3 && (t & 1))) : (L1S == 1 ? r == 1 : false);
+  };
+  // The histogram row address of a bin-table pair: (sign of e - x) << lut_sh plus the entry's row
+  // address, plus this lane's column; an L1 entry holds the row's offset, the LDS copy its address.
+  const uint32_t l1_base = hist_addr + col4;
+  auto lut_row_address = [&](float x, uint2 ent, bool from_l1, bool &trip) __attribute__((always_inline)) {
+    return lut_word_address(x, ent, bp, trip) + (from_l1 ? l1_base : col4);
+  };
+
   auto step = [&](real xj, real yj, real zj, int64_t jg, auto generic_tag) __attribute__((always_inline)) {
     constexpr bool GENERIC = decltype(generic_tag)::value;
     if constexpr (LUT && !GENERIC) {
@@ -510,48 +559,18 @@ pairs_kernel(const PairArgs A) {
       for (int k = 0; k < K; ++k) {
         float c_unused;
         xv[k] = fmaf(ix[k], xj, fmaf(iy[k], yj, iz[k] * zj));
-        const float key = lut_key(xv[k], bp, c_unused);
-        // A random 64-lane LDS read costs ~7 CU cycles, the same read through the vector L1
-        // ~36; the LDS also takes every pair's atomic.  Reading the table of 3 pairs in 8 from
-        // global memory (the workspace copy, L1-resident) balances the two paths.
-        if (k % 3 == 1) {
-          ev[k] = lut_read_l1(key);
-          ev[k].y += hist_addr;  // (the LDS copy holds this sum; 0 when the histogram starts LDS)
-        } else {
-          ev[k] = lut_read_lds(key, tab_bias);
-        }
+        const float key = lut_key(xv[k], bp, mb_v, c_unused);
+        if (l1_scalar(k)) ev[k] = lut_read_l1(key);
+        else ev[k] = lut_read_lds(key, tab_bias);
       }
 #pragma unroll
       for (int k = 0; k < K; ++k) {
         bool tp;
-        const uint32_t a = lut_word_address(xv[k], ev[k], bp, tp);
+        const uint32_t a = lut_row_address(xv[k], ev[k], l1_scalar(k), tp);
         __hip_atomic_fetch_add(reinterpret_cast<lds_word_t *>(static_cast<uintptr_t>(a)), W, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_WORKGROUP);
-        enqueue(tp, ((a - hist_addr) >> 2) + 1, k, jg);
-        if ((k + 1) % drain_span(K, CORE) == 0 && k + 1 < K) drain_full();
-      }
-    } else if constexpr (ETAB && !GENERIC) {
-      // all K edge-cosine reads first, so one LDS wait covers them
-      float xv[K], ev[K];
-      uint32_t av[K];
-#pragma unroll
-      for (int k = 0; k < K; ++k) {
-        xv[k] = fmaf(ix[k], xj, fmaf(iy[k], yj, iz[k] * zj));
-        const float key = EFOLD ? etab_t(xv[k], bp, hk_v) : etab_key(xv[k], bp, c_v);
-        av[k] = (__float_as_uint(key) << 2) + etab_bias;
-        ev[k] = *reinterpret_cast<__attribute__((address_space(3))) const float *>(static_cast<uintptr_t>(av[k]));
-      }
-#pragma unroll
-      for (int k = 0; k < K; ++k) {
-        const float d = ev[k] - xv[k];
-        const bool tp = !(fabsf(d) >= bp.lut_g);
-        // e of bin r - [d < 0]'s upper edge; the bin's count sits kEtabTableWords + 1 words on
-        // (the atomic's constant offset)
-        const uint32_t a = (static_cast<uint32_t>(__float_as_int(d) >> 31) << bp.lut_sh) + av[k];
-        __hip_atomic_fetch_add(reinterpret_cast<lds_word_t *>(static_cast<uintptr_t>(a)) + (kEtabTableWords + 1), W,
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        enqueue(tp, ((a - etab_base) >> 2) + 1, k, jg);
-        if ((k + 1) % drain_span(K, CORE) == 0 && k + 1 < K) drain_full();
+        enqueue(tp, ((a - hist_addr) >> bp.lut_sh) + 1, k, jg);
+        if ((k + 1) % drain_span(K, CORE, D64) == 0 && k + 1 < K) drain_full();
       }
     } else {
 #pragma unroll
@@ -570,12 +589,12 @@ pairs_kernel(const PairArgs A) {
           const bool self = F.sym && jg == ig;  // only a self family pairs a galaxy with itself
           if (self) kk = 0u;                     // separation 0
           tp = tp && valid && !self;
-          if (valid) atomicAdd(hist + kk, self ? 1u : W);
+          if (valid) atomicAdd(hist + kk * COLS + colw, self ? 1u : W);
         } else {
-          atomicAdd(hist + kk, W);
+          atomicAdd(hist + kk * COLS + colw, W);
         }
         enqueue(tp, kk + 1, k, jg);
-        if ((k + 1) % drain_span(K, CORE) == 0 && k + 1 < K) drain_full();
+        if ((k + 1) % drain_span(K, CORE, D64) == 0 && k + 1 < K) drain_full();
       }
     }
     drain_full();
@@ -644,7 +663,7 @@ pairs_kernel(const PairArgs A) {
   // lane l receives the dot products of i = i0 + 16 t + 4 (l / 16) + r, r = 0..3, with
   // j = j0 + l % 16.  The i-block of BI galaxies is BI / 16 such tiles, held as one VGPR each; a
   // chunk of 16 j-galaxies takes one vector load per lane.  The matrix cores run beside the VALU,
-  // which keeps only the binning (9 instructions a pair instead of 12).
+  // which keeps only the binning.
   constexpr int NT = LUT ? BI / 16 : 1;
   const int comp = lane >> 4, sub = lane & 15;
   float at[NT];
@@ -671,28 +690,31 @@ pairs_kernel(const PairArgs A) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           float c_unused;
-          const float key = lut_key(d[r], bp, c_unused);
-          // 3 pairs in 8 read the table through the vector L1, as in the scalar-j step
-          if (r == 1 || (r == 3 && (t & 1))) {
-            ev[r] = lut_read_l1(key);
-            ev[r].y += hist_addr;
-          } else {
-            ev[r] = lut_read_lds(key, tab_bias);
-          }
+          const float key = lut_key(d[r], bp, mb_v, c_unused);
+          if (l1_tile(r, t)) ev[r] = lut_read_l1(key);
+          else ev[r] = lut_read_lds(key, tab_bias);
         }
         // the atomics issue at raised wave priority, so one wave's LDS burst goes out while the
         // others bin (7.93 -> 7.82 ms on the 720-bin workload)
         __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
+        auto bin_pair = [&](int r) __attribute__((always_inline)) {
           bool tp;
-          const uint32_t a = lut_word_address(d[r], ev[r], bp, tp);
+          const uint32_t a = lut_row_address(d[r], ev[r], l1_tile(r, t), tp);
           __hip_atomic_fetch_add(reinterpret_cast<lds_word_t *>(static_cast<uintptr_t>(a)), W, __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_WORKGROUP);
-          enqueue_ij(tp, ((a - hist_addr) >> 2) + 1, static_cast<uint32_t>(16 * t + 4 * comp + r), jl);
-        }
+          enqueue_ij(tp, ((a - hist_addr) >> bp.lut_sh) + 1, static_cast<uint32_t>(16 * t + 4 * comp + r), jl);
+        };
+        // a drain point after every drain_span pairs of the lane's four (one or two)
+        constexpr int DS = drain_span(K, CORE, D64);
+        bin_pair(0);
+        if (DS == 1) drain_full();
+        bin_pair(1);
+        drain_full();
+        bin_pair(2);
+        if (DS == 1) drain_full();
+        bin_pair(3);
         __builtin_amdgcn_s_setprio(0);
-        drain_full();  // a tile adds at most 4 entries a lane
+        drain_full();
       }
       since_flush += 16;
       check_flush();
@@ -772,7 +794,7 @@ pairs_kernel(const PairArgs A) {
       j = F.sym ? (b + 1) * BI : 0;
     }
   }
-  flush();
+  final_flush();
 }
 
 // ------------------------------------------------------------------------------- edges
@@ -788,19 +810,24 @@ __global__ void __launch_bounds__(256) edges_kernel(int32_t nbins, double w_deg,
 // Entry q of the bin-table core (q = 0 .. 2M): c in [(q - 1/2)/M - 1, (q + 1/2)/M - 1] (the
 // index rounds), widened by `margin` on both sides.  An edge at angle e w (e = 1 .. nbins-1) sits
 // at c = sqrt2 sin(e w / 2) when e w <= 90 deg and at c = -sqrt2 cos(e w / 2) when e w >= 90 deg
-// (both for exactly 90).  With one edge in range: {cos(e w) rounded to fp32, 4 e (the byte offset
-// of the histogram word of the bin above the edge)}; with none: {4, 4 x the bin of the entry's
-// middle}.  The host only selects this core when no widened range can hold two edges.
+// (both for exactly 90).  With one edge in range: {cos(e w) rounded to fp32, the byte offset of the
+// histogram row of the bin above the edge}; with none: {4, the row of the bin of the entry's
+// middle}.  A row offset is 4 x cols x the row (cols: the histogram's columns).  s_star > 0: an
+// entry whose |c| may lie below s_star, where the error of c can exceed the margin, holds NaN
+// (every pair in it is rechecked) and the row of its middle's bin, bin 0 for the middle entry;
+// s_star == 0: the middle entry holds {0, row `alias`}.  The host only selects this core when no
+// widened range can hold two edges (and nbins >= 2, so rows 0 and 1 exist).
 __device__ __forceinline__ double lut_angle_deg(double c) {  // inverse of the map above
   constexpr double kSqrtHalf = 0.70710678118654752440, kDeg = 57.295779513082320877;
   return c >= 0.0 ? 2.0 * asin(fmin(c, 1.0) * kSqrtHalf) * kDeg : 180.0 - 2.0 * asin(fmin(-c, 1.0) * kSqrtHalf) * kDeg;
 }
 
-__global__ void __launch_bounds__(256) lut_kernel(int32_t nbins, double w_deg, int32_t m, double margin,
-                                                  uint2 *lut) {
+__global__ void __launch_bounds__(256) lut_kernel(int32_t nbins, double w_deg, int32_t m, double margin, int32_t cols,
+                                                  int32_t alias, double s_star, uint2 *lut) {
   const int q = blockIdx.x * blockDim.x + threadIdx.x;
   if (q > 2 * m) return;
   constexpr double kSqrt2 = 1.41421356237309504880, kRad = 3.14159265358979323846 / 180.0;
+  const uint32_t row_bytes = 4u * static_cast<uint32_t>(cols);
   const double lo = (static_cast<double>(q) - 0.5) / m - 1.0 - margin;
   const double hi = (static_cast<double>(q) + 0.5) / m - 1.0 + margin;
   int count = 0, edge = 0;
@@ -833,49 +860,32 @@ __global__ void __launch_bounds__(256) lut_kernel(int32_t nbins, double w_deg, i
       }
     }
   }
-  uint2 ent;
-  if (q == m && count == 0) {
-    ent.x = __float_as_uint(0.0f);                       // the middle entry (x near +-1)
-    ent.y = 4u * static_cast<uint32_t>(nbins + kWave + 1);  // x < 0: word nbins + 65; x > 0: nbins + 64
-  } else if (count >= 1) {
-    ent.x = __float_as_uint(static_cast<float>(cos(static_cast<double>(edge) * w_deg * kRad)));
-    ent.y = 4u * static_cast<uint32_t>(edge);  // the bin above the edge; the one below is edge - 1
-  } else {
+  // the smallest |c| of the entry's own (unwidened) range
+  const double c_lo = (static_cast<double>(q) - 0.5) / m - 1.0, c_hi = (static_cast<double>(q) + 0.5) / m - 1.0;
+  const double s_min = (c_lo <= 0.0 && c_hi >= 0.0) ? 0.0 : fmin(fabs(c_lo), fabs(c_hi));
+  auto mid_bin = [&]() {
     const double mid = fmin(fmax(static_cast<double>(q) / m - 1.0, -1.0), 1.0);
     int b = static_cast<int>(floor(lut_angle_deg(mid) / w_deg));
-    b = b < 0 ? 0 : (b > nbins - 1 ? nbins - 1 : b);
+    return b < 0 ? 0 : (b > nbins - 1 ? nbins - 1 : b);
+  };
+  uint2 ent;
+  if (s_star > 0.0 && s_min < s_star) {
+    // always recheck; the row is at least 1, so that B - 1 is a row too whatever sign e - x takes
+    // (the recheck moves the count from either to the exact bin)
+    ent.x = __float_as_uint(__builtin_nanf(""));
+    const int b = q == m ? 1 : mid_bin();
+    ent.y = row_bytes * static_cast<uint32_t>(b < 1 ? 1 : b);
+  } else if (q == m && count == 0) {
+    ent.x = __float_as_uint(0.0f);                        // the middle entry (x near +-1)
+    ent.y = row_bytes * static_cast<uint32_t>(alias);     // x < 0: row alias; x > 0: row alias - 1
+  } else if (count >= 1) {
+    ent.x = __float_as_uint(static_cast<float>(cos(static_cast<double>(edge) * w_deg * kRad)));
+    ent.y = row_bytes * static_cast<uint32_t>(edge);  // the bin above the edge; the one below is edge - 1
+  } else {
     ent.x = __float_as_uint(4.0f);  // e - x > 0 for every cosine: bin = B
-    ent.y = 4u * static_cast<uint32_t>(b);
+    ent.y = row_bytes * static_cast<uint32_t>(mid_bin());
   }
   lut[q] = ent;
-}
-
-// ------------------------------------------------------------------------------ edge table
-// e_r for r = 0 .. nbins + 1 (fp32 bits).  Entry r serves the pairs with t~ in [r - 1/2, r + 1/2].
-// Their true angle lies within err = (2.02 g_x / s + e3) / w + 2^-24 (t + 2h) 1.01 bins of t~,
-// where s >= the smallest sqrt(1 - |cos theta|) over the entry's angles widened by e3 (the
-// arccos error, rad): s is monotone on each side of 90 deg, so the ends decide.  When err <
-// 0.45 the true bin is r - 1 or r, and e_r = cos(r w) (edge r; -4 past 180 deg); otherwise NaN.
-__global__ void __launch_bounds__(256) etab_kernel(int32_t nbins, double w_deg, double g_x, double e3,
-                                                   uint32_t *et) {
-  const int r = blockIdx.x * blockDim.x + threadIdx.x;
-  if (r > nbins + 1) return;
-  constexpr double kPiD = 3.14159265358979323846;
-  const double w = w_deg * (kPiD / 180.0);
-  const double lo = (r - 0.5) * w - e3, hi = (r + 0.5) * w + e3;
-  float e;
-  if (!(lo > 0.0) || !(hi < kPiD)) {
-    e = __builtin_nanf("");
-  } else {
-    const double s_lo = sqrt(1.0 - fabs(cos(lo))), s_hi = sqrt(1.0 - fabs(cos(hi)));
-    const double s = fmin(s_lo, s_hi) * 0.999;
-    const double h = 0.5 * kPiD / w;
-    const double err = (2.02 * g_x / s + e3) / w + 0x1p-24 * (r + 0.5 + 2.0 * h) * 1.01;
-    if (!(err < 0.45)) e = __builtin_nanf("");
-    else if (r >= nbins || static_cast<double>(r) * w_deg >= 180.0) e = -4.0f;
-    else e = static_cast<float>(cos(static_cast<double>(r) * w));
-  }
-  et[r] = __float_as_uint(e);
 }
 
 // ------------------------------------------------------------------------------- merge
@@ -971,24 +981,15 @@ __global__ void __launch_bounds__(256) eval_core_kernel(const float *x32, const 
     xe = static_cast<double>(xf);
     if constexpr (CORE == 2) {
       core_lut(xf, bp, lut, k, trip, t);  // (fp32 dot: CORE 2 is the table)
-    } else if constexpr (CORE >= 3) {
-      // edge table in global memory, e_r at index r; t_out = t~ (unrounded)
-      t = etab_t(xf, bp, bp.h);
-      const float key = CORE == 4 ? etab_t(xf, bp, bp.etab_hk) : t + 8388608.0f;
-      const uint32_t r = __float_as_uint(key) - kLutKeyBias;
-      const float d = __uint_as_float(reinterpret_cast<const uint32_t *>(lut)[r]) - xf;
-      trip = !(fabsf(d) >= bp.lut_g);
-      const int kb = static_cast<int>(r) - (__float_as_int(d) < 0 ? 1 : 0);
-      k = static_cast<uint32_t>(kb < 0 ? 0 : kb);
     } else {
       core32<SPAN>(xf, bp, bp.h, bp.tmax, k, trip, t);
     }
   }
   // k >= nbins: the full-span kernel's spare bins, which the flush folds into bin nbins - 1;
-  // the table's words nbins + 64 and nbins + 65 are bins 0 and b180
+  // the table's alias rows lut_alias - 1 and lut_alias are bins 0 and b180
   const uint32_t last = static_cast<uint32_t>(bp.nbins - 1);
-  if (CORE == 2 && !dot64 && k == static_cast<uint32_t>(bp.nbins + kWave)) k = 0;
-  if (CORE == 2 && !dot64 && k == static_cast<uint32_t>(bp.nbins + kWave + 1)) k = static_cast<uint32_t>(bp.b180);
+  if (CORE == 2 && !dot64 && k == static_cast<uint32_t>(bp.lut_alias - 1)) k = 0;
+  if (CORE == 2 && !dot64 && k == static_cast<uint32_t>(bp.lut_alias)) k = static_cast<uint32_t>(bp.b180);
   k = k < last ? k : last;
   bin_out[idx] = static_cast<int32_t>(k);
   trip_out[idx] = trip ? 1 : 0;
@@ -1028,39 +1029,51 @@ hipError_t launch_prepare(const float *ra, const float *dec, int64_t n, void *bl
   return hipGetLastError();
 }
 
-template <int K, bool D64, int CORE> static const void *pairs_fn() {
-  return reinterpret_cast<const void *>(&pairs_kernel<K, D64, CORE>);
+template <int K, bool D64, int CORE, int COLS = 1, int L1S = 2> static const void *pairs_fn() {
+  return reinterpret_cast<const void *>(&pairs_kernel<K, D64, CORE, COLS, L1S>);
 }
 
-// Instantiations: K in {4, 8} x {fp32, fp64 dot} x {generic, span-specialised core}, plus the
-// fp32 bin-table core and the fp64 series core.
-static const void *select_pairs(bool dot64, int k, int core) {
+template <int K> static const void *select_lut(LutVariant lv) {
+  if (lv.cols == kHistCols) {
+    if (lv.l1 == 2) return pairs_fn<K, false, 2, kHistCols, 2>();
+    if (lv.l1 == 1) return pairs_fn<K, false, 2, kHistCols, 1>();
+    return pairs_fn<K, false, 2, kHistCols, 0>();
+  }
+  if (lv.l1 == 2) return pairs_fn<K, false, 2, 1, 2>();
+  if (lv.l1 == 1) return pairs_fn<K, false, 2, 1, 1>();
+  return pairs_fn<K, false, 2, 1, 0>();
+}
+
+// Instantiations: K in {4, 8} x {fp32, fp64 dot} x {generic, span-specialised core}, the fp64
+// series core and the fp32 bin-table core's variants (columns x L1 share),
+// the bin-table core also at K = 2 (<= 64 VGPRs: eight waves per SIMD).
+static const void *select_pairs(bool dot64, int k, int core, LutVariant lv) {
   if (dot64) {
     if (core == 2) return k == 4 ? pairs_fn<4, true, 2>() : pairs_fn<8, true, 2>();
     if (core) return k == 4 ? pairs_fn<4, true, 1>() : pairs_fn<8, true, 1>();
     return k == 4 ? pairs_fn<4, true, 0>() : pairs_fn<8, true, 0>();
   }
-  if (core == 4) return k == 4 ? pairs_fn<4, false, 4>() : pairs_fn<8, false, 4>();
-  if (core == 3) return k == 4 ? pairs_fn<4, false, 3>() : pairs_fn<8, false, 3>();
-  if (core == 2) return k == 4 ? pairs_fn<4, false, 2>() : pairs_fn<8, false, 2>();
+  if (core == 2) return k == 2 ? select_lut<2>(lv) : (k == 4 ? select_lut<4>(lv) : select_lut<8>(lv));
   if (core) return k == 4 ? pairs_fn<4, false, 1>() : pairs_fn<8, false, 1>();
   return k == 4 ? pairs_fn<4, false, 0>() : pairs_fn<8, false, 0>();
 }
 
-hipError_t pairs_occupancy(bool dot64, int k, int core, size_t lds_bytes, int *blocks_per_cu) {
-  const void *fn = select_pairs(dot64, k, core);
+hipError_t pairs_occupancy(bool dot64, int k, int core, LutVariant lv, size_t lds_bytes, int threads,
+                           int *blocks_per_cu) {
+  const void *fn = select_pairs(dot64, k, core, lv);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      static_cast<int>(lds_bytes));
   if (e != hipSuccess) return e;
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, fn, kWGThreads, lds_bytes);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, fn, threads, lds_bytes);
 }
 
-hipError_t launch_pairs(const PairArgs &a, int num_wg, bool dot64, int k, int core, hipStream_t st) {
+hipError_t launch_pairs(const PairArgs &a, int num_wg, bool dot64, int k, int core, LutVariant lv, hipStream_t st) {
   const bool table = core >= 2 && !dot64;
-  const size_t lds = pairs_lds_bytes(a.hist_words, table || a.shared_hist != 0, k, core, table_words(a, dot64, core));
-  const void *fn = select_pairs(dot64, k, core);
+  const size_t lds = pairs_lds_bytes(a.hist_words, table || a.shared_hist != 0, k, core, dot64, a.waves,
+                                     table_words(a.bp.lut_n, dot64, core));
+  const void *fn = select_pairs(dot64, k, core, lv);
   void *args[] = {const_cast<PairArgs *>(&a)};
-  return hipLaunchKernel(fn, dim3(num_wg), dim3(kWGThreads), args, lds, st);
+  return hipLaunchKernel(fn, dim3(num_wg), dim3(a.waves * kWave), args, lds, st);
 }
 
 hipError_t launch_merge(const unsigned long long *slots, int32_t nbins, const int32_t wb[3],
@@ -1091,13 +1104,10 @@ hipError_t launch_eval_dot_mfma(const float *ax, const float *ay, const float *a
   return hipGetLastError();
 }
 
-hipError_t launch_etab(int32_t nbins, double w_deg, double g_x, double e3, uint32_t *et, hipStream_t st) {
-  hipLaunchKernelGGL(etab_kernel, dim3((nbins + 2 + 255) / 256), dim3(256), 0, st, nbins, w_deg, g_x, e3, et);
-  return hipGetLastError();
-}
-
-hipError_t launch_lut(int32_t nbins, double w_deg, int32_t m, double margin, uint2 *lut, hipStream_t st) {
-  hipLaunchKernelGGL(lut_kernel, dim3((2 * m + 1 + 255) / 256), dim3(256), 0, st, nbins, w_deg, m, margin, lut);
+hipError_t launch_lut(int32_t nbins, double w_deg, int32_t m, double margin, int cols, int32_t alias, double s_star,
+                      uint2 *lut, hipStream_t st) {
+  hipLaunchKernelGGL(lut_kernel, dim3((2 * m + 1 + 255) / 256), dim3(256), 0, st, nbins, w_deg, m, margin,
+                     static_cast<int32_t>(cols), alias, s_star, lut);
   return hipGetLastError();
 }
 
@@ -1111,13 +1121,7 @@ hipError_t launch_eval_core(const float *x32, const double *x64, int64_t n, cons
                             uint8_t *trip_out, int32_t *exact_out, float *t_out, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>((n + 255) / 256));
   const int d = dot64 ? 1 : 0;
-  if (core == 4)
-    hipLaunchKernelGGL(eval_core_kernel<4>, grid, dim3(256), 0, st, x32, x64, n, bp, d, lut, edge_cos, bin_out,
-                       trip_out, exact_out, t_out);
-  else if (core == 3)
-    hipLaunchKernelGGL(eval_core_kernel<3>, grid, dim3(256), 0, st, x32, x64, n, bp, d, lut, edge_cos, bin_out,
-                       trip_out, exact_out, t_out);
-  else if (core == 2)
+  if (core == 2)
     hipLaunchKernelGGL(eval_core_kernel<2>, grid, dim3(256), 0, st, x32, x64, n, bp, d, lut, edge_cos, bin_out,
                        trip_out, exact_out, t_out);
   else if (core == 1)
