@@ -20,8 +20,8 @@
  *   rung 2  + sin/cos of each declination computed once per galaxy (a prepass
  *           into the workspace) instead of per pair ("L2: precomputed sin/cos").
  *   rung 3  + tiling: one thread per i galaxy, a block of `tile` threads, the
- *           j-tile of `tile` galaxies of both catalogs staged in LDS ("L3: block
- *           tiling").
+ *           j-tile of `tile` galaxies of both catalogs staged in LDS as 16-byte
+ *           records, one broadcast read per catalog and pair ("L3: block tiling").
  *   rung 4  + a polynomial arccos in place of acosf ("L4: fast acos"): the
  *           handbook approximation of Abramowitz and Stegun, formula 4.4.45,
  *           acos(x) ~ sqrt(1 - x) (a0 + a1 x + a2 x^2 + a3 x^3) on [0, 1], whose
@@ -71,7 +71,7 @@ size_t gc_ladder_workspace_bytes(int64_t n_d, int64_t n_r);
  *   d_workspace   gc_ladder_workspace_bytes(n_d, n_r) bytes, 256-byte aligned.
  * Errors: GC_ERR_INVALID_ARGUMENT (bad rung, acos_kind, tile, stride, null or
  * misaligned pointer, bad bins), GC_ERR_UNSUPPORTED (n or nbins too large, or the
- * LDS footprint 4 (3 stride + 6 tile) bytes above 160 KiB), GC_ERR_WORKSPACE,
+ * LDS footprint, 12 stride + 32 tile bytes, above 160 KiB), GC_ERR_WORKSPACE,
  * GC_ERR_DEVICE. */
 gc_status gc_ladder_histogram(int32_t rung, int32_t acos_kind, int32_t tile, int32_t bin_stride,
                               const float *d_ra_d, const float *d_dec_d, int64_t n_d,

@@ -96,13 +96,13 @@ __device__ __forceinline__ uint32_t ladder_bin(float cos_theta, const LadderArgs
   return k < last ? k : last;
 }
 
+// Add a workgroup's three LDS histograms (DD | DR | RR, A.stride words apart) to the outputs,
+// taking the 3 stride words as one run: padding words (bin >= nbins) and zero words are skipped.
 __device__ __forceinline__ void flush_block(const uint32_t *h, const LadderArgs &A, int tid, int nthreads) {
-  for (int b = tid; b < A.nbins; b += nthreads) {
-#pragma unroll
-    for (int f = 0; f < 3; ++f) {
-      const uint32_t v = h[f * A.stride + b];
-      if (v) atomicAdd(A.out[f] + b, static_cast<unsigned long long>(v));
-    }
+  for (int q = tid; q < 3 * A.stride; q += nthreads) {
+    const int f = q / A.stride, bin = q - f * A.stride;
+    const uint32_t v = h[q];
+    if (bin < A.nbins && v != 0u) atomicAdd(A.out[f] + bin, static_cast<unsigned long long>(v));
   }
 }
 
@@ -156,64 +156,61 @@ __global__ void __launch_bounds__(kPairBlock *kPairBlock) ladder_pair_kernel(con
   flush_block(h, A, tid, kThreads);
 }
 
-// Rungs 3-5: one thread per i; the block stages a j-tile of TILE galaxies of both catalogs in
-// LDS and every thread walks it.  TUNED (rung 5): inner loop unrolled by 8, launch bounds of
-// exactly TILE threads, and no DD/RR work in blocks wholly below the diagonal.
+// Rungs 3-5 (sections "L3: block tiling", "L4: fast acos", "L5: the last 8%").  A workgroup of
+// TILE threads takes tile column x (i = x TILE + thread, one galaxy per thread, its values kept in
+// registers) against tile row y (TILE consecutive j).  The row's per-galaxy values of both
+// catalogs are staged once in LDS as 16-byte records {sin delta, cos delta, alpha, 0}, so a pair
+// reads its j values with one broadcast ds_read_b128 per catalog; the three histograms follow the
+// records.  DD and RR keep the per-pair upper-triangle test of rung 1.  TUNED (rung 5): the j loop
+// unrolled by 8, launch bounds of exactly TILE threads, and a workgroup whose row lies wholly
+// before its column (y < x: every j of the row is below every i) does no DD/RR work at all.
 template <int TILE, int ACOS, bool TUNED>
 __global__ void __launch_bounds__(TUNED ? TILE : 1024) ladder_tile_kernel(const LadderArgs A) {
-  extern __shared__ uint32_t lds[];
-  float *const tj = reinterpret_cast<float *>(lds);  // [6][TILE]: D s, c, a; R s, c, a
-  uint32_t *const h = lds + 6 * TILE;
-  const int tid = threadIdx.x;
-  for (int b = tid; b < 3 * A.stride; b += TILE) h[b] = 0u;
-  const int64_t i_base = static_cast<int64_t>(blockIdx.x) * TILE;
-  const int64_t j_base = static_cast<int64_t>(blockIdx.y) * TILE;
-  const int64_t jl = j_base + tid;
-  if (jl < A.n_d) {
-    const Gal g = prep_gal(A.d, jl);
-    tj[0 * TILE + tid] = g.s;
-    tj[1 * TILE + tid] = g.c;
-    tj[2 * TILE + tid] = g.a;
-  }
-  if (jl < A.n_r) {
-    const Gal g = prep_gal(A.r, jl);
-    tj[3 * TILE + tid] = g.s;
-    tj[4 * TILE + tid] = g.c;
-    tj[5 * TILE + tid] = g.a;
-  }
-  const int64_t i = i_base + tid;
-  const bool di = i < A.n_d, ri = i < A.n_r;
-  Gal gdi = {0.0f, 0.0f, 0.0f}, gri = gdi;
-  if (di) gdi = prep_gal(A.d, i);
-  if (ri) gri = prep_gal(A.r, i);
-  const int64_t nmax = A.n_d > A.n_r ? A.n_d : A.n_r;
-  const int j_count = static_cast<int>(nmax - j_base < TILE ? nmax - j_base : TILE);
-  const bool do_sym = !TUNED || j_base + j_count - 1 >= i_base;
+  extern __shared__ float4 rec[];
+  float4 *const rec_d = rec;          // [TILE] D records of the row
+  float4 *const rec_r = rec + TILE;   // [TILE] R records of the row
+  uint32_t *const hist = reinterpret_cast<uint32_t *>(rec + 2 * TILE);  // DD | DR | RR, A.stride apart
+  const int t = threadIdx.x;
+  const int64_t row0 = static_cast<int64_t>(blockIdx.y) * TILE;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * TILE + t;
+  for (int q = t; q < 3 * A.stride; q += TILE) hist[q] = 0u;
+  auto stage = [&](const LadderCat &cat, int64_t n, float4 *dst) __attribute__((always_inline)) {
+    const int64_t k = row0 + t;
+    dst[t] = k < n ? make_float4(cat.s[k], cat.c[k], cat.a[k], 0.0f) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  };
+  stage(A.d, A.n_d, rec_d);
+  stage(A.r, A.n_r, rec_r);
+  const bool in_d = i < A.n_d, in_r = i < A.n_r;
+  const Gal none = {0.0f, 0.0f, 0.0f};
+  const Gal gi_d = in_d ? prep_gal(A.d, i) : none;
+  const Gal gi_r = in_r ? prep_gal(A.r, i) : none;
+  const int64_t n_max = A.n_d > A.n_r ? A.n_d : A.n_r;
+  const int len = static_cast<int>(n_max - row0 < TILE ? n_max - row0 : TILE);  // ragged last row
+  const bool upper_possible = !TUNED || blockIdx.y >= blockIdx.x;
+  uint32_t *const h_dd = hist, *const h_dr = hist + A.stride, *const h_rr = hist + 2 * A.stride;
   __syncthreads();
-  auto body = [&](int jj) __attribute__((always_inline)) {
-    const int64_t j = j_base + jj;
-    if (di && j < A.n_r)
-      atomicAdd(h + 1 * A.stride + ladder_bin<ACOS>(law_of_cosines(gdi, tj[3 * TILE + jj], tj[4 * TILE + jj],
-                                                                   tj[5 * TILE + jj]), A), 1u);
-    if (do_sym && j >= i) {
-      const uint32_t inc = 1u + (j != i ? 1u : 0u);
-      if (di && j < A.n_d)
-        atomicAdd(h + 0 * A.stride + ladder_bin<ACOS>(law_of_cosines(gdi, tj[0 * TILE + jj], tj[1 * TILE + jj],
-                                                                     tj[2 * TILE + jj]), A), inc);
-      if (ri && j < A.n_r)
-        atomicAdd(h + 2 * A.stride + ladder_bin<ACOS>(law_of_cosines(gri, tj[3 * TILE + jj], tj[4 * TILE + jj],
-                                                                     tj[5 * TILE + jj]), A), inc);
+  auto count = [&](uint32_t *h, const Gal &g, const float4 &r, uint32_t weight) __attribute__((always_inline)) {
+    atomicAdd(h + ladder_bin<ACOS>(law_of_cosines(g, r.x, r.y, r.z), A), weight);
+  };
+  auto visit = [&](int u) __attribute__((always_inline)) {
+    const int64_t j = row0 + u;
+    const float4 rr = rec_r[u];
+    if (in_d && j < A.n_r) count(h_dr, gi_d, rr, 1u);
+    if (upper_possible && j >= i) {
+      const uint32_t weight = j == i ? 1u : 2u;  // the diagonal once, every other pair for both orders
+      if (in_d && j < A.n_d) count(h_dd, gi_d, rec_d[u], weight);
+      if (in_r && j < A.n_r) count(h_rr, gi_r, rr, weight);
     }
   };
   if constexpr (TUNED) {
 #pragma unroll 8
-    for (int jj = 0; jj < j_count; ++jj) body(jj);
+    for (int u = 0; u < len; ++u) visit(u);
   } else {
 #pragma unroll 1
-    for (int jj = 0; jj < j_count; ++jj) body(jj);
+    for (int u = 0; u < len; ++u) visit(u);
   }
   __syncthreads();
-  flush_block(h, A, tid, TILE);
+  flush_block(hist, A, t, TILE);
 }
 
 template <int RUNG, int ACOS> const void *pair_fn() {
@@ -284,7 +281,8 @@ gc_status gc_ladder_histogram(int32_t rung, int32_t acos_kind, int32_t tile, int
   if (bin_stride != 0 && bin_stride < nbins) return GC_ERR_INVALID_ARGUMENT;
   const int t = tiled ? (tile ? tile : 512) : 0;
   const int stride = bin_stride ? bin_stride : nbins;
-  const size_t lds = (3 * static_cast<size_t>(stride) + 6 * static_cast<size_t>(t)) * sizeof(uint32_t);
+  // rungs 0-2: three histograms; rungs 3-5: also two rows of 16-byte records
+  const size_t lds = 3 * static_cast<size_t>(stride) * sizeof(uint32_t) + 2 * static_cast<size_t>(t) * sizeof(float4);
   if (lds > kMaxLdsBytes) return GC_ERR_UNSUPPORTED;
   if ((n_d > 0 && (!ra_d || !dec_d || !aligned_to(ra_d, 4) || !aligned_to(dec_d, 4))) ||
       (n_r > 0 && (!ra_r || !dec_r || !aligned_to(ra_r, 4) || !aligned_to(dec_r, 4))))
