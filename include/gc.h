@@ -171,6 +171,33 @@ gc_status gc_histogram_part(const void *d_prepared_d, int64_t n_d,
                             void *d_workspace, size_t workspace_bytes,
                             const gc_tuning *tuning, gc_stream_t stream);
 
+/* ------------------------------------------------- allocation-free variant ----
+ * For callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  gc_histogram_dd_dr_rr
+ * without the workspace argument: its scratch (the edge cosines, the bin table and
+ * one 64-bit partial histogram per workgroup) is an array of GC_STATIC_SCRATCH_BYTES
+ * in the library's own device memory, one per GPU, held until the process ends.
+ * The call allocates nothing; its first call on a device resolves that device's
+ * array address (a runtime query that enqueues nothing).  The persistent grid is
+ * capped to the workgroups whose partial histograms fit beside the tables
+ * (2048 at 720 bins, 253 at GC_MAX_BINS), which changes no count: the results are
+ * those of gc_histogram_dd_dr_rr, bit for bit.
+ *
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (ignored on entry: every word a call reads, it has written first).
+ * Calls that overlap on one GPU -- different streams, or threads without
+ * ordering -- RACE and return wrong counts; order them on one stream.
+ * Arguments, results and errors are those of gc_histogram_dd_dr_rr;
+ * GC_ERR_UNSUPPORTED if a job's tables and three partial histograms (one per
+ * family) would not fit the array (no nbins <= GC_MAX_BINS comes near).
+ */
+#define GC_STATIC_SCRATCH_BYTES (16u << 20)
+gc_status gc_histogram_dd_dr_rr_noalloc(const void *d_prepared_d, int64_t n_d,
+                                        const void *d_prepared_r, int64_t n_r,
+                                        int32_t nbins, double bin_width_deg,
+                                        uint64_t *d_dd, uint64_t *d_dr, uint64_t *d_rr,
+                                        gc_stream_t stream);
+
 /* ----------------------------------------------------------------- totals ----
  * The three histogram sums, for the exact-total check of section "The problem"
  * (each family must sum to N_a * N_b).  d_totals: device, 3 uint64 (DD, DR, RR

@@ -119,6 +119,7 @@ def load():
                                               ctypes.POINTER(_Tuning), vp]),
         "gc_histogram_part": (i32, [vp, i64, vp, i64, i32, ctypes.c_double, i64, i64, vp, vp, vp, vp, sz,
                                     ctypes.POINTER(_Tuning), vp]),
+        "gc_histogram_dd_dr_rr_noalloc": (i32, [vp, i64, vp, i64, i32, ctypes.c_double, vp, vp, vp, vp]),
         "gc_histogram_totals": (i32, [vp, vp, vp, i32, vp, vp]),
         "gc_omega": (i32, [vp, vp, vp, i32, i64, i64, vp, vp]),
         "gc_eval_angle_core": (i32, [vp, vp, i64, i32, ctypes.c_double, i32, vp, vp, vp, vp, vp, sz, vp]),
@@ -288,6 +289,26 @@ def histogram_dd_dr_rr(prep_d, n_d: int, prep_r, n_r: int, nbins: int, bin_width
         tc = tuning._c()
         st = lib.gc_histogram_dd_dr_rr_tuned(*args, ctypes.byref(tc), _stream(stream))
     _check(st, "gc_histogram_dd_dr_rr")
+    return dd, dr, rr
+
+
+def histogram_dd_dr_rr_noalloc(prep_d, n_d: int, prep_r, n_r: int, nbins: int, bin_width_deg: float, out,
+                               stream=None):
+    """histogram_dd_dr_rr with the library's own per-GPU scratch (gc_histogram_dd_dr_rr_noalloc):
+    nothing is allocated, so `out` ((3, nbins) int64 device tensor) is required.  Calls that
+    overlap on one GPU share that scratch and race."""
+    torch = _torch()
+    n_d = _count(n_d, "n_d", MAX_GALAXIES)
+    n_r = _count(n_r, "n_r", MAX_GALAXIES)
+    nbins = _bins(nbins)
+    _buf(prep_d, "prep_d", torch.uint8, prepared_bytes(n_d), optional=n_d == 0)
+    _buf(prep_r, "prep_r", torch.uint8, prepared_bytes(n_r), optional=n_r == 0)
+    _buf(out, "out", torch.int64, shape=(3, nbins))
+    _on_gpu(prep_d=prep_d, prep_r=prep_r, out=out)
+    dd, dr, rr = out[0], out[1], out[2]
+    _check(load().gc_histogram_dd_dr_rr_noalloc(_ptr(prep_d), n_d, _ptr(prep_r), n_r, nbins, float(bin_width_deg),
+                                                _ptr(dd), _ptr(dr), _ptr(rr), _stream(stream)),
+           "gc_histogram_dd_dr_rr_noalloc")
     return dd, dr, rr
 
 

@@ -332,10 +332,14 @@ gc_status check_catalog(const void *prep, int64_t n) {
   return GC_OK;
 }
 
-size_t workspace_bytes(int32_t nbins) {
+// Scratch of a launch with at most max_wg workgroups: the edge cosines, the bin table and one
+// 64-bit partial histogram per workgroup.
+size_t scratch_bytes(int32_t nbins, int32_t max_wg) {
   return edge_table_bytes(nbins) + kLutBytes +
-         static_cast<size_t>(kMaxWorkgroups) * static_cast<size_t>(nbins) * sizeof(unsigned long long);
+         static_cast<size_t>(max_wg) * static_cast<size_t>(nbins) * sizeof(unsigned long long);
 }
+
+size_t workspace_bytes(int32_t nbins) { return scratch_bytes(nbins, kMaxWorkgroups); }
 
 // j-steps of one family in its two segments.  Cross: fast = full blocks x n_j, generic = the
 // ragged block's n_j steps.  Self (upper triangle by blocks): fast = sum over full blocks b of
@@ -411,7 +415,7 @@ namespace {
 gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, int64_t n_r, int32_t nbins,
                          double w_deg, uint64_t *dd, uint64_t *dr, uint64_t *rr, void *workspace, size_t ws_bytes,
                          const gc_tuning *tuning, int64_t part, int64_t parts, bool accumulate, gc_stream_t stream,
-                         gc_plan *plan_out = nullptr) {
+                         gc_plan *plan_out = nullptr, int32_t max_wg = kMaxWorkgroups) {
   gc_status st;
   if ((st = check_bins(nbins, w_deg)) != GC_OK) return st;
   if (plan_out) {
@@ -423,7 +427,7 @@ gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, in
     if (!dd || !dr || !rr || !aligned(dd, 8) || !aligned(dr, 8) || !aligned(rr, 8))
       return GC_ERR_INVALID_ARGUMENT;
     if (!workspace || !aligned(workspace, GC_ALIGNMENT)) return GC_ERR_INVALID_ARGUMENT;
-    if (ws_bytes < workspace_bytes(nbins)) return GC_ERR_WORKSPACE;
+    if (ws_bytes < scratch_bytes(nbins, max_wg)) return GC_ERR_WORKSPACE;
   }
   gc_tuning tu;
   memset(&tu, 0, sizeof(tu));
@@ -548,7 +552,7 @@ gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, in
     int per_cu = tu.blocks_per_cu ? tu.blocks_per_cu : (occ < kMaxBlocksPerCU ? occ : kMaxBlocksPerCU);
     if (per_cu < 1) return GC_ERR_UNSUPPORTED;
     int64_t g = static_cast<int64_t>(per_cu) * cus;
-    if (g > kMaxWorkgroups) g = kMaxWorkgroups;
+    if (g > max_wg) g = max_wg;
     // at least ~32 j-steps per wave
     const int64_t want = (total + 32 * a.waves - 1) / (32 * a.waves);
     if (g > want) g = want;
@@ -654,6 +658,62 @@ gc_status gc_launch_plan(int64_t n_d, int64_t n_r, int32_t nbins, double w_deg, 
   if (!plan) return GC_ERR_INVALID_ARGUMENT;
   return histogram_impl(nullptr, n_d, nullptr, n_r, nbins, w_deg, nullptr, nullptr, nullptr, nullptr, 0, tuning, 0, 1,
                         false, nullptr, plan);
+}
+
+}  // extern "C"
+
+// The allocation-free entry point's scratch: one array per GPU, in device memory that the runtime
+// sets up with the library's code, held until the process ends.  In host code `scratch` names a
+// host-side stand-in, never the device array: its device address is taken once per device with
+// hipGetSymbolAddress (that device current), and only that address reaches kernels.
+static __device__ __align__(256) unsigned char scratch[GC_STATIC_SCRATCH_BYTES];
+
+namespace gc {
+namespace {
+
+void *g_scratch[kMaxDevices];  // the current device's array address, guarded by g_mu
+
+hipError_t static_scratch(void **ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (!g_scratch[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p || !aligned(p, GC_ALIGNMENT)) return hipErrorInvalidSymbol;
+    g_scratch[dev] = p;
+  }
+  *ptr = g_scratch[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+}  // namespace gc
+
+extern "C" {
+
+gc_status gc_histogram_dd_dr_rr_noalloc(const void *prep_d, int64_t n_d, const void *prep_r, int64_t n_r,
+                                        int32_t nbins, double w_deg, uint64_t *dd, uint64_t *dr, uint64_t *rr,
+                                        gc_stream_t stream) {
+  // the checks of histogram_impl that precede any HIP call, so a bad call reaches none
+  gc_status st;
+  if ((st = check_bins(nbins, w_deg)) != GC_OK) return st;
+  if ((st = check_catalog(prep_d, n_d)) != GC_OK) return st;
+  if ((st = check_catalog(prep_r, n_r)) != GC_OK) return st;
+  if (!dd || !dr || !rr || !aligned(dd, 8) || !aligned(dr, 8) || !aligned(rr, 8)) return GC_ERR_INVALID_ARGUMENT;
+  // the workgroups whose partial histograms fit beside the tables; one per family at least
+  const size_t fixed = scratch_bytes(nbins, 0), per_wg = static_cast<size_t>(nbins) * sizeof(unsigned long long);
+  if (fixed + 3 * per_wg > GC_STATIC_SCRATCH_BYTES) return GC_ERR_UNSUPPORTED;
+  const size_t fit = (GC_STATIC_SCRATCH_BYTES - fixed) / per_wg;
+  const int32_t max_wg = fit < static_cast<size_t>(kMaxWorkgroups) ? static_cast<int32_t>(fit) : kMaxWorkgroups;
+  void *ws = nullptr;
+  const hipError_t e = static_scratch(&ws);
+  if (e != hipSuccess) return device_error(e);
+  return histogram_impl(prep_d, n_d, prep_r, n_r, nbins, w_deg, dd, dr, rr, ws, GC_STATIC_SCRATCH_BYTES, nullptr, 0,
+                        1, false, stream, nullptr, max_wg);
 }
 
 gc_status gc_histogram_dd_dr_rr(const void *prep_d, int64_t n_d, const void *prep_r, int64_t n_r,
