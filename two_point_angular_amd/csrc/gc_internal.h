@@ -25,6 +25,8 @@ constexpr int queue_words(int k, int core, bool d64) { return 2 * kWave * (drain
 constexpr int kMaxWorkgroups = 2048; // partial-histogram slots held by the workspace
 constexpr int kMaxBins = 8192;       // GC_MAX_BINS (include/gc.h; gc_api.cpp checks they agree)
 constexpr int kMaxBlocksPerCU = 8;
+constexpr int kOversubscribe = 3;      // workgroups launched per resident workgroup slot
+constexpr int kMinStepsPerWave = 256;  // j-steps per wave below which the grid shrinks
 
 // ---- prepared catalog layout ---------------------------------------------------
 // Six structure-of-arrays vectors of `padded` elements each: fp32 x, y, z then fp64
