@@ -250,10 +250,12 @@ constexpr size_t kLdsPerCU = 160 * 1024;
 
 // The bin-table kernel's layout: sixteen histogram columns when two workgroups of 8 waves (12 at
 // K = 4, 16 at K = 2) fit in a compute unit's LDS beside their tables and queues; else one column
-// in one workgroup of 16 waves.  Every table read goes to LDS by default: with the conflict-free
-// sixteen-column atomics, moving a quarter of the reads to the vector L1 measured 1 % slower
-// (6.68 against 6.74 ms on 100k + 100k at 720 bins), and the large tables of fine bins do not stay
-// in the L1.  Overrides may pick any layout that fits.  Returns false when none fits.
+// in one workgroup of 16 waves.  With sixteen columns every table read goes to LDS: with the
+// conflict-free atomics, moving a quarter of the reads to the vector L1 measured 1 % slower (6.68
+// against 6.74 ms on 100k + 100k at 720 bins).  With one column, whose conflicting atomics keep the
+// LDS busiest, an eighth of the reads go through the L1 (3600 bins: 9.09 -> 8.79 ms; a quarter,
+// 10.5 ms, waits on the L2 for the large table).  Overrides may pick any layout that fits.  Returns
+// false when none fits.
 bool lut_layout(const LutPlan &lp, int32_t nbins, int k, const gc_tuning &tu, LutVariant *lv, int *waves) {
   const int32_t tw = 2 * (2 * lp.m + 1);
   auto lds = [&](int cols, int nw) { return pairs_lds_bytes(lut_hist_words(nbins, cols), true, k, 2, false, nw, tw); };
@@ -266,7 +268,7 @@ bool lut_layout(const LutPlan &lp, int32_t nbins, int k, const gc_tuning &tu, Lu
   if (nw == 0) nw = cols == kHistCols ? nw2 : kMaxWavesPerWG;
   if (lds(cols, nw) > kLdsPerCU) return false;
   lv->cols = cols;
-  lv->l1 = tu.l1_share ? tu.l1_share - 1 : 0;
+  lv->l1 = tu.l1_share ? tu.l1_share - 1 : (cols == kHistCols ? 0 : 1);
   *waves = nw;
   return true;
 }

@@ -134,7 +134,7 @@ struct PairArgs {
 };
 
 // The bin-table kernel's variants: histogram columns (1 or kHistCols) and the share of table
-// reads made through the vector L1 instead of LDS (0: none; 1: a quarter; 2: three eighths).
+// reads made through the vector L1 instead of LDS (0: none; 1: an eighth; 2: a quarter).
 struct LutVariant {
   int cols = 1;
   int l1 = 2;

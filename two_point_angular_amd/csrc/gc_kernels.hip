@@ -323,8 +323,8 @@ __device__ __forceinline__ void drain_queue(uint32_t *hist, const uint32_t *queu
 // the 100k workloads, each step up in waves per SIMD outweighed the few spills it costs outside
 // the pair loop.  The bin-table core also builds at K = 2 for eight waves per SIMD (<= 64 VGPRs).
 // The bin-table core (CORE 2, fp32 dot) also takes COLS, its histogram's columns (1 or
-// kHistCols), and L1S, the share of its table reads made through the vector L1 (0 none, 1 a
-// quarter, 2 three eighths); its workgroups hold up to kMaxWavesPerWG waves (A.waves), all sharing
+// kHistCols), and L1S, the share of its table reads made through the vector L1 (0 none, 1 an
+// eighth, 2 a quarter); its workgroups hold up to kMaxWavesPerWG waves (A.waves), all sharing
 // one table and one histogram.  The other cores run kWavesPerWG waves per workgroup.
 template <int K, bool D64, int CORE, int COLS = 1, int L1S = 2>
 __global__ void __launch_bounds__((CORE == 2 && !D64) ? kMaxWavesPerWG * kWave : kWGThreads)
@@ -541,12 +541,12 @@ pairs_kernel(const PairArgs A) {
 
   // Which of a lane's table reads go through the vector L1 (the rest read the LDS copy): a random
   // 64-lane LDS read costs ~7 CU cycles, the same read through the vector L1 ~37, and the LDS also
-  // takes every pair's atomic, so a share of the reads goes to the L1.  Scalar-j steps: pairs
-  // k = 1, 4, 7 of 8 (three eighths) or k = 1, 5 (a quarter); matrix-core tiles: result r = 1, and
-  // r = 3 of odd tiles (three eighths), or r = 1 (a quarter).
-  auto l1_scalar = [](int k) constexpr { return L1S == 2 ? k % 3 == 1 : (L1S == 1 ? k % 4 == 1 : false); };
+  // takes every pair's atomic, so a share of the reads may go to the L1.  Scalar-j steps: pairs
+  // k = 1, 5 (a quarter) or k = 1 of 8 (an eighth); matrix-core tiles: result r = 1 (a quarter),
+  // or r = 1 of odd tiles (an eighth).
+  auto l1_scalar = [](int k) constexpr { return L1S == 2 ? k % 4 == 1 : (L1S == 1 ? k % 8 == 1 : false); };
   auto l1_tile = [](int r, int t) constexpr {
-    return L1S == 2 ? (r == 1 || (r == 3 && (t & 1))) : (L1S == 1 ? r == 1 : false);
+    return L1S == 2 ? r == 1 : (L1S == 1 ? r == 1 && (t & 1) : false);
   };
   // The histogram row address of a bin-table pair: (sign of e - x) << lut_sh plus the entry's row
   // address, plus this lane's column; an L1 entry holds the row's offset, the LDS copy its address.
