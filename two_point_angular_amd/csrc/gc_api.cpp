@@ -231,18 +231,21 @@ void apply_lut(BinParams &bp, const LutPlan &lp, int cols, int32_t nbins) {
 
 bool lut_layout(const LutPlan &lp, int32_t nbins, int k, const gc_tuning &tu, LutVariant *lv, int *waves);
 
-// The bin-table kernel's K and layout: K = 8 unless overridden; where the sixteen-column histogram
-// fits, K = 4 (two workgroups of 12 waves: six per SIMD, measured faster than K = 8 with 8 and
-// K = 2 with 16).  *k receives the K chosen.
+// The bin-table kernel's K and layout, unless overridden: K = 2 where the sixteen-column
+// histogram fits (two workgroups of 16 waves: eight per SIMD), else K = 4 with one column (one
+// workgroup of 16 waves).  With the waves of a workgroup sharing its steps through the cursor,
+// the larger groups measured fastest: 100k + 100k at 720 bins 6.35 ms at K = 2 against 6.41 at
+// K = 4 and 7.15 at K = 8; 3600 bins 8.76 ms at K = 4 against 9.3 at K = 2 and 10.0 at K = 8.
+// *k receives the K chosen.
 bool lut_choose(const LutPlan &lp, int32_t nbins, const gc_tuning &tu, int *k, LutVariant *lv, int *waves) {
   if (tu.i_per_lane) {
     *k = tu.i_per_lane;
     return lut_layout(lp, nbins, *k, tu, lv, waves);
   }
+  *k = 2;
+  if (lut_layout(lp, nbins, 2, tu, lv, waves) && lv->cols == kHistCols) return true;
   *k = 4;
-  if (lut_layout(lp, nbins, 4, tu, lv, waves) && lv->cols == kHistCols) return true;
-  *k = 8;
-  return lut_layout(lp, nbins, 8, tu, lv, waves);
+  return lut_layout(lp, nbins, 4, tu, lv, waves);
 }
 
 // LDS of one compute unit on gfx950.
@@ -250,12 +253,11 @@ constexpr size_t kLdsPerCU = 160 * 1024;
 
 // The bin-table kernel's layout: sixteen histogram columns when two workgroups of 8 waves (12 at
 // K = 4, 16 at K = 2) fit in a compute unit's LDS beside their tables and queues; else one column
-// in one workgroup of 16 waves.  With sixteen columns every table read goes to LDS: with the
-// conflict-free atomics, moving a quarter of the reads to the vector L1 measured 1 % slower (6.68
-// against 6.74 ms on 100k + 100k at 720 bins).  With one column, whose conflicting atomics keep the
-// LDS busiest, an eighth of the reads go through the L1 (3600 bins: 9.09 -> 8.79 ms; a quarter,
-// 10.5 ms, waits on the L2 for the large table).  Overrides may pick any layout that fits.  Returns
-// false when none fits.
+// in one workgroup of 16 waves.  Every table read goes to LDS unless overridden: a share through
+// the vector L1 measured slower in both layouts once the waves of a workgroup shared its steps
+// (720 bins: an eighth 6.40 against 6.35 ms; 3600 bins: an eighth 9.46 against 8.76 ms), and the
+// large tables of fine bins do not stay in the L1.  Overrides may pick any layout that fits.
+// Returns false when none fits.
 bool lut_layout(const LutPlan &lp, int32_t nbins, int k, const gc_tuning &tu, LutVariant *lv, int *waves) {
   const int32_t tw = 2 * (2 * lp.m + 1);
   auto lds = [&](int cols, int nw) { return pairs_lds_bytes(lut_hist_words(nbins, cols), true, k, 2, false, nw, tw); };
@@ -268,7 +270,7 @@ bool lut_layout(const LutPlan &lp, int32_t nbins, int k, const gc_tuning &tu, Lu
   if (nw == 0) nw = cols == kHistCols ? nw2 : kMaxWavesPerWG;
   if (lds(cols, nw) > kLdsPerCU) return false;
   lv->cols = cols;
-  lv->l1 = tu.l1_share ? tu.l1_share - 1 : (cols == kHistCols ? 0 : 1);
+  lv->l1 = tu.l1_share ? tu.l1_share - 1 : 0;
   *waves = nw;
   return true;
 }
@@ -447,9 +449,9 @@ gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, in
   // Plan.  Bins narrower than 0.01 deg put most pairs where the fp32 dot product cannot
   // certify the bin; those use the fp64 dot-product instantiation.
   const bool dot64 = tu.dot_precision == 64 || (tu.dot_precision == 0 && w_deg < 0.01);
-  // Galaxies per lane: 8 for the fp32 kernel; 4 for the fp64 kernel, whose fp64 i-galaxies
-  // at K = 8 leave room for only three waves per SIMD; 4 for the bin-table core with a sixteen-
-  // column histogram (below), whose two workgroups of 12 waves then fill six waves per SIMD.
+  // Galaxies per lane: 8 for the fp32 arccos kernels; 4 for the fp64 kernel, whose fp64
+  // i-galaxies at K = 8 leave room for only three waves per SIMD; the bin-table core picks its
+  // own (lut_choose: 2 with the sixteen-column histogram, else 4).
   int k = tu.i_per_lane ? tu.i_per_lane : (dot64 ? 4 : 8);
   // Span-specialised cores: when the bins reach 180 deg (up to half a bin), t cannot exceed
   // nbins + 1 and the fp32 kernel needs no clamp of t (a spare bin takes t = nbins); when they

@@ -141,13 +141,14 @@ struct LutVariant {
 };
 
 // LDS bytes of one pair-kernel workgroup: histogram(s), the core's table (table_words, shared-
-// histogram mode only) and one recheck queue per wave.
+// histogram mode only), one recheck queue per wave and the workgroup's 64-bit step cursor.
+constexpr int kCursorWords = 2;
 inline size_t pairs_lds_bytes(int32_t hist_words, bool shared_hist, int k, int core, bool d64, int waves,
                               int32_t table_words = 0) {
   const size_t qw = static_cast<size_t>(queue_words(k, core, d64));
   const size_t words = shared_hist ? hist_words + static_cast<size_t>(table_words) + static_cast<size_t>(waves) * qw
                                    : static_cast<size_t>(waves) * (hist_words + qw);
-  return words * sizeof(uint32_t);
+  return (words + kCursorWords) * sizeof(uint32_t);
 }
 // Histogram words of the bin-table core: one column with 64 spare rows and the two alias rows, or
 // kHistCols columns of nbins + 3 rows (one spare row, two alias rows).

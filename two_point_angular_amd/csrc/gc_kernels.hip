@@ -356,6 +356,10 @@ pairs_kernel(const PairArgs A) {
   uint32_t *const hist = shared_hist ? lds : lds + wv * (A.hist_words + QW);
   uint2 *const tab = reinterpret_cast<uint2 *>(lds + A.hist_words);
   uint32_t *const queue = shared_hist ? lds + A.hist_words + tab_words + wv * QW : hist + A.hist_words;
+  // the workgroup's cursor into its fast steps (64-bit, after the queues; every offset before it
+  // is an even number of words)
+  unsigned long long *const cursor = reinterpret_cast<unsigned long long *>(
+      shared_hist ? lds + A.hist_words + tab_words + nw * QW : lds + nw * (A.hist_words + QW));
   const uint32_t hist_addr = lds_address(hist);
   // a multi-column histogram: this lane's column, and its byte offset within a row
   const int colw = COLS > 1 ? (lane & (COLS - 1)) : 0;
@@ -393,26 +397,33 @@ pairs_kernel(const PairArgs A) {
   } else {
     for (int b = lane; b < A.hist_words; b += kWave) hist[b] = 0u;
   }
-  __threadfence();
+  if (threadIdx.x == 0) *cursor = 0ull;
+  // (The barrier orders the slot zeroing before this workgroup's flush atomics: both reach the
+  // same L2.  A device-scope fence here, which writes back the L2 on gfx950, cost each workgroup
+  // ~20 us: an eighth of the 10k + 10k job.)
   __syncthreads();
 
-  // The family's j-steps form two segments, each split evenly among the family's waves (V of
-  // them; this is wave v), so every wave gets the same share of both kinds of work:
+  // The family's j-steps form two segments:
   //   fast    - the off-diagonal steps of full i-blocks: batched, unrolled, no per-pair checks;
   //   generic - the diagonal steps j in [i0, i0 + BI) of a self family and every step of a
   //             ragged last i-block: per-pair weights and validity, a rolled loop, slower.
-  // (Giving each wave one contiguous range of all steps left the generic-heavy tail of the
-  // triangle, and the ragged block, to the last few waves, which then finished late.)
-  const int64_t V = static_cast<int64_t>(F.wg_end - F.wg_begin) * nw;
-  const int64_t v = static_cast<int64_t>(g - F.wg_begin) * nw + wv;
-  auto share = [&](int64_t begin, int64_t total, int64_t &lo, int64_t &hi) __attribute__((always_inline)) {
-    const int64_t q = total / V, r = total % V;
-    lo = begin + q * v + (r * v) / V;
-    hi = begin + q * (v + 1) + (r * (v + 1)) / V;
+  // The generic steps are split evenly among the family's waves (V of them; this is wave v), so
+  // every wave gets the same share of the slower work.  The fast steps are split evenly among the
+  // family's workgroups (U; this is workgroup u), and the waves of a workgroup take them in chunks
+  // from its cursor, so they end together however fast each one runs: a workgroup holds its LDS
+  // until its last wave ends, and with equal fixed shares the waves of one workgroup ended up to
+  // 40 % apart (per-wave timestamps, 100k + 100k at 720 bins).
+  const int64_t U = F.wg_end - F.wg_begin, u = g - F.wg_begin;
+  const int64_t V = U * nw, v = u * nw + wv;
+  auto share = [](int64_t begin, int64_t total, int64_t parts, int64_t idx, int64_t &lo, int64_t &hi)
+      __attribute__((always_inline)) {
+    const int64_t q = total / parts, r = total % parts;
+    lo = begin + q * idx + (r * idx) / parts;
+    hi = begin + q * (idx + 1) + (r * (idx + 1)) / parts;
   };
   int64_t fs, fe, gs, ge;
-  share(F.fast_begin, F.fast_steps, fs, fe);
-  share(F.gen_begin, F.gen_steps, gs, ge);
+  share(F.fast_begin, F.fast_steps, U, u, fs, fe);
+  share(F.gen_begin, F.gen_steps, V, v, gs, ge);
   const int64_t nbf = F.n_i / BI;  // full i-blocks
 
   int64_t since_flush = 0;
@@ -791,44 +802,74 @@ pairs_kernel(const PairArgs A) {
 
   // Fast segment over the full blocks.  Cross family: block b has steps j in [0, n_j), prefix
   // b n_j.  Self family: block b has j in [(b+1) BI, n), prefix Pf(b) = b n - BI b (b+1) / 2.
-  {
-    int64_t s = fs, b = 0, j = 0;
-    if (s < fe) {
-      if (!F.sym) {
-        b = s / F.n_j;
-        j = s - b * F.n_j;
-      } else {
-        int64_t lo = 0, hi = nbf - 1;
-        while (lo < hi) {
-          const int64_t mid = (lo + hi + 1) >> 1;
-          const int64_t pm = mid * F.n_j - static_cast<int64_t>(BI) * mid * (mid + 1) / 2;
-          if (pm <= s) lo = mid; else hi = mid - 1;
-        }
-        b = lo;
-        j = (b + 1) * BI + (s - (b * F.n_j - static_cast<int64_t>(BI) * b * (b + 1) / 2));
+  // One chunk [s0, s1) of the workgroup's range may span blocks; the i-tiles (and the scalar-j
+  // i-block) stay loaded while the next chunk is in the same block.
+  int64_t tiles_b = -1, iblk_b = -1;
+  auto run_fast_range = [&](int64_t s0, int64_t s1) __attribute__((always_inline)) {
+    int64_t s = s0, b = 0, j = 0;
+    if (!F.sym) {
+      b = s / F.n_j;
+      j = s - b * F.n_j;
+    } else {
+      int64_t lo = 0, hi = nbf - 1;
+      while (lo < hi) {
+        const int64_t mid = (lo + hi + 1) >> 1;
+        const int64_t pm = mid * F.n_j - static_cast<int64_t>(BI) * mid * (mid + 1) / 2;
+        if (pm <= s) lo = mid; else hi = mid - 1;
       }
+      b = lo;
+      j = (b + 1) * BI + (s - (b * F.n_j - static_cast<int64_t>(BI) * b * (b + 1) / 2));
     }
-    while (s < fe) {
-      const int64_t nsteps = (fe - s) < (F.n_j - j) ? (fe - s) : (F.n_j - j);
+    while (s < s1) {
+      const int64_t nsteps = (s1 - s) < (F.n_j - j) ? (s1 - s) : (F.n_j - j);
       if (nsteps <= 0) break;  // unreachable for consistent step counts; keeps every wave finite
       if constexpr (LUT) {
         const int64_t full = nsteps & ~static_cast<int64_t>(15);
         if (full > 0) {
-          load_tiles(b);
+          if (b != tiles_b) {
+            load_tiles(b);
+            tiles_b = b;
+          }
+          i0 = b * BI;
           run_fast_mfma(j, j + full);
         }
         if (full < nsteps) {
-          load_i_block(b);
+          if (b != iblk_b) {
+            load_i_block(b);
+            iblk_b = b;
+          }
+          i0 = b * BI;
           run_fast(j + full, j + nsteps);
         }
       } else {
-        load_i_block(b);
+        if (b != iblk_b) {
+          load_i_block(b);
+          iblk_b = b;
+        }
+        i0 = b * BI;
         run_fast(j, j + nsteps);
       }
       drain_all();
       s += nsteps;
       ++b;
       j = F.sym ? (b + 1) * BI : 0;
+    }
+  };
+  {
+    // chunks of a multiple of 16 steps (whole matrix-core j-tiles), about 24 per wave, at least 32
+    const int64_t len = fe - fs;
+    const int64_t per = len / (static_cast<int64_t>(nw) * 24);
+    const int64_t CH = per < 32 ? 32 : (per + 15) & ~static_cast<int64_t>(15);
+    while (true) {
+      unsigned long long c = 0;
+      if (lane == 0)
+        c = __hip_atomic_fetch_add(cursor, static_cast<unsigned long long>(CH), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+      const int64_t c0 = static_cast<int64_t>(
+          (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(c >> 32))) << 32) |
+          __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(c)));
+      if (c0 >= len) break;
+      run_fast_range(fs + c0, fs + c0 + CH < fe ? fs + c0 + CH : fe);
     }
   }
   final_flush();
