@@ -93,9 +93,13 @@ gc_status gc_prepare(const float *d_ra_arcmin, const float *d_dec_arcmin, int64_
  *                       go to bin nbins-1.
  *   d_dd, d_dr, d_rr  : device, nbins uint64 each, 8-byte aligned; OVERWRITTEN.
  *                       Sums: n_d^2, n_d*n_r, n_r^2.  A family with no pairs is all zero.
- *   d_workspace       : device scratch of at least gc_workspace_bytes(nbins) bytes,
+ *   d_workspace       : device scratch of at least gc_workspace_bytes(nbins) bytes
+ *                       (the fp64 edge cosines and the bin table: at most 177 KiB),
  *                       GC_ALIGNMENT-aligned; contents on entry are ignored.  Must not
  *                       be used by another call until this one has completed.
+ * The outputs are zeroed first and the pair kernel's workgroups add their counts
+ * into them with 64-bit atomics, so they must not be read or written by other work
+ * until the call has completed.
  * Returns GC_OK once the work is enqueued.
  */
 size_t gc_workspace_bytes(int32_t nbins);
@@ -175,24 +179,21 @@ gc_status gc_histogram_part(const void *d_prepared_d, int64_t n_d,
 /* ------------------------------------------------- allocation-free variant ----
  * For callers that cannot allocate device memory: code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc.  gc_histogram_dd_dr_rr
- * without the workspace argument: its scratch (the edge cosines, the bin table and
- * one 64-bit partial histogram per workgroup) is an array of GC_STATIC_SCRATCH_BYTES
- * in the library's own device memory, one per GPU, held until the process ends.
- * The call allocates nothing; its first call on a device resolves that device's
- * array address (a runtime query that enqueues nothing).  The persistent grid is
- * capped to the workgroups whose partial histograms fit beside the tables
- * (2048 at 720 bins, 253 at GC_MAX_BINS), which changes no count: the results are
- * those of gc_histogram_dd_dr_rr, bit for bit.
+ * without the workspace argument: its scratch (the edge cosines and the bin table)
+ * is an array of GC_STATIC_SCRATCH_BYTES in the library's own device memory, one
+ * per GPU, held until the process ends.  The call allocates nothing; its first
+ * call on a device resolves that device's array address (a runtime query that
+ * enqueues nothing).  The results are those of gc_histogram_dd_dr_rr, bit for bit.
  *
  * Every call on one GPU shares that GPU's array, which keeps the last call's
  * contents (ignored on entry: every word a call reads, it has written first).
  * Calls that overlap on one GPU -- different streams, or threads without
  * ordering -- RACE and return wrong counts; order them on one stream.
  * Arguments, results and errors are those of gc_histogram_dd_dr_rr;
- * GC_ERR_UNSUPPORTED if a job's tables and three partial histograms (one per
- * family) would not fit the array (no nbins <= GC_MAX_BINS comes near).
+ * GC_ERR_UNSUPPORTED if a job's tables would not fit the array (the library checks
+ * at build time that those of every nbins <= GC_MAX_BINS do).
  */
-#define GC_STATIC_SCRATCH_BYTES (16u << 20)
+#define GC_STATIC_SCRATCH_BYTES (256u << 10)
 gc_status gc_histogram_dd_dr_rr_noalloc(const void *d_prepared_d, int64_t n_d,
                                         const void *d_prepared_r, int64_t n_r,
                                         int32_t nbins, double bin_width_deg,

@@ -48,8 +48,9 @@ def test_sizes(lib):
     assert lib.gc_prepared_bytes(10**5) % gc.ALIGNMENT == 0
     assert lib.gc_workspace_bytes(0) == 0
     assert lib.gc_workspace_bytes(gc.MAX_BINS + 1) == 0
-    # edge cosines, the bin table (up to 14337 8-byte entries), 2048 per-workgroup partial histograms
-    assert lib.gc_workspace_bytes(720) == 2048 * 720 * 8 + (721 * 8 + 255) // 256 * 256 + (14337 * 8 + 255) // 256 * 256
+    # the edge cosines and the bin table (up to 14337 8-byte entries), each 256-byte aligned
+    assert lib.gc_workspace_bytes(720) == (721 * 8 + 255) // 256 * 256 + (14337 * 8 + 255) // 256 * 256
+    assert lib.gc_workspace_bytes(gc.MAX_BINS) <= 256 * 1024  # fits the allocation-free call's scratch
 
 
 def test_status_strings(lib):

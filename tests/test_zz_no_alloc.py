@@ -2,8 +2,8 @@
 
 CPU: every argument check returns before any HIP call.  GPU: two calls in a row, the second on a
 smaller job (fewer galaxies, fewer bins, another core) than the first, each bit-identical to
-gc_histogram_dd_dr_rr on the same inputs; the first call's bin count makes the scratch cap the
-persistent grid (253 workgroups at 8192 bins), which must change no count.
+gc_histogram_dd_dr_rr on the same inputs; the first call fills the scratch with the largest edge
+table (8192 bins), over which the second call's smaller tables are built.
 """
 import ctypes
 import os
@@ -67,8 +67,8 @@ def test_noalloc_matches_workspace_call_twice():
         pytest.skip("no GPU")
     gc.load()
     jobs = [
-        # (D, R, nbins, width): the first fills the scratch with 8192-bin partial histograms of
-        # a capped grid; the second is smaller and runs the bin-table core over the stale contents
+        # (D, R, nbins, width): the first fills the scratch with an 8192-bin edge table; the
+        # second is smaller and runs the bin-table core over the stale contents
         (catalogs.clustered(20000, 41), catalogs.uniform_sphere(18000, 42), 8192, 180.0 / 8192),
         (catalogs.clustered(3000, 43), catalogs.uniform_sphere(2500, 44), 720, 0.25),
     ]

@@ -337,14 +337,8 @@ gc_status check_catalog(const void *prep, int64_t n) {
   return GC_OK;
 }
 
-// Scratch of a launch with at most max_wg workgroups: the edge cosines, the bin table and one
-// 64-bit partial histogram per workgroup.
-size_t scratch_bytes(int32_t nbins, int32_t max_wg) {
-  return edge_table_bytes(nbins) + kLutBytes +
-         static_cast<size_t>(max_wg) * static_cast<size_t>(nbins) * sizeof(unsigned long long);
-}
-
-size_t workspace_bytes(int32_t nbins) { return scratch_bytes(nbins, kMaxWorkgroups); }
+// Scratch of a histogram call: the edge cosines and the bin table.
+size_t workspace_bytes(int32_t nbins) { return edge_table_bytes(nbins) + kLutBytes; }
 
 // j-steps of one family in its two segments.  Cross: fast = full blocks x n_j, generic = the
 // ragged block's n_j steps.  Self (upper triangle by blocks): fast = sum over full blocks b of
@@ -420,7 +414,7 @@ namespace {
 gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, int64_t n_r, int32_t nbins,
                          double w_deg, uint64_t *dd, uint64_t *dr, uint64_t *rr, void *workspace, size_t ws_bytes,
                          const gc_tuning *tuning, int64_t part, int64_t parts, bool accumulate, gc_stream_t stream,
-                         gc_plan *plan_out = nullptr, int32_t max_wg = kMaxWorkgroups) {
+                         gc_plan *plan_out = nullptr) {
   gc_status st;
   if ((st = check_bins(nbins, w_deg)) != GC_OK) return st;
   if (plan_out) {
@@ -432,7 +426,7 @@ gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, in
     if (!dd || !dr || !rr || !aligned(dd, 8) || !aligned(dr, 8) || !aligned(rr, 8))
       return GC_ERR_INVALID_ARGUMENT;
     if (!workspace || !aligned(workspace, GC_ALIGNMENT)) return GC_ERR_INVALID_ARGUMENT;
-    if (ws_bytes < scratch_bytes(nbins, max_wg)) return GC_ERR_WORKSPACE;
+    if (ws_bytes < workspace_bytes(nbins)) return GC_ERR_WORKSPACE;
   }
   gc_tuning tu;
   memset(&tu, 0, sizeof(tu));
@@ -493,8 +487,9 @@ gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, in
   a.lut = use_lut ? lut_dev : nullptr;
   double *edge_cos = static_cast<double *>(workspace);
   a.edge_cos = edge_cos;
-  a.slots = reinterpret_cast<unsigned long long *>(static_cast<char *>(workspace) + edge_table_bytes(nbins) +
-                                                    kLutBytes);
+  a.out[0] = dd;
+  a.out[1] = dr;
+  a.out[2] = rr;
 
   const Prepared pd = prepared_view(prep_d, n_d), pr = prepared_view(prep_r, n_r);
   const int64_t nn[3][2] = {{n_d, n_d}, {n_d, n_r}, {n_r, n_r}};
@@ -554,18 +549,17 @@ gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, in
     const int64_t auto_flush = static_cast<int64_t>(0x7fffffffll / max_inc) - 32;
     a.flush_interval = tu.flush_interval ? (tu.flush_interval < auto_flush ? tu.flush_interval : auto_flush)
                                          : auto_flush;
-    // Workgroups: kOversubscribe times as many as fit on the compute units at once (at most
-    // kMaxBlocksPerCU per CU).  Each takes a static share of its family's steps; as workgroups
-    // finish, the dispatcher starts the waiting ones on the freed slots, so the families' unequal
-    // cost per step (and the ragged end of the triangles) leaves a tail of one short workgroup
-    // instead of one whole persistent share (100k + 100k at 720 bins: 7.39 -> 6.85 ms).
+    // Workgroups: kOversubscribe times as many as fit on the compute units at once (whole
+    // rounds).  Each takes a static share of its family's steps; as workgroups finish, the
+    // dispatcher starts the waiting ones on the freed slots, so the families' unequal cost per
+    // step (and the ragged end of the triangles) leaves a tail of one short workgroup instead of
+    // one whole persistent share (100k + 100k at 720 bins: 7.39 -> 6.85 ms).
     if (occ < 1 && !tu.blocks_per_cu) return GC_ERR_UNSUPPORTED;
-    const int over = kOversubscribe * occ;
-    int per_cu = tu.blocks_per_cu ? tu.blocks_per_cu : (over < kMaxBlocksPerCU ? over : kMaxBlocksPerCU);
+    const int per_cu = tu.blocks_per_cu ? tu.blocks_per_cu : kOversubscribe * occ;
     int64_t g = static_cast<int64_t>(per_cu) * cus;
-    if (g > max_wg) g = max_wg;
+    if (g > kMaxWorkgroups) g = kMaxWorkgroups;
     // at least kMinStepsPerWave j-steps per wave: a small job takes fewer workgroups, so each
-    // one's fixed cost (slot zeroing, table copy, final flush) spreads over more pairs
+    // one's fixed cost (table copy, histogram zeroing, final flush) spreads over more pairs
     // (rounded to whole rounds of one workgroup per CU: 261 workgroups on 256 CUs left five CUs
     // with two, and the job waited for them: 0.236 against 0.195 ms for 10k + 10k)
     int64_t want = (total + kMinStepsPerWave * a.waves - 1) / (kMinStepsPerWave * a.waves);
@@ -625,25 +619,43 @@ gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, in
       plan_out->always_recheck = use_lut && lp.s_star > 0.0 ? 1 : 0;
       return GC_OK;
     }
-    e = launch_edges(nbins, w_deg, edge_cos, hs);
-    if (e != hipSuccess) return device_error(e);
-    if (use_lut) {
-      e = launch_lut(nbins, w_deg, lp.m, lp.margin, lv.cols, a.bp.lut_alias, lp.s_star, lut_dev, hs);
-      if (e != hipSuccess) return device_error(e);
-    }
-    e = launch_pairs(a, num_wg, dot64, k, core, lv, hs);
-    if (e != hipSuccess) return device_error(e);
   }
-  if (plan_out) {  // no work: nothing to launch but the merge
-    memset(plan_out, 0, sizeof(*plan_out));
-    plan_out->core = core;
-    plan_out->dot_precision = dot64 ? 64 : 32;
-    plan_out->i_per_lane = k;
+  if (plan_out) {
+    if (total == 0) {  // no work: nothing to launch but the zeroing of the outputs
+      memset(plan_out, 0, sizeof(*plan_out));
+      plan_out->core = core;
+      plan_out->dot_precision = dot64 ? 64 : 32;
+      plan_out->i_per_lane = k;
+    }
     return GC_OK;
   }
-  uint64_t *outs[3] = {dd, dr, rr};
-  hipError_t e = launch_merge(a.slots, nbins, wb, we, outs, accumulate, hs);
-  if (e != hipSuccess) return device_error(e);
+  // One launch builds the tables and, unless the call accumulates, zeroes the outputs that the
+  // pair kernel's flushes then add into; the pair kernel follows on the same stream.
+  if (total > 0 || !accumulate) {
+    TablesArgs t;
+    t.nbins = nbins;
+    t.w_deg = w_deg;
+    t.edge_cos = edge_cos;
+    if (use_lut && total > 0) {
+      t.lut = lut_dev;
+      t.m = lp.m;
+      t.margin = lp.margin;
+      t.cols = lv.cols;
+      t.alias = a.bp.lut_alias;
+      t.s_star = lp.s_star;
+    }
+    if (!accumulate) {
+      t.out[0] = dd;
+      t.out[1] = dr;
+      t.out[2] = rr;
+    }
+    hipError_t e = launch_tables(t, hs);
+    if (e != hipSuccess) return device_error(e);
+  }
+  if (total > 0) {
+    hipError_t e = launch_pairs(a, num_wg, dot64, k, core, lv, hs);
+    if (e != hipSuccess) return device_error(e);
+  }
   return GC_OK;
 }
 
@@ -682,6 +694,8 @@ gc_status gc_launch_plan(int64_t n_d, int64_t n_r, int32_t nbins, double w_deg, 
 // host-side stand-in, never the device array: its device address is taken once per device with
 // hipGetSymbolAddress (that device current), and only that address reaches kernels.
 static __device__ __align__(256) unsigned char scratch[GC_STATIC_SCRATCH_BYTES];
+static_assert(((GC_MAX_BINS + 1) * sizeof(double) + 255) / 256 * 256 + gc::kLutBytes <= GC_STATIC_SCRATCH_BYTES,
+              "the static scratch holds the tables of every bin count");
 
 namespace gc {
 namespace {
@@ -719,16 +733,13 @@ gc_status gc_histogram_dd_dr_rr_noalloc(const void *prep_d, int64_t n_d, const v
   if ((st = check_catalog(prep_d, n_d)) != GC_OK) return st;
   if ((st = check_catalog(prep_r, n_r)) != GC_OK) return st;
   if (!dd || !dr || !rr || !aligned(dd, 8) || !aligned(dr, 8) || !aligned(rr, 8)) return GC_ERR_INVALID_ARGUMENT;
-  // the workgroups whose partial histograms fit beside the tables; one per family at least
-  const size_t fixed = scratch_bytes(nbins, 0), per_wg = static_cast<size_t>(nbins) * sizeof(unsigned long long);
-  if (fixed + 3 * per_wg > GC_STATIC_SCRATCH_BYTES) return GC_ERR_UNSUPPORTED;
-  const size_t fit = (GC_STATIC_SCRATCH_BYTES - fixed) / per_wg;
-  const int32_t max_wg = fit < static_cast<size_t>(kMaxWorkgroups) ? static_cast<int32_t>(fit) : kMaxWorkgroups;
+  // the tables of every bin count the library accepts fit the array (checked at compile time)
+  if (workspace_bytes(nbins) > GC_STATIC_SCRATCH_BYTES) return GC_ERR_UNSUPPORTED;
   void *ws = nullptr;
   const hipError_t e = static_scratch(&ws);
   if (e != hipSuccess) return device_error(e);
   return histogram_impl(prep_d, n_d, prep_r, n_r, nbins, w_deg, dd, dr, rr, ws, GC_STATIC_SCRATCH_BYTES, nullptr, 0,
-                        1, false, stream, nullptr, max_wg);
+                        1, false, stream);
 }
 
 gc_status gc_histogram_dd_dr_rr(const void *prep_d, int64_t n_d, const void *prep_r, int64_t n_r,
@@ -789,10 +800,21 @@ gc_status gc_eval_angle_core(const float *x32, const double *x64, int64_t n, int
   double *edge_cos = static_cast<double *>(workspace);
   uint2 *lut = need_ws ? reinterpret_cast<uint2 *>(static_cast<char *>(workspace) + edge_table_bytes(nbins)) : nullptr;
   hipError_t e = hipSuccess;
-  if (exact_out) e = launch_edges(nbins, w_deg, edge_cos, hs);
-  if (e == hipSuccess && use_lut) {
-    apply_lut(bp, lp, lv.cols, nbins);
-    e = launch_lut(nbins, w_deg, lp.m, lp.margin, lv.cols, bp.lut_alias, lp.s_star, lut, hs);
+  if (use_lut) apply_lut(bp, lp, lv.cols, nbins);
+  if (need_ws) {
+    TablesArgs t;
+    t.nbins = nbins;
+    t.w_deg = w_deg;
+    t.edge_cos = edge_cos;
+    if (use_lut) {
+      t.lut = lut;
+      t.m = lp.m;
+      t.margin = lp.margin;
+      t.cols = lv.cols;
+      t.alias = bp.lut_alias;
+      t.s_star = lp.s_star;
+    }
+    e = launch_tables(t, hs);
   }
   if (e == hipSuccess)
     e = launch_eval_core(x32, x64, n, bp, d64, core, lut, exact_out ? edge_cos : nullptr, bin_out, trip_out,

@@ -22,7 +22,7 @@ constexpr int drain_span(int k, int core, bool d64) {
   return (core == 2 && !d64) ? (k == 2 ? 1 : 2) : (k > 4 ? k / 2 : k);
 }
 constexpr int queue_words(int k, int core, bool d64) { return 2 * kWave * (drain_span(k, core, d64) + 1); }
-constexpr int kMaxWorkgroups = 2048; // partial-histogram slots held by the workspace
+constexpr int kMaxWorkgroups = 8192; // pair-kernel grid limit
 constexpr int kMaxBins = 8192;       // GC_MAX_BINS (include/gc.h; gc_api.cpp checks they agree)
 constexpr int kMaxBlocksPerCU = 8;
 constexpr int kOversubscribe = 3;      // workgroups launched per resident workgroup slot
@@ -124,7 +124,7 @@ struct PairArgs {
   FamilyWork fam[3];           // DD, DR, RR
   BinParams bp;
   const uint2 *lut;            // bin table (lut_n + 1 entries) in the workspace, or null
-  unsigned long long *slots;   // [num_workgroups][nbins] 64-bit partial histograms
+  uint64_t *out[3];            // DD, DR, RR outputs [nbins]; flushes add into them
   const double *edge_cos;      // [nbins + 1] cos(e w) in fp64, for the exact recheck
   int64_t flush_interval;      // j-steps between flushes of the 32-bit LDS histograms
   int32_t nbins;
@@ -174,24 +174,31 @@ hipError_t pairs_occupancy(bool dot64, int k, int core, LutVariant lv, size_t ld
 // The bin table: 2 m + 1 entries; cols: the histogram's columns (scales the row offsets);
 // alias: the middle entry's row when it holds no recheck zone; s_star > 0: entries whose |c| may
 // lie below s_star hold NaN (always recheck).
-hipError_t launch_lut(int32_t nbins, double w_deg, int32_t m, double margin, int cols, int32_t alias, double s_star,
-                      uint2 *lut, hipStream_t s);
 hipError_t launch_eval_dot_mfma(const float *ax, const float *ay, const float *az, const float *bx, const float *by,
                                 const float *bz, int64_t ntiles, float *out, hipStream_t s);
 // accumulate: add the sums to the outputs instead of overwriting them
-hipError_t launch_merge(const unsigned long long *slots, int32_t nbins, const int32_t wg_begin[3],
-                        const int32_t wg_end[3], uint64_t *out[3], bool accumulate, hipStream_t s);
 hipError_t launch_totals(const uint64_t *dd, const uint64_t *dr, const uint64_t *rr, int32_t nbins,
                          uint64_t *totals, hipStream_t s);
 hipError_t launch_omega(const uint64_t *dd, const uint64_t *dr, const uint64_t *rr, int32_t nbins,
                         int64_t n_d, int64_t n_r, double *omega, hipStream_t s);
-hipError_t launch_edges(int32_t nbins, double w_deg, double *edge_cos, hipStream_t s);
+// The edge cosines c[e] = cos(e w) (e = 0..nbins, -inf past 180 deg), the bin table when
+// lut is set (entries 0..2m) and, when out[0] is set, zeroed outputs (DD, DR, RR): one launch.
+struct TablesArgs {
+  int32_t nbins = 0;
+  double w_deg = 0.0;
+  double *edge_cos = nullptr;
+  uint2 *lut = nullptr;
+  int32_t m = 0, cols = 1, alias = 0;
+  double margin = 0.0, s_star = 0.0;
+  uint64_t *out[3] = {nullptr, nullptr, nullptr};
+  int32_t edge_blocks = 0;  // set by launch_tables
+};
+hipError_t launch_tables(const TablesArgs &t, hipStream_t s);
 hipError_t launch_eval_core(const float *x32, const double *x64, int64_t n, const BinParams &bp,
                             bool dot64, int core, const uint2 *lut, const double *edge_cos, int32_t *bin_out,
                             uint8_t *trip_out, int32_t *exact_out, float *t_out, hipStream_t s);
 
-// Workspace layout: the edge-cosine table, the bin table, then the per-workgroup 64-bit
-// partial histograms.
+// Workspace layout: the edge-cosine table, then the bin table.
 inline size_t edge_table_bytes(int32_t nbins) {
   return ((static_cast<size_t>(nbins) + 1) * sizeof(double) + 255) / 256 * 256;
 }

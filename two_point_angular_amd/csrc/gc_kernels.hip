@@ -7,9 +7,11 @@
 // Kernels:
 //   prepare_kernel - (alpha, delta) arcmin -> unit radius vector, fp64 math, stored
 //                    as SoA fp32 (correctly rounded) and fp64.
-//   pairs_kernel   - the hot loop.  Persistent grid; every wavefront takes an even share of
-//                    its family's "j-steps" (one j galaxy against an i-block of 64*K
-//                    galaxies held K per lane in VGPRs).  j is wave-uniform, so it is
+//   tables_kernel  - the fp64 edge cosines and the bin table; zeroes the outputs.
+//   pairs_kernel   - the hot loop.  Each workgroup takes an even share of its family's
+//                    "j-steps" (one j galaxy against an i-block of 64*K galaxies held K per
+//                    lane in VGPRs), which its waves split among themselves in chunks; the
+//                    grid holds several rounds of workgroups.  j is wave-uniform, so it is
 //                    streamed through the scalar unit (s_load into SGPRs, used directly
 //                    as VALU operands) instead of being staged in LDS; the bin-table core
 //                    instead takes its dot products from the matrix cores, 16 i x 16 j at a
@@ -17,9 +19,8 @@
 //                    sqrt times a fitted polynomial; the bin table; the series), bin index,
 //                    certified guard; ds_add_u32 into an LDS histogram.
 //                    Pairs the guard cannot certify are queued in LDS and re-binned in fp64,
-//                    64 at a time with all lanes busy.
-//   lut_kernel     - builds the bin table (fp64).
-//   merge_kernel   - sums the per-workgroup 64-bit partial histograms into the outputs.
+//                    64 at a time with all lanes busy.  A workgroup's histogram is added
+//                    into the 64-bit outputs with atomics.
 //   totals_kernel  - per-family sums (wave-shuffle reduction) for the exact N^2 check.
 //   omega_kernel   - Landy-Szalay estimator in fp64.
 //   eval_core_kernel - the pair kernel's angle-to-bin core on given cosines (diagnostic).
@@ -385,8 +386,9 @@ pairs_kernel(const PairArgs A) {
   const float mb_v = in_vgpr(LUT ? bp.lut_mb : 0.0f);
   const float tmax_v = bp.tmax + static_cast<float>(lane);
 
-  unsigned long long *const slot = A.slots + static_cast<size_t>(g) * A.nbins;
-  for (int b = threadIdx.x; b < A.nbins; b += nthreads) slot[b] = 0ull;
+  // the family's output histogram: every flush adds into it with 64-bit atomics (it was zeroed
+  // before the launch, or holds the counts that a part adds to)
+  unsigned long long *const slot = reinterpret_cast<unsigned long long *>(A.out[fi]);
   if (shared_hist) {
     for (int b = threadIdx.x; b < A.hist_words; b += nthreads) hist[b] = 0u;
     if constexpr (LUT)
@@ -398,9 +400,9 @@ pairs_kernel(const PairArgs A) {
     for (int b = lane; b < A.hist_words; b += kWave) hist[b] = 0u;
   }
   if (threadIdx.x == 0) *cursor = 0ull;
-  // (The barrier orders the slot zeroing before this workgroup's flush atomics: both reach the
-  // same L2.  A device-scope fence here, which writes back the L2 on gfx950, cost each workgroup
-  // ~20 us: an eighth of the 10k + 10k job.)
+  // (A device-scope fence before this barrier, which writes back the L2 on gfx950, cost each
+  // workgroup ~20 us: an eighth of the 10k + 10k job.  Nothing here needs one: the set-up writes
+  // only LDS.)
   __syncthreads();
 
   // The family's j-steps form two segments:
@@ -456,7 +458,7 @@ pairs_kernel(const PairArgs A) {
     if (LUT && row == A.bp.lut_alias) return static_cast<int>(A.bp.b180);
     return A.nbins - 1;
   };
-  // Move the LDS histogram into the workgroup's 64-bit slot.  Each word is taken with an
+  // Add the LDS histogram into the family's 64-bit output.  Each word is taken with an
   // atomic exchange, so in shared mode other waves may keep adding meanwhile; the value is
   // read as signed because a pending recheck may have moved a count out of a bin that an
   // earlier flush already emptied (the flush interval keeps every word within +-2^31).  The
@@ -877,8 +879,7 @@ pairs_kernel(const PairArgs A) {
 
 // ------------------------------------------------------------------------------- edges
 // c[e] = cos(e w) for e = 0..nbins (fp64); -inf where e w exceeds 180 degrees.
-__global__ void __launch_bounds__(256) edges_kernel(int32_t nbins, double w_deg, double *c) {
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+__device__ __forceinline__ void edge_entry(int e, int32_t nbins, double w_deg, double *c) {
   if (e > nbins) return;
   const double deg = static_cast<double>(e) * w_deg;
   c[e] = deg <= 180.0 ? cos(deg * (3.14159265358979323846 / 180.0)) : -__builtin_inf();
@@ -900,9 +901,8 @@ __device__ __forceinline__ double lut_angle_deg(double c) {  // inverse of the m
   return c >= 0.0 ? 2.0 * asin(fmin(c, 1.0) * kSqrtHalf) * kDeg : 180.0 - 2.0 * asin(fmin(-c, 1.0) * kSqrtHalf) * kDeg;
 }
 
-__global__ void __launch_bounds__(256) lut_kernel(int32_t nbins, double w_deg, int32_t m, double margin, int32_t cols,
-                                                  int32_t alias, double s_star, uint2 *lut) {
-  const int q = blockIdx.x * blockDim.x + threadIdx.x;
+__device__ __forceinline__ void lut_entry(int q, int32_t nbins, double w_deg, int32_t m, double margin, int32_t cols,
+                                          int32_t alias, double s_star, uint2 *lut) {
   if (q > 2 * m) return;
   constexpr double kSqrt2 = 1.41421356237309504880, kRad = 3.14159265358979323846 / 180.0;
   const uint32_t row_bytes = 4u * static_cast<uint32_t>(cols);
@@ -966,36 +966,22 @@ __global__ void __launch_bounds__(256) lut_kernel(int32_t nbins, double w_deg, i
   lut[q] = ent;
 }
 
-// ------------------------------------------------------------------------------- merge
-// out_f[bin] = sum of slots of family f's workgroups (plus out_f[bin] itself when
-// accumulating).  Grid (ceil(nbins / 64), 3): one block of 16 waves per 64 bins of a family,
-// one bin per lane; each wave sums every 16th workgroup's slot (several loads in flight), then
-// wave 0 adds the 16 sums.
-__global__ void __launch_bounds__(1024) merge_kernel(const unsigned long long *__restrict__ slots,
-                                                     int32_t nbins, int32_t b0, int32_t b1, int32_t b2,
-                                                     int32_t e0, int32_t e1, int32_t e2, uint64_t *o0,
-                                                     uint64_t *o1, uint64_t *o2, int32_t accumulate) {
-  constexpr int kMergeWaves = 16;
-  __shared__ unsigned long long part[kMergeWaves][kWave];
-  const int f = blockIdx.y;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wv = threadIdx.x / kWave;
-  const int bin = blockIdx.x * kWave + lane;
-  const int gb = f == 0 ? b0 : (f == 1 ? b1 : b2);
-  const int ge = f == 0 ? e0 : (f == 1 ? e1 : e2);
-  unsigned long long acc = 0ull;
-  if (bin < nbins) {
-#pragma unroll 4
-    for (int gg = gb + wv; gg < ge; gg += kMergeWaves) acc += slots[static_cast<size_t>(gg) * nbins + bin];
-  }
-  part[wv][lane] = acc;
-  __syncthreads();
-  if (wv == 0 && bin < nbins) {
-    uint64_t *o = f == 0 ? o0 : (f == 1 ? o1 : o2);
-    uint64_t sum = 0;
-#pragma unroll
-    for (int q = 0; q < kMergeWaves; ++q) sum += part[q][lane];
-    o[bin] = accumulate ? o[bin] + sum : sum;
+// ------------------------------------------------------------------------------ tables
+// One launch before the pair kernel: blocks [0, edge_blocks) write the edge cosines and, when
+// the call overwrites its outputs, zero them (the pair kernel's flushes add into them); the
+// blocks after them build the bin table when there is one.
+__global__ void __launch_bounds__(256) tables_kernel(const TablesArgs T) {
+  if (static_cast<int>(blockIdx.x) < T.edge_blocks) {
+    const int e = blockIdx.x * blockDim.x + threadIdx.x;
+    edge_entry(e, T.nbins, T.w_deg, T.edge_cos);
+    if (T.out[0] && e < T.nbins) {
+      T.out[0][e] = 0;
+      T.out[1][e] = 0;
+      T.out[2][e] = 0;
+    }
+  } else {
+    const int q = (blockIdx.x - T.edge_blocks) * blockDim.x + threadIdx.x;
+    lut_entry(q, T.nbins, T.w_deg, T.m, T.margin, T.cols, T.alias, T.s_star, T.lut);
   }
 }
 
@@ -1154,14 +1140,6 @@ hipError_t launch_pairs(const PairArgs &a, int num_wg, bool dot64, int k, int co
   return hipLaunchKernel(fn, dim3(num_wg), dim3(a.waves * kWave), args, lds, st);
 }
 
-hipError_t launch_merge(const unsigned long long *slots, int32_t nbins, const int32_t wb[3],
-                        const int32_t we[3], uint64_t *out[3], bool accumulate, hipStream_t st) {
-  dim3 grid((nbins + kWave - 1) / kWave, 3);
-  hipLaunchKernelGGL(merge_kernel, grid, dim3(1024), 0, st, slots, nbins, wb[0], wb[1], wb[2], we[0], we[1],
-                     we[2], out[0], out[1], out[2], accumulate ? 1 : 0);
-  return hipGetLastError();
-}
-
 hipError_t launch_totals(const uint64_t *dd, const uint64_t *dr, const uint64_t *rr, int32_t nbins,
                          uint64_t *totals, hipStream_t st) {
   hipLaunchKernelGGL(totals_kernel, dim3(3), dim3(256), 0, st, dd, dr, rr, nbins, totals);
@@ -1182,15 +1160,11 @@ hipError_t launch_eval_dot_mfma(const float *ax, const float *ay, const float *a
   return hipGetLastError();
 }
 
-hipError_t launch_lut(int32_t nbins, double w_deg, int32_t m, double margin, int cols, int32_t alias, double s_star,
-                      uint2 *lut, hipStream_t st) {
-  hipLaunchKernelGGL(lut_kernel, dim3((2 * m + 1 + 255) / 256), dim3(256), 0, st, nbins, w_deg, m, margin,
-                     static_cast<int32_t>(cols), alias, s_star, lut);
-  return hipGetLastError();
-}
-
-hipError_t launch_edges(int32_t nbins, double w_deg, double *edge_cos, hipStream_t st) {
-  hipLaunchKernelGGL(edges_kernel, dim3((nbins + 1 + 255) / 256), dim3(256), 0, st, nbins, w_deg, edge_cos);
+hipError_t launch_tables(const TablesArgs &t, hipStream_t st) {
+  TablesArgs a = t;
+  a.edge_blocks = (a.nbins + 1 + 255) / 256;
+  const int lut_blocks = a.lut ? (2 * a.m + 1 + 255) / 256 : 0;
+  hipLaunchKernelGGL(tables_kernel, dim3(a.edge_blocks + lut_blocks), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
