@@ -350,6 +350,15 @@ def measure(gc, wl, args, tuning, steps, warmup):
     return line
 
 
+# The LDS and L1 ceiling probes: (name, probe kind, LDS or table words (a multiple of 128), threads,
+# histogram columns).  11520 words: about the sixteen-column histogram of 720 bins; 3712 words:
+# about the bin table of 0.25-degree bins.
+LDS_CEILINGS = (("lds_atomic_random", "add", 11520, 1024, 0),
+                ("lds_atomic_16_columns", "add", 11520, 1024, 16),
+                ("lds_read64_random", "read64", 3712, 256, 0))
+L1_CEILING = ("l1_read64_random", 3712, 256)
+
+
 def measure_ceilings(gc):
     """This GPU's measured rates for the resources the pair kernel uses: VALU (independent fp32 and
     fp64 FMA chains, fp32 square roots) and LDS (random ds_add_u32 into one histogram, into a
@@ -364,11 +373,10 @@ def measure_ceilings(gc):
         "fp32_sqrt_lane_ops_per_s": gc.ceiling_valu(1, iters=2048),
         "fp64_fma_lane_ops_per_s": gc.ceiling_valu(2),
         **{name: {"instr_per_s": r, "cu_cycles_per_instr": 256 * 2.4e9 / r}
-           for name, r in (("lds_atomic_random", gc.ceiling_lds("add", 11584, 1024)),
-                           ("lds_atomic_16_columns", gc.ceiling_lds("add", 11584, 1024, cols=16)),
-                           ("lds_atomic_one_word", gc.ceiling_lds_atomic(720, same_bin=True, iters=256) / 64),
-                           ("lds_read64_random", gc.ceiling_lds("read64", 3712, 256)),
-                           ("l1_read64_random", gc.ceiling_l1(3712, 256)))},
+           for name, r in ([(n, gc.ceiling_lds(kind, words, threads, cols=cols))
+                            for n, kind, words, threads, cols in LDS_CEILINGS] +
+                           [("lds_atomic_one_word", gc.ceiling_lds_atomic(720, same_bin=True, iters=256) / 64),
+                            (L1_CEILING[0], gc.ceiling_l1(L1_CEILING[1], L1_CEILING[2]))])},
     }
 
 

@@ -247,3 +247,19 @@ def test_checkpoint_files(tmp_path):
     with pytest.raises(ValueError, match="another job"):
         parts.load_checkpoint(path, other)
     assert sorted(os.listdir(tmp_path)) == ["ck.npz"]          # the temporary file was renamed
+
+
+@pytest.mark.skipif(not NO_GPU, reason="checks the no-device status; only without a GPU")
+def test_bench_ceiling_probe_arguments_are_valid(lib):
+    """The probe arguments bench.py uses pass every host check (no GPU here: GC_ERR_DEVICE)."""
+    import sys
+    sys.path.insert(0, ROOT)
+    import bench
+    out = ctypes.c_uint64(0)
+    sink = ctypes.c_void_p(A)
+    big = 1 << 30
+    for _, kind, words, threads, cols in bench.LDS_CEILINGS:
+        assert lib.gc_ceiling_lds(gc.LDS_PROBES[kind], words, threads, 1, cols, 512, sink, big,
+                                  ctypes.byref(out), None) == DEVICE, (kind, words, cols)
+    _, words, threads = bench.L1_CEILING
+    assert lib.gc_ceiling_l1(words, threads, 256, sink, big, ctypes.byref(out), None) == DEVICE
