@@ -337,14 +337,11 @@ def test_fp64_span_variants(gc, case):
         np.testing.assert_array_equal(x, y)
 
 
-BI = 512  # galaxies per i-block with 8 per lane (the fp32 kernels' default, forced below)
-
-
-def _fast_rects(n_i, n_j, sym, s0, s1):
+def _fast_rects(n_i, n_j, sym, s0, s1, BI):
     """The off-diagonal work units [s0, s1) of one family as rectangles (row0, row1, col0, col1) of
     (i, j) pairs, following the decomposition gc_histogram_part documents: unit s of a cross family
     is i-block s // n_j against j = s % n_j; a self family takes, block by block, j from the end of
-    the block to n_j (the upper triangle by blocks)."""
+    the block to n_j (the upper triangle by blocks).  BI: galaxies per i-block (64 per lane)."""
     rects, s, nbf = [], s0, n_i // BI
     while s < s1:
         if not sym:
@@ -380,17 +377,19 @@ def _oracle_rects(A, B, rects, nbins, w, weight):
 
 def test_million_catalogs(gc):
     """1M + 1M (3e12 ordered pairs), clustered D and uniform R at 720 x 0.25 deg, in the default
-    launch plan: exact totals; DD == DR(D, D) and RR == DR(R, R) bitwise (every pair's bin is fixed
-    by the pair alone, so the self families' triangle schedule - a binary search over 1953 blocks'
-    prefix sums - must reproduce the cross family's full square); and three parts of the same job
-    (gc_histogram_part, 2e6 parts) against the oracle on exactly the pairs each part covers, with
-    the moved-pair budget enforced."""
+    launch plan (bench's): exact totals; DD == DR(D, D) and RR == DR(R, R) bitwise (every pair's
+    bin is fixed by the pair alone, so the self families' triangle schedule - a binary search over
+    the full blocks' prefix sums, 7812 of them at 2 galaxies per lane - must reproduce the cross
+    family's full square); and three parts of the same job (gc_histogram_part, 2e6 parts, the same
+    plan) against the oracle on exactly the pairs each part covers, with the moved-pair budget
+    enforced."""
     import torch
     print("[gpu] clustered1m_720: totals, self == cross, parts against the oracle", flush=True)
     wl = catalogs.WORKLOADS["clustered1m_720"]
     D, R = wl.catalogs()
     n, nbins, w = wl.n, wl.nbins, wl.bin_width_deg
-    tun = gc.Tuning(i_per_lane=8)
+    tun = None
+    BI = 64 * gc.launch_plan(n, n, nbins, w)["i_per_lane"]
     dd, dr, rr, tot, om = run_gpu(gc, D, R, nbins, w, tuning=tun)
     assert list(tot) == [n * n] * 3
     pd = gc.prepare(_dev(D.ra), _dev(D.dec))
@@ -415,7 +414,7 @@ def test_million_catalogs(gc):
         h = out.cpu().numpy().view(np.uint64)
         cases = (("DD", D, D, True, t_self, 2), ("DR", D, R, False, t_cross, 1), ("RR", R, R, True, t_self, 2))
         for k, (fam, A, B, sym, total, weight) in enumerate(cases):
-            rects = _fast_rects(n, n, sym, *_part_units(total, p, parts))
+            rects = _fast_rects(n, n, sym, *_part_units(total, p, parts), BI)
             ref = _oracle_rects(A, B, rects, nbins, w, weight)
             pairs = weight * sum((r1 - r0) * (c1 - c0) for r0, r1, c0, c1 in rects)
             assert pairs > 0
