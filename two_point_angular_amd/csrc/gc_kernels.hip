@@ -323,8 +323,8 @@ __device__ __forceinline__ void drain_queue(uint32_t *hist, const uint32_t *queu
 // 32 matrix-core tiles), fp64 K = 8 for four (48 VGPRs of fp64 i-coordinates).  Measured on
 // the 100k workloads, each step up in waves per SIMD outweighed the few spills it costs outside
 // the pair loop.  The bin-table core also builds at K = 2 for eight waves per SIMD (<= 64 VGPRs).
-// The bin-table core (CORE 2, fp32 dot) also takes COLS, its histogram's columns (1 or
-// kHistCols), and L1S, the share of its table reads made through the vector L1 (0 none, 1 an
+// The bin-table core (CORE 2, fp32 dot) also takes COLS, its histogram's columns (1,
+// kHistColsNarrow or kHistCols), and L1S, the share of its table reads made through the vector L1 (0 none, 1 an
 // eighth, 2 a quarter); its workgroups hold up to kMaxWavesPerWG waves (A.waves), all sharing
 // one table and one histogram.  The other cores run kWavesPerWG waves per workgroup.
 template <int K, bool D64, int CORE, int COLS = 1, int L1S = 2>
@@ -336,7 +336,8 @@ pairs_kernel(const PairArgs A) {
   constexpr bool LUT = CORE == 2 && !D64;  // fp64 dot: CORE 2 is the series core
   constexpr int BI = kWave * K;       // i-block: galaxies per wave
   constexpr int JB = D64 ? 4 : 8;     // j galaxies per scalar batch
-  static_assert(COLS == 1 || (LUT && COLS == kHistCols), "multi-column histograms belong to the bin-table core");
+  static_assert(COLS == 1 || (LUT && (COLS == kHistColsNarrow || COLS == kHistCols)),
+                "multi-column histograms belong to the bin-table core");
   static_assert(L1S == 2 || LUT, "the L1 share is a bin-table core variant");
   // queue entries pack (i - i0) and the fast-path row + 1 into 16 bits each
   static_assert(BI <= 0x10000 && kMaxBins + kWave + kLutAliasWords + 1 < 0x10000, "queue fields overflow");
@@ -713,9 +714,6 @@ pairs_kernel(const PairArgs A) {
           if (l1_tile(r, t)) ev[r] = lut_read_l1(key);
           else ev[r] = lut_read_lds(key, tab_bias);
         }
-        // the atomics issue at raised wave priority, so one wave's LDS burst goes out while the
-        // others bin (7.93 -> 7.82 ms on the 720-bin workload)
-        __builtin_amdgcn_s_setprio(1);
         if constexpr (COLS > 1) {
           float dl[4];
           uint32_t a[4];
@@ -726,7 +724,6 @@ pairs_kernel(const PairArgs A) {
             __hip_atomic_fetch_add(reinterpret_cast<lds_word_t *>(static_cast<uintptr_t>(a[r])), W, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_WORKGROUP);
           }
-          __builtin_amdgcn_s_setprio(0);
           // One guard test for the four pairs: the smallest |e - x| of them (v_minimum3_f32, which
           // returns NaN if any operand is NaN, so an always-recheck entry still trips).  Only when
           // some lane's four hold a flagged pair are they tested one by one and queued, with a
@@ -762,7 +759,6 @@ pairs_kernel(const PairArgs A) {
           bin_pair(2);
           if (DS == 1) drain_full();
           bin_pair(3);
-          __builtin_amdgcn_s_setprio(0);
           drain_full();
         }
       }
@@ -858,9 +854,10 @@ pairs_kernel(const PairArgs A) {
     }
   };
   {
-    // chunks of a multiple of 16 steps (whole matrix-core j-tiles), about 24 per wave, at least 32
+    // chunks of a multiple of 16 steps (whole matrix-core j-tiles), about 8 per wave, at least 32
+    // (100k + 100k at 720 bins: 6.34 ms with 24 per wave, 6.16-6.19 with 6, 8 or 12)
     const int64_t len = fe - fs;
-    const int64_t per = len / (static_cast<int64_t>(nw) * 24);
+    const int64_t per = len / (static_cast<int64_t>(nw) * 8);
     const int64_t CH = per < 32 ? 32 : (per + 15) & ~static_cast<int64_t>(15);
     while (true) {
       unsigned long long c = 0;
@@ -1098,6 +1095,7 @@ template <int K, bool D64, int CORE, int COLS = 1, int L1S = 2> static const voi
 }
 
 template <int K> static const void *select_lut(LutVariant lv) {
+  if (lv.cols == kHistColsNarrow) return pairs_fn<K, false, 2, kHistColsNarrow, 0>();
   if (lv.cols == kHistCols) {
     if (lv.l1 == 2) return pairs_fn<K, false, 2, kHistCols, 2>();
     if (lv.l1 == 1) return pairs_fn<K, false, 2, kHistCols, 1>();
