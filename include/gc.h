@@ -131,11 +131,9 @@ typedef struct {
                                 applies */
     int64_t flush_interval;  /* 0 auto; else j-steps between flushes of the 32-bit LDS
                                 histograms into 64-bit totals (>= 1) */
-    int32_t hist_columns;    /* bin-table core: 0 auto; 1, 4 or 16 LDS histogram columns (16:
-                                one word per bin for each lane mod 16, so an atomic's 16-lane
-                                group never shares a bank; 4: lanes of different columns never
-                                share one; invalid where it does not fit in LDS, and 4 with an
-                                l1_share other than 0 or 1) */
+    int32_t hist_columns;    /* bin-table core: 0 auto; 1 or 16 LDS histogram columns (16: one
+                                word per bin for each lane mod 16, so an atomic's 16-lane group
+                                never shares a bank; invalid where it does not fit in LDS) */
     int32_t waves_per_group; /* bin-table core: 0 auto, else 4..16 wavefronts per workgroup */
     int32_t l1_share;        /* bin-table core: 0 auto; share of table reads made through the
                                 vector L1 instead of LDS: 1 none (the choice of auto), 2 an

@@ -95,7 +95,7 @@ typedef struct {
                                   (fp32 dot) or series (fp64 dot) */
     int32_t dot_precision;     /* 32 or 64 */
     int32_t i_per_lane;        /* 4 or 8 */
-    int32_t hist_columns;      /* 1, 4 or 16 */
+    int32_t hist_columns;      /* 1 or 16 */
     int32_t waves_per_group;   /* wavefronts per workgroup */
     int32_t l1_share;          /* bin table: 1 none, 2 an eighth, 3 a quarter; else 0 */
     int32_t shared_histogram;  /* 1: one histogram per workgroup */

@@ -218,16 +218,15 @@ LutPlan plan_lut(int32_t nbins, double w_deg) {
   return p;
 }
 
-// The bin-table kernel's histogram rows: 4 or 16 columns keep one spare row (nbins) and the alias
-// rows nbins + 1, nbins + 2; one column keeps 64 spare words and the alias words nbins + 64,
-// nbins + 65.  A row is 4 cols bytes: lut_sh = log2 of that.
+// The bin-table kernel's histogram rows: cols 16 keeps one spare row (nbins) and the alias rows
+// nbins + 1, nbins + 2; one column keeps 64 spare words and the alias words nbins + 64, nbins + 65.
 void apply_lut(BinParams &bp, const LutPlan &lp, int cols, int32_t nbins) {
   bp.lut_m = static_cast<float>(lp.m);
   bp.lut_mb = static_cast<float>(lp.m) + 8388608.0f;  // exact: M < 2^23
   bp.lut_g = lp.g;
   bp.lut_n = 2 * lp.m;
-  bp.lut_sh = cols == kHistCols ? 6 : (cols == kHistColsNarrow ? 4 : 2);
-  bp.lut_alias = cols > 1 ? nbins + 2 : nbins + kWave + 1;
+  bp.lut_sh = cols == kHistCols ? 6 : 2;
+  bp.lut_alias = cols == kHistCols ? nbins + 2 : nbins + kWave + 1;
 }
 
 bool lut_layout(const LutPlan &lp, int32_t nbins, int k, const gc_tuning &tu, LutVariant *lv, int *waves);
@@ -436,10 +435,7 @@ gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, in
       (tu.i_per_lane != 0 && tu.i_per_lane != 2 && tu.i_per_lane != 4 && tu.i_per_lane != 8) || tu.blocks_per_cu < 0 ||
       tu.blocks_per_cu > kMaxBlocksPerCU || tu.shared_histogram < 0 || tu.shared_histogram > 2 ||
       tu.span_kernel < 0 || tu.span_kernel > 2 || tu.fast_core < 0 || tu.fast_core > 2 ||
-      tu.flush_interval < 0 ||
-      (tu.hist_columns != 0 && tu.hist_columns != 1 && tu.hist_columns != kHistColsNarrow &&
-       tu.hist_columns != kHistCols) ||
-      (tu.hist_columns == kHistColsNarrow && tu.l1_share > 1) ||
+      tu.flush_interval < 0 || (tu.hist_columns != 0 && tu.hist_columns != 1 && tu.hist_columns != kHistCols) ||
       (tu.waves_per_group != 0 && (tu.waves_per_group < kWavesPerWG || tu.waves_per_group > kMaxWavesPerWG)) ||
       tu.l1_share < 0 || tu.l1_share > 3 || tu.reserved_ != 0)
     return GC_ERR_INVALID_ARGUMENT;

@@ -97,7 +97,6 @@ constexpr int kLutAliasWords = 2;
 // Histogram columns of the bin-table core: one, or sixteen - row b holds one word per lane mod 16,
 // so the 16 lanes an LDS atomic serves together always hit 16 different banks.
 constexpr int kHistCols = 16;
-constexpr int kHistColsNarrow = 4;  // the bin-table histogram's other multi-column layout
 // The bin-table core's bound on |x~ - x| in units of 2^-24 (see plan_lut in gc_api.cpp).
 constexpr double kLutDotErr = 12.0;
 // ---- pair-kernel work description ---------------------------------------------------
@@ -134,9 +133,8 @@ struct PairArgs {
   int32_t waves;               // waves per workgroup (kWavesPerWG, or up to kMaxWavesPerWG for the bin table)
 };
 
-// The bin-table kernel's variants: histogram columns (1, kHistColsNarrow or kHistCols) and the
-// share of table reads made through the vector L1 instead of LDS (0: none; 1: an eighth; 2: a
-// quarter; kHistColsNarrow columns read LDS only).
+// The bin-table kernel's variants: histogram columns (1 or kHistCols) and the share of table
+// reads made through the vector L1 instead of LDS (0: none; 1: an eighth; 2: a quarter).
 struct LutVariant {
   int cols = 1;
   int l1 = 2;
@@ -153,7 +151,7 @@ inline size_t pairs_lds_bytes(int32_t hist_words, bool shared_hist, int k, int c
   return (words + kCursorWords) * sizeof(uint32_t);
 }
 // Histogram words of the bin-table core: one column with 64 spare rows and the two alias rows, or
-// cols columns (kHistColsNarrow or kHistCols) of nbins + 3 rows (one spare row, two alias rows).
+// kHistCols columns of nbins + 3 rows (one spare row, two alias rows).
 inline int32_t lut_hist_words(int32_t nbins, int cols) {
   return cols == 1 ? (nbins + kWave + kLutAliasWords + 63) / 64 * 64 : (cols * (nbins + 3) + 63) / 64 * 64;
 }

@@ -323,8 +323,8 @@ __device__ __forceinline__ void drain_queue(uint32_t *hist, const uint32_t *queu
 // 32 matrix-core tiles), fp64 K = 8 for four (48 VGPRs of fp64 i-coordinates).  Measured on
 // the 100k workloads, each step up in waves per SIMD outweighed the few spills it costs outside
 // the pair loop.  The bin-table core also builds at K = 2 for eight waves per SIMD (<= 64 VGPRs).
-// The bin-table core (CORE 2, fp32 dot) also takes COLS, its histogram's columns (1,
-// kHistColsNarrow or kHistCols), and L1S, the share of its table reads made through the vector L1 (0 none, 1 an
+// The bin-table core (CORE 2, fp32 dot) also takes COLS, its histogram's columns (1 or
+// kHistCols), and L1S, the share of its table reads made through the vector L1 (0 none, 1 an
 // eighth, 2 a quarter); its workgroups hold up to kMaxWavesPerWG waves (A.waves), all sharing
 // one table and one histogram.  The other cores run kWavesPerWG waves per workgroup.
 template <int K, bool D64, int CORE, int COLS = 1, int L1S = 2>
@@ -336,8 +336,7 @@ pairs_kernel(const PairArgs A) {
   constexpr bool LUT = CORE == 2 && !D64;  // fp64 dot: CORE 2 is the series core
   constexpr int BI = kWave * K;       // i-block: galaxies per wave
   constexpr int JB = D64 ? 4 : 8;     // j galaxies per scalar batch
-  static_assert(COLS == 1 || (LUT && (COLS == kHistColsNarrow || COLS == kHistCols)),
-                "multi-column histograms belong to the bin-table core");
+  static_assert(COLS == 1 || (LUT && COLS == kHistCols), "multi-column histograms belong to the bin-table core");
   static_assert(L1S == 2 || LUT, "the L1 share is a bin-table core variant");
   // queue entries pack (i - i0) and the fast-path row + 1 into 16 bits each
   static_assert(BI <= 0x10000 && kMaxBins + kWave + kLutAliasWords + 1 < 0x10000, "queue fields overflow");
@@ -1095,7 +1094,6 @@ template <int K, bool D64, int CORE, int COLS = 1, int L1S = 2> static const voi
 }
 
 template <int K> static const void *select_lut(LutVariant lv) {
-  if (lv.cols == kHistColsNarrow) return pairs_fn<K, false, 2, kHistColsNarrow, 0>();
   if (lv.cols == kHistCols) {
     if (lv.l1 == 2) return pairs_fn<K, false, 2, kHistCols, 2>();
     if (lv.l1 == 1) return pairs_fn<K, false, 2, kHistCols, 1>();
