@@ -4,7 +4,8 @@ Workload (default): 100,000 clustered D galaxies + 100,000 uniform R galaxies (f
 arcmin, seeds 1 and 2), 720 bins of 0.25 deg -- the shape of the 100k + 100k problem of
 "CUDA Deep Dive: 10B Galaxy Pairs on an RTX 5080", section "The problem", on synthetic
 catalogs.  One step = the whole path on device-resident inputs: prepare D and R (unit
-vectors), the pair kernel + merge (DD, DR, RR), the totals reduction and omega.
+vectors), the histogram call (the tables launch, then the pair kernel: DD, DR, RR), the totals
+reduction and omega.
 
 Prints one JSON line.  value = ordered pairs per second (N_D^2 + N_D N_R + N_R^2 per step).
 roofline: the pair kernel's algorithmic FP32 work (25 flops per evaluated pair, where the
@@ -331,7 +332,8 @@ def measure(gc, wl, args, tuning, steps, warmup):
                    "parallelism": "1 GPU", **({"parts": args.parts} if args.parts != 1 else {})},
         "kernel_ms": {"mean": float(np.mean(kern_ms)), "median": float(np.median(kern_ms)),
                       "min": float(np.min(kern_ms)),
-                      "what": "pair kernel + merge, HIP events over the timed steps" +
+                      "what": "the histogram call (tables launch + pair kernel), HIP events over the "
+                              "timed steps" +
                               (f" ({args.parts} parts)" if args.parts != 1 else "")},
         "protocol": {"cold_ms": float(all_ms[0]),
                      "runs_2_9_median_ms": float(np.median(runs_2_9)) if len(runs_2_9) else None,
