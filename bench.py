@@ -53,7 +53,7 @@ def measured_traffic(workload):
     return float(vals["traffic_bytes_per_launch"])
 
 
-def cpu_baseline(D, R, nbins, w, target_s=12.0):
+def cpu_baseline(D, R, nbins, w, target_s=16.0):
     import numpy as np
     from oracle import oracle
 
