@@ -537,14 +537,28 @@ pairs_kernel(const PairArgs A) {
     }
   };
 
-  // The same for a pair whose j varies across the wave (the MFMA fast path): i_local = i - i0.
-  auto enqueue_ij = [&](bool tp, uint32_t kslot, uint32_t i_local, int64_t jl) __attribute__((always_inline)) {
+  // The same for a pair of a matrix-core tile, whose j varies across the wave: i_local = i - i0 =
+  // 16 t + 4 comp + r (comp = lane / 16).  The compiler keeps the lane's part in a register
+  // across the tile loop, and the kernels spill it, so an enqueue reloads it from scratch and
+  // waits.  The one-column layout enqueues after every pair, and with four waves per SIMD those
+  // waits cost time (3600 bins: 8.63 -> 8.41 ms), so there the caller passes il = 16 t + r and the
+  // lane id is recomputed here: two ALU instructions in a volatile asm statement, which (unlike
+  // the equivalent builtins) the compiler cannot hoist out of this rare branch.  The
+  // sixteen-column layout passes the whole i_local: it enqueues rarely at eight waves per SIMD,
+  // and the other form measured slower there (720 bins: 6.20 against 6.26 ms).
+  auto enqueue_ij = [&](bool tp, uint32_t kslot, uint32_t il, int64_t jl) __attribute__((always_inline)) {
     const unsigned long long m = __ballot(tp);
     if (__builtin_expect(m != 0, 0)) {
       if (tp) {
         const uint32_t e = __builtin_amdgcn_mbcnt_hi(
             static_cast<uint32_t>(m >> 32),
             __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), static_cast<uint32_t>(qcount)));
+        uint32_t i_local = il;
+        if constexpr (COLS == 1) {
+          uint32_t ln;
+          asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+          i_local += (ln >> 4) << 2;
+        }
         queue[2 * e] = static_cast<uint32_t>(jl);
         queue[2 * e + 1] = (i_local << 16) | kslot;
       }
@@ -747,7 +761,7 @@ pairs_kernel(const PairArgs A) {
             const uint32_t a = lut_row_address(d[r], ev[r], l1_tile(r, t), tp);
             __hip_atomic_fetch_add(reinterpret_cast<lds_word_t *>(static_cast<uintptr_t>(a)), W, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_WORKGROUP);
-            enqueue_ij(tp, ((a - hist_addr) >> bp.lut_sh) + 1, static_cast<uint32_t>(16 * t + 4 * comp + r), jl);
+            enqueue_ij(tp, ((a - hist_addr) >> bp.lut_sh) + 1, static_cast<uint32_t>(16 * t + r), jl);
           };
           // a drain point after every drain_span pairs of the lane's four (one or two)
           constexpr int DS = drain_span(K, CORE, D64);
