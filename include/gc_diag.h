@@ -94,7 +94,7 @@ typedef struct {
     int32_t core;              /* 0 arccos (generic), 1 arccos (span-specialised), 2 bin table
                                   (fp32 dot) or series (fp64 dot) */
     int32_t dot_precision;     /* 32 or 64 */
-    int32_t i_per_lane;        /* 4 or 8 */
+    int32_t i_per_lane;        /* 2, 4 or 8 */
     int32_t hist_columns;      /* 1 or 16 */
     int32_t waves_per_group;   /* wavefronts per workgroup */
     int32_t l1_share;          /* bin table: 1 none, 2 an eighth, 3 a quarter; else 0 */
@@ -104,7 +104,7 @@ typedef struct {
     int32_t lds_bytes;         /* LDS per workgroup */
     int64_t flush_interval;    /* j-steps between flushes of the 32-bit LDS histograms */
     int32_t always_recheck;    /* bin table: 1 when entries near 0 and 180 deg always recheck */
-    int32_t reserved_;
+    int32_t lut_m;             /* bin table: M, the table holding 2 M + 1 entries; else 0 */
 } gc_plan;
 
 gc_status gc_launch_plan(int64_t n_d, int64_t n_r, int32_t nbins, double bin_width_deg, const gc_tuning *tuning,

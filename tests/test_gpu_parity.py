@@ -460,7 +460,12 @@ def test_bin_table_maps_every_entry(gc, nbins, w):
     assert st == 0
     torch.cuda.synchronize()
     w_rad = np.radians(w)
-    m = int(np.ceil(4 / w_rad))
+    # M: ceil(4 / w), or the largest sound M >= 2.5 / w that lets two one-column workgroups share a
+    # compute unit (3600 x 0.05 deg)
+    m = int(gc.launch_plan(1000, 1000, nbins, w)["lut_m"])
+    assert np.ceil(2.5 / w_rad) <= m <= np.ceil(4 / w_rad)
+    if nbins == 720:
+        assert m == np.ceil(4 / w_rad)
     off = ((nbins + 1) * 8 + 255) // 256 * 256
     tab = ws[off: off + (2 * m + 1) * 8].cpu().numpy().view(np.uint32).reshape(-1, 2)
     e = tab[:, 0].view(np.float32).astype(np.float64)

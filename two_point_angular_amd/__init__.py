@@ -66,7 +66,7 @@ class _Plan(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("core", "dot_precision", "i_per_lane", "hist_columns", "waves_per_group",
                                               "l1_share", "shared_histogram", "blocks_per_cu", "workgroups",
                                               "lds_bytes")] + \
-               [("flush_interval", ctypes.c_int64), ("always_recheck", ctypes.c_int32), ("reserved_", ctypes.c_int32)]
+               [("flush_interval", ctypes.c_int64), ("always_recheck", ctypes.c_int32), ("lut_m", ctypes.c_int32)]
 
 
 @dataclass

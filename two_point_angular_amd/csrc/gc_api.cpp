@@ -158,7 +158,8 @@ BinParams make_bins(int32_t nbins, double w_deg) {
 // g_c = 1.1 (g_x + 2^-23) (for |x~| < 1/2, s > 0.7 and the subtraction's 2^-25 fits the 10 %).
 // The table is sound when
 //  (a) no widened entry range can hold two edges: 1/M + 2 margin < the smallest gap between
-//      consecutive edges in c (M = ceil(4 / w_rad), margin = 0.45 (gap - 1/M));
+//      consecutive edges in c (M = ceil(4 / w_rad) unless the layout asks for a smaller table,
+//      margin = 0.45 (gap - 1/M));
 //  (b) where the error of c may exceed the margin (s~ < S* = g_c / margin), no pair can reach an
 //      edge: 1 - |x| <= y + g_x <= s~^2 (1 + 2^-22) + g_x, so |c| <= sqrt(S*^2 (1 + 2^-22) + g_x)
 //      must stay below the |c| of the first and last edges;
@@ -181,11 +182,12 @@ struct LutPlan {
 // edge the only one the pair can be near.  Entries closer to c = 0 (angles within about
 // 2 asin(S* / sqrt2) of 0 or 180 deg, the middle entry among them) hold NaN, and their pairs are
 // rechecked; S* is kept at or below 0.05 (about 4 deg), so the rechecked share stays small.
-LutPlan plan_lut(int32_t nbins, double w_deg) {
+// m: the table's M, or 0 for ceil(4 / w_rad).
+LutPlan plan_lut(int32_t nbins, double w_deg, int32_t m = 0) {
   LutPlan p;
   if (!((static_cast<double>(nbins) + 0.5) * w_deg >= 180.0) || nbins < 2) return p;
   const double w = w_deg * (kPi / 180.0);
-  const double md = ceil(4.0 / w);
+  const double md = m > 0 ? static_cast<double>(m) : ceil(4.0 / w);
   if (2.0 * md + 1.0 > static_cast<double>(kLutMaxEntries)) return p;
   const double sqrt2 = 1.41421356237309504880;
   auto c_right = [&](int e) { return sqrt2 * sin(0.5 * e * w); };
@@ -231,25 +233,53 @@ void apply_lut(BinParams &bp, const LutPlan &lp, int cols, int32_t nbins) {
 
 bool lut_layout(const LutPlan &lp, int32_t nbins, int k, const gc_tuning &tu, LutVariant *lv, int *waves);
 
+// LDS of one compute unit on gfx950.
+constexpr size_t kLdsPerCU = 160 * 1024;
+
 // The bin-table kernel's K and layout, unless overridden: K = 2 where the sixteen-column
-// histogram fits (two workgroups of 16 waves: eight per SIMD), else K = 4 with one column (one
-// workgroup of 16 waves).  With the waves of a workgroup sharing its steps through the cursor,
-// the larger groups measured fastest: 100k + 100k at 720 bins 6.35 ms at K = 2 against 6.41 at
-// K = 4 and 7.15 at K = 8; 3600 bins 8.76 ms at K = 4 against 9.3 at K = 2 and 10.0 at K = 8.
-// *k receives the K chosen.
-bool lut_choose(const LutPlan &lp, int32_t nbins, const gc_tuning &tu, int *k, LutVariant *lv, int *waves) {
+// histogram fits (two workgroups of 16 waves: eight per SIMD).  Else one column: K = 2 with two
+// workgroups of 16 waves per compute unit where they fit beside the table, taking, where the
+// table of ceil(4 / w) entries leaves no room for them, the largest sound table that does, down
+// to M = 2.5 / w (a smaller M widens the always-recheck zone near 0 and 180 deg: S* grows as
+// 1 / margin); else K = 4 with one workgroup of 16 waves (its 80 VGPRs would allow six waves per
+// SIMD, the LDS not two workgroups).  With the waves of a workgroup sharing its steps through the
+// cursor, the larger groups measured fastest: 100k + 100k at 720 bins 6.35 ms at K = 2 against
+// 6.41 at K = 4 and 7.15 at K = 8.  3600 bins: K = 4 with M = 4 / w 8.39 ms; two workgroups of
+// K = 2 with M = 2.5 / w 8.21 ms (M = 2.5 / w with one workgroup: 8.61, the rechecks alone).
+// lp may be replaced by the smaller table's plan; *k receives the K chosen.
+bool lut_choose(LutPlan &lp, int32_t nbins, double w_deg, const gc_tuning &tu, int *k, LutVariant *lv,
+                int *waves) {
   if (tu.i_per_lane) {
     *k = tu.i_per_lane;
     return lut_layout(lp, nbins, *k, tu, lv, waves);
   }
   *k = 2;
   if (lut_layout(lp, nbins, 2, tu, lv, waves) && lv->cols == kHistCols) return true;
+  if (tu.hist_columns == 0 && tu.waves_per_group == 0) {
+    const size_t base = pairs_lds_bytes(lut_hist_words(nbins, 1), true, 2, 2, false, kMaxWavesPerWG, 0);
+    if (2 * base < kLdsPerCU) {
+      const int64_t tw_max = static_cast<int64_t>((kLdsPerCU / 2 - base) / sizeof(uint32_t));
+      const int64_t m_fit = (tw_max / 2 - 1) / 2;  // 2 (2 M + 1) table words
+      const double w = w_deg * (kPi / 180.0);
+      if (static_cast<double>(m_fit) >= ceil(2.5 / w)) {
+        const LutPlan p2 = m_fit < lp.m ? plan_lut(nbins, w_deg, static_cast<int32_t>(m_fit)) : lp;
+        gc_tuning t2 = tu;
+        t2.hist_columns = 1;
+        t2.waves_per_group = kMaxWavesPerWG;
+        LutVariant lv2;
+        int w2 = 0;
+        if (p2.ok && lut_layout(p2, nbins, 2, t2, &lv2, &w2)) {
+          lp = p2;
+          *lv = lv2;
+          *waves = w2;
+          return true;
+        }
+      }
+    }
+  }
   *k = 4;
   return lut_layout(lp, nbins, 4, tu, lv, waves);
 }
-
-// LDS of one compute unit on gfx950.
-constexpr size_t kLdsPerCU = 160 * 1024;
 
 // The bin-table kernel's layout: sixteen histogram columns when two workgroups of 8 waves (12 at
 // K = 4, 16 at K = 2) fit in a compute unit's LDS beside their tables and queues; else one column
@@ -445,7 +475,8 @@ gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, in
   const bool dot64 = tu.dot_precision == 64 || (tu.dot_precision == 0 && w_deg < 0.01);
   // Galaxies per lane: 8 for the fp32 arccos kernels; 4 for the fp64 kernel, whose fp64
   // i-galaxies at K = 8 leave room for only three waves per SIMD; the bin-table core picks its
-  // own (lut_choose: 2 with the sixteen-column histogram, else 4).
+  // own (lut_choose: 2, or 4 where neither the sixteen-column histogram nor two workgroups of the
+  // one-column one fit).
   int k = tu.i_per_lane ? tu.i_per_lane : (dot64 ? 4 : 8);
   // Span-specialised cores: when the bins reach 180 deg (up to half a bin), t cannot exceed
   // nbins + 1 and the fp32 kernel needs no clamp of t (a spare bin takes t = nbins); when they
@@ -455,12 +486,12 @@ gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, in
   const bool span = span_ok && tu.span_kernel != 1;
   // The arccos-free cores where they are sound: the bin table (fp32 dot, full span, shared
   // histogram) and the series (fp64 dot, bins ending by ~9 deg).
-  const LutPlan lp = dot64 ? LutPlan() : plan_lut(nbins, w_deg);
+  LutPlan lp = dot64 ? LutPlan() : plan_lut(nbins, w_deg);
   const SeriesPlan sp = dot64 ? plan_series(nbins, w_deg) : SeriesPlan();
   LutVariant lv;
   int lut_waves = kWavesPerWG;
   int k_lut = k;
-  const bool lut_fits = lp.ok && lut_choose(lp, nbins, tu, &k_lut, &lv, &lut_waves);
+  const bool lut_fits = lp.ok && lut_choose(lp, nbins, w_deg, tu, &k_lut, &lv, &lut_waves);
   if (lp.ok && !lut_fits && (tu.hist_columns || tu.waves_per_group)) return GC_ERR_INVALID_ARGUMENT;
   const bool lut_ok = lut_fits && span && tu.shared_histogram != 1;
   const bool series_ok = sp.ok && span;
@@ -617,6 +648,7 @@ gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, in
       plan_out->lds_bytes = static_cast<int32_t>(shared ? lds_shared : lds_private);
       plan_out->flush_interval = a.flush_interval;
       plan_out->always_recheck = use_lut && lp.s_star > 0.0 ? 1 : 0;
+      plan_out->lut_m = use_lut ? lp.m : 0;
       return GC_OK;
     }
   }
@@ -781,13 +813,13 @@ gc_status gc_eval_angle_core(const float *x32, const double *x64, int64_t n, int
   if (n > 0 && ((d64 && !x64) || (!d64 && !x32) || !bin_out || !trip_out)) return GC_ERR_INVALID_ARGUMENT;
   // the same core the histogram call would use for these bins
   const bool span = d64 ? span_narrow(nbins, w_deg) : span_full(nbins, w_deg);
-  const LutPlan lp = d64 ? LutPlan() : plan_lut(nbins, w_deg);
+  LutPlan lp = d64 ? LutPlan() : plan_lut(nbins, w_deg);
   const SeriesPlan sp = d64 ? plan_series(nbins, w_deg) : SeriesPlan();
   gc_tuning tu0;
   memset(&tu0, 0, sizeof(tu0));
   LutVariant lv;
   int lut_waves = 0, lut_k = 0;
-  const bool use_lut = lp.ok && span && lut_choose(lp, nbins, tu0, &lut_k, &lv, &lut_waves);
+  const bool use_lut = lp.ok && span && lut_choose(lp, nbins, w_deg, tu0, &lut_k, &lv, &lut_waves);
   const bool use_series = sp.ok && span;
   const int core = (use_lut || use_series) ? 2 : (span ? 1 : 0);
   if (n == 0) return GC_OK;
