@@ -266,6 +266,12 @@ bool lut_choose(LutPlan &lp, int32_t nbins, double w_deg, const gc_tuning &tu, i
         gc_tuning t2 = tu;
         t2.hist_columns = 1;
         t2.waves_per_group = kMaxWavesPerWG;
+        // With two workgroups per CU the LDS is the tighter resource, and a share of the table
+        // reads goes through the vector L1: a quarter while the table stays mostly in its 32 KB,
+        // an eighth for larger ones.  Measured, none / an eighth / a quarter: 1440 x 0.125 deg
+        // (29 KB table) 7.87 / 7.50 / 7.14 ms; 1800 x 0.1 (37 KB) 7.89 / 7.53 / 7.35; 2400 x 0.075
+        // (49 KB) 7.97 / 7.60 / 7.92; 3600 x 0.05 (51 KB) 8.30 / 7.98 / 8.53.
+        if (t2.l1_share == 0) t2.l1_share = 8 * (2 * static_cast<size_t>(p2.m) + 1) <= 40 * 1024 ? 3 : 2;
         LutVariant lv2;
         int w2 = 0;
         if (p2.ok && lut_layout(p2, nbins, 2, t2, &lv2, &w2)) {
@@ -283,10 +289,11 @@ bool lut_choose(LutPlan &lp, int32_t nbins, double w_deg, const gc_tuning &tu, i
 
 // The bin-table kernel's layout: sixteen histogram columns when two workgroups of 8 waves (12 at
 // K = 4, 16 at K = 2) fit in a compute unit's LDS beside their tables and queues; else one column
-// in one workgroup of 16 waves.  Every table read goes to LDS unless overridden: a share through
-// the vector L1 measured slower in both layouts once the waves of a workgroup shared its steps
-// (720 bins: an eighth 6.40 against 6.35 ms; 3600 bins: an eighth 9.46 against 8.76 ms), and the
-// large tables of fine bins do not stay in the L1.  Overrides may pick any layout that fits.
+// in one workgroup of 16 waves.  Every table read goes to LDS unless overridden (or unless
+// lut_choose picks the one-column layout of two workgroups per CU): a share through the vector
+// L1 measured slower where the VALU is as busy as the LDS (720 bins: an eighth 6.40 against
+// 6.35 ms) and with one workgroup per CU (3600 bins: an eighth 9.46 against 8.76 ms).  Overrides
+// may pick any layout that fits.
 // Returns false when none fits.
 bool lut_layout(const LutPlan &lp, int32_t nbins, int k, const gc_tuning &tu, LutVariant *lv, int *waves) {
   const int32_t tw = 2 * (2 * lp.m + 1);
