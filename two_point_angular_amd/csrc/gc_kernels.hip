@@ -428,7 +428,12 @@ pairs_kernel(const PairArgs A) {
   share(F.gen_begin, F.gen_steps, V, v, gs, ge);
   const int64_t nbf = F.n_i / BI;  // full i-blocks
 
-  int64_t since_flush = 0;
+  // j-steps since the last flush, and the interval, as 32-bit wave-uniform values so that the
+  // test stays on the scalar unit (the host caps the interval near 2^31 / (2 * 64 K * waves),
+  // at most ~8.4e6 steps)
+  int32_t since_flush = 0;
+  const int32_t flush_every = __builtin_amdgcn_readfirstlane(
+      static_cast<int32_t>(A.flush_interval < 0x7fff0000 ? A.flush_interval : 0x7fff0000));
   int qcount = 0;  // queue entries [0, qcount) are pending
   // histogram rows: bins, spare rows and the bin table's alias rows
   const int hist_rows = COLS > 1 ? A.nbins + 3 : A.hist_words;
@@ -634,7 +639,7 @@ pairs_kernel(const PairArgs A) {
   };
 
   auto check_flush = [&]() __attribute__((always_inline)) {
-    if (__builtin_expect(since_flush >= A.flush_interval, 0)) {
+    if (__builtin_expect(since_flush >= flush_every, 0)) {
       drain_all();
       flush();
       since_flush = 0;
@@ -707,12 +712,16 @@ pairs_kernel(const PairArgs A) {
     for (int t = 0; t < NT; ++t) at[t] = comp < 3 ? src[i0 + 16 * t + sub] : 0.0f;
   };
   // Full chunks of 16 j in [ja, jb) (fewer than 16 remain; the caller runs them the usual way).
+  // The chunk count is a wave-uniform 32-bit value, so the loop's control runs on the scalar unit
+  // (with 64-bit j bounds the compiler kept it on the VALU: ~8 instructions per chunk); each lane's
+  // j pointer advances by 16, and its j index is formed only where a pair is queued.
   auto run_fast_mfma = [&](int64_t ja, int64_t jb) __attribute__((always_inline)) {
-    const float *jsrc = comp == 0 ? F.cj.x : (comp == 1 ? F.cj.y : F.cj.z);
+    const float *jp = (comp == 0 ? F.cj.x : (comp == 1 ? F.cj.y : F.cj.z)) + ja + sub;
     const float4v zero = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int64_t j0 = ja; j0 + 16 <= jb; j0 += 16) {
-      const int64_t jl = j0 + sub;
-      const float bj = comp < 3 ? jsrc[jl] : 0.0f;
+    const int32_t nch = __builtin_amdgcn_readfirstlane(static_cast<int32_t>((jb - ja) >> 4));
+    for (int32_t ch = 0; ch < nch; ++ch) {
+      const int64_t jl = ja + 16 * static_cast<int64_t>(ch) + sub;
+      const float bj = comp < 3 ? jp[16 * ch] : 0.0f;
       // each tile's product is requested one tile ahead, so its latency overlaps the binning
       float4v dn = __builtin_amdgcn_mfma_f32_16x16x4f32(at[0], bj, zero, 0, 0, 0);
 #pragma unroll
