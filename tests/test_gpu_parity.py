@@ -544,6 +544,28 @@ def test_duplicates_and_antipodes(gc, nbins, w):
     assert list(tot) == [700 * 700, 700 * 600, 600 * 600]
 
 
+@pytest.mark.parametrize("nbins,w,want", [
+    (720, 0.25, dict(core=2, i_per_lane=2, hist_columns=16, waves_per_group=16, l1_share=1, always_recheck=0)),
+    (3600, 0.05, dict(core=2, i_per_lane=2, hist_columns=1, waves_per_group=16, l1_share=2, lut_m=3167,
+                      always_recheck=1)),
+    (1440, 0.125, dict(core=2, i_per_lane=2, hist_columns=1, waves_per_group=16, l1_share=3, lut_m=1834)),
+    (1500, 0.001, dict(core=2, dot_precision=64, i_per_lane=4, lut_m=0)),
+])
+def test_launch_plan_choices(gc, nbins, w, want):
+    """The planner's choices for representative bins (each the fastest layout measured for its
+    case): the sixteen-column table at 720 bins with every read from LDS; for finer bins one
+    column in two workgroups of 16 waves per compute unit, the 3600-bin table shrunk to M = 3167
+    so that they fit, with an eighth (51 KB table) or a quarter (29 KB) of the reads through the
+    L1; the fp64 series core for the patch's 0.001 deg bins.  The results do not depend on these
+    choices (the tuning tests); this pins the choices themselves."""
+    p = gc.launch_plan(100000, 100000, nbins, w)
+    print(f"[gpu] launch plan {nbins} x {w}: {p}", flush=True)
+    for k, v in want.items():
+        assert p[k] == v, (k, p)
+    if p["hist_columns"] == 1 and p["i_per_lane"] == 2:
+        assert 2 * p["lds_bytes"] <= 160 * 1024 and p["blocks_per_cu"] % 2 == 0  # two workgroups per CU
+
+
 @pytest.mark.parametrize("nbins,w,tuning", [(3600, 0.05, dict(fast_core=1)), (3600, 0.05, dict(i_per_lane=4)),
                                             (3600, 0.05, dict(i_per_lane=2)), (3600, 0.05, dict(waves_per_group=8)),
                                             (3600, 0.05, dict(l1_share=2)), (3600, 0.05, dict(l1_share=3, i_per_lane=4)),
@@ -551,9 +573,10 @@ def test_duplicates_and_antipodes(gc, nbins, w):
                                             (3601, 0.0499972, dict(fast_core=1))])
 def test_fine_bin_table_tuning_invariance(gc, nbins, w, tuning):
     """Bins through the fine bin table (one-column histogram in workgroups of 16 waves, entries near
-    0 and 180 deg always rechecked) against the arccos core, other galaxies per lane (2, 4), other
-    workgroup sizes and L1 shares, frequent flushes and the fp64 dot: the same histograms, all
-    within the oracle's edge flow; 3601 x 0.0499972 deg puts the edges off the round angles."""
+    0 and 180 deg always rechecked) against the arccos core, other galaxies per lane (2, 4; K = 4
+    takes the table of M = ceil(4 / w), the default a smaller one), other workgroup sizes and L1
+    shares, frequent flushes and the fp64 dot: the same histograms, all within the oracle's edge
+    flow; 3601 x 0.0499972 deg puts the edges off the round angles."""
     print(f"[gpu] fine bin table nbins={nbins} w={w} tuning {tuning}", flush=True)
     D, R = catalogs.WORKLOADS["clustered100k_3600"].catalogs(n=5000)
     fams = oracle_fams(D, R, nbins, w)
