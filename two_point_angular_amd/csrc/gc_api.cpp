@@ -287,9 +287,10 @@ bool lut_choose(LutPlan &lp, int32_t nbins, double w_deg, const gc_tuning &tu, i
   return lut_layout(lp, nbins, 4, tu, lv, waves);
 }
 
-// The bin-table kernel's layout: sixteen histogram columns when two workgroups of 8 waves (12 at
-// K = 4, 16 at K = 2) fit in a compute unit's LDS beside their tables and queues; else one column
-// in one workgroup of 16 waves.  Every table read goes to LDS unless overridden (or unless
+// The bin-table kernel's layout at a given K: sixteen histogram columns when two workgroups of 8
+// waves (12 at K = 4, 16 at K = 2) fit in a compute unit's LDS beside their tables and queues;
+// else one column in workgroups of 16 waves (lut_choose sizes the table so that two of them fit
+// where it can).  Every table read goes to LDS unless overridden (or unless
 // lut_choose picks the one-column layout of two workgroups per CU): a share through the vector
 // L1 measured slower where the VALU is as busy as the LDS (720 bins: an eighth 6.40 against
 // 6.35 ms) and with one workgroup per CU (3600 bins: an eighth 9.46 against 8.76 ms).  Overrides
