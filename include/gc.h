@@ -136,10 +136,10 @@ typedef struct {
                                 never shares a bank; invalid where it does not fit in LDS) */
     int32_t waves_per_group; /* bin-table core: 0 auto, else 4..16 wavefronts per workgroup */
     int32_t l1_share;        /* bin-table core: 0 auto; share of table reads made through the
-                                vector L1 instead of LDS: 1 none, 2 an eighth, 3 a quarter (auto:
-                                none, except in the one-column layout of two workgroups per
-                                compute unit: a quarter for tables up to 40 KiB, else an
-                                eighth) */
+                                vector L1 instead of LDS: 1 none, 2 an eighth, 3 a quarter,
+                                4 three sixteenths (one-column histogram only).  Auto: none,
+                                except in the one-column layout of two workgroups per compute
+                                unit, where the share depends on the table's size */
     int32_t reserved_;       /* must be 0 */
 } gc_tuning;
 

@@ -97,7 +97,8 @@ typedef struct {
     int32_t i_per_lane;        /* 2, 4 or 8 */
     int32_t hist_columns;      /* 1 or 16 */
     int32_t waves_per_group;   /* wavefronts per workgroup */
-    int32_t l1_share;          /* bin table: 1 none, 2 an eighth, 3 a quarter; else 0 */
+    int32_t l1_share;          /* bin table: 1 none, 2 an eighth, 3 a quarter, 4 three
+                                  sixteenths; else 0 */
     int32_t shared_histogram;  /* 1: one histogram per workgroup */
     int32_t blocks_per_cu;     /* workgroups per compute unit the grid was sized for */
     int32_t workgroups;        /* grid size */

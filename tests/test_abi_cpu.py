@@ -108,7 +108,7 @@ def test_histogram_validation(lib):
                 T(0, 0, -1, 0, 0, 0, 0), T(0, 0, 0, 3, 0, 0, 0), T(0, 0, 0, -1, 0, 0, 0),
                 T(0, 0, 0, 0, 3, 0, 0), T(0, 0, 0, 0, 0, 4, 0), T(0, 0, 0, 0, 0, -1, 0), T(0, 0, 0, 0, 0, 0, -3),
                 T(0, 0, 0, 0, 0, 0, 0, 2), T(0, 0, 0, 0, 0, 0, 0, 8), T(0, 0, 0, 0, 0, 0, 0, 0, 3),
-                T(0, 0, 0, 0, 0, 0, 0, 0, 17), T(0, 0, 0, 0, 0, 0, 0, 0, 0, 4), T(0, 0, 0, 0, 0, 0, 0, 0, 0, -1),
+                T(0, 0, 0, 0, 0, 0, 0, 0, 17), T(0, 0, 0, 0, 0, 0, 0, 0, 0, 5), T(0, 0, 0, 0, 0, 0, 0, 0, 0, -1),
                 T(0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 1),
                 T(0, 0, 0, 0, 0, 0, 0, 4),
                 T(64, 0, 0, 0, 2, 0, 0)):                      # fp64 narrow core: 180 deg > 90 deg

@@ -303,7 +303,8 @@ def test_outputs_overwritten_and_self_pairs(gc):
                                     dict(hist_columns=16, i_per_lane=8), dict(i_per_lane=2),
                                     dict(i_per_lane=2, l1_share=1, flush_interval=9), dict(waves_per_group=16),
                                     dict(waves_per_group=5, l1_share=3), dict(l1_share=1),
-                                    dict(hist_columns=16, waves_per_group=4, flush_interval=2)])
+                                    dict(hist_columns=16, waves_per_group=4, flush_interval=2),
+                                    dict(l1_share=4)])
 def test_tuning_does_not_change_results(gc, tuning):
     print(f"[gpu] tuning {tuning}", flush=True)
     D, R = catalogs.WORKLOADS["clustered100k_720"].catalogs(n=6000)
@@ -546,7 +547,7 @@ def test_duplicates_and_antipodes(gc, nbins, w):
 
 @pytest.mark.parametrize("nbins,w,want", [
     (720, 0.25, dict(core=2, i_per_lane=2, hist_columns=16, waves_per_group=16, l1_share=1, always_recheck=0)),
-    (3600, 0.05, dict(core=2, i_per_lane=2, hist_columns=1, waves_per_group=16, l1_share=2, lut_m=3167,
+    (3600, 0.05, dict(core=2, i_per_lane=2, hist_columns=1, waves_per_group=16, l1_share=4, lut_m=3167,
                       always_recheck=1)),
     (1440, 0.125, dict(core=2, i_per_lane=2, hist_columns=1, waves_per_group=16, l1_share=3, lut_m=1834)),
     (1500, 0.001, dict(core=2, dot_precision=64, i_per_lane=4, lut_m=0)),
@@ -555,8 +556,8 @@ def test_launch_plan_choices(gc, nbins, w, want):
     """The planner's choices for representative bins (each the fastest layout measured for its
     case): the sixteen-column table at 720 bins with every read from LDS; for finer bins one
     column in two workgroups of 16 waves per compute unit, the 3600-bin table shrunk to M = 3167
-    so that they fit, with an eighth (51 KB table) or a quarter (29 KB) of the reads through the
-    L1; the fp64 series core for the patch's 0.001 deg bins.  The results do not depend on these
+    so that they fit, with three sixteenths (51 KB table) or a quarter (29 KB) of the reads
+    through the L1; the fp64 series core for the patch's 0.001 deg bins.  The results do not depend on these
     choices (the tuning tests); this pins the choices themselves."""
     p = gc.launch_plan(100000, 100000, nbins, w)
     print(f"[gpu] launch plan {nbins} x {w}: {p}", flush=True)
@@ -569,6 +570,7 @@ def test_launch_plan_choices(gc, nbins, w, want):
 @pytest.mark.parametrize("nbins,w,tuning", [(3600, 0.05, dict(fast_core=1)), (3600, 0.05, dict(i_per_lane=4)),
                                             (3600, 0.05, dict(i_per_lane=2)), (3600, 0.05, dict(waves_per_group=8)),
                                             (3600, 0.05, dict(l1_share=2)), (3600, 0.05, dict(l1_share=3, i_per_lane=4)),
+                                            (3600, 0.05, dict(l1_share=4)), (3600, 0.05, dict(l1_share=4, i_per_lane=4)),
                                             (3600, 0.05, dict(flush_interval=5)), (3600, 0.05, dict(dot_precision=64)),
                                             (3601, 0.0499972, dict(fast_core=1))])
 def test_fine_bin_table_tuning_invariance(gc, nbins, w, tuning):

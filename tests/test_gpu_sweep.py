@@ -181,7 +181,7 @@ def test_seeded_sweep_tunings_and_parts(gc):
                        span_kernel=int(rng.choice([0, 1, 2])), fast_core=int(rng.choice([0, 1, 2])),
                        flush_interval=int(rng.choice([0, 0, 1, 7, 100])),
                        hist_columns=int(rng.choice([0, 0, 1, 16])), waves_per_group=int(rng.choice([0, 0, 4, 8, 16])),
-                       l1_share=int(rng.choice([0, 1, 2, 3])))
+                       l1_share=int(rng.choice([0, 1, 2, 3, 4])))
         parts = int(rng.choice([1, 1, 1, 2, 3, 7, 40]))
         print(f"[gpu] sweep+tuning case {c}: nbins {nbins} w {w!r} n {len(D)},{len(R)} parts {parts} {tun}",
               flush=True)

@@ -268,10 +268,11 @@ bool lut_choose(LutPlan &lp, int32_t nbins, double w_deg, const gc_tuning &tu, i
         t2.waves_per_group = kMaxWavesPerWG;
         // With two workgroups per CU the LDS is the tighter resource, and a share of the table
         // reads goes through the vector L1: a quarter while the table stays mostly in its 32 KB,
-        // an eighth for larger ones.  Measured, none / an eighth / a quarter: 1440 x 0.125 deg
-        // (29 KB table) 7.87 / 7.50 / 7.14 ms; 1800 x 0.1 (37 KB) 7.89 / 7.53 / 7.35; 2400 x 0.075
-        // (49 KB) 7.97 / 7.60 / 7.92; 3600 x 0.05 (51 KB) 8.30 / 7.98 / 8.53.
-        if (t2.l1_share == 0) t2.l1_share = 8 * (2 * static_cast<size_t>(p2.m) + 1) <= 40 * 1024 ? 3 : 2;
+        // three sixteenths for larger ones.  Measured, an eighth / three sixteenths / a quarter:
+        // 1440 x 0.125 deg (29 KB table) 7.46 / 7.26 / 7.08 ms; 1800 x 0.1 (37 KB) 7.48 / 7.28 /
+        // 7.13; 2400 x 0.075 (49 KB) 7.57 / 7.37 / 7.32; 3600 x 0.05 (51 KB) 7.92 / 7.75 / 7.83
+        // (none: 8.30 at 3600 bins).
+        if (t2.l1_share == 0) t2.l1_share = 8 * (2 * static_cast<size_t>(p2.m) + 1) <= 40 * 1024 ? 3 : 4;
         LutVariant lv2;
         int w2 = 0;
         if (p2.ok && lut_layout(p2, nbins, 2, t2, &lv2, &w2)) {
@@ -309,6 +310,7 @@ bool lut_layout(const LutPlan &lp, int32_t nbins, int k, const gc_tuning &tu, Lu
   if (lds(cols, nw) > kLdsPerCU) return false;
   lv->cols = cols;
   lv->l1 = tu.l1_share ? tu.l1_share - 1 : 0;
+  if (cols == kHistCols && lv->l1 == 3) return false;  // three sixteenths: the one-column layout only
   *waves = nw;
   return true;
 }
@@ -475,7 +477,7 @@ gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, in
       tu.span_kernel < 0 || tu.span_kernel > 2 || tu.fast_core < 0 || tu.fast_core > 2 ||
       tu.flush_interval < 0 || (tu.hist_columns != 0 && tu.hist_columns != 1 && tu.hist_columns != kHistCols) ||
       (tu.waves_per_group != 0 && (tu.waves_per_group < kWavesPerWG || tu.waves_per_group > kMaxWavesPerWG)) ||
-      tu.l1_share < 0 || tu.l1_share > 3 || tu.reserved_ != 0)
+      tu.l1_share < 0 || tu.l1_share > 4 || tu.reserved_ != 0)
     return GC_ERR_INVALID_ARGUMENT;
 
   // Plan.  Bins narrower than 0.01 deg put most pairs where the fp32 dot product cannot

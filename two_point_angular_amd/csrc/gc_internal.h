@@ -134,7 +134,8 @@ struct PairArgs {
 };
 
 // The bin-table kernel's variants: histogram columns (1 or kHistCols) and the share of table
-// reads made through the vector L1 instead of LDS (0: none; 1: an eighth; 2: a quarter).
+// reads made through the vector L1 instead of LDS (0: none; 1: an eighth; 2: a quarter; 3: three
+// sixteenths, one column only).
 struct LutVariant {
   int cols = 1;
   int l1 = 2;

@@ -345,6 +345,7 @@ pairs_kernel(const PairArgs A) {
   constexpr int JB = D64 ? 4 : 8;     // j galaxies per scalar batch
   static_assert(COLS == 1 || (LUT && COLS == kHistCols), "multi-column histograms belong to the bin-table core");
   static_assert(L1S == 2 || LUT, "the L1 share is a bin-table core variant");
+  static_assert(L1S != 3 || COLS == 1, "three sixteenths through the L1: the one-column layout only");
   // queue entries pack (i - i0) and the fast-path row + 1 into 16 bits each
   static_assert(BI <= 0x10000 && kMaxBins + kWave + kLutAliasWords + 1 < 0x10000, "queue fields overflow");
   extern __shared__ uint32_t lds[];
@@ -581,11 +582,16 @@ pairs_kernel(const PairArgs A) {
   // Which of a lane's table reads go through the vector L1 (the rest read the LDS copy): a random
   // 64-lane LDS read costs ~7 CU cycles, the same read through the vector L1 ~37, and the LDS also
   // takes every pair's atomic, so a share of the reads may go to the L1.  Scalar-j steps: pairs
-  // k = 1, 5 (a quarter) or k = 1 of 8 (an eighth); matrix-core tiles: result r = 1 (a quarter),
-  // or r = 1 of odd tiles (an eighth).
-  auto l1_scalar = [](int k) constexpr { return L1S == 2 ? k % 4 == 1 : (L1S == 1 ? k % 8 == 1 : false); };
+  // k = 1, 5 (a quarter) or k = 1 of 8 (an eighth, and for three sixteenths); matrix-core tiles:
+  // result r = 1 (a quarter), r = 1 of odd tiles (an eighth), and with it r = 3 of tiles 1 and 5
+  // of every 8 (three sixteenths).
+  auto l1_scalar = [](int k) constexpr {
+    return L1S == 2 ? k % 4 == 1 : ((L1S == 1 || L1S == 3) ? k % 8 == 1 : false);
+  };
   auto l1_tile = [](int r, int t) constexpr {
-    return L1S == 2 ? r == 1 : (L1S == 1 ? r == 1 && (t & 1) : false);
+    return L1S == 2 ? r == 1
+                    : (L1S == 1 ? r == 1 && (t & 1)
+                                : (L1S == 3 ? (r == 1 && (t & 1)) || (r == 3 && (t & 3) == 1) : false));
   };
   // The histogram row address of a bin-table pair: (sign of e - x) << lut_sh plus the entry's row
   // address, plus this lane's column; an L1 entry holds the row's offset, the LDS copy its address.
@@ -1134,6 +1140,7 @@ template <int K> static const void *select_lut(LutVariant lv) {
     if (lv.l1 == 1) return pairs_fn<K, false, 2, kHistCols, 1>();
     return pairs_fn<K, false, 2, kHistCols, 0>();
   }
+  if (lv.l1 == 3) return pairs_fn<K, false, 2, 1, 3>();
   if (lv.l1 == 2) return pairs_fn<K, false, 2, 1, 2>();
   if (lv.l1 == 1) return pairs_fn<K, false, 2, 1, 1>();
   return pairs_fn<K, false, 2, 1, 0>();
