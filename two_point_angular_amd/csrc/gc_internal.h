@@ -25,7 +25,7 @@ constexpr int queue_words(int k, int core, bool d64) { return 2 * kWave * (drain
 constexpr int kMaxWorkgroups = 8192; // pair-kernel grid limit
 constexpr int kMaxBins = 8192;       // GC_MAX_BINS (include/gc.h; gc_api.cpp checks they agree)
 constexpr int kMaxBlocksPerCU = 8;
-constexpr int kOversubscribe = 3;      // workgroups launched per resident workgroup slot
+constexpr int kOversubscribe = 4;      // workgroups launched per resident workgroup slot
 constexpr int kMinStepsPerWave = 256;  // j-steps per wave below which the grid shrinks
 
 // ---- prepared catalog layout ---------------------------------------------------
