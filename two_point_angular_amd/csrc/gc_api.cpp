@@ -447,8 +447,9 @@ namespace {
 
 // The histogram call and its parts.  Part p of P takes, in each segment of every family, the
 // j-steps floor(T p / P) .. floor(T (p+1) / P) of the same decomposition; with accumulate the
-// merge adds to the outputs.  Every pair's bin is fixed by the pair alone (the lane always holds the lower
-// index of a self pair, and the recheck is exact), so the parts sum to the single call's result.
+// outputs are not zeroed first, so the pair kernel's flushes add to them.  Every pair's bin is
+// fixed by the pair alone (the lane always holds the lower index of a self pair, and the recheck
+// is exact), so the parts sum to the single call's result.
 // plan_out non-null: only plan (sizes and tuning are checked; the pointers may be null) and
 // describe the launch in *plan_out; nothing is enqueued.
 gc_status histogram_impl(const void *prep_d, int64_t n_d, const void *prep_r, int64_t n_r, int32_t nbins,
