@@ -135,6 +135,33 @@ def test_bins_narrower_than_the_parity_window(gc, nbins, w):
         assert rep.ok, f"{f}: {rep.message}"
 
 
+def test_seeded_sweep_mid_sizes(gc):
+    """Eight draws of 3k to 20k galaxies (R of 0 to 20k), where the grid holds from a part of one
+    round of workgroups to several, every family has full i-blocks and a ragged one, and the
+    workgroups' step shares and chunks cross block boundaries: the workloads' bin counts (180 to
+    7200 bins over 180 degrees, and widths of 0.01 to 0.5 deg that stop short of it), over
+    clustered, uniform and 2 x 2 degree catalogs.  Every family passes the edge-flow check within
+    the 1e-6 N_a N_b moved-pair budget."""
+    rng = np.random.default_rng(303)
+    for c in range(8):
+        n_d, n_r = int(rng.integers(3000, 20000)), int(rng.integers(0, 20000))
+        nbins = int(rng.choice([180, 360, 720, 1440, 1500, 3600, 7200]))
+        w = 180.0 / nbins if rng.random() < 0.7 else float(rng.uniform(0.01, 0.5))
+        kind = int(rng.integers(0, 3))
+        seed = int(rng.integers(1, 10**6))
+        if kind == 0:
+            D = catalogs.clustered(n_d, seed)
+        elif kind == 1:
+            D = catalogs.uniform_sphere(n_d, seed)
+        else:
+            D = catalogs.patch(n_d, seed)
+        R = catalogs.uniform_sphere(max(n_r, 1), int(rng.integers(1, 10**6))).subset(0, n_r)
+        print(f"[gpu] mid-size sweep case {c}: nbins {nbins} w {w!r} kind {kind} n {n_d},{n_r} "
+              f"plan {gc.launch_plan(n_d, n_r, nbins, w)}", flush=True)
+        for f, rep in run_case(gc, nbins, w, D, R):
+            assert rep.ok, f"case {c} (nbins {nbins}, w {w!r}, n {n_d},{n_r}) {f}: {rep.message}"
+
+
 def test_seeded_sweep_narrow_widths(gc):
     """20 random widths, log-uniform over 1e-7 .. 0.03 deg, and 1 .. 8192 bins, over catalogs half
     made of near-duplicates (offsets 1e-6 .. 1 arcmin around an eighth of the galaxies), R of 0 to
