@@ -237,16 +237,19 @@ def test_part_validation(lib):
 def test_checkpoint_files(tmp_path):
     from two_point_angular_amd import parts
     import numpy as np
-    meta = parts._meta(10, 12, 720, 0.25, 7, "k", None)
+    meta = parts._meta(10, 12, 720, 0.25, 7, "k", None, 2)
     path = str(tmp_path / "ck.npz")
     assert parts.load_checkpoint(path, meta) is None
     h = np.arange(3 * 720, dtype=np.uint64).reshape(3, 720) * np.uint64(1 << 40)
     parts.save_checkpoint(path, meta, 3, h)
     nxt, back = parts.load_checkpoint(path, meta)
     assert nxt == 3 and np.array_equal(back, h)
-    other = parts._meta(10, 12, 720, 0.25, 8, "k", None)
-    with pytest.raises(ValueError, match="another job"):
-        parts.load_checkpoint(path, other)
+    # another part count, another planned i-block height (the parts then cover other pairs), or
+    # another tuning field is another job
+    for other in (parts._meta(10, 12, 720, 0.25, 8, "k", None, 2), parts._meta(10, 12, 720, 0.25, 7, "k", None, 4),
+                  parts._meta(10, 12, 720, 0.25, 7, "k", gc.Tuning(hist_columns=1), 2)):
+        with pytest.raises(ValueError, match="another job"):
+            parts.load_checkpoint(path, other)
     assert sorted(os.listdir(tmp_path)) == ["ck.npz"]          # the temporary file was renamed
 
 

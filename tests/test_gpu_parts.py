@@ -95,6 +95,10 @@ def test_checkpointed_run_resumes(gc, tmp_path):
     assert nxt == 7 and np.array_equal(h.cpu().numpy(), ref)
     with pytest.raises(ValueError):
         parts.run_in_parts(pd, 4000, pr, 4000, 720, 0.25, 7, checkpoint=ck, key="other catalogs")
+    # a plan with another i-block height splits the job into other pairs per part: not resumed
+    assert gc.launch_plan(4000, 4000, 720, 0.25, gc.Tuning(i_per_lane=4))["i_per_lane"] == 4
+    with pytest.raises(ValueError):
+        parts.run_in_parts(pd, 4000, pr, 4000, 720, 0.25, 7, checkpoint=ck, key=key, tuning=gc.Tuning(i_per_lane=4))
 
 
 def test_million_catalogs_in_parts(gc):

@@ -23,15 +23,21 @@ import os
 
 import numpy as np
 
-from . import Tuning, histogram_part, workspace_bytes
+from . import Tuning, histogram_part, launch_plan, workspace_bytes
+
+_TUNING_FIELDS = ("dot_precision", "i_per_lane", "blocks_per_cu", "shared_histogram", "span_kernel", "fast_core",
+                  "flush_interval", "hist_columns", "waves_per_group", "l1_share")
 
 
-def _meta(n_d, n_r, nbins, w, parts, key, tuning):
-    t = None if tuning is None else [tuning.dot_precision, tuning.i_per_lane, tuning.blocks_per_cu,
-                                     tuning.shared_histogram, tuning.span_kernel, tuning.fast_core,
-                                     tuning.flush_interval]
+def _meta(n_d, n_r, nbins, w, parts, key, tuning, i_per_lane=0):
+    """The job a checkpoint belongs to.  i_per_lane is the launch plan's galaxies per lane: part p
+    of P covers the steps of an i-block of 64 of them per lane, so a part's pairs depend on it (a
+    resume under another plan, or another library build that plans differently, would mix two
+    decompositions); the tuning fields are kept whole."""
+    t = None if tuning is None else [int(getattr(tuning, f)) for f in _TUNING_FIELDS]
     return json.dumps({"n_d": int(n_d), "n_r": int(n_r), "nbins": int(nbins), "bin_width_deg": float(w),
-                       "parts": int(parts), "key": str(key), "tuning": t}, sort_keys=True)
+                       "parts": int(parts), "key": str(key), "tuning": t, "i_per_lane": int(i_per_lane)},
+                      sort_keys=True)
 
 
 def load_checkpoint(path: str, meta: str):
@@ -62,7 +68,8 @@ def run_in_parts(prep_d, n_d: int, prep_r, n_r: int, nbins: int, bin_width_deg: 
     has completed."""
     import torch
     dev = prep_d.device if prep_d is not None else prep_r.device
-    meta = _meta(n_d, n_r, nbins, bin_width_deg, parts, key, tuning)
+    k = launch_plan(n_d, n_r, nbins, bin_width_deg, tuning)["i_per_lane"]
+    meta = _meta(n_d, n_r, nbins, bin_width_deg, parts, key, tuning, k)
     hist = torch.zeros((3, nbins), dtype=torch.int64, device=dev)
     start = 0
     if checkpoint:
