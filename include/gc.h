@@ -165,7 +165,9 @@ gc_status gc_histogram_dd_dr_rr_tuned(const void *d_prepared_d, int64_t n_d,
  * d_dd, d_dr, d_rr (zero them before part 0).  Arguments are those of
  * gc_histogram_dd_dr_rr_tuned (tuning may be null), plus:
  *   part, parts : 1 <= parts <= GC_MAX_PARTS, 0 <= part < parts.  Every part of one
- *                 job must use the same catalogs, bins and tuning.
+ *                 job must use the same catalogs, bins and tuning, and the same build of
+ *                 this library: the work units are those of the launch plan (their size
+ *                 follows its galaxies per lane, gc_launch_plan's i_per_lane).
  * A part that holds no work for a family adds nothing to it.  Calls that add into the
  * same outputs must be ordered (the same stream, or synchronised).
  */
