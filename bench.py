@@ -341,7 +341,9 @@ def measure(gc, wl, args, tuning, steps, warmup):
                      "what": "the histogram call's HIP-event time: run 1 cold (first launch in the process), "
                              "median and minimum of runs 2-9 (warm-up steps included)"},
         "roofline": {"bound": "alu", "achieved": achieved, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / FP32_PEAK_TFLOPS, "traffic": measured_traffic(wl.name),
+                     "frac": achieved / FP32_PEAK_TFLOPS,
+                     # the profile's counters hold for the default plan of one call only
+                     "traffic": measured_traffic(wl.name) if tuning is None and args.parts == 1 else None,
                      "note": f"{FLOPS_PER_PAIR:.0f} algorithmic FP32 flops per evaluated pair; achieved over the "
                              "mean event time of the timed steps"},
         "cpu_baseline": None,
