@@ -76,7 +76,7 @@ def run_case(gc, nbins, w, D, R, budget=MOVED_BUDGET):
             for k, f in enumerate(oracle.FAMILIES)]
 
 
-@pytest.mark.parametrize("seed", [1, 2])
+@pytest.mark.parametrize("seed", [1, 2, 3, 4, 5, 6])
 def test_seeded_sweep(gc, seed):
     rng = np.random.default_rng(seed)
     for c in range(30):
@@ -199,7 +199,7 @@ def test_seeded_sweep_tunings_and_parts(gc):
     import torch
     rng = np.random.default_rng(21)
     accepted = 0
-    for c in range(30):
+    for c in range(90):
         regime, kind, nbins, w, D, R = draw_case(rng)
         tun = {}
         if rng.random() < 0.7:
@@ -235,7 +235,7 @@ def test_seeded_sweep_tunings_and_parts(gc):
         for k, f in enumerate(oracle.FAMILIES):
             rep = oracle.flow_check(h[k], res.family(f), want[f], moved_budget=MOVED_BUDGET)
             assert rep.ok, f"case {c} (nbins {nbins}, w {w!r}, parts {parts}, {tun}) {f}: {rep.message}"
-    assert accepted >= 20
+    assert accepted >= 60
 
 
 def test_seeded_core_sweep_on_exact_cosines(gc):
